@@ -1,0 +1,89 @@
+"""Seeded synthetic inputs for exact attention.
+
+This module only draws random numbers and names workload shapes; it holds none
+of attention's arithmetic.  Both the oracle checks and the HIP library receive
+the tensors it returns, so the two sides always see identical inputs.
+
+Recipe: a CPU ``torch.Generator`` seeded with ``seed`` draws float32 standard
+normals for q, k, v and dO, in that order; each is multiplied by
+``input_scale`` (0.5 for the long non-causal workload, an exact power of two)
+and then rounded to the compute dtype with round-to-nearest-even.
+
+Workloads (layout [B, H, T, D], contiguous):
+  C1  fp32, B=1, H=1,  T=128,   D=64,  causal, scale 1/8
+  C2  bf16, B=2, H=8,  T=512,   D=64,  causal, scale 1/8
+  C3  bf16, B=2, H=8,  T=4096,  D=64,  causal, scale 1/8 (the fp32 score tensor
+      of the unfused form would be 1 GiB: "L'attention fusionnée",
+      «Ce que l'attention écrit en mémoire»)
+  C4  bf16, B=1, H=16, T=16384, D=64,  non-causal, scale 1/8, inputs x0.5,
+      forward only (N = 16384 as in the cuTile page's memory example)
+  C5  bf16, B=1, Hq=32, Hkv=8, T=16384, D=128, causal, scale 1/sqrt(128)
+  C5-share  one kv group of C5 (B=1, Hq=4, Hkv=1), the part of C5 one GPU
+      would own if C5 were split by kv group.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: torch.dtype
+    B: int
+    Hq: int
+    Hkv: int
+    T: int
+    D: int
+    causal: bool
+    scale: float
+    seed: int
+    input_scale: float = 1.0
+    backward: bool = True
+
+    @property
+    def fwd_flop(self) -> float:
+        """Credited forward FLOP: 4*B*Hq*T^2*D, halved when causal."""
+        f = 4.0 * self.B * self.Hq * self.T * self.T * self.D
+        return f / 2 if self.causal else f
+
+    @property
+    def bwd_flop(self) -> float:
+        """Credited backward FLOP: 2.5x the forward."""
+        return 2.5 * self.fwd_flop if self.backward else 0.0
+
+
+WORKLOADS = {
+    "C1": Workload("C1", torch.float32, 1, 1, 1, 128, 64, True, 1 / 8, 1000),
+    "C2": Workload("C2", torch.bfloat16, 2, 8, 8, 512, 64, True, 1 / 8, 2000),
+    "C3": Workload("C3", torch.bfloat16, 2, 8, 8, 4096, 64, True, 1 / 8, 3000),
+    "C4": Workload("C4", torch.bfloat16, 1, 16, 16, 16384, 64, False, 1 / 8, 4000,
+                   input_scale=0.5, backward=False),
+    "C5": Workload("C5", torch.bfloat16, 1, 32, 8, 16384, 128, True, 1 / math.sqrt(128), 5000),
+    "C5-share": Workload("C5-share", torch.bfloat16, 1, 4, 1, 16384, 128, True,
+                         1 / math.sqrt(128), 5500),
+}
+
+
+def make_inputs(B: int, Hq: int, Hkv: int, T: int, D: int, dtype: torch.dtype, seed: int,
+                input_scale: float = 1.0, with_dout: bool = True) -> dict:
+    """Return CPU tensors q [B,Hq,T,D], k and v [B,Hkv,T,D] and (optionally)
+    dout [B,Hq,T,D], drawn as described in the module docstring."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    out = {}
+    for name, h in (("q", Hq), ("k", Hkv), ("v", Hkv), ("dout", Hq)):
+        if name == "dout" and not with_dout:
+            break
+        x = torch.randn((B, h, T, D), generator=g, dtype=torch.float32)
+        if input_scale != 1.0:
+            x = x * input_scale
+        out[name] = x.to(dtype).contiguous()
+    return out
+
+
+def workload_inputs(w: Workload) -> dict:
+    return make_inputs(w.B, w.Hq, w.Hkv, w.T, w.D, w.dtype, w.seed, w.input_scale, w.backward)

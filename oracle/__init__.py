@@ -81,38 +81,58 @@ class Oracle:
         lib = ctypes.CDLL(lib_path)
         i, d, l = ctypes.c_int, ctypes.c_double, ctypes.c_long
         dp, ip = _dp, _ip
-        lib.oracle_fwd.argtypes = [dp, dp, dp, dp, dp, i, i, i, i, i, d, i]
-        lib.oracle_bwd.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, i, i, i, i, i, d, i]
+        lib.oracle_fwd.argtypes = [dp, dp, dp, dp, dp, dp, i, i, i, i, i, d, i]
+        lib.oracle_bwd.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, i, i, i, i, i, d, i]
         lib.oracle_fwd_rows.argtypes = [dp, dp, dp, ip, l, dp, dp, i, i, i, i, i, d, i]
         lib.oracle_dq_rows.argtypes = [dp, dp, dp, dp, ip, l, dp, i, i, i, i, i, d, i]
         lib.oracle_dkdv_rows.argtypes = [dp, dp, dp, dp, ip, l, dp, dp, i, i, i, i, i, d, i]
         for f in (lib.oracle_fwd, lib.oracle_bwd, lib.oracle_fwd_rows, lib.oracle_dq_rows,
                   lib.oracle_dkdv_rows):
             f.restype = ctypes.c_int
+        lib.oracle_threads.argtypes = []
+        lib.oracle_threads.restype = ctypes.c_int
         self.lib = lib
 
-    def fwd(self, q, k, v, scale: float, causal: bool):
-        """Return (o [B,Hq,T,D], lse [B,Hq,T]) in float64."""
+    def threads(self) -> int:
+        """OpenMP threads the oracle's parallel loops use."""
+        return int(self.lib.oracle_threads())
+
+    def fwd(self, q, k, v, scale: float, causal: bool, return_mag: bool = False):
+        """Return (o [B,Hq,T,D], lse [B,Hq,T]) in float64; with return_mag also
+        o_mag, the per-element sum of absolute terms sum_j |P_ij v_jd|."""
         q, k, v = _f64(q), _f64(k), _f64(v)
         B, Hq, Hkv, T, D = _shapes(q, k, v)
         o = np.zeros((B, Hq, T, D))
         lse = np.zeros((B, Hq, T))
-        _check(self.lib.oracle_fwd(_p(q), _p(k), _p(v), _p(o), _p(lse), B, Hq, Hkv, T, D,
+        om = np.zeros((B, Hq, T, D)) if return_mag else None
+        _check(self.lib.oracle_fwd(_p(q), _p(k), _p(v), _p(o), _p(lse),
+                                   _p(om) if return_mag else None, B, Hq, Hkv, T, D,
                                    float(scale), int(bool(causal))))
-        return o, lse
+        return (o, lse, om) if return_mag else (o, lse)
 
-    def bwd(self, q, k, v, dout, scale: float, causal: bool, return_jac: bool = False):
+    def bwd(self, q, k, v, dout, scale: float, causal: bool, return_jac: bool = False,
+            return_mag: bool = False):
         """Return (dq, dk, dv) of the loss sum(O * dout); with return_jac also
-        the per-row Jacobian term c_i = sum_j P_ij dP_ij ([B,Hq,T])."""
+        the per-row Jacobian term c_i = sum_j P_ij dP_ij ([B,Hq,T]); with
+        return_mag also (dq_mag, dk_mag, dv_mag), the per-element sums of the
+        absolute values of the terms."""
         q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
         B, Hq, Hkv, T, D = _shapes(q, k, v, dout)
         dq = np.zeros_like(q)
         dk = np.zeros_like(k)
         dv = np.zeros_like(v)
         jac = np.zeros((B, Hq, T))
+        mags = (np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)) if return_mag else None
+        mp = [_p(m) for m in mags] if return_mag else [None, None, None]
         _check(self.lib.oracle_bwd(_p(q), _p(k), _p(v), _p(dout), _p(dq), _p(dk), _p(dv),
-                                   _p(jac), B, Hq, Hkv, T, D, float(scale), int(bool(causal))))
-        return (dq, dk, dv, jac) if return_jac else (dq, dk, dv)
+                                   _p(jac), *mp, B, Hq, Hkv, T, D, float(scale),
+                                   int(bool(causal))))
+        out = (dq, dk, dv)
+        if return_jac:
+            out = out + (jac,)
+        if return_mag:
+            out = out + (mags,)
+        return out
 
     def fwd_rows(self, q, k, v, idx, scale: float, causal: bool):
         """Output rows for query rows idx = [(b, h, i), ...]: (o [n,D], lse [n])."""
@@ -164,12 +184,13 @@ def default() -> Oracle:
     return _default
 
 
-def fwd(q, k, v, scale: float, causal: bool):
-    return default().fwd(q, k, v, scale, causal)
+def fwd(q, k, v, scale: float, causal: bool, return_mag: bool = False):
+    return default().fwd(q, k, v, scale, causal, return_mag)
 
 
-def bwd(q, k, v, dout, scale: float, causal: bool, return_jac: bool = False):
-    return default().bwd(q, k, v, dout, scale, causal, return_jac)
+def bwd(q, k, v, dout, scale: float, causal: bool, return_jac: bool = False,
+        return_mag: bool = False):
+    return default().bwd(q, k, v, dout, scale, causal, return_jac, return_mag)
 
 
 def fwd_rows(q, k, v, idx, scale: float, causal: bool):

@@ -128,8 +128,8 @@ static double lse_of(double m, double l)
 
 /* Forward for one (b, h, i): writes o_i (D values) and lse_i. */
 static void fwd_one_row(const shape_t* s, const double* q, const double* k, const double* v,
-                        int b, int h, int i, double* o_i, double* lse_i, double* s_buf,
-                        double* p)
+                        int b, int h, int i, double* o_i, double* lse_i, double* om_i,
+                        double* s_buf, double* p)
 {
     const int G = s->Hq / s->Hkv, hk = h / G, D = s->D, T = s->T;
     const double* k_head = kvrow(k, s, b, hk, 0);
@@ -138,10 +138,14 @@ static void fwd_one_row(const shape_t* s, const double* q, const double* k, cons
     softmax_row(s, qrow(q, s, b, h, i), k_head, i, s_buf, p, &m, &l);
     /* step 3: o_i = sum_j P_ij v_j */
     for (int d = 0; d < D; ++d) o_i[d] = 0.0;
+    if (om_i)
+        for (int d = 0; d < D; ++d) om_i[d] = 0.0;
     for (int j = 0; j < T; ++j) {
         if (p[j] == 0.0) continue;
         const double* vj = v_head + (size_t)j * D;
         for (int d = 0; d < D; ++d) o_i[d] += p[j] * vj[d];
+        if (om_i)
+            for (int d = 0; d < D; ++d) om_i[d] += fabs(p[j] * vj[d]);
     }
     *lse_i = lse_of(m, l);
 }
@@ -187,9 +191,17 @@ static double* scratch_of(double* base, int nbuf, int T, int which)
 /* Public C ABI                                                               */
 /* ------------------------------------------------------------------------- */
 
-/* Full forward: o [B,Hq,T,D], lse [B,Hq,T]. */
-int oracle_fwd(const double* q, const double* k, const double* v, double* o, double* lse, int B,
-               int Hq, int Hkv, int T, int D, double scale, int causal)
+/* Number of OpenMP threads a parallel region of the oracle uses. */
+int oracle_threads(void) { return omp_get_max_threads(); }
+
+/*
+ * Full forward: o [B,Hq,T,D], lse [B,Hq,T].  o_mag (nullable) [B,Hq,T,D]
+ * receives, per output element, the sum of the absolute values of its terms,
+ * sum_j |P_ij v_jd|: the scale of the rounding error a finite-precision
+ * evaluation of that sum can make.
+ */
+int oracle_fwd(const double* q, const double* k, const double* v, double* o, double* lse,
+               double* o_mag, int B, int Hq, int Hkv, int T, int D, double scale, int causal)
 {
     shape_t s = {B, Hq, Hkv, T, D, scale, causal};
     if (check_shape(&s) != ORACLE_OK) return ORACLE_ERR_ARG;
@@ -200,7 +212,8 @@ int oracle_fwd(const double* q, const double* k, const double* v, double* o, dou
 #pragma omp parallel for schedule(dynamic, 16)
     for (long r = 0; r < rows; ++r) {
         const int i = (int)(r % T), h = (int)((r / T) % Hq), b = (int)(r / ((long)T * Hq));
-        fwd_one_row(&s, q, k, v, b, h, i, o + (size_t)r * D, lse + r, scratch_of(scr, 2, T, 0),
+        fwd_one_row(&s, q, k, v, b, h, i, o + (size_t)r * D, lse + r,
+                    o_mag ? o_mag + (size_t)r * D : NULL, scratch_of(scr, 2, T, 0),
                     scratch_of(scr, 2, T, 1));
     }
     free(scr);
@@ -209,7 +222,9 @@ int oracle_fwd(const double* q, const double* k, const double* v, double* o, dou
 
 /*
  * Full backward: dq [B,Hq,T,D], dk/dv [B,Hkv,T,D]; jac (nullable) [B,Hq,T]
- * receives c_i.
+ * receives c_i.  dq_mag, dk_mag, dv_mag (nullable, shaped like dq, dk, dv)
+ * receive per element the sum of the absolute values of its terms
+ * (|scale dS_ij k_jd|, |scale dS_ij q_id|, |P_ij dO_id|).
  *
  * Pass 1 (one task per query row) computes dq_i and keeps the row statistics
  * m_i, l_i, c_i.  Pass 2 (one task per key row j of a kv head) sums the
@@ -217,8 +232,8 @@ int oracle_fwd(const double* q, const double* k, const double* v, double* o, dou
  * ascending (h, i) order, rebuilding P_ij = exp(s_ij - m_i) / l_i and dP_ij.
  */
 int oracle_bwd(const double* q, const double* k, const double* v, const double* dout, double* dq,
-               double* dk, double* dv, double* jac, int B, int Hq, int Hkv, int T, int D,
-               double scale, int causal)
+               double* dk, double* dv, double* jac, double* dq_mag, double* dk_mag,
+               double* dv_mag, int B, int Hq, int Hkv, int T, int D, double scale, int causal)
 {
     shape_t s = {B, Hq, Hkv, T, D, scale, causal};
     if (check_shape(&s) != ORACLE_OK) return ORACLE_ERR_ARG;
@@ -251,14 +266,21 @@ int oracle_bwd(const double* q, const double* k, const double* v, const double* 
         lst[r] = l;
         cst[r] = c;
         double* dq_i = dq + (size_t)r * D;
+        double* dqm_i = dq_mag ? dq_mag + (size_t)r * D : NULL;
         for (int d = 0; d < D; ++d) dq_i[d] = 0.0;
+        if (dqm_i)
+            for (int d = 0; d < D; ++d) dqm_i[d] = 0.0;
         for (int j = 0; j < T; ++j) {
             if (!visible(&s, i, j)) continue;
             const double ds = p[j] * (dp[j] - c);
             const double* kj = kvrow(k, &s, b, hk, j);
             for (int d = 0; d < D; ++d) dq_i[d] += ds * kj[d];
+            if (dqm_i)
+                for (int d = 0; d < D; ++d) dqm_i[d] += fabs(ds * kj[d]);
         }
         for (int d = 0; d < D; ++d) dq_i[d] *= scale;
+        if (dqm_i)
+            for (int d = 0; d < D; ++d) dqm_i[d] *= fabs(scale);
     }
 
     /* pass 2: per key row */
@@ -269,7 +291,13 @@ int oracle_bwd(const double* q, const double* k, const double* v, const double* 
         const double* vj = kvrow(v, &s, b, hk, j);
         double* dk_j = dk + (size_t)r * D;
         double* dv_j = dv + (size_t)r * D;
+        double* dkm_j = dk_mag ? dk_mag + (size_t)r * D : NULL;
+        double* dvm_j = dv_mag ? dv_mag + (size_t)r * D : NULL;
         for (int d = 0; d < D; ++d) dk_j[d] = dv_j[d] = 0.0;
+        if (dkm_j)
+            for (int d = 0; d < D; ++d) dkm_j[d] = 0.0;
+        if (dvm_j)
+            for (int d = 0; d < D; ++d) dvm_j[d] = 0.0;
         for (int g = 0; g < G; ++g) {
             const int h = hk * G + g;
             for (int i = 0; i < T; ++i) {
@@ -286,9 +314,15 @@ int oracle_bwd(const double* q, const double* k, const double* v, const double* 
                     dk_j[d] += ds * q_i[d];
                     dv_j[d] += pij * do_i[d];
                 }
+                if (dkm_j)
+                    for (int d = 0; d < D; ++d) dkm_j[d] += fabs(ds * q_i[d]);
+                if (dvm_j)
+                    for (int d = 0; d < D; ++d) dvm_j[d] += fabs(pij * do_i[d]);
             }
         }
         for (int d = 0; d < D; ++d) dk_j[d] *= scale;
+        if (dkm_j)
+            for (int d = 0; d < D; ++d) dkm_j[d] *= fabs(scale);
     }
     if (jac) memcpy(jac, cst, sizeof(double) * (size_t)qrows);
 
@@ -325,7 +359,7 @@ int oracle_fwd_rows(const double* q, const double* k, const double* v, const int
 #pragma omp parallel for schedule(dynamic, 1)
     for (long r = 0; r < n; ++r)
         fwd_one_row(&s, q, k, v, (int)idx[3 * r], (int)idx[3 * r + 1], (int)idx[3 * r + 2],
-                    o_rows + (size_t)r * D, lse_rows + r, scratch_of(scr, 2, T, 0),
+                    o_rows + (size_t)r * D, lse_rows + r, NULL, scratch_of(scr, 2, T, 0),
                     scratch_of(scr, 2, T, 1));
     free(scr);
     return ORACLE_OK;

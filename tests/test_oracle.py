@@ -364,3 +364,45 @@ def test_bad_shapes_are_rejected():
         oracle.fwd(q, k, k, 1.0, True)
     with pytest.raises(RuntimeError):
         oracle.fwd_rows(np.zeros((1, 2, 4, 2)), k, k, [(0, 0, 4)], 1.0, True)
+
+
+def test_term_magnitudes():
+    """The oracle's per-element sums of absolute terms: at least |value|,
+    equal to it when every term has one sign, and equal to a brute-force
+    numpy evaluation of sum |terms| on a tiny case."""
+    B, Hq, Hkv, T, D, scale = 1, 2, 1, 9, 3, 0.7
+    q, k, v, do = rnd((B, Hq, T, D), 40), rnd((B, Hkv, T, D), 41), rnd((B, Hkv, T, D), 42), rnd((B, Hq, T, D), 43)
+    for causal in (True, False):
+        o, _, om = oracle.fwd(q, k, v, scale, causal, return_mag=True)
+        dq, dk, dv, (mq, mk, mv) = oracle.bwd(q, k, v, do, scale, causal, return_mag=True)
+        for val, mag in ((o, om), (dq, mq), (dk, mk), (dv, mv)):
+            assert np.all(mag >= np.abs(val) - 1e-14)
+        o2, _, om2 = oracle.fwd(q, k, np.abs(v), scale, causal, return_mag=True)
+        np.testing.assert_allclose(om2, o2, rtol=1e-14)
+        _, _, dv2, (_, _, mv2) = oracle.bwd(q, k, v, np.abs(do), scale, causal, return_mag=True)
+        np.testing.assert_allclose(mv2, dv2, rtol=1e-14)
+        # brute force with full matrices, one query head at a time
+        mask = np.tril(np.ones((T, T), bool)) if causal else np.ones((T, T), bool)
+        mk_bf = np.zeros_like(mk)
+        for h in range(Hq):
+            s = np.where(mask, scale * q[0, h] @ k[0, 0].T, -np.inf)
+            p = np.exp(s - s.max(1, keepdims=True))
+            p /= p.sum(1, keepdims=True)
+            dp = do[0, h] @ v[0, 0].T
+            ds = p * (dp - (p * dp).sum(1, keepdims=True))
+            np.testing.assert_allclose(mq[0, h], scale * np.abs(ds) @ np.abs(k[0, 0]), rtol=1e-12)
+            np.testing.assert_allclose(om[0, h], p @ np.abs(v[0, 0]), rtol=1e-12)
+            mk_bf[0, 0] += scale * np.abs(ds).T @ np.abs(q[0, h])
+        np.testing.assert_allclose(mk, mk_bf, rtol=1e-12)
+
+
+def test_kdk_equals_dqq():
+    """K^T dK = dQ^T Q per kv group (both are scale * sum_ij dS_ij k_j q_i^T);
+    the full-size GPU checks rely on this identity."""
+    B, Hq, Hkv, T, D = 1, 4, 2, 50, 8
+    q, k, v, do = rnd((B, Hq, T, D), 44), rnd((B, Hkv, T, D), 45), rnd((B, Hkv, T, D), 46), rnd((B, Hq, T, D), 47)
+    for causal in (True, False):
+        dq, dk, _ = oracle.bwd(q, k, v, do, 0.3, causal)
+        lhs = np.einsum("bhtd,bhte->bhde", k, dk)
+        rhs = np.einsum("bhgtd,bhgte->bhde", dq.reshape(B, Hkv, 2, T, D), q.reshape(B, Hkv, 2, T, D))
+        np.testing.assert_allclose(lhs, rhs, atol=1e-12)

@@ -1,0 +1,270 @@
+"""Benchmark: causal attention forward + backward on one MI355X.
+
+One step = the whole hot path once: fa_fwd, then the three stages of fa_bwd
+(Delta preprocess, dK/dV, dQ), on seeded synthetic inputs already resident in
+HBM.  W untimed warm-up steps, then K timed steps bracketed by device
+synchronisation; HIP events recorded on the launch stream around every kernel
+give per-kernel averages over the timed region.
+
+Throughput is credited FLOP / time with forward FLOP = 4*B*Hq*T^2*D (halved
+when causal) and backward = 2.5x forward ("FlashAttention: l'attenzione che non
+spreca memoria", «L'idea: lavorare a tessere»: 4N^2d forward, 10N^2d backward
+with recomputation).
+
+The roofline entry is for the slowest kernel, against the bf16 dense MFMA
+peak; its "achieved" counts the GEMM FLOP that kernel's own math needs (see
+KERNEL_GEMMS).  The CPU baseline times the fp64 oracle on a bounded sample of
+the same workload (whole kv groups, or a causal prefix of one head).
+
+Prints one JSON line.  Usage: python bench.py [--steps K] [--warmup W]
+[--workload C5] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_FP32_TFLOPS = 157.3    # MI355X dense fp32 MFMA, published
+METRIC = "causal attention fwd+bwd TFLOP/s on 1 MI355X; % of bf16 MFMA peak"
+
+# GEMMs each kernel performs, in units of one T x T x D product over the
+# visible (causal: lower-triangular) score entries: 2 FLOP per multiply-add.
+#   fwd : S = Q K^T, O = P V                      -> 2
+#   dkdv: S, dP = dO V^T, dV = P^T dO, dK = dS^T Q -> 4
+#   dq  : S, dP, dQ = dS K                        -> 3
+KERNEL_GEMMS = {"fwd": 2, "dkdv": 4, "dq": 3}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="C5")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="target duration of the oracle sample")
+    return p.parse_args()
+
+
+def gemm_flop(w, n_gemm):
+    """FLOP of n_gemm T x T x D products over the visible score entries."""
+    pairs = w.B * w.Hq * w.T * w.T * (0.5 if w.causal else 1.0)
+    return 2.0 * n_gemm * pairs * w.D
+
+
+def source_hash(kernel_file: str) -> str:
+    h = hashlib.sha256()
+    for f in ("fa_device.hpp", kernel_file):
+        with open(os.path.join(ROOT, "exact_attention_30_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel: str, kernel_file: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current source of that kernel; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = data.get(f"{kernel}:{workload}")
+    if not e or e.get("source_hash") != source_hash(kernel_file):
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, x, target_s: float):
+    """Time the oracle's fwd + bwd on a bounded sample of the workload, sized
+    to take about target_s seconds: whole kv groups (all their query heads,
+    every position) when one head is cheap enough, else a causal prefix of
+    query head 0 and its kv head."""
+    import oracle
+
+    orc = oracle.default()
+    G = w.Hq // w.Hkv
+
+    def run(ngroups, tp):
+        sl = (slice(0, 1), slice(0, ngroups * G), slice(0, tp))
+        kl = (slice(0, 1), slice(0, ngroups), slice(0, tp))
+        q, do = x["q"][sl].double().numpy(), x["dout"][sl].double().numpy()
+        k, v = x["k"][kl].double().numpy(), x["v"][kl].double().numpy()
+        t0 = time.perf_counter()
+        orc.fwd(q, k, v, w.scale, w.causal)
+        orc.bwd(q, k, v, do, w.scale, w.causal)
+        return time.perf_counter() - t0
+
+    # calibrate on one query head (one kv head, G = 1 slice) and a short prefix
+    def run_head(tp):
+        q, do = x["q"][:1, :1, :tp].double().numpy(), x["dout"][:1, :1, :tp].double().numpy()
+        k, v = x["k"][:1, :1, :tp].double().numpy(), x["v"][:1, :1, :tp].double().numpy()
+        t0 = time.perf_counter()
+        orc.fwd(q, k, v, w.scale, w.causal)
+        orc.bwd(q, k, v, do, w.scale, w.causal)
+        return time.perf_counter() - t0
+
+    cal = min(2048, w.T)
+    t_cal = run_head(cal)
+    t_head = t_cal * (w.T / cal) ** 2  # work grows as T^2
+    if t_head * G <= target_s:
+        ngroups = max(1, min(w.B * w.Hkv, int(target_s / (t_head * G))))
+        ngroups = min(ngroups, w.Hkv)
+        tp, nheads = w.T, ngroups * G
+        elapsed = run(ngroups, tp)
+        what = (f"all {tp} positions of query heads 0-{nheads - 1} and kv heads 0-{ngroups - 1} "
+                f"of {w.name}")
+    else:
+        tp = int(cal * math.sqrt(max(target_s, 0.1) / max(t_cal, 1e-3)))
+        tp = max(cal, min(w.T, tp // 128 * 128))
+        nheads = 1
+        elapsed = run_head(tp)
+        what = f"the first {tp} positions of query head 0 and its kv head of {w.name}"
+    credited = 3.5 * 4.0 * nheads * tp * tp * w.D * (0.5 if w.causal else 1.0)  # fwd + 2.5x fwd
+    return {
+        "value": credited / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": orc.threads(),
+        "kind": "oracle",
+        "sample": f"fp64 oracle fwd+bwd on {what} ({elapsed:.1f} s)",
+        "seconds": round(elapsed, 2),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the multi-GPU sharding is described in DESIGN.md but not built.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_attention_30_amd as fa
+    from workloads import WORKLOADS, workload_inputs
+
+    w = WORKLOADS[args.workload]
+    if not w.backward:
+        raise SystemExit(f"{w.name} is forward-only; the benchmark step needs a backward")
+    print(f"[bench] workload {w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} T={w.T} D={w.D} "
+          f"causal={w.causal} {w.dtype}", file=sys.stderr, flush=True)
+    x = workload_inputs(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d = {k: v.to(dev) for k, v in x.items()}
+    q, k, v, do = d["q"], d["k"], d["v"], d["dout"]
+    o = torch.empty_like(q)
+    lse = torch.empty(w.B, w.Hq, w.T, dtype=torch.float32, device=dev)
+    delta = torch.empty(w.B, w.Hq, w.T, dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        fa.fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse)
+        if ev:
+            ev[1].record()
+        fa.bwd_preprocess(o, do, delta)
+        if ev:
+            ev[2].record()
+        fa.bwd_dkdv(q, k, v, do, lse, delta, scale=w.scale, causal=w.causal, dk=dk, dv=dv)
+        if ev:
+            ev[3].record()
+        fa.bwd_dq(q, k, v, do, lse, delta, scale=w.scale, causal=w.causal, dq=dq)
+        if ev:
+            ev[4].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warm-up done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    print(f"[bench] timed {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
+
+    names = ["fwd", "pre", "dkdv", "dq"]
+    per = {n: 0.0 for n in names}
+    for ev in events:
+        for i, n in enumerate(names):
+            per[n] += ev[i].elapsed_time(ev[i + 1])
+    per = {n: t / args.steps for n, t in per.items()}
+    gpu_span = events[0][0].elapsed_time(events[-1][4]) / args.steps
+    ms_per_step = max(wall * 1e3 / args.steps, gpu_span)
+
+    fwd_flop, bwd_flop = w.fwd_flop, w.bwd_flop
+    value = (fwd_flop + bwd_flop) / (ms_per_step * 1e-3) / 1e12
+    fwd_tflops = fwd_flop / (per["fwd"] * 1e-3) / 1e12
+    bwd_ms = per["pre"] + per["dkdv"] + per["dq"]
+    bwd_tflops = bwd_flop / (bwd_ms * 1e-3) / 1e12
+    pre_bytes = 2 * w.B * w.Hq * w.T * w.D * q.element_size() + 4 * w.B * w.Hq * w.T
+
+    dom = max(("fwd", "dkdv", "dq"), key=lambda n: per[n])
+    kfile = {"fwd": "fa_fwd.hip", "dkdv": "fa_bwd.hip", "dq": "fa_bwd.hip"}[dom]
+    achieved = gemm_flop(w, KERNEL_GEMMS[dom]) / (per[dom] * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == torch.bfloat16 else PEAK_FP32_TFLOPS
+    roofline = {
+        "kernel": {"fwd": "fwd_kernel", "dkdv": "bwd_dkdv_kernel", "dq": "bwd_dq_kernel"}[dom],
+        "bound": "mfma",
+        "achieved": round(achieved, 2),
+        "peak": peak,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / peak, 4),
+        "traffic": traffic_for(dom, kfile, w.name),
+        "avg_launch_ms": round(per[dom], 4),
+        "algorithmic_flop_per_launch": gemm_flop(w, KERNEL_GEMMS[dom]),
+    }
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == torch.bfloat16 else "fp32",
+        "data": "synthetic (seeded N(0,1) inputs of the workload's shape)",
+        "config": {
+            "workload": f"{w.name}: causal GQA attention fwd+bwd, B={w.B} Hq={w.Hq} Hkv={w.Hkv} "
+                        f"T={w.T} D={w.D}, scale={w.scale:.6g}",
+            "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "T": w.T, "D": w.D, "causal": w.causal,
+            "parallelism": "single GPU",
+        },
+        "pct_of_peak": round(100 * value / peak, 2),
+        "breakdown": {
+            "fwd_ms": round(per["fwd"], 4), "pre_ms": round(per["pre"], 4),
+            "dkdv_ms": round(per["dkdv"], 4), "dq_ms": round(per["dq"], 4),
+            "fwd_tflops": round(fwd_tflops, 2), "fwd_pct_peak": round(100 * fwd_tflops / peak, 2),
+            "bwd_tflops": round(bwd_tflops, 2), "bwd_pct_peak": round(100 * bwd_tflops / peak, 2),
+            "pre_gbps": round(pre_bytes / (per["pre"] * 1e-3) / 1e9, 1),
+        },
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on a bounded sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,186 @@
+// C ABI of the library: argument checks on the host, then kernel launches on
+// the caller's stream.  No device memory is allocated here and no host
+// synchronisation is done.  The contract is stated in include/fa.h.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/fa.h"
+#include "fa_kernels.hpp"
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Shape and option checks shared by every entry point; `D`/`dt` may be
+// ignored by passing D = 64, dt = FA_BF16.
+fa_status check_common(int B, int Hq, int Hkv, int T, int D, fa_dtype dt)
+{
+    if (B < 0 || T < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return FA_ERR_SHAPE;
+    // every tensor index must fit the 64-bit offsets and every grid the
+    // 32-bit workgroup count: B*Hq*ceil(T/32) workgroups at most
+    const long long rows = (long long)B * Hq * (((long long)T + 31) / 32);
+    if (rows > 0x7fffffffLL) return FA_ERR_SHAPE;
+    if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+    if (dt != FA_BF16 && dt != FA_FP32) return FA_ERR_UNSUPPORTED;
+    return FA_OK;
+}
+
+fa_status check_scale(float scale)
+{
+    return (isfinite(scale) && scale > 0.f) ? FA_OK : FA_ERR_UNSUPPORTED;
+}
+
+fa_status from_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+int dtype_code(fa_dtype dt) { return dt == FA_BF16 ? 0 : 1; }
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_version(void) { return "0.1.0"; }
+
+const char* fa_status_string(fa_status s)
+{
+    switch (s) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "null pointer";
+    case FA_ERR_SHAPE: return "invalid shape";
+    case FA_ERR_UNSUPPORTED: return "unsupported head dimension, dtype or scale";
+    case FA_ERR_ALIGN: return "misaligned pointer";
+    case FA_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                 int Hkv, int T, int D, float scale, int causal, fa_dtype dt, void* stream)
+{
+    fa_status st = check_common(B, Hq, Hkv, T, D, dt);
+    if (st != FA_OK) return st;
+    if ((st = check_scale(scale)) != FA_OK) return st;
+    if ((long long)B * T == 0) return FA_OK;
+    if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+        return FA_ERR_ALIGN;
+    fa::FwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.T = T;
+    a.c = scale * kLog2e;
+    a.scale = scale;
+    return from_hip(fa::launch_fwd(a, D, dtype_code(dt), causal != 0, static_cast<hipStream_t>(stream)));
+}
+
+size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int T, int D, fa_dtype dt)
+{
+    if (check_common(B, Hq, Hkv, T, D, dt) != FA_OK) return 0;
+    const size_t bytes = (size_t)B * (size_t)Hq * (size_t)T * sizeof(float);
+    return (bytes + 255) / 256 * 256;
+}
+
+fa_status fa_bwd_preprocess(const void* o, const void* dout, float* delta, int B, int Hq, int T,
+                            int D, fa_dtype dt, void* stream)
+{
+    fa_status st = check_common(B, Hq, 1, T, D, dt);
+    if (st != FA_OK) return st;
+    if ((long long)B * T == 0) return FA_OK;
+    if (!o || !dout || !delta) return FA_ERR_NULL;
+    if (!aligned(o, 16) || !aligned(dout, 16) || !aligned(delta, 4)) return FA_ERR_ALIGN;
+    fa::PreArgs a;
+    a.o = o;
+    a.dout = dout;
+    a.delta = delta;
+    a.rows = (long)B * Hq * T;
+    return from_hip(fa::launch_bwd_pre(a, D, dtype_code(dt), static_cast<hipStream_t>(stream)));
+}
+
+static fa_status bwd_args(const void* q, const void* k, const void* v, const void* dout,
+                          const float* lse, const float* delta, int B, int Hq, int Hkv, int T,
+                          int D, float scale, fa_dtype dt, fa::BwdArgs& a, bool& empty)
+{
+    fa_status st = check_common(B, Hq, Hkv, T, D, dt);
+    if (st != FA_OK) return st;
+    if ((st = check_scale(scale)) != FA_OK) return st;
+    empty = (long long)B * T == 0;
+    if (empty) return FA_OK;
+    if (!q || !k || !v || !dout || !lse || !delta) return FA_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) ||
+        !aligned(lse, 4) || !aligned(delta, 4))
+        return FA_ERR_ALIGN;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.dout = dout;
+    a.lse = lse;
+    a.delta = delta;
+    a.dq = a.dk = a.dv = nullptr;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.T = T;
+    a.c = scale * kLog2e;
+    a.scale = scale;
+    return FA_OK;
+}
+
+fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
+                      const float* lse, const float* delta, void* dk, void* dv, int B, int Hq,
+                      int Hkv, int T, int D, float scale, int causal, fa_dtype dt, void* stream)
+{
+    fa::BwdArgs a;
+    bool empty = false;
+    fa_status st = bwd_args(q, k, v, dout, lse, delta, B, Hq, Hkv, T, D, scale, dt, a, empty);
+    if (st != FA_OK || empty) return st;
+    if (!dk || !dv) return FA_ERR_NULL;
+    if (!aligned(dk, 16) || !aligned(dv, 16)) return FA_ERR_ALIGN;
+    a.dk = dk;
+    a.dv = dv;
+    return from_hip(fa::launch_bwd_dkdv(a, D, dtype_code(dt), causal != 0, static_cast<hipStream_t>(stream)));
+}
+
+fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
+                    const float* lse, const float* delta, void* dq, int B, int Hq, int Hkv, int T,
+                    int D, float scale, int causal, fa_dtype dt, void* stream)
+{
+    fa::BwdArgs a;
+    bool empty = false;
+    fa_status st = bwd_args(q, k, v, dout, lse, delta, B, Hq, Hkv, T, D, scale, dt, a, empty);
+    if (st != FA_OK || empty) return st;
+    if (!dq) return FA_ERR_NULL;
+    if (!aligned(dq, 16)) return FA_ERR_ALIGN;
+    a.dq = dq;
+    return from_hip(fa::launch_bwd_dq(a, D, dtype_code(dt), causal != 0, static_cast<hipStream_t>(stream)));
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, void* workspace, int B, int Hq,
+                 int Hkv, int T, int D, float scale, int causal, fa_dtype dt, void* stream)
+{
+    // validate everything before enqueuing anything
+    fa_status st = check_common(B, Hq, Hkv, T, D, dt);
+    if (st != FA_OK) return st;
+    if ((st = check_scale(scale)) != FA_OK) return st;
+    if ((long long)B * T == 0) return FA_OK;
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) return FA_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+        !aligned(dout, 16) || !aligned(lse, 4) || !aligned(dq, 16) || !aligned(dk, 16) ||
+        !aligned(dv, 16) || !aligned(workspace, 16))
+        return FA_ERR_ALIGN;
+    float* delta = static_cast<float*>(workspace);
+    if ((st = fa_bwd_preprocess(o, dout, delta, B, Hq, T, D, dt, stream)) != FA_OK) return st;
+    if ((st = fa_bwd_dkdv(q, k, v, dout, lse, delta, dk, dv, B, Hq, Hkv, T, D, scale, causal, dt,
+                          stream)) != FA_OK)
+        return st;
+    return fa_bwd_dq(q, k, v, dout, lse, delta, dq, B, Hq, Hkv, T, D, scale, causal, dt, stream);
+}
+
+}  // extern "C"

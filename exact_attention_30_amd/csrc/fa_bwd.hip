@@ -1,0 +1,467 @@
+// Backward kernels ("L'attention fusionnée", «La passe arrière»).
+//
+// P is never stored: every kernel rebuilds it tile by tile from the scores and
+// the saved row log-sum-exp, P = exp(S * scale - L) (computed as
+// exp2(S * scale*log2(e) - L*log2(e))).  The softmax Jacobian term of each query
+// row is replaced by Delta_i = sum_d dO_id O_id, produced by a row-reduction
+// kernel before the other two.  Gradients:
+//     dV = P^T dO,   dP = dO V^T,   dS = P * (dP - Delta),
+//     dQ = dS K * scale,   dK = dS^T Q * scale.
+// As on that page, the gradients come from two kernels and no atomic
+// additions: one walks query tiles for a fixed key tile (dK, dV), the other
+// walks key tiles for a fixed query tile (dQ), so results do not depend on the
+// order in which workgroups run.  With grouped-query attention the dK/dV
+// kernel also loops over the query heads that share the kv head, which keeps
+// the group sum inside one workgroup.
+#include "fa_device.hpp"
+#include "fa_kernels.hpp"
+
+namespace fa {
+
+// ---------------------------------------------------------------------------
+// Delta_i = sum_d dO_id * O_id.  HBM-bound: each row is read once, 16 bytes per
+// lane, and reduced over the lanes of the row in a fixed order.
+// ---------------------------------------------------------------------------
+template <class E, int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(PreArgs a)
+{
+    constexpr int CH = 16 / (int)sizeof(E);
+    constexpr int LPR = D / CH;      // lanes per row (8 or 16 or 32)
+    constexpr int RPB = 256 / LPR;   // rows per workgroup
+    const int tid = threadIdx.x;
+    const long row = (long)blockIdx.x * RPB + tid / LPR;
+    const int col = (tid % LPR) * CH;
+    float acc = 0.f;
+    if (row < a.rows) {
+        const E* o = static_cast<const E*>(a.o) + row * D + col;
+        const E* d = static_cast<const E*>(a.dout) + row * D + col;
+        if constexpr (sizeof(E) == 2) {
+            const bf16x8 x = *reinterpret_cast<const bf16x8*>(o);
+            const bf16x8 y = *reinterpret_cast<const bf16x8*>(d);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc = fmaf((float)x[e], (float)y[e], acc);
+        } else {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(o);
+            const f32x4 y = *reinterpret_cast<const f32x4*>(d);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc = fmaf(x[e], y[e], acc);
+        }
+    }
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
+    if (row < a.rows && (tid % LPR) == 0) a.delta[row] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV.  One workgroup per (batch, kv head, key tile of NW*32 keys); wave w
+// owns keys key0 + 32w .. +31 and keeps K, V of those keys in registers as B
+// operands.  Query tiles of BQ rows (of every query head of the group) stream
+// through LDS in natural layout (A operands of S = Q K^T and dP = dO V^T) and
+// transposed (A operands of dK^T += Q^T dS and dV^T += dO^T P).  S, dP, P and
+// dS live in one 32x32 accumulator layout: rows = queries, columns = keys, so
+// P and dS feed the next products straight from registers.
+// ---------------------------------------------------------------------------
+template <class E, int D, int NW, int BQ>
+struct DkdvCfg {
+    static constexpr int NT = NW * 64;
+    static constexpr int BK = NW * 32;
+    using Stage = TileStage<E, BQ, D, NT>;
+    static constexpr int NSZ = BQ * Stage::NSTRIDE;       // natural tile (elements)
+    static constexpr int TSZ = D * Stage::TSTRIDE;        // transposed tile (elements)
+    static constexpr int FSZ = 2 * BQ * 4 / (int)sizeof(E);  // L and Delta rows (floats)
+    static constexpr int BUF = 2 * NSZ + 2 * TSZ + FSZ;
+    static constexpr size_t SMEM = 2 * (size_t)BUF * sizeof(E);
+};
+
+template <class E, int D, int NW, int BQ, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdArgs a)
+{
+    using Cfg = DkdvCfg<E, D, NW, BQ>;
+    using Stage = typename Cfg::Stage;
+    constexpr int NT = Cfg::NT, BK = Cfg::BK;
+    constexpr int NS = Stage::NSTRIDE, TS = Stage::TSTRIDE;
+    constexpr int NQB = BQ / 32;
+    constexpr int NDB = D / 32;
+    constexpr int NKS = D / 16;
+
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    E* smem = reinterpret_cast<E*>(smem_raw);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 5;
+    const int c = lane & 31;
+    const int G = a.Hq / a.Hkv;
+
+    const int nkt = (a.T + BK - 1) / BK;
+    // causal: the first key tiles see the most query rows
+    const TileId id = map_tile(blockIdx.x, a.B, a.Hq, a.Hkv, 1, nkt, false);
+    const int b = id.b, hk = id.h;
+    const int key0 = id.tile * BK;
+    const int krow = key0 + w * 32 + c;  // the key this lane owns
+
+    const size_t kvoff = (size_t)(b * a.Hkv + hk) * a.T * D;
+    const E* kh = static_cast<const E*>(a.k) + kvoff;
+    const E* vh = static_cast<const E*>(a.v) + kvoff;
+
+    Frag<E> kf[NKS], vf[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        kf[ks] = global_frag<E>(kh, krow, a.T, D, 16 * ks + 8 * g);
+        vf[ks] = global_frag<E>(vh, krow, a.T, D, 16 * ks + 8 * g);
+    }
+
+    f32x16 dk[NDB], dv[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) dk[db] = dv[db] = f32x16{};
+
+    // query tiles that see this key tile, for each of the G query heads
+    const int nq = (a.T + BQ - 1) / BQ;
+    const int i0 = CAUSAL ? key0 / BQ : 0;
+    const int niq = nq - i0;
+    const int nit = G * niq;
+
+    Stage qst, dst;
+    auto head_of = [&](int it) { return hk * G + it / niq; };
+    auto tile_of = [&](int it) { return i0 + it % niq; };
+    auto load_tile = [&](int it) {
+        const int hq = head_of(it), i = tile_of(it);
+        const size_t qoff = (size_t)(b * a.Hq + hq) * a.T * D;
+        qst.load(static_cast<const E*>(a.q) + qoff, i * BQ, a.T, tid);
+        dst.load(static_cast<const E*>(a.dout) + qoff, i * BQ, a.T, tid);
+    };
+    // L * log2(e) and Delta of the tile's rows (0 past the end)
+    auto store_tile = [&](int it, E* buf) {
+        const int hq = head_of(it), i = tile_of(it);
+        qst.store_natural(buf, tid);
+        dst.store_natural(buf + Cfg::NSZ, tid);
+        qst.store_transposed(buf + 2 * Cfg::NSZ, tid);
+        dst.store_transposed(buf + 2 * Cfg::NSZ + Cfg::TSZ, tid);
+        float* f = reinterpret_cast<float*>(buf + 2 * Cfg::NSZ + 2 * Cfg::TSZ);
+        if (tid < 2 * BQ) {
+            const int r = tid % BQ, qi = i * BQ + r;
+            const size_t off = (size_t)(b * a.Hq + hq) * a.T + qi;
+            float x = 0.f;
+            if (qi < a.T) x = tid < BQ ? a.lse[off] * kLog2e : a.delta[off];
+            f[tid] = x;
+        }
+    };
+
+    if (nit > 0) {
+        load_tile(0);
+        store_tile(0, smem);
+    }
+    __syncthreads();
+
+    for (int it = 0; it < nit; ++it) {
+        const E* buf = smem + (it & 1) * Cfg::BUF;
+        const E* Qs = buf;
+        const E* dOs = buf + Cfg::NSZ;
+        const E* Qt = buf + 2 * Cfg::NSZ;
+        const E* dOt = Qt + Cfg::TSZ;
+        const float* Ls = reinterpret_cast<const float*>(dOt + Cfg::TSZ);
+        const float* Ds = Ls + BQ;
+        const bool more = it + 1 < nit;
+        if (more) load_tile(it + 1);
+
+        const int i = tile_of(it);
+        const int qbase = i * BQ;
+        const bool need_mask = (CAUSAL && qbase < key0 + BK - 1) || (qbase + BQ > a.T);
+
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+            f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                mma(s, lds_frag(Qs + (qb * 32 + c) * NS + 16 * ks + 8 * g), kf[ks]);
+                mma(dp, lds_frag(dOs + (qb * 32 + c) * NS + 16 * ks + 8 * g), vf[ks]);
+            }
+            // rows of this lane's registers: queries qb*32 + 8*(r/4) + 4g + r%4
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const int q = qb * 32 + 8 * rg + 4 * g;
+                const f32x4 L4 = *reinterpret_cast<const f32x4*>(Ls + q);
+                const f32x4 D4 = *reinterpret_cast<const f32x4*>(Ds + q);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 4 * rg + e;
+                    float p = fast_exp2(fmaf(s[r], a.c, -L4[e]));
+                    if (need_mask) {
+                        const int qi = qbase + q + e;
+                        const bool vis = (qi < a.T) && (!CAUSAL || krow <= qi);
+                        if (!vis) p = 0.f;
+                    }
+                    s[r] = p;                      // P
+                    dp[r] = p * (dp[r] - D4[e]);   // dS
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const Frag<E> pf = acc_frag<E>(s, t);
+                const Frag<E> sf = acc_frag<E>(dp, t);
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    const int off = (db * 32 + c) * TS + qb * 32 + 16 * t + 8 * g;
+                    mma(dv[db], lds_frag(dOt + off), pf);
+                    mma(dk[db], lds_frag(Qt + off), sf);
+                }
+            }
+        }
+
+        if (more) store_tile(it + 1, smem + ((it + 1) & 1) * Cfg::BUF);
+        __syncthreads();
+    }
+
+    // this lane: key krow, columns 32db + 8rg + 4g + e
+    if (krow < a.T) {
+        E* dkh = static_cast<E*>(a.dk) + kvoff + (size_t)krow * D;
+        E* dvh = static_cast<E*>(a.dv) + kvoff + (size_t)krow * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const int col = db * 32 + 8 * rg + 4 * g;
+                if constexpr (sizeof(E) == 2) {
+                    bf16x4 x, y;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        x[e] = (bf16)(dk[db][4 * rg + e] * a.scale);
+                        y[e] = (bf16)dv[db][4 * rg + e];
+                    }
+                    *reinterpret_cast<bf16x4*>(dkh + col) = x;
+                    *reinterpret_cast<bf16x4*>(dvh + col) = y;
+                } else {
+                    f32x4 x, y;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        x[e] = dk[db][4 * rg + e] * a.scale;
+                        y[e] = dv[db][4 * rg + e];
+                    }
+                    *reinterpret_cast<f32x4*>(dkh + col) = x;
+                    *reinterpret_cast<f32x4*>(dvh + col) = y;
+                }
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dQ.  One workgroup per (batch, query head, query tile of NW*32 rows); wave w
+// owns 32 queries, keeps Q and dO of them in registers and walks key tiles in
+// the forward's order.  S^T = K Q^T and dP^T = V dO^T are formed with keys as
+// rows, so dS^T feeds dQ^T += K^T dS^T from registers; K is staged both
+// naturally and transposed, V naturally.
+// ---------------------------------------------------------------------------
+template <class E, int D, int NW, int BC>
+struct DqCfg {
+    static constexpr int NT = NW * 64;
+    static constexpr int BR = NW * 32;
+    using Stage = TileStage<E, BC, D, NT>;
+    static constexpr int NSZ = BC * Stage::NSTRIDE;
+    static constexpr int TSZ = D * Stage::TSTRIDE;
+    static constexpr int BUF = 2 * NSZ + TSZ;
+    static constexpr size_t SMEM = 2 * (size_t)BUF * sizeof(E);
+};
+
+template <class E, int D, int NW, int BC, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdArgs a)
+{
+    using Cfg = DqCfg<E, D, NW, BC>;
+    using Stage = typename Cfg::Stage;
+    constexpr int NT = Cfg::NT, BR = Cfg::BR;
+    constexpr int NS = Stage::NSTRIDE, TS = Stage::TSTRIDE;
+    constexpr int NKB = BC / 32;
+    constexpr int NDB = D / 32;
+    constexpr int NKS = D / 16;
+
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    E* smem = reinterpret_cast<E*>(smem_raw);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 5;
+    const int c = lane & 31;
+
+    const int nqt = (a.T + BR - 1) / BR;
+    const TileId id = map_tile(blockIdx.x, a.B, a.Hq, a.Hkv, a.Hq / a.Hkv, nqt, CAUSAL);
+    const int b = id.b, hq = id.h;
+    const int hk = hq / (a.Hq / a.Hkv);
+    const int q0 = id.tile * BR;
+    const int qrow = q0 + w * 32 + c;
+
+    const size_t qoff = (size_t)(b * a.Hq + hq) * a.T * D;
+    const size_t kvoff = (size_t)(b * a.Hkv + hk) * a.T * D;
+    const E* kh = static_cast<const E*>(a.k) + kvoff;
+    const E* vh = static_cast<const E*>(a.v) + kvoff;
+
+    Frag<E> qf[NKS], of[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        qf[ks] = global_frag<E>(static_cast<const E*>(a.q) + qoff, qrow, a.T, D, 16 * ks + 8 * g);
+        of[ks] = global_frag<E>(static_cast<const E*>(a.dout) + qoff, qrow, a.T, D, 16 * ks + 8 * g);
+    }
+    float L2 = 0.f, Dl = 0.f;
+    if (qrow < a.T) {
+        const size_t r = (size_t)(b * a.Hq + hq) * a.T + qrow;
+        L2 = a.lse[r] * kLog2e;
+        Dl = a.delta[r];
+    }
+
+    const int kend = CAUSAL ? min(q0 + BR, a.T) : a.T;
+    const int nkv = (kend + BC - 1) / BC;
+    const int nfull = CAUSAL ? (q0 + 1) / BC : a.T / BC;
+
+    f32x16 dq[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) dq[db] = f32x16{};
+
+    Stage kst, vst;
+    kst.load(kh, 0, a.T, tid);
+    vst.load(vh, 0, a.T, tid);
+    kst.store_natural(smem, tid);
+    vst.store_natural(smem + Cfg::NSZ, tid);
+    kst.store_transposed(smem + 2 * Cfg::NSZ, tid);
+    __syncthreads();
+
+    for (int j = 0; j < nkv; ++j) {
+        const E* Ks = smem + (j & 1) * Cfg::BUF;
+        const E* Vs = Ks + Cfg::NSZ;
+        const E* Kt = Ks + 2 * Cfg::NSZ;
+        const bool more = j + 1 < nkv;
+        if (more) {
+            kst.load(kh, (j + 1) * BC, a.T, tid);
+            vst.load(vh, (j + 1) * BC, a.T, tid);
+        }
+        const bool need_mask = j >= nfull;
+
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                mma(s, lds_frag(Ks + (kb * 32 + c) * NS + 16 * ks + 8 * g), qf[ks]);
+                mma(dp, lds_frag(Vs + (kb * 32 + c) * NS + 16 * ks + 8 * g), of[ks]);
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float p = fast_exp2(fmaf(s[r], a.c, -L2));
+                if (need_mask) {
+                    const int kj = j * BC + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+                    const bool vis = CAUSAL ? (kj <= qrow) : (kj < a.T);
+                    if (!vis) p = 0.f;
+                }
+                dp[r] = p * (dp[r] - Dl);  // dS^T
+            }
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const Frag<E> sf = acc_frag<E>(dp, t);
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    mma(dq[db], lds_frag(Kt + (db * 32 + c) * TS + kb * 32 + 16 * t + 8 * g), sf);
+            }
+        }
+
+        if (more) {
+            E* nb = smem + ((j + 1) & 1) * Cfg::BUF;
+            kst.store_natural(nb, tid);
+            vst.store_natural(nb + Cfg::NSZ, tid);
+            kst.store_transposed(nb + 2 * Cfg::NSZ, tid);
+        }
+        __syncthreads();
+    }
+
+    if (qrow < a.T) {
+        E* dqh = static_cast<E*>(a.dq) + qoff + (size_t)qrow * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const int col = db * 32 + 8 * rg + 4 * g;
+                if constexpr (sizeof(E) == 2) {
+                    bf16x4 x;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) x[e] = (bf16)(dq[db][4 * rg + e] * a.scale);
+                    *reinterpret_cast<bf16x4*>(dqh + col) = x;
+                } else {
+                    f32x4 x;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) x[e] = dq[db][4 * rg + e] * a.scale;
+                    *reinterpret_cast<f32x4*>(dqh + col) = x;
+                }
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+template <class E, int D>
+static hipError_t launch_pre_t(const PreArgs& a, hipStream_t stream)
+{
+    constexpr int LPR = D / (16 / (int)sizeof(E));
+    constexpr int RPB = 256 / LPR;
+    const long grid = (a.rows + RPB - 1) / RPB;
+    hipLaunchKernelGGL((bwd_pre_kernel<E, D>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_pre(const PreArgs& a, int D, int dtype, hipStream_t stream)
+{
+    if (dtype == 0) return D == 64 ? launch_pre_t<bf16, 64>(a, stream) : launch_pre_t<bf16, 128>(a, stream);
+    return D == 64 ? launch_pre_t<float, 64>(a, stream) : launch_pre_t<float, 128>(a, stream);
+}
+
+template <class E, int D, bool CAUSAL>
+static hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t stream)
+{
+    constexpr int NW = 4, BQ = (sizeof(E) == 4 && D == 128) ? 32 : 64;
+    using Cfg = DkdvCfg<E, D, NW, BQ>;
+    static_assert(Cfg::SMEM <= 160 * 1024, "LDS budget");
+    auto kern = bwd_dkdv_kernel<E, D, NW, BQ, CAUSAL>;
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cfg::SMEM);
+    if (attr != hipSuccess) return attr;
+    const int nkt = (a.T + Cfg::BK - 1) / Cfg::BK;
+    const long grid = (long)nkt * a.B * a.Hkv;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Cfg::NT), Cfg::SMEM, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv(const BwdArgs& a, int D, int dtype, bool causal, hipStream_t stream)
+{
+    if (dtype == 0) {
+        if (D == 64) return causal ? launch_dkdv_t<bf16, 64, true>(a, stream) : launch_dkdv_t<bf16, 64, false>(a, stream);
+        return causal ? launch_dkdv_t<bf16, 128, true>(a, stream) : launch_dkdv_t<bf16, 128, false>(a, stream);
+    }
+    if (D == 64) return causal ? launch_dkdv_t<float, 64, true>(a, stream) : launch_dkdv_t<float, 64, false>(a, stream);
+    return causal ? launch_dkdv_t<float, 128, true>(a, stream) : launch_dkdv_t<float, 128, false>(a, stream);
+}
+
+template <class E, int D, bool CAUSAL>
+static hipError_t launch_dq_t(const BwdArgs& a, hipStream_t stream)
+{
+    constexpr int NW = 4, BC = (sizeof(E) == 4 && D == 128) ? 32 : 64;
+    using Cfg = DqCfg<E, D, NW, BC>;
+    static_assert(Cfg::SMEM <= 160 * 1024, "LDS budget");
+    auto kern = bwd_dq_kernel<E, D, NW, BC, CAUSAL>;
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cfg::SMEM);
+    if (attr != hipSuccess) return attr;
+    const int nqt = (a.T + Cfg::BR - 1) / Cfg::BR;
+    const long grid = (long)nqt * a.B * a.Hq;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Cfg::NT), Cfg::SMEM, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq(const BwdArgs& a, int D, int dtype, bool causal, hipStream_t stream)
+{
+    if (dtype == 0) {
+        if (D == 64) return causal ? launch_dq_t<bf16, 64, true>(a, stream) : launch_dq_t<bf16, 64, false>(a, stream);
+        return causal ? launch_dq_t<bf16, 128, true>(a, stream) : launch_dq_t<bf16, 128, false>(a, stream);
+    }
+    if (D == 64) return causal ? launch_dq_t<float, 64, true>(a, stream) : launch_dq_t<float, 64, false>(a, stream);
+    return causal ? launch_dq_t<float, 128, true>(a, stream) : launch_dq_t<float, 128, false>(a, stream);
+}
+
+}  // namespace fa

@@ -1,0 +1,289 @@
+// Device building blocks shared by the attention kernels (gfx950 / CDNA4).
+//
+// Matrix products use the 32x32 MFMA shape with fp32 accumulators:
+//   bf16: v_mfma_f32_32x32x16_bf16 (one instruction per 16-deep step)
+//   fp32: v_mfma_f32_32x32x2_f32   (eight instructions per 16-deep step)
+// Register layouts of a 64-lane wave (lane = 32*g + c, g in {0,1}, c in 0..31):
+//   A operand (32 x K):  lane holds A[c][8g .. 8g+7] of each 16-deep step
+//   B operand (K x 32):  lane holds B[8g .. 8g+7][c]
+//   accumulator (32x32): register r holds C[8*(r/4) + 4g + r%4][c]
+// A "fragment" below is the 8 contraction elements one lane feeds to one
+// 16-deep step.  Because the contraction index of a product may be permuted
+// freely (as long as both operands use the same permutation), the
+// accumulator of one product can feed the B operand of the next product
+// without leaving registers: register r = 8t + e of a 32-row accumulator block
+// becomes element e of the fragment for step t, which stands for contraction
+// row 16t + 8*(e/4) + 4g + e%4.  The partner operand is then read from a
+// tile stored with rows permuted by `perm16` (swap bits 2 and 3), so that the
+// same 8 elements are contiguous in LDS.
+//
+// This is the MFMA form of the register-resident weights that "L'attention
+// fusionnée" describes for mma.sync in «Sur les Tensor Cores».
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <class E>
+struct Frag;
+template <>
+struct Frag<bf16> {
+    bf16x8 v;
+};
+template <>
+struct Frag<float> {
+    f32x8 v;
+};
+
+// acc += A_frag x B_frag over one 16-deep contraction step.
+__device__ __forceinline__ void mma(f32x16& acc, const Frag<bf16>& a, const Frag<bf16>& b)
+{
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x16& acc, const Frag<float>& a, const Frag<float>& b)
+{
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.v[e], b.v[e], acc, 0, 0, 0);
+}
+
+// 8 contiguous elements from LDS (16-byte aligned).
+__device__ __forceinline__ Frag<bf16> lds_frag(const bf16* p)
+{
+    Frag<bf16> f;
+    f.v = *reinterpret_cast<const bf16x8*>(p);
+    return f;
+}
+__device__ __forceinline__ Frag<float> lds_frag(const float* p)
+{
+    Frag<float> f;
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 hi = *reinterpret_cast<const f32x4*>(p + 4);
+    f.v = f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return f;
+}
+
+// 8 contiguous elements of row `row` of a [nrows][D] global array, or zeros
+// when the row is past the end.
+template <class E>
+__device__ __forceinline__ Frag<E> global_frag(const E* base, int row, int nrows, int D, int col)
+{
+    Frag<E> f;
+    if (row < nrows) {
+        const E* p = base + (size_t)row * D + col;
+        if constexpr (sizeof(E) == 2) {
+            f.v = *reinterpret_cast<const bf16x8*>(p);
+        } else {
+            const f32x4 lo = *reinterpret_cast<const f32x4*>(p);
+            const f32x4 hi = *reinterpret_cast<const f32x4*>(p + 4);
+            f.v = f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+    } else {
+        if constexpr (sizeof(E) == 2) {
+            f.v = bf16x8{};
+        } else {
+            f.v = f32x8{};
+        }
+    }
+    return f;
+}
+
+// Registers 8t .. 8t+7 of an accumulator block as a B-operand fragment
+// (rounded to nearest even for bf16).
+template <class E>
+__device__ __forceinline__ Frag<E> acc_frag(const f32x16& s, int t);
+template <>
+__device__ __forceinline__ Frag<bf16> acc_frag<bf16>(const f32x16& s, int t)
+{
+    Frag<bf16> f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f.v[e] = (bf16)s[8 * t + e];
+    return f;
+}
+template <>
+__device__ __forceinline__ Frag<float> acc_frag<float>(const f32x16& s, int t)
+{
+    Frag<float> f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f.v[e] = s[8 * t + e];
+    return f;
+}
+
+// Row permutation of transposed tiles inside each group of 16: swap bits 2, 3.
+__device__ __forceinline__ constexpr int perm16(int r)
+{
+    return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+
+// Combine a value of lane c with the value of lane c ^ 32 (the two lanes of a
+// wave that hold the same accumulator column).  v_permlane32_swap exchanges
+// the upper half of its first operand with the lower half of its second; with
+// both operands equal to x, element 0 of the result holds x of lane c - 32 in
+// the upper lanes (x itself below) and element 1 holds x of lane c + 32 in the
+// lower lanes (x itself above).  The lower lane's value always comes first,
+// so both lanes compute bit-identical sums.
+__device__ __forceinline__ float pair_max(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
+// Tile staging: global [nrows][D] rows row0 .. row0+ROWS-1 -> LDS.
+// Loads go to registers first (issued early), stores to LDS come later, so a
+// tile can be fetched while the previous one is being used.
+//
+// Work unit: 4 consecutive rows x one 16-byte column chunk (CH elements).
+// Both layouts can be written from the same registers:
+//   natural    lds[r][col]          row stride D + CH   (16-byte pad)
+//   transposed lds[col][perm16(r)]  row stride ROWS + CH
+// Rows past the end of the sequence are loaded as zeros.
+// ---------------------------------------------------------------------------
+template <class E, int ROWS, int D, int NT>
+struct TileStage {
+    static constexpr int CH = 16 / (int)sizeof(E);
+    static constexpr int RG = ROWS / 4;  // row groups
+    static constexpr int DG = D / CH;    // column chunks
+    static constexpr int NU = RG * DG;   // units per tile
+    static constexpr int N = (NU + NT - 1) / NT;  // units per thread (last may be idle)
+    static constexpr bool EVEN = (NU % NT) == 0;
+    static constexpr int NSTRIDE = D + CH;
+    static constexpr int TSTRIDE = ROWS + CH;
+
+    u32x4 buf[N][4];
+
+    // unit u -> (row group, column chunk); consecutive threads take
+    // consecutive row groups so that transposed stores of a wave fill whole
+    // LDS rows.
+    __device__ __forceinline__ static void unit(int u, int& rg, int& dg)
+    {
+        rg = u % RG;
+        dg = u / RG;
+    }
+
+    __device__ __forceinline__ void load(const E* head, int row0, int nrows, int tid)
+    {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            if (!EVEN && i * NT + tid >= NU) break;
+            int rg, dg;
+            unit(i * NT + tid, rg, dg);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int row = row0 + 4 * rg + c;
+                if (row < nrows)
+                    buf[i][c] = *reinterpret_cast<const u32x4*>(head + (size_t)row * D + dg * CH);
+                else
+                    buf[i][c] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+    }
+
+    __device__ __forceinline__ void store_natural(E* lds, int tid) const
+    {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            if (!EVEN && i * NT + tid >= NU) break;
+            int rg, dg;
+            unit(i * NT + tid, rg, dg);
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                *reinterpret_cast<u32x4*>(lds + (4 * rg + c) * NSTRIDE + dg * CH) = buf[i][c];
+        }
+    }
+
+    __device__ __forceinline__ void store_transposed(E* lds, int tid) const
+    {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            if (!EVEN && i * NT + tid >= NU) break;
+            int rg, dg;
+            unit(i * NT + tid, rg, dg);
+            const int pos = perm16(4 * rg);  // the 4 rows stay contiguous
+            if constexpr (sizeof(E) == 2) {
+#pragma unroll
+                for (int e = 0; e < CH; ++e) {
+                    // element e of each of the 4 rows: 16-bit halves of dword e/2
+                    const int dw = e >> 1;
+                    const int sh = (e & 1) * 16;
+                    const uint32_t r0 = (buf[i][0][dw] >> sh) & 0xffffu;
+                    const uint32_t r1 = (buf[i][1][dw] >> sh) & 0xffffu;
+                    const uint32_t r2 = (buf[i][2][dw] >> sh) & 0xffffu;
+                    const uint32_t r3 = (buf[i][3][dw] >> sh) & 0xffffu;
+                    *reinterpret_cast<u32x2*>(lds + (dg * CH + e) * TSTRIDE + pos) =
+                        u32x2{r0 | (r1 << 16), r2 | (r3 << 16)};
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < CH; ++e)
+                    *reinterpret_cast<u32x4*>(lds + (dg * CH + e) * TSTRIDE + pos) =
+                        u32x4{buf[i][0][e], buf[i][1][e], buf[i][2][e], buf[i][3][e]};
+            }
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Work mapping.  Workgroups are dispatched round-robin over the 8 XCDs
+// (workgroup id w runs on XCD w % 8).  When the number of kv groups
+// (B * Hkv) is a multiple of 8, every XCD gets whole kv groups, so the query
+// heads that share K/V also share that XCD's L2; inside an XCD, tiles are
+// handed out heaviest first (for causal attention the last query tiles see the
+// most keys).  Otherwise tiles are handed out heaviest first over all heads.
+// `ntile` = tiles per head; `heavy_first_desc` says whether the heaviest tile
+// has the largest index.
+// ---------------------------------------------------------------------------
+struct TileId {
+    int b, h, tile;  // h: query head (per-query-tile kernels) or kv head
+};
+
+__device__ __forceinline__ TileId map_tile(int wg, int B, int Hq, int Hkv, int heads_per_group,
+                                           int ntile, bool heavy_last_index)
+{
+    // heads_per_group: how many work heads share one kv head (Hq/Hkv for
+    // query-tile kernels, 1 for key-tile kernels); total heads = Hkv * hpg.
+    const int ngroups = B * Hkv;
+    TileId id;
+    int rank, grp, sub;
+    if ((ngroups & 7) == 0) {
+        const int x = wg & 7, s = wg >> 3;
+        const int per = (ngroups >> 3) * heads_per_group;  // items per tile rank on one XCD
+        rank = s / per;
+        const int rem = s % per;
+        grp = (rem / heads_per_group) * 8 + x;
+        sub = rem % heads_per_group;
+    } else {
+        const int per = ngroups * heads_per_group;
+        rank = wg / per;
+        const int rem = wg % per;
+        grp = rem / heads_per_group;
+        sub = rem % heads_per_group;
+    }
+    id.b = grp / Hkv;
+    id.h = (grp % Hkv) * heads_per_group + sub;
+    id.tile = heavy_last_index ? (ntile - 1 - rank) : rank;
+    (void)Hq;
+    return id;
+}
+
+}  // namespace fa

@@ -1,0 +1,225 @@
+// Forward kernel: O = softmax(Q K^T * scale [+ causal mask]) V and the row
+// log-sum-exp, without ever writing the T x T scores.
+//
+// Algorithm ("L'attention fusionnée", «Le softmax en ligne»; "FlashAttention:
+// l'attenzione che non spreca memoria", «L'idea: lavorare a tessere»): a
+// workgroup keeps a block of BR query rows in registers and streams key/value
+// tiles of BC rows through LDS.  For every tile it updates a running max m, a
+// running sum l and the output numerator o, rescaling both by exp(m - m') when
+// the max rises; o is divided by l once at the end, and L = m + ln l is saved.
+//
+// MI355X mapping:
+//   * NW waves, each owning 32 query rows; one wave computes S^T = K Q^T with
+//     the 32x32 MFMA so that a lane owns one query column: its row max/sum is
+//     an in-lane reduction plus one exchange with lane c ^ 32.
+//   * The S^T accumulator is exponentiated in place (exp2 with scale*log2(e)
+//     folded in: the cuTile page's INV_LOG_2 trick) and fed straight back as
+//     the B operand of O^T += V^T P^T, so P never touches LDS.
+//   * K tiles are stored naturally in LDS, V tiles transposed (row-permuted)
+//     so that the V^T fragments are contiguous 16-byte reads.  Tiles are
+//     double-buffered: the next tile's global loads are issued before the
+//     current tile's MFMAs and stored to the other buffer after them.
+//   * Causal: tiles wholly in the future are never visited; tiles wholly in
+//     the past run without mask code; only diagonal (and, non-causal, the
+//     ragged last) tiles take the per-element mask, derived from the lane's
+//     query index and the key index ("Optimización de Flash Attention ...",
+//     «Atención causal» and the K-loop split of «La pila de optimización»).
+#include "fa_device.hpp"
+#include "fa_kernels.hpp"
+
+namespace fa {
+
+template <class E, int D, int NW, int BC>
+struct FwdCfg {
+    static constexpr int NT = NW * 64;
+    static constexpr int BR = NW * 32;
+    using KStage = TileStage<E, BC, D, NT>;
+    static constexpr int KSZ = BC * KStage::NSTRIDE;  // natural K tile (elements)
+    static constexpr int VSZ = D * KStage::TSTRIDE;   // transposed V tile (elements)
+    static constexpr int BUF = KSZ + VSZ;
+    static constexpr size_t SMEM = 2 * (size_t)BUF * sizeof(E);
+};
+
+template <class E, int D, int NW, int BC, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a)
+{
+    using Cfg = FwdCfg<E, D, NW, BC>;
+    using Stage = typename Cfg::KStage;
+    constexpr int NT = Cfg::NT, BR = Cfg::BR;
+    constexpr int KS = Stage::NSTRIDE, VS = Stage::TSTRIDE;
+    constexpr int NKB = BC / 32;  // 32-key blocks per tile
+    constexpr int NDB = D / 32;   // 32-column blocks of the head dimension
+    constexpr int NKS = D / 16;   // 16-deep steps over the head dimension
+
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    E* smem = reinterpret_cast<E*>(smem_raw);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 5;
+    const int c = lane & 31;
+
+    const int nqt = (a.T + BR - 1) / BR;
+    const TileId id = map_tile(blockIdx.x, a.B, a.Hq, a.Hkv, a.Hq / a.Hkv, nqt, CAUSAL);
+    const int b = id.b, hq = id.h;
+    const int hk = hq / (a.Hq / a.Hkv);
+    const int q0 = id.tile * BR;
+    const int qrow = q0 + w * 32 + c;  // the query this lane owns
+
+    const E* qh = static_cast<const E*>(a.q) + (size_t)(b * a.Hq + hq) * a.T * D;
+    const E* kh = static_cast<const E*>(a.k) + (size_t)(b * a.Hkv + hk) * a.T * D;
+    const E* vh = static_cast<const E*>(a.v) + (size_t)(b * a.Hkv + hk) * a.T * D;
+
+    // B operand of S^T = K Q^T: this lane's query row, 8 columns per step
+    Frag<E> qf[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qf[ks] = global_frag<E>(qh, qrow, a.T, D, 16 * ks + 8 * g);
+
+    // key tiles to visit, and how many of them need no mask
+    const int kend = CAUSAL ? min(q0 + BR, a.T) : a.T;
+    const int nkv = (kend + BC - 1) / BC;
+    const int nfull = CAUSAL ? (q0 + 1) / BC : a.T / BC;
+
+    f32x16 o[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
+    float m = -INFINITY;  // running max of raw scores (q.k), per query
+    float l = 0.f;        // this lane's share of the running sum
+
+    Stage kst, vst;
+    kst.load(kh, 0, a.T, tid);
+    vst.load(vh, 0, a.T, tid);
+    kst.store_natural(smem, tid);
+    vst.store_transposed(smem + Cfg::KSZ, tid);
+    __syncthreads();
+
+    for (int j = 0; j < nkv; ++j) {
+        const E* Ks = smem + (j & 1) * Cfg::BUF;
+        const E* Vt = Ks + Cfg::KSZ;
+        const bool more = j + 1 < nkv;
+        if (more) {
+            kst.load(kh, (j + 1) * BC, a.T, tid);
+            vst.load(vh, (j + 1) * BC, a.T, tid);
+        }
+
+        // S^T block kb: rows = keys 32kb.., columns = this wave's 32 queries
+        f32x16 s[NKB];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            s[kb] = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+                mma(s[kb], lds_frag(Ks + (kb * 32 + c) * KS + 16 * ks + 8 * g), qf[ks]);
+        }
+
+        if (j >= nfull) {  // diagonal or ragged tile: mask from indices
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int kj = j * BC + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+                    const bool vis = CAUSAL ? (kj <= qrow) : (kj < a.T);
+                    if (!vis) s[kb][r] = -INFINITY;
+                }
+        }
+
+        // online softmax update for this lane's query
+        float mt = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
+        mt = pair_max(mt);
+        const float mnew = fmaxf(m, mt);
+        const float msub = (mnew == -INFINITY) ? 0.f : mnew * a.c;
+        const float alpha = fast_exp2(m * a.c - msub);
+        float rs = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = fast_exp2(fmaf(s[kb][r], a.c, -msub));
+                s[kb][r] = p;
+                rs += p;
+            }
+        l = l * alpha + rs;
+        m = mnew;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+
+        // O^T += V^T P^T, P straight from the S^T registers
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const Frag<E> pf = acc_frag<E>(s[kb], t);
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    mma(o[db], lds_frag(Vt + (db * 32 + c) * VS + kb * 32 + 16 * t + 8 * g), pf);
+            }
+
+        if (more) {
+            E* nb = smem + ((j + 1) & 1) * Cfg::BUF;
+            kst.store_natural(nb, tid);
+            vst.store_transposed(nb + Cfg::KSZ, tid);
+        }
+        __syncthreads();
+    }
+
+    // epilogue: divide by l, store O (this lane: query qrow, columns
+    // 32db + 8rg + 4g + i) and lse
+    const float lt = pair_sum(l);
+    const float inv = 1.f / lt;
+    if (qrow < a.T) {
+        E* oh = static_cast<E*>(a.o) + ((size_t)(b * a.Hq + hq) * a.T + qrow) * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                E* p = oh + db * 32 + 8 * rg + 4 * g;
+                if constexpr (sizeof(E) == 2) {
+                    bf16x4 x;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) x[i] = (bf16)(o[db][4 * rg + i] * inv);
+                    *reinterpret_cast<bf16x4*>(p) = x;
+                } else {
+                    f32x4 x;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) x[i] = o[db][4 * rg + i] * inv;
+                    *reinterpret_cast<f32x4*>(p) = x;
+                }
+            }
+        if (g == 0)
+            a.lse[(size_t)(b * a.Hq + hq) * a.T + qrow] = (m * a.c + __log2f(lt)) * kLn2;
+    }
+}
+
+// Tile configuration per (dtype, D): NW waves of 32 query rows, BC keys per tile.
+template <class E, int D, bool CAUSAL>
+static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream)
+{
+    constexpr int NW = 4, BC = 64;
+    using Cfg = FwdCfg<E, D, NW, BC>;
+    static_assert(Cfg::SMEM <= 160 * 1024, "LDS budget");
+    auto kern = fwd_kernel<E, D, NW, BC, CAUSAL>;
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cfg::SMEM);
+    if (attr != hipSuccess) return attr;
+    const int nqt = (a.T + Cfg::BR - 1) / Cfg::BR;
+    const long grid = (long)nqt * a.B * a.Hq;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Cfg::NT), Cfg::SMEM, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_fwd(const FwdArgs& a, int D, int dtype, bool causal, hipStream_t stream)
+{
+    if (dtype == 0) {
+        if (D == 64) return causal ? launch_fwd_t<bf16, 64, true>(a, stream) : launch_fwd_t<bf16, 64, false>(a, stream);
+        return causal ? launch_fwd_t<bf16, 128, true>(a, stream) : launch_fwd_t<bf16, 128, false>(a, stream);
+    }
+    if (D == 64) return causal ? launch_fwd_t<float, 64, true>(a, stream) : launch_fwd_t<float, 64, false>(a, stream);
+    return causal ? launch_fwd_t<float, 128, true>(a, stream) : launch_fwd_t<float, 128, false>(a, stream);
+}
+
+}  // namespace fa

@@ -1,0 +1,48 @@
+// Kernel argument blocks and launcher declarations (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace fa {
+
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    int B, Hq, Hkv, T;
+    float c;      // scale * log2(e): scores are exponentiated in base 2
+    float scale;  // for the natural-log lse
+};
+
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* dout;
+    const float* lse;
+    const float* delta;
+    void* dq;
+    void* dk;
+    void* dv;
+    int B, Hq, Hkv, T;
+    float c;      // scale * log2(e)
+    float scale;
+};
+
+struct PreArgs {
+    const void* o;
+    const void* dout;
+    float* delta;
+    long rows;
+};
+
+// Each launcher enqueues one kernel on `stream` and returns the launch status.
+// dtype: 0 = bf16, 1 = fp32.  Shapes have been validated by the caller.
+hipError_t launch_fwd(const FwdArgs& a, int D, int dtype, bool causal, hipStream_t stream);
+hipError_t launch_bwd_pre(const PreArgs& a, int D, int dtype, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, int D, int dtype, bool causal, hipStream_t stream);
+hipError_t launch_bwd_dq(const BwdArgs& a, int D, int dtype, bool causal, hipStream_t stream);
+
+}  // namespace fa

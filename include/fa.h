@@ -1,0 +1,143 @@
+/*
+ * fa.h — C ABI of exact_attention_30_amd: fused exact attention (forward and
+ * backward) for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  For every batch b and query head h, with kv head
+ * hk = h / (Hq / Hkv) (grouped-query attention, consecutive grouping: see
+ * "FlashAttention" note, «Grouped-Query Attention» paragraph, and the cuTile
+ * page's QUERY_GROUP_SIZE, "Optimización de Flash Attention ... NVIDIA CUDA
+ * Tile", «Parte 1 ... interfaz del kernel»):
+ *
+ *     O = softmax(Q K^T * scale + mask) V
+ *
+ * where the causal mask lets query i see key j iff i >= j ("Optimización de
+ * Flash Attention ...", «Atención causal»).  The T x T score and weight
+ * matrices are never written to memory: the forward walks key tiles with the
+ * online softmax (running max m, sum l, rescale by exp(m - m')), as in
+ * "L'attention fusionnée", «Le softmax en ligne», and stores per query row the
+ * log-sum-exp L = m + ln(l).  The backward recomputes P = exp(S - L) tile by
+ * tile and uses the row reduction Delta_i = sum_d dO_id O_id in place of the
+ * softmax Jacobian term ("L'attention fusionnée", «La passe arrière»):
+ *
+ *     dV = P^T dO,  dS = P * (dO V^T - Delta),  dQ = dS K * scale,
+ *     dK = dS^T Q * scale.
+ *
+ * Layouts.  All tensors are contiguous, row-major, element type `dt`:
+ *     q, o, dout, dq : [B][Hq][T][D]
+ *     k, v, dk, dv   : [B][Hkv][T][D]
+ *     lse            : [B][Hq][T] float32, natural log, in units of the scaled
+ *                      scores (lse_i = log sum_j exp(scale * q_i . k_j)).
+ * Query and key sequences have the same length T.
+ *
+ * Ownership and execution.  The caller owns every buffer; the library never
+ * allocates device memory and keeps no pointer after a call returns.  Each call
+ * enqueues kernels on `stream` (a hipStream_t; NULL is the default stream) and
+ * returns without waiting for them.  Outputs are overwritten, never
+ * accumulated.  Inputs and outputs must not overlap.  Two calls on one stream
+ * run in order; calls on different streams that share an output race.
+ *
+ * Errors.  Arguments are checked on the host before anything is enqueued, in
+ * this order, and the first failure is returned:
+ *     FA_ERR_SHAPE        B < 0, T < 0, Hq < 1, Hkv < 1, Hq % Hkv != 0, or a
+ *                         grid or tensor too large to index;
+ *     FA_ERR_UNSUPPORTED  D not in {64, 128}, unknown dtype, or scale not a
+ *                         finite positive number;
+ *     FA_ERR_NULL         a required pointer is NULL (pointers are not needed
+ *                         when B * T == 0, which is a valid no-op);
+ *     FA_ERR_ALIGN        a tensor pointer is not 16-byte aligned (lse and the
+ *                         workspace: 4-byte and 16-byte);
+ *     FA_ERR_HIP          the HIP runtime reported an error while launching.
+ * NaN or Inf inside the inputs is not checked and propagates.
+ * No exception or abort crosses this interface.
+ */
+#ifndef EXACT_ATTENTION_30_AMD_FA_H
+#define EXACT_ATTENTION_30_AMD_FA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FA_BF16 = 0, /* bfloat16 inputs/outputs; bf16 MFMA with fp32 accumulation */
+    FA_FP32 = 1  /* float32 inputs/outputs; fp32 MFMA with fp32 accumulation */
+} fa_dtype;
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_NULL = 1,
+    FA_ERR_SHAPE = 2,
+    FA_ERR_UNSUPPORTED = 3,
+    FA_ERR_ALIGN = 4,
+    FA_ERR_HIP = 5
+} fa_status;
+
+/*
+ * Forward pass: o = softmax(q k^T * scale [+ causal mask]) v and lse.
+ * Source: "L'attention fusionnée", «Le softmax en ligne» (tiled online softmax,
+ * division by l at the end) and «La passe arrière» (L = m + ln l saved for the
+ * backward); "FlashAttention: l'attenzione che non spreca memoria",
+ * «L'idea: lavorare a tessere» (a query block stays on chip while key/value
+ * blocks stream past it).
+ *   q [B,Hq,T,D], k/v [B,Hkv,T,D]  (device, read)
+ *   o [B,Hq,T,D]                   (device, written)
+ *   lse [B,Hq,T] float32           (device, written)
+ *   causal: nonzero applies the causal mask.
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                 int Hkv, int T, int D, float scale, int causal, fa_dtype dt, void* stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs: one float32 Delta per query row,
+ * B * Hq * T * 4, rounded up to 256.  Returns 0 for invalid or empty shapes.
+ */
+size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int T, int D, fa_dtype dt);
+
+/*
+ * Backward pass of fa_fwd for the upstream gradient dout: writes dq, dk, dv.
+ * Source: "L'attention fusionnée", «La passe arrière»: P is recomputed from
+ * lse, Delta = rowsum(dout * o) replaces the Jacobian term, and two kernels
+ * (one for dK/dV per key tile, one for dQ per query tile walking keys in the
+ * forward's order) avoid atomic additions, so results are bitwise
+ * reproducible run to run.  Equivalent to fa_bwd_preprocess, fa_bwd_dkdv and
+ * fa_bwd_dq enqueued in that order.
+ *   q, k, v, o, lse: as produced for/by fa_fwd with the same scale and causal;
+ *   dout [B,Hq,T,D] (device, read); dq [B,Hq,T,D], dk/dv [B,Hkv,T,D]
+ *   (device, written); workspace: fa_bwd_workspace_bytes(...) bytes of device
+ *   memory (scratch, contents on return unspecified).
+ */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, void* workspace, int B, int Hq,
+                 int Hkv, int T, int D, float scale, int causal, fa_dtype dt, void* stream);
+
+/*
+ * The three stages of fa_bwd, for callers that schedule or time them
+ * separately.  `delta` is a [B,Hq,T] float32 device buffer (for instance the
+ * start of the fa_bwd workspace).
+ *   fa_bwd_preprocess: delta_i = sum_d dout_id * o_id ("L'attention
+ *       fusionnée", «La passe arrière», the row reduction run before the rest).
+ *   fa_bwd_dkdv: dk, dv for every key row (per key tile, summed over the query
+ *       heads of the kv group).
+ *   fa_bwd_dq: dq for every query row.
+ */
+fa_status fa_bwd_preprocess(const void* o, const void* dout, float* delta, int B, int Hq, int T,
+                            int D, fa_dtype dt, void* stream);
+fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
+                      const float* lse, const float* delta, void* dk, void* dv, int B, int Hq,
+                      int Hkv, int T, int D, float scale, int causal, fa_dtype dt, void* stream);
+fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
+                    const float* lse, const float* delta, void* dq, int B, int Hq, int Hkv, int T,
+                    int D, float scale, int causal, fa_dtype dt, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* fa_status_string(fa_status s);
+
+/* Library version string, e.g. "0.1.0". */
+const char* fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_ATTENTION_30_AMD_FA_H */

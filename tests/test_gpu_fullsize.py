@@ -1,0 +1,141 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times (the library's default tiles, one fa_fwd and one fa_bwd call).
+
+The oracle cannot redo these in full, so it checks sampled rows it can afford
+one by one: query rows (O, lse, dQ) spread over heads and positions, and key
+rows near the end of the sequence (dK, dV), where few query rows see the key.
+Every row, early keys included, is also held to identities that exact
+gradients satisfy at any size, per kv group:
+    sum_j dK_j = 0                  (each row of dS sums to zero)
+    sum_j dV_j = sum_i dO_i         (each row of P sums to one)
+    K^T dK = dQ^T Q                 (both equal scale * sum_ij dS_ij k_j q_i^T)
+"""
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_30_amd as fa
+import oracle
+from tests.gpu_util import BF16_MAX_ABS, BF16_REL_L2, assert_close, assert_lse_close, f64, say
+from workloads import WORKLOADS, workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+_cache = {}
+
+
+def run(name):
+    """Inputs (CPU) and GPU outputs (CPU copies) of one workload."""
+    if name in _cache:
+        return _cache[name]
+    w = WORKLOADS[name]
+    x = workload_inputs(w)
+    d = {k: v.cuda() for k, v in x.items()}
+    say(f"full-size {name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} T={w.T} D={w.D} causal={w.causal}")
+    o, lse = fa.fwd(d["q"], d["k"], d["v"], scale=w.scale, causal=w.causal)
+    out = {"o": o, "lse": lse}
+    if w.backward:
+        out["dq"], out["dk"], out["dv"] = fa.bwd(d["q"], d["k"], d["v"], o, d["dout"], lse,
+                                                 scale=w.scale, causal=w.causal)
+    torch.cuda.synchronize()
+    out = {k: v.cpu() for k, v in out.items()}
+    del d
+    torch.cuda.empty_cache()
+    _cache.clear()
+    _cache[name] = (w, x, out)
+    return _cache[name]
+
+
+def query_rows(w):
+    T = w.T
+    pos = sorted({0, 1, 63, 64, 127, 128, 129, 255, 256, T // 2 - 1, T // 2, T - 129, T - 128,
+                  T - 65, T - 64, T - 2, T - 1})
+    heads = sorted({0, w.Hq // 2, w.Hq - 1})
+    return [(b, h, i) for b in sorted({0, w.B - 1}) for h in heads for i in pos if 0 <= i < T]
+
+
+def head_slice(x, b, h0, h1):
+    return x[b:b + 1, h0:h1].double().numpy()
+
+
+@pytest.mark.parametrize("name", ["C3", "C4", "C5"])
+def test_forward_sampled_rows(name):
+    w, x, out = run(name)
+    G = w.Hq // w.Hkv
+    got_o, got_l, ref_o, ref_l = [], [], [], []
+    for b, h, i in query_rows(w):
+        hk = h // G
+        ro, rl = oracle.fwd_rows(head_slice(x["q"], b, h, h + 1), head_slice(x["k"], b, hk, hk + 1),
+                                 head_slice(x["v"], b, hk, hk + 1), [(0, 0, i)], w.scale, w.causal)
+        ref_o.append(ro[0])
+        ref_l.append(rl[0])
+        got_o.append(out["o"][b, h, i].double().numpy())
+        got_l.append(float(out["lse"][b, h, i]))
+    assert_close("O rows", np.array(got_o), np.array(ref_o), w.dtype)
+    assert_lse_close(np.array(got_l), np.array(ref_l), w.dtype)
+
+
+@pytest.mark.parametrize("name", ["C3", "C5"])
+def test_dq_sampled_rows(name):
+    w, x, out = run(name)
+    G = w.Hq // w.Hkv
+    got, ref = [], []
+    for b, h, i in query_rows(w):
+        hk = h // G
+        r = oracle.dq_rows(head_slice(x["q"], b, h, h + 1), head_slice(x["k"], b, hk, hk + 1),
+                           head_slice(x["v"], b, hk, hk + 1), head_slice(x["dout"], b, h, h + 1),
+                           [(0, 0, i)], w.scale, w.causal)
+        ref.append(r[0])
+        got.append(out["dq"][b, h, i].double().numpy())
+    assert_close("dQ rows", np.array(got), np.array(ref), w.dtype)
+
+
+@pytest.mark.parametrize("name", ["C3", "C5"])
+def test_dkdv_sampled_rows(name):
+    w, x, out = run(name)
+    G = w.Hq // w.Hkv
+    T = w.T
+    keys = [T - 1, T - 2, T - 33, T - 64, T - 65, T - 100, T - 128]
+    if name == "C3":  # short enough for early keys too
+        keys += [0, 1, 63, 64, 1000]
+    got_k, got_v, ref_k, ref_v = [], [], [], []
+    for b in sorted({0, w.B - 1}):
+        for hk in sorted({0, w.Hkv - 1}):
+            rk, rv = oracle.dkdv_rows(head_slice(x["q"], b, hk * G, (hk + 1) * G),
+                                      head_slice(x["k"], b, hk, hk + 1),
+                                      head_slice(x["v"], b, hk, hk + 1),
+                                      head_slice(x["dout"], b, hk * G, (hk + 1) * G),
+                                      [(0, 0, j) for j in keys], w.scale, w.causal)
+            ref_k.extend(rk)
+            ref_v.extend(rv)
+            got_k.extend(out["dk"][b, hk, keys].double().numpy())
+            got_v.extend(out["dv"][b, hk, keys].double().numpy())
+    assert_close("dK rows", np.array(got_k), np.array(ref_k), w.dtype)
+    assert_close("dV rows", np.array(got_v), np.array(ref_v), w.dtype)
+
+
+@pytest.mark.parametrize("name", ["C3", "C5"])
+def test_gradient_identities_all_rows(name):
+    w, x, out = run(name)
+    G = w.Hq // w.Hkv
+    dk = out["dk"].double()
+    dv = out["dv"].double()
+    dq = out["dq"].double()
+    q = x["q"].double()
+    k = x["k"].double()
+    do = x["dout"].double()
+    B, Hkv, T, D = dk.shape
+    # sum_j dK_j = 0, relative to the size of dK's columns
+    s = dk.sum(dim=2)
+    col = dk.norm(dim=2)
+    assert float((s.abs() / col).max()) < 2e-2
+    # sum_j dV_j = sum over the group's heads and rows of dO
+    want = do.reshape(B, Hkv, G, T, D).sum(dim=(2, 3))
+    col = dv.norm(dim=2)
+    assert float(((dv.sum(dim=2) - want).abs() / col).max()) < 2e-2
+    # K^T dK = sum over the group's heads of dQ^T Q
+    lhs = torch.einsum("bhtd,bhte->bhde", k, dk)
+    rhs = torch.einsum("bhgtd,bhgte->bhde", dq.reshape(B, Hkv, G, T, D), q.reshape(B, Hkv, G, T, D))
+    rel = float((lhs - rhs).norm() / rhs.norm())
+    assert rel < 1e-2, rel
+    assert torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all()

@@ -21,8 +21,11 @@ ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 # -packed-fp32-ops: keep the compiler from forming packed fp32 arithmetic.
+# -fno-honor-nans: max/min need no NaN canonicalisation of their inputs (NaN
+# inputs are documented to propagate unchecked); infinities are still honoured
+# (the masks use -inf).
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-fno-honor-nans",
          "-I", os.path.join(ROOT, "include"), "-Wall"]
 
 

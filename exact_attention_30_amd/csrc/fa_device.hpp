@@ -122,6 +122,26 @@ __device__ __forceinline__ Frag<float> acc_frag<float>(const f32x16& s, int t)
     return f;
 }
 
+// acc + the sum of a fragment's 8 elements (bf16: four v_dot2 with ones, so
+// the sum is of the rounded values).
+__device__ __forceinline__ float frag_sum(const Frag<bf16>& f, float acc)
+{
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+        const bf16x2 pr = {f.v[e], f.v[e + 1]};
+        acc = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, acc, false);
+    }
+    return acc;
+}
+__device__ __forceinline__ float frag_sum(const Frag<float>& f, float acc)
+{
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += f.v[e];
+    return acc;
+}
+
 // Row permutation of transposed tiles inside each group of 16: swap bits 2, 3.
 __device__ __forceinline__ constexpr int perm16(int r)
 {
@@ -242,6 +262,142 @@ struct TileStage {
         }
     }
 };
+
+// ---------------------------------------------------------------------------
+// Tiles loaded straight from global memory into LDS (global_load_lds_dwordx4:
+// each lane of a wave moves one 16-byte chunk; lane L of an instruction lands
+// at byte 16*L of a 1 KiB LDS block whose base the instruction names).  No
+// registers are involved, so the next tile streams in while the current one
+// is used.  A tile is ROWS rows of D elements kept in natural [row][col]
+// order; the 16-byte chunks of each row are XOR-swizzled so that the reads
+// below hit distinct LDS banks.  Rows past the end of the sequence are loaded
+// as copies of the last row: finite values that the masks then exclude.
+// ---------------------------------------------------------------------------
+template <class E, int D>
+struct RowFmt {
+    static constexpr int CH = 16 / (int)sizeof(E);  // elements per chunk
+    static constexpr int CPR = D / CH;              // chunks per row
+    static_assert(CPR >= 8, "rows must hold at least 8 chunks");
+};
+
+// Swizzle for row-major fragment reads (8 contiguous elements per lane, 32
+// consecutive rows per wave): consecutive rows land on different chunks.
+template <int CPR>
+__device__ __forceinline__ constexpr int swz_rows(int row)
+{
+    return row & ((CPR < 16 ? CPR : 16) - 1);
+}
+// Swizzle for transposed reads (4 consecutive rows x 2 adjacent chunks per
+// 16 lanes): chunk pairs of consecutive rows land on different banks.
+template <int CPR>
+__device__ __forceinline__ constexpr int swz_cols(int row)
+{
+    return 2 * (row & 3);
+}
+
+template <class E, int D, int ROWS, int NT, bool COLS>
+struct DmaTile {
+    using F = RowFmt<E, D>;
+    static constexpr int CPR = F::CPR;
+    static constexpr int NCH = ROWS * CPR;  // chunks per tile
+    static_assert(NCH % NT == 0, "tile chunks must divide over the threads");
+    static constexpr int NI = NCH / NT;     // instructions per thread
+    static constexpr int BYTES = ROWS * D * (int)sizeof(E);
+
+    __device__ __forceinline__ static int swz(int row)
+    {
+        return COLS ? swz_cols<CPR>(row) : swz_rows<CPR>(row);
+    }
+
+    // Byte offset in the tile of element (row, col).
+    __device__ __forceinline__ static int offset(int row, int col)
+    {
+        const int ch = col / F::CH;
+        return (row * CPR + (ch ^ swz(row))) * 16 + (col % F::CH) * (int)sizeof(E);
+    }
+
+    // Issue the loads of rows row0 .. row0+ROWS-1 of a [nrows][D] array.
+    __device__ __forceinline__ static void load(unsigned char* lds_tile, const E* head, int row0,
+                                                int nrows, int tid)
+    {
+        const int lane = tid & 63, w = tid >> 6;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int block = i * (NT / 64) + w;  // 64-chunk block of this instruction
+            const int p = block * 64 + lane;      // chunk position in the tile
+            const int row = p / CPR;
+            const int ch = (p % CPR) ^ swz(row);  // global chunk stored there
+            const int grow = min(row0 + row, nrows - 1);
+            const E* src = head + (size_t)grow * D + ch * F::CH;
+            __builtin_amdgcn_global_load_lds(
+                (const void*)src, (__attribute__((address_space(3))) void*)(lds_tile + block * 1024),
+                16, 0, 0);
+        }
+    }
+};
+
+// Wait for this thread's outstanding global loads (including LDS-bound ones).
+__device__ __forceinline__ void wait_global_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// 8 consecutive elements (cols col .. col+7) of one row of a DMA tile.
+template <class Tile>
+__device__ __forceinline__ Frag<bf16> tile_frag(const unsigned char* t, int row, int col, bf16*)
+{
+    Frag<bf16> f;
+    f.v = *reinterpret_cast<const bf16x8*>(t + Tile::offset(row, col));
+    return f;
+}
+template <class Tile>
+__device__ __forceinline__ Frag<float> tile_frag(const unsigned char* t, int row, int col, float*)
+{
+    Frag<float> f;
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(t + Tile::offset(row, col));
+    const f32x4 hi = *reinterpret_cast<const f32x4*>(t + Tile::offset(row, col + 4));
+    f.v = f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return f;
+}
+
+// A-operand fragment of a transposed product, read from a natural tile:
+// lane (g, c) receives element (rows k(e), column col0 + c) for the 8
+// contraction rows k(e) = rowbase + 8*(e/4) + 4g + e%4, the row order of the
+// accumulator-to-operand reuse described at the top of this file.
+//
+// bf16: two ds_read_b64_tr_b16.  Within each group of 16 lanes that
+// instruction hands lane i element (i % 4) of the 8 bytes addressed by lane
+// 4e + i/4 of the group, for e = 0..3.  Lane 16m + j therefore addresses row
+// rowbase + 8h + 4(m/2) + j/4 at column col0 + 16(m%2) + 4(j%4), and the 16
+// lanes of the group receive 4 rows at 16 consecutive columns.
+template <class Tile>
+__device__ __forceinline__ Frag<bf16> tile_frag_tr(const unsigned char* t, int rowbase, int col0,
+                                                  int lane, bf16*)
+{
+    const int m = lane >> 4, j = lane & 15;
+    const int col = col0 + 16 * (m & 1) + 4 * (j & 3);
+    const int row = rowbase + 4 * (m >> 1) + (j >> 2);
+    // (whole-vector results only: extracting single elements of the
+    // transposed load's result has been miscompiled)
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (__attribute__((address_space(3))) bf16x4*)(t + Tile::offset(row, col)));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (__attribute__((address_space(3))) bf16x4*)(t + Tile::offset(row + 8, col)));
+    Frag<bf16> f;
+    f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return f;
+}
+// fp32: eight single-element reads.
+template <class Tile>
+__device__ __forceinline__ Frag<float> tile_frag_tr(const unsigned char* t, int rowbase, int col0,
+                                                   int lane, float*)
+{
+    const int g = lane >> 5, c = lane & 31;
+    Frag<float> f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int row = rowbase + 8 * (e >> 2) + 4 * g + (e & 3);
+        f.v[e] = *reinterpret_cast<const float*>(t + Tile::offset(row, col0 + c));
+    }
+    return f;
+}
 
 // ---------------------------------------------------------------------------
 // Work mapping.  Workgroups are dispatched round-robin over the 8 XCDs

@@ -15,10 +15,14 @@
 //   * The S^T accumulator is exponentiated in place (exp2 with scale*log2(e)
 //     folded in: the cuTile page's INV_LOG_2 trick) and fed straight back as
 //     the B operand of O^T += V^T P^T, so P never touches LDS.
-//   * K tiles are stored naturally in LDS, V tiles transposed (row-permuted)
-//     so that the V^T fragments are contiguous 16-byte reads.  Tiles are
-//     double-buffered: the next tile's global loads are issued before the
-//     current tile's MFMAs and stored to the other buffer after them.
+//   * K and V tiles move from HBM to LDS with asynchronous global_load_lds
+//     (no register staging), double-buffered: the next tile streams in while
+//     the current one is used.  V^T fragments come from the natural V tile
+//     through the transposing LDS read (ds_read_b64_tr_b16).
+//   * The reference max of a row is only moved when the row max rises by more
+//     than 8 in log2 units, so most tiles skip rescaling O and l; the weights
+//     then stay below 2^8 and the result is unchanged (o and l share the
+//     reference).
 //   * Causal: tiles wholly in the future are never visited; tiles wholly in
 //     the past run without mask code; only diagonal (and, non-causal, the
 //     ragged last) tiles take the per-element mask, derived from the lane's
@@ -33,26 +37,28 @@ template <class E, int D, int NW, int BC>
 struct FwdCfg {
     static constexpr int NT = NW * 64;
     static constexpr int BR = NW * 32;
-    using KStage = TileStage<E, BC, D, NT>;
-    static constexpr int KSZ = BC * KStage::NSTRIDE;  // natural K tile (elements)
-    static constexpr int VSZ = D * KStage::TSTRIDE;   // transposed V tile (elements)
-    static constexpr int BUF = KSZ + VSZ;
-    static constexpr size_t SMEM = 2 * (size_t)BUF * sizeof(E);
+    using KTile = DmaTile<E, D, BC, NT, false>;  // read row-wise (K as A operand)
+    using VTile = DmaTile<E, D, BC, NT, true>;   // read transposed (V^T as A operand)
+    static constexpr int BUF = KTile::BYTES + VTile::BYTES;
+    static constexpr size_t SMEM = 2 * (size_t)BUF;
 };
 
+// Threshold (log2 units) by which a row max must exceed the reference max
+// before the accumulators are rescaled.
+constexpr float kRescaleThreshold = 8.0f;
+
 template <class E, int D, int NW, int BC, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a)
+__global__ __launch_bounds__(NW * 64, sizeof(E) == 2 ? 8 / NW : 1) void fwd_kernel(FwdArgs a)
 {
     using Cfg = FwdCfg<E, D, NW, BC>;
-    using Stage = typename Cfg::KStage;
+    using KT = typename Cfg::KTile;
+    using VT = typename Cfg::VTile;
     constexpr int NT = Cfg::NT, BR = Cfg::BR;
-    constexpr int KS = Stage::NSTRIDE, VS = Stage::TSTRIDE;
     constexpr int NKB = BC / 32;  // 32-key blocks per tile
     constexpr int NDB = D / 32;   // 32-column blocks of the head dimension
     constexpr int NKS = D / 16;   // 16-deep steps over the head dimension
 
-    extern __shared__ __align__(16) unsigned char smem_raw[];
-    E* smem = reinterpret_cast<E*>(smem_raw);
+    extern __shared__ __align__(16) unsigned char smem[];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -71,36 +77,35 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a)
     const E* kh = static_cast<const E*>(a.k) + (size_t)(b * a.Hkv + hk) * a.T * D;
     const E* vh = static_cast<const E*>(a.v) + (size_t)(b * a.Hkv + hk) * a.T * D;
 
-    // B operand of S^T = K Q^T: this lane's query row, 8 columns per step
-    Frag<E> qf[NKS];
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) qf[ks] = global_frag<E>(qh, qrow, a.T, D, 16 * ks + 8 * g);
-
     // key tiles to visit, and how many of them need no mask
     const int kend = CAUSAL ? min(q0 + BR, a.T) : a.T;
     const int nkv = (kend + BC - 1) / BC;
     const int nfull = CAUSAL ? (q0 + 1) / BC : a.T / BC;
 
+    KT::load(smem, kh, 0, a.T, tid);
+    VT::load(smem + KT::BYTES, vh, 0, a.T, tid);
+
+    // B operand of S^T = K Q^T: this lane's query row, 8 columns per step
+    Frag<E> qf[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qf[ks] = global_frag<E>(qh, qrow, a.T, D, 16 * ks + 8 * g);
+
     f32x16 o[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
-    float m = -INFINITY;  // running max of raw scores (q.k), per query
-    float l = 0.f;        // this lane's share of the running sum
+    float mref = -INFINITY;  // reference max, log2 units (scores * scale * log2 e)
+    float l = 0.f;           // this lane's share of the row sum
 
-    Stage kst, vst;
-    kst.load(kh, 0, a.T, tid);
-    vst.load(vh, 0, a.T, tid);
-    kst.store_natural(smem, tid);
-    vst.store_transposed(smem + Cfg::KSZ, tid);
+    wait_global_loads();
     __syncthreads();
 
     for (int j = 0; j < nkv; ++j) {
-        const E* Ks = smem + (j & 1) * Cfg::BUF;
-        const E* Vt = Ks + Cfg::KSZ;
-        const bool more = j + 1 < nkv;
-        if (more) {
-            kst.load(kh, (j + 1) * BC, a.T, tid);
-            vst.load(vh, (j + 1) * BC, a.T, tid);
+        const unsigned char* Ks = smem + (j & 1) * Cfg::BUF;
+        const unsigned char* Vs = Ks + KT::BYTES;
+        if (j + 1 < nkv) {
+            unsigned char* nb = smem + ((j + 1) & 1) * Cfg::BUF;
+            KT::load(nb, kh, (j + 1) * BC, a.T, tid);
+            VT::load(nb + KT::BYTES, vh, (j + 1) * BC, a.T, tid);
         }
 
         // S^T block kb: rows = keys 32kb.., columns = this wave's 32 queries
@@ -110,7 +115,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a)
             s[kb] = f32x16{};
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks)
-                mma(s[kb], lds_frag(Ks + (kb * 32 + c) * KS + 16 * ks + 8 * g), qf[ks]);
+                mma(s[kb], tile_frag<KT>(Ks, kb * 32 + c, 16 * ks + 8 * g, (E*)nullptr), qf[ks]);
         }
 
         if (j >= nfull) {  // diagonal or ragged tile: mask from indices
@@ -124,46 +129,43 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a)
                 }
         }
 
-        // online softmax update for this lane's query
+        // row max of this tile (raw scores), then the lazy reference update
         float mt = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
-        mt = pair_max(mt);
-        const float mnew = fmaxf(m, mt);
-        const float msub = (mnew == -INFINITY) ? 0.f : mnew * a.c;
-        const float alpha = fast_exp2(m * a.c - msub);
-        float rs = 0.f;
+            for (int r = 0; r < 16; r += 2) mt = fmaxf(mt, fmaxf(s[kb][r], s[kb][r + 1]));
+        mt = pair_max(mt) * a.c;
+        const bool need = mt > mref + kRescaleThreshold;
+        if (__builtin_amdgcn_ballot_w64(need)) {
+            const float mnew = need ? mt : mref;
+            const float alpha = fast_exp2(mref - mnew);  // 0 on the first visit
+            l *= alpha;
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
+            for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+            mref = mnew;
+        }
+        const float msub = (mref == -INFINITY) ? 0.f : mref;
+
+        // P = exp2(S c - mref): fp32 row sums (lse keeps full precision), then
+        // rounded for the P V product
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float p = fast_exp2(fmaf(s[kb][r], a.c, -msub));
-                s[kb][r] = p;
-                rs += p;
+                s[kb][r] = fast_exp2(fmaf(s[kb][r], a.c, -msub));
+                l += s[kb][r];
             }
-        l = l * alpha + rs;
-        m = mnew;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) o[db] *= alpha;
-
-        // O^T += V^T P^T, P straight from the S^T registers
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 const Frag<E> pf = acc_frag<E>(s[kb], t);
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)
-                    mma(o[db], lds_frag(Vt + (db * 32 + c) * VS + kb * 32 + 16 * t + 8 * g), pf);
+                    mma(o[db], tile_frag_tr<VT>(Vs, kb * 32 + 16 * t, db * 32, lane, (E*)nullptr), pf);
             }
-
-        if (more) {
-            E* nb = smem + ((j + 1) & 1) * Cfg::BUF;
-            kst.store_natural(nb, tid);
-            vst.store_transposed(nb + Cfg::KSZ, tid);
         }
+
+        wait_global_loads();
         __syncthreads();
     }
 
@@ -191,7 +193,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a)
                 }
             }
         if (g == 0)
-            a.lse[(size_t)(b * a.Hq + hq) * a.T + qrow] = (m * a.c + __log2f(lt)) * kLn2;
+            a.lse[(size_t)(b * a.Hq + hq) * a.T + qrow] = (mref + __log2f(lt)) * kLn2;
     }
 }
 

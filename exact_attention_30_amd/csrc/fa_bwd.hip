@@ -56,36 +56,34 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(PreArgs a)
 // dK, dV.  One workgroup per (batch, kv head, key tile of NW*32 keys); wave w
 // owns keys key0 + 32w .. +31 and keeps K, V of those keys in registers as B
 // operands.  Query tiles of BQ rows (of every query head of the group) stream
-// through LDS in natural layout (A operands of S = Q K^T and dP = dO V^T) and
-// transposed (A operands of dK^T += Q^T dS and dV^T += dO^T P).  S, dP, P and
-// dS live in one 32x32 accumulator layout: rows = queries, columns = keys, so
-// P and dS feed the next products straight from registers.
+// into LDS in natural layout (asynchronous loads, double-buffered); they are
+// read row-wise as A operands of S = Q K^T and dP = dO V^T, and transposed
+// (ds_read_b64_tr_b16) as A operands of dK^T += Q^T dS and dV^T += dO^T P.  S,
+// dP, P and dS share one accumulator layout (rows = queries, columns = keys),
+// so P and dS feed the next products straight from registers.
 // ---------------------------------------------------------------------------
 template <class E, int D, int NW, int BQ>
 struct DkdvCfg {
     static constexpr int NT = NW * 64;
     static constexpr int BK = NW * 32;
-    using Stage = TileStage<E, BQ, D, NT>;
-    static constexpr int NSZ = BQ * Stage::NSTRIDE;       // natural tile (elements)
-    static constexpr int TSZ = D * Stage::TSTRIDE;        // transposed tile (elements)
-    static constexpr int FSZ = 2 * BQ * 4 / (int)sizeof(E);  // L and Delta rows (floats)
-    static constexpr int BUF = 2 * NSZ + 2 * TSZ + FSZ;
-    static constexpr size_t SMEM = 2 * (size_t)BUF * sizeof(E);
+    using QTile = DmaTile<E, D, BQ, NT>;
+    static constexpr int STATS = 2 * BQ * 4;  // L*log2(e) and Delta rows (floats)
+    static constexpr int BUF = 2 * QTile::BYTES + STATS;
+    static constexpr size_t SMEM = 2 * (size_t)BUF;
 };
 
 template <class E, int D, int NW, int BQ, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdArgs a)
+__global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdArgs a)
 {
     using Cfg = DkdvCfg<E, D, NW, BQ>;
-    using Stage = typename Cfg::Stage;
+    using QT = typename Cfg::QTile;
     constexpr int NT = Cfg::NT, BK = Cfg::BK;
-    constexpr int NS = Stage::NSTRIDE, TS = Stage::TSTRIDE;
     constexpr int NQB = BQ / 32;
     constexpr int NDB = D / 32;
     constexpr int NKS = D / 16;
+    static_assert(2 * BQ <= NT, "one thread per L / Delta row");
 
-    extern __shared__ __align__(16) unsigned char smem_raw[];
-    E* smem = reinterpret_cast<E*>(smem_raw);
+    extern __shared__ __align__(16) unsigned char smem[];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -105,6 +103,29 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdArgs a)
     const E* kh = static_cast<const E*>(a.k) + kvoff;
     const E* vh = static_cast<const E*>(a.v) + kvoff;
 
+    // query tiles that see this key tile, for each of the G query heads
+    const int nq = (a.T + BQ - 1) / BQ;
+    const int i0 = CAUSAL ? key0 / BQ : 0;
+    const int niq = nq - i0;
+    const int nit = G * niq;
+
+    // issue the loads of flattened iteration `it` (query head, query tile);
+    // the L / Delta row of this thread (if any) goes to a register
+    auto issue = [&](int it, unsigned char* buf, float& stat) {
+        const int hq = hk * G + it / niq, i = i0 + it % niq;
+        const size_t qoff = (size_t)(b * a.Hq + hq) * a.T * D;
+        QT::load(buf, static_cast<const E*>(a.q) + qoff, i * BQ, a.T, tid);
+        QT::load(buf + QT::BYTES, static_cast<const E*>(a.dout) + qoff, i * BQ, a.T, tid);
+        if (tid < 2 * BQ) {
+            const int qi = min(i * BQ + (tid % BQ), a.T - 1);
+            const size_t off = (size_t)(b * a.Hq + hq) * a.T + qi;
+            stat = tid < BQ ? a.lse[off] * kLog2e : a.delta[off];
+        }
+    };
+
+    float stat = 0.f;
+    issue(0, smem, stat);
+
     Frag<E> kf[NKS], vf[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
@@ -116,67 +137,31 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdArgs a)
 #pragma unroll
     for (int db = 0; db < NDB; ++db) dk[db] = dv[db] = f32x16{};
 
-    // query tiles that see this key tile, for each of the G query heads
-    const int nq = (a.T + BQ - 1) / BQ;
-    const int i0 = CAUSAL ? key0 / BQ : 0;
-    const int niq = nq - i0;
-    const int nit = G * niq;
-
-    Stage qst, dst;
-    auto head_of = [&](int it) { return hk * G + it / niq; };
-    auto tile_of = [&](int it) { return i0 + it % niq; };
-    auto load_tile = [&](int it) {
-        const int hq = head_of(it), i = tile_of(it);
-        const size_t qoff = (size_t)(b * a.Hq + hq) * a.T * D;
-        qst.load(static_cast<const E*>(a.q) + qoff, i * BQ, a.T, tid);
-        dst.load(static_cast<const E*>(a.dout) + qoff, i * BQ, a.T, tid);
-    };
-    // L * log2(e) and Delta of the tile's rows (0 past the end)
-    auto store_tile = [&](int it, E* buf) {
-        const int hq = head_of(it), i = tile_of(it);
-        qst.store_natural(buf, tid);
-        dst.store_natural(buf + Cfg::NSZ, tid);
-        qst.store_transposed(buf + 2 * Cfg::NSZ, tid);
-        dst.store_transposed(buf + 2 * Cfg::NSZ + Cfg::TSZ, tid);
-        float* f = reinterpret_cast<float*>(buf + 2 * Cfg::NSZ + 2 * Cfg::TSZ);
-        if (tid < 2 * BQ) {
-            const int r = tid % BQ, qi = i * BQ + r;
-            const size_t off = (size_t)(b * a.Hq + hq) * a.T + qi;
-            float x = 0.f;
-            if (qi < a.T) x = tid < BQ ? a.lse[off] * kLog2e : a.delta[off];
-            f[tid] = x;
-        }
-    };
-
-    if (nit > 0) {
-        load_tile(0);
-        store_tile(0, smem);
-    }
+    if (tid < 2 * BQ) reinterpret_cast<float*>(smem + 2 * QT::BYTES)[tid] = stat;
+    wait_global_loads();
     __syncthreads();
 
     for (int it = 0; it < nit; ++it) {
-        const E* buf = smem + (it & 1) * Cfg::BUF;
-        const E* Qs = buf;
-        const E* dOs = buf + Cfg::NSZ;
-        const E* Qt = buf + 2 * Cfg::NSZ;
-        const E* dOt = Qt + Cfg::TSZ;
-        const float* Ls = reinterpret_cast<const float*>(dOt + Cfg::TSZ);
+        const unsigned char* Qs = smem + (it & 1) * Cfg::BUF;
+        const unsigned char* dOs = Qs + QT::BYTES;
+        const float* Ls = reinterpret_cast<const float*>(dOs + QT::BYTES);
         const float* Ds = Ls + BQ;
+        unsigned char* nb = smem + ((it + 1) & 1) * Cfg::BUF;
         const bool more = it + 1 < nit;
-        if (more) load_tile(it + 1);
+        if (more) issue(it + 1, nb, stat);
 
-        const int i = tile_of(it);
-        const int qbase = i * BQ;
+        const int qbase = (i0 + it % niq) * BQ;
         const bool need_mask = (CAUSAL && qbase < key0 + BK - 1) || (qbase + BQ > a.T);
 
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
             f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                mma(s, lds_frag(Qs + (qb * 32 + c) * NS + 16 * ks + 8 * g), kf[ks]);
-                mma(dp, lds_frag(dOs + (qb * 32 + c) * NS + 16 * ks + 8 * g), vf[ks]);
-            }
+            for (int ks = 0; ks < NKS; ++ks)
+                mma(s, tile_frag<QT>(Qs, qb * 32 + c, 16 * ks + 8 * g, (E*)nullptr), kf[ks]);
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+                mma(dp, tile_frag<QT>(dOs, qb * 32 + c, 16 * ks + 8 * g, (E*)nullptr), vf[ks]);
             // rows of this lane's registers: queries qb*32 + 8*(r/4) + 4g + r%4
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
@@ -192,8 +177,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdArgs a)
                         const bool vis = (qi < a.T) && (!CAUSAL || krow <= qi);
                         if (!vis) p = 0.f;
                     }
-                    s[r] = p;                      // P
-                    dp[r] = p * (dp[r] - D4[e]);   // dS
+                    s[r] = p;                     // P
+                    dp[r] = p * (dp[r] - D4[e]);  // dS
                 }
             }
 #pragma unroll
@@ -202,14 +187,14 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdArgs a)
                 const Frag<E> sf = acc_frag<E>(dp, t);
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
-                    const int off = (db * 32 + c) * TS + qb * 32 + 16 * t + 8 * g;
-                    mma(dv[db], lds_frag(dOt + off), pf);
-                    mma(dk[db], lds_frag(Qt + off), sf);
+                    mma(dv[db], tile_frag_tr<QT>(dOs, qb * 32 + 16 * t, db * 32, lane, (E*)nullptr), pf);
+                    mma(dk[db], tile_frag_tr<QT>(Qs, qb * 32 + 16 * t, db * 32, lane, (E*)nullptr), sf);
                 }
             }
         }
 
-        if (more) store_tile(it + 1, smem + ((it + 1) & 1) * Cfg::BUF);
+        if (more && tid < 2 * BQ) reinterpret_cast<float*>(nb + 2 * QT::BYTES)[tid] = stat;
+        wait_global_loads();
         __syncthreads();
     }
 
@@ -249,33 +234,29 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(BwdArgs a)
 // dQ.  One workgroup per (batch, query head, query tile of NW*32 rows); wave w
 // owns 32 queries, keeps Q and dO of them in registers and walks key tiles in
 // the forward's order.  S^T = K Q^T and dP^T = V dO^T are formed with keys as
-// rows, so dS^T feeds dQ^T += K^T dS^T from registers; K is staged both
-// naturally and transposed, V naturally.
+// rows, so dS^T feeds dQ^T += K^T dS^T from registers; the K^T operand is read
+// transposed from the natural K tile.
 // ---------------------------------------------------------------------------
 template <class E, int D, int NW, int BC>
 struct DqCfg {
     static constexpr int NT = NW * 64;
     static constexpr int BR = NW * 32;
-    using Stage = TileStage<E, BC, D, NT>;
-    static constexpr int NSZ = BC * Stage::NSTRIDE;
-    static constexpr int TSZ = D * Stage::TSTRIDE;
-    static constexpr int BUF = 2 * NSZ + TSZ;
-    static constexpr size_t SMEM = 2 * (size_t)BUF * sizeof(E);
+    using KTile = DmaTile<E, D, BC, NT>;
+    static constexpr int BUF = 2 * KTile::BYTES;
+    static constexpr size_t SMEM = 2 * (size_t)BUF;
 };
 
 template <class E, int D, int NW, int BC, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdArgs a)
+__global__ __launch_bounds__(NW * 64, sizeof(E) == 2 ? 8 / NW : 1) void bwd_dq_kernel(BwdArgs a)
 {
     using Cfg = DqCfg<E, D, NW, BC>;
-    using Stage = typename Cfg::Stage;
+    using KT = typename Cfg::KTile;
     constexpr int NT = Cfg::NT, BR = Cfg::BR;
-    constexpr int NS = Stage::NSTRIDE, TS = Stage::TSTRIDE;
     constexpr int NKB = BC / 32;
     constexpr int NDB = D / 32;
     constexpr int NKS = D / 16;
 
-    extern __shared__ __align__(16) unsigned char smem_raw[];
-    E* smem = reinterpret_cast<E*>(smem_raw);
+    extern __shared__ __align__(16) unsigned char smem[];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -295,6 +276,13 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdArgs a)
     const E* kh = static_cast<const E*>(a.k) + kvoff;
     const E* vh = static_cast<const E*>(a.v) + kvoff;
 
+    const int kend = CAUSAL ? min(q0 + BR, a.T) : a.T;
+    const int nkv = (kend + BC - 1) / BC;
+    const int nfull = CAUSAL ? (q0 + 1) / BC : a.T / BC;
+
+    KT::load(smem, kh, 0, a.T, tid);
+    KT::load(smem + KT::BYTES, vh, 0, a.T, tid);
+
     Frag<E> qf[NKS], of[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
@@ -308,30 +296,20 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdArgs a)
         Dl = a.delta[r];
     }
 
-    const int kend = CAUSAL ? min(q0 + BR, a.T) : a.T;
-    const int nkv = (kend + BC - 1) / BC;
-    const int nfull = CAUSAL ? (q0 + 1) / BC : a.T / BC;
-
     f32x16 dq[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) dq[db] = f32x16{};
 
-    Stage kst, vst;
-    kst.load(kh, 0, a.T, tid);
-    vst.load(vh, 0, a.T, tid);
-    kst.store_natural(smem, tid);
-    vst.store_natural(smem + Cfg::NSZ, tid);
-    kst.store_transposed(smem + 2 * Cfg::NSZ, tid);
+    wait_global_loads();
     __syncthreads();
 
     for (int j = 0; j < nkv; ++j) {
-        const E* Ks = smem + (j & 1) * Cfg::BUF;
-        const E* Vs = Ks + Cfg::NSZ;
-        const E* Kt = Ks + 2 * Cfg::NSZ;
-        const bool more = j + 1 < nkv;
-        if (more) {
-            kst.load(kh, (j + 1) * BC, a.T, tid);
-            vst.load(vh, (j + 1) * BC, a.T, tid);
+        const unsigned char* Ks = smem + (j & 1) * Cfg::BUF;
+        const unsigned char* Vs = Ks + KT::BYTES;
+        if (j + 1 < nkv) {
+            unsigned char* nb = smem + ((j + 1) & 1) * Cfg::BUF;
+            KT::load(nb, kh, (j + 1) * BC, a.T, tid);
+            KT::load(nb + KT::BYTES, vh, (j + 1) * BC, a.T, tid);
         }
         const bool need_mask = j >= nfull;
 
@@ -339,10 +317,11 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdArgs a)
         for (int kb = 0; kb < NKB; ++kb) {
             f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                mma(s, lds_frag(Ks + (kb * 32 + c) * NS + 16 * ks + 8 * g), qf[ks]);
-                mma(dp, lds_frag(Vs + (kb * 32 + c) * NS + 16 * ks + 8 * g), of[ks]);
-            }
+            for (int ks = 0; ks < NKS; ++ks)
+                mma(s, tile_frag<KT>(Ks, kb * 32 + c, 16 * ks + 8 * g, (E*)nullptr), qf[ks]);
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+                mma(dp, tile_frag<KT>(Vs, kb * 32 + c, 16 * ks + 8 * g, (E*)nullptr), of[ks]);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 float p = fast_exp2(fmaf(s[r], a.c, -L2));
@@ -358,16 +337,11 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(BwdArgs a)
                 const Frag<E> sf = acc_frag<E>(dp, t);
 #pragma unroll
                 for (int db = 0; db < NDB; ++db)
-                    mma(dq[db], lds_frag(Kt + (db * 32 + c) * TS + kb * 32 + 16 * t + 8 * g), sf);
+                    mma(dq[db], tile_frag_tr<KT>(Ks, kb * 32 + 16 * t, db * 32, lane, (E*)nullptr), sf);
             }
         }
 
-        if (more) {
-            E* nb = smem + ((j + 1) & 1) * Cfg::BUF;
-            kst.store_natural(nb, tid);
-            vst.store_natural(nb + Cfg::NSZ, tid);
-            kst.store_transposed(nb + 2 * Cfg::NSZ, tid);
-        }
+        wait_global_loads();
         __syncthreads();
     }
 
@@ -415,7 +389,7 @@ hipError_t launch_bwd_pre(const PreArgs& a, int D, int dtype, hipStream_t stream
 template <class E, int D, bool CAUSAL>
 static hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t stream)
 {
-    constexpr int NW = 4, BQ = (sizeof(E) == 4 && D == 128) ? 32 : 64;
+    constexpr int NW = 4, BQ = 64;
     using Cfg = DkdvCfg<E, D, NW, BQ>;
     static_assert(Cfg::SMEM <= 160 * 1024, "LDS budget");
     auto kern = bwd_dkdv_kernel<E, D, NW, BQ, CAUSAL>;
@@ -441,7 +415,7 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, int D, int dtype, bool causal, hipS
 template <class E, int D, bool CAUSAL>
 static hipError_t launch_dq_t(const BwdArgs& a, hipStream_t stream)
 {
-    constexpr int NW = 4, BC = (sizeof(E) == 4 && D == 128) ? 32 : 64;
+    constexpr int NW = 4, BC = 64;
     using Cfg = DqCfg<E, D, NW, BC>;
     static_assert(Cfg::SMEM <= 160 * 1024, "LDS budget");
     auto kern = bwd_dq_kernel<E, D, NW, BC, CAUSAL>;

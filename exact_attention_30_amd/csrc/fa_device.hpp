@@ -280,22 +280,22 @@ struct RowFmt {
     static_assert(CPR >= 8, "rows must hold at least 8 chunks");
 };
 
-// Swizzle for row-major fragment reads (8 contiguous elements per lane, 32
-// consecutive rows per wave): consecutive rows land on different chunks.
+// Chunk swizzle of tile rows.  Two read patterns must both spread over the
+// LDS banks, whether a cycle serves 128 or 256 bytes:
+//   * fragment reads: consecutive rows, one chunk each (ds_read_b128);
+//   * transposed reads: 4 aligned consecutive rows, 2 or 4 adjacent chunks
+//     (an aligned block) per 16 or 32 lanes (ds_read_b64_tr_b16).
+// With i = r % 4, f(r) = 4i + 2(((i/2) ^ (r/8)) % 2) + (r/4) % 2 is distinct
+// over 16 consecutive rows (and over 8 modulo 8), while over 4 aligned rows
+// both f/2 % 4 and f/4 % 4 are distinct.  Rows of 8 chunks use it modulo 8.
 template <int CPR>
-__device__ __forceinline__ constexpr int swz_rows(int row)
+__device__ __forceinline__ constexpr int swz(int row)
 {
-    return row & ((CPR < 16 ? CPR : 16) - 1);
-}
-// Swizzle for transposed reads (4 consecutive rows x 2 adjacent chunks per
-// 16 lanes): chunk pairs of consecutive rows land on different banks.
-template <int CPR>
-__device__ __forceinline__ constexpr int swz_cols(int row)
-{
-    return 2 * (row & 3);
+    const int i = row & 3;
+    return (4 * i + 2 * (((i >> 1) ^ (row >> 3)) & 1) + ((row >> 2) & 1)) & (CPR - 1);
 }
 
-template <class E, int D, int ROWS, int NT, bool COLS>
+template <class E, int D, int ROWS, int NT>
 struct DmaTile {
     using F = RowFmt<E, D>;
     static constexpr int CPR = F::CPR;
@@ -304,16 +304,11 @@ struct DmaTile {
     static constexpr int NI = NCH / NT;     // instructions per thread
     static constexpr int BYTES = ROWS * D * (int)sizeof(E);
 
-    __device__ __forceinline__ static int swz(int row)
-    {
-        return COLS ? swz_cols<CPR>(row) : swz_rows<CPR>(row);
-    }
-
     // Byte offset in the tile of element (row, col).
     __device__ __forceinline__ static int offset(int row, int col)
     {
         const int ch = col / F::CH;
-        return (row * CPR + (ch ^ swz(row))) * 16 + (col % F::CH) * (int)sizeof(E);
+        return (row * CPR + (ch ^ fa::swz<CPR>(row))) * 16 + (col % F::CH) * (int)sizeof(E);
     }
 
     // Issue the loads of rows row0 .. row0+ROWS-1 of a [nrows][D] array.
@@ -326,7 +321,7 @@ struct DmaTile {
             const int block = i * (NT / 64) + w;  // 64-chunk block of this instruction
             const int p = block * 64 + lane;      // chunk position in the tile
             const int row = p / CPR;
-            const int ch = (p % CPR) ^ swz(row);  // global chunk stored there
+            const int ch = (p % CPR) ^ fa::swz<CPR>(row);  // global chunk stored there
             const int grow = min(row0 + row, nrows - 1);
             const E* src = head + (size_t)grow * D + ch * F::CH;
             __builtin_amdgcn_global_load_lds(

@@ -37,8 +37,8 @@ template <class E, int D, int NW, int BC>
 struct FwdCfg {
     static constexpr int NT = NW * 64;
     static constexpr int BR = NW * 32;
-    using KTile = DmaTile<E, D, BC, NT, false>;  // read row-wise (K as A operand)
-    using VTile = DmaTile<E, D, BC, NT, true>;   // read transposed (V^T as A operand)
+    using KTile = DmaTile<E, D, BC, NT>;  // read row-wise (K as A operand)
+    using VTile = DmaTile<E, D, BC, NT>;  // read transposed (V^T as A operand)
     static constexpr int BUF = KTile::BYTES + VTile::BYTES;
     static constexpr size_t SMEM = 2 * (size_t)BUF;
 };

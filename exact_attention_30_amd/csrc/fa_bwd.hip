@@ -54,29 +54,33 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(PreArgs a)
 
 // ---------------------------------------------------------------------------
 // dK, dV.  One workgroup per (batch, kv head, key tile of NW*32 keys); wave w
-// owns keys key0 + 32w .. +31 and keeps K, V of those keys in registers as B
-// operands.  Query tiles of BQ rows (of every query head of the group) stream
-// into LDS in natural layout (asynchronous loads, double-buffered); they are
-// read row-wise as A operands of S = Q K^T and dP = dO V^T, and transposed
-// (ds_read_b64_tr_b16) as A operands of dK^T += Q^T dS and dV^T += dO^T P.  S,
-// dP, P and dS share one accumulator layout (rows = queries, columns = keys),
-// so P and dS feed the next products straight from registers.
+// owns keys key0 + 32w .. +31.  K of those keys stays in registers (B operand
+// of S = Q K^T); V of the workgroup's keys is loaded once into LDS and read as
+// the B operand of dP = dO V^T, which keeps the kernel within the register
+// budget of two waves per SIMD.  Query tiles of BQ rows (of every query head
+// of the group) stream into LDS in natural layout (asynchronous loads,
+// double-buffered); they are read row-wise as A operands of S and dP, and
+// transposed (ds_read_b64_tr_b16) as A operands of dK^T += Q^T dS and
+// dV^T += dO^T P.  S, dP, P and dS share one accumulator layout (rows =
+// queries, columns = keys), so P and dS feed those products from registers.
 // ---------------------------------------------------------------------------
 template <class E, int D, int NW, int BQ>
 struct DkdvCfg {
     static constexpr int NT = NW * 64;
     static constexpr int BK = NW * 32;
     using QTile = DmaTile<E, D, BQ, NT>;
+    using VTile = DmaTile<E, D, BK, NT>;
     static constexpr int STATS = 2 * BQ * 4;  // L*log2(e) and Delta rows (floats)
     static constexpr int BUF = 2 * QTile::BYTES + STATS;
-    static constexpr size_t SMEM = 2 * (size_t)BUF;
+    static constexpr size_t SMEM = (size_t)VTile::BYTES + 2 * (size_t)BUF;
 };
 
 template <class E, int D, int NW, int BQ, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdArgs a)
+__global__ __launch_bounds__(NW * 64, sizeof(E) == 2 ? 8 / NW : 1) void bwd_dkdv_kernel(BwdArgs a)
 {
     using Cfg = DkdvCfg<E, D, NW, BQ>;
     using QT = typename Cfg::QTile;
+    using VT = typename Cfg::VTile;
     constexpr int NT = Cfg::NT, BK = Cfg::BK;
     constexpr int NQB = BQ / 32;
     constexpr int NDB = D / 32;
@@ -84,6 +88,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdArgs a)
     static_assert(2 * BQ <= NT, "one thread per L / Delta row");
 
     extern __shared__ __align__(16) unsigned char smem[];
+    unsigned char* Vs = smem;
+    unsigned char* qbuf = smem + VT::BYTES;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -123,30 +129,28 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdArgs a)
         }
     };
 
+    VT::load(Vs, vh, key0, a.T, tid);
     float stat = 0.f;
-    issue(0, smem, stat);
+    issue(0, qbuf, stat);
 
-    Frag<E> kf[NKS], vf[NKS];
+    Frag<E> kf[NKS];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-        kf[ks] = global_frag<E>(kh, krow, a.T, D, 16 * ks + 8 * g);
-        vf[ks] = global_frag<E>(vh, krow, a.T, D, 16 * ks + 8 * g);
-    }
+    for (int ks = 0; ks < NKS; ++ks) kf[ks] = global_frag<E>(kh, krow, a.T, D, 16 * ks + 8 * g);
 
     f32x16 dk[NDB], dv[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) dk[db] = dv[db] = f32x16{};
 
-    if (tid < 2 * BQ) reinterpret_cast<float*>(smem + 2 * QT::BYTES)[tid] = stat;
+    if (tid < 2 * BQ) reinterpret_cast<float*>(qbuf + 2 * QT::BYTES)[tid] = stat;
     wait_global_loads();
     __syncthreads();
 
     for (int it = 0; it < nit; ++it) {
-        const unsigned char* Qs = smem + (it & 1) * Cfg::BUF;
+        const unsigned char* Qs = qbuf + (it & 1) * Cfg::BUF;
         const unsigned char* dOs = Qs + QT::BYTES;
         const float* Ls = reinterpret_cast<const float*>(dOs + QT::BYTES);
         const float* Ds = Ls + BQ;
-        unsigned char* nb = smem + ((it + 1) & 1) * Cfg::BUF;
+        unsigned char* nb = qbuf + ((it + 1) & 1) * Cfg::BUF;
         const bool more = it + 1 < nit;
         if (more) issue(it + 1, nb, stat);
 
@@ -161,7 +165,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdArgs a)
                 mma(s, tile_frag<QT>(Qs, qb * 32 + c, 16 * ks + 8 * g, (E*)nullptr), kf[ks]);
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks)
-                mma(dp, tile_frag<QT>(dOs, qb * 32 + c, 16 * ks + 8 * g, (E*)nullptr), vf[ks]);
+                mma(dp, tile_frag<QT>(dOs, qb * 32 + c, 16 * ks + 8 * g, (E*)nullptr),
+                    tile_frag<VT>(Vs, w * 32 + c, 16 * ks + 8 * g, (E*)nullptr));
             // rows of this lane's registers: queries qb*32 + 8*(r/4) + 4g + r%4
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
@@ -389,7 +394,7 @@ hipError_t launch_bwd_pre(const PreArgs& a, int D, int dtype, hipStream_t stream
 template <class E, int D, bool CAUSAL>
 static hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t stream)
 {
-    constexpr int NW = 4, BQ = 64;
+    constexpr int NW = 4, BQ = 32;
     using Cfg = DkdvCfg<E, D, NW, BQ>;
     static_assert(Cfg::SMEM <= 160 * 1024, "LDS budget");
     auto kern = bwd_dkdv_kernel<E, D, NW, BQ, CAUSAL>;

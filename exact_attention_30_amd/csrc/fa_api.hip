@@ -24,6 +24,10 @@ fa_status check_common(int B, int Hq, int Hkv, int T, int D, fa_dtype dt)
     if (rows > 0x7fffffffLL) return FA_ERR_SHAPE;
     if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
     if (dt != FA_BF16 && dt != FA_FP32) return FA_ERR_UNSUPPORTED;
+    // one head of one tensor is addressed through a buffer resource whose
+    // byte range is a signed 32-bit count
+    const long long head_bytes = (long long)T * D * (dt == FA_BF16 ? 2 : 4);
+    if (head_bytes > 0x7fffffffLL) return FA_ERR_SHAPE;
     return FA_OK;
 }
 

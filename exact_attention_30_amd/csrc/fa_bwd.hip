@@ -13,6 +13,8 @@
 // order in which workgroups run.  With grouped-query attention the dK/dV
 // kernel also loops over the query heads that share the kv head, which keeps
 // the group sum inside one workgroup.
+#include <type_traits>
+
 #include "fa_device.hpp"
 #include "fa_kernels.hpp"
 
@@ -81,11 +83,11 @@ __global__ __launch_bounds__(NW * 64, sizeof(E) == 2 ? 8 / NW : 1) void bwd_dkdv
     using Cfg = DkdvCfg<E, D, NW, BQ>;
     using QT = typename Cfg::QTile;
     using VT = typename Cfg::VTile;
-    constexpr int NT = Cfg::NT, BK = Cfg::BK;
+    constexpr int BK = Cfg::BK;
     constexpr int NQB = BQ / 32;
     constexpr int NDB = D / 32;
     constexpr int NKS = D / 16;
-    static_assert(2 * BQ <= NT, "one thread per L / Delta row");
+    static_assert(2 * BQ <= Cfg::NT, "one thread per L / Delta row");
 
     extern __shared__ __align__(16) unsigned char smem[];
     unsigned char* Vs = smem;
@@ -115,13 +117,15 @@ __global__ __launch_bounds__(NW * 64, sizeof(E) == 2 ? 8 / NW : 1) void bwd_dkdv
     const int niq = nq - i0;
     const int nit = G * niq;
 
+    QT qdma;
+    qdma.init(tid);
     // issue the loads of flattened iteration `it` (query head, query tile);
     // the L / Delta row of this thread (if any) goes to a register
     auto issue = [&](int it, unsigned char* buf, float& stat) {
         const int hq = hk * G + it / niq, i = i0 + it % niq;
         const size_t qoff = (size_t)(b * a.Hq + hq) * a.T * D;
-        QT::load(buf, static_cast<const E*>(a.q) + qoff, i * BQ, a.T, tid);
-        QT::load(buf + QT::BYTES, static_cast<const E*>(a.dout) + qoff, i * BQ, a.T, tid);
+        qdma.load(buf, static_cast<const E*>(a.q) + qoff, i * BQ, a.T, w);
+        qdma.load(buf + QT::BYTES, static_cast<const E*>(a.dout) + qoff, i * BQ, a.T, w);
         if (tid < 2 * BQ) {
             const int qi = min(i * BQ + (tid % BQ), a.T - 1);
             const size_t off = (size_t)(b * a.Hq + hq) * a.T + qi;
@@ -129,13 +133,25 @@ __global__ __launch_bounds__(NW * 64, sizeof(E) == 2 ? 8 / NW : 1) void bwd_dkdv
         }
     };
 
-    VT::load(Vs, vh, key0, a.T, tid);
+    {
+        VT vdma;
+        vdma.init(tid);
+        vdma.load(Vs, vh, key0, a.T, w);
+    }
     float stat = 0.f;
     issue(0, qbuf, stat);
 
     Frag<E> kf[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) kf[ks] = global_frag<E>(kh, krow, a.T, D, 16 * ks + 8 * g);
+
+    // Q and dO rows (A of S, dP); the V tile has the same row format, so the
+    // same offsets read V rows w*32 + c (B of dP)
+    RowReader<QT, E, D> qrd;
+    qrd.init(c, g);
+    static_assert(QT::ROWBYTES == VT::ROWBYTES, "Q and V tiles share a row format");
+    TrReader<QT, E, D> trd;   // Q^T and dO^T (A of dK^T, dV^T)
+    trd.init(lane);
 
     f32x16 dk[NDB], dv[NDB];
 #pragma unroll
@@ -146,11 +162,12 @@ __global__ __launch_bounds__(NW * 64, sizeof(E) == 2 ? 8 / NW : 1) void bwd_dkdv
     __syncthreads();
 
     for (int it = 0; it < nit; ++it) {
-        const unsigned char* Qs = qbuf + (it & 1) * Cfg::BUF;
+        const int BI = it & 1;
+        const unsigned char* Qs = qbuf + BI * Cfg::BUF;
         const unsigned char* dOs = Qs + QT::BYTES;
         const float* Ls = reinterpret_cast<const float*>(dOs + QT::BYTES);
         const float* Ds = Ls + BQ;
-        unsigned char* nb = qbuf + ((it + 1) & 1) * Cfg::BUF;
+        unsigned char* nb = qbuf + (1 - BI) * Cfg::BUF;
         const bool more = it + 1 < nit;
         if (more) issue(it + 1, nb, stat);
 
@@ -161,12 +178,9 @@ __global__ __launch_bounds__(NW * 64, sizeof(E) == 2 ? 8 / NW : 1) void bwd_dkdv
         for (int qb = 0; qb < NQB; ++qb) {
             f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
-                mma(s, tile_frag<QT>(Qs, qb * 32 + c, 16 * ks + 8 * g, (E*)nullptr), kf[ks]);
+            for (int ks = 0; ks < NKS; ++ks) mma(s, qrd.frag(Qs, qb * 32, ks), kf[ks]);
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
-                mma(dp, tile_frag<QT>(dOs, qb * 32 + c, 16 * ks + 8 * g, (E*)nullptr),
-                    tile_frag<VT>(Vs, w * 32 + c, 16 * ks + 8 * g, (E*)nullptr));
+            for (int ks = 0; ks < NKS; ++ks) mma(dp, qrd.frag(dOs, qb * 32, ks), qrd.frag(Vs, w * 32, ks));
             // rows of this lane's registers: queries qb*32 + 8*(r/4) + 4g + r%4
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
@@ -192,8 +206,8 @@ __global__ __launch_bounds__(NW * 64, sizeof(E) == 2 ? 8 / NW : 1) void bwd_dkdv
                 const Frag<E> sf = acc_frag<E>(dp, t);
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
-                    mma(dv[db], tile_frag_tr<QT>(dOs, qb * 32 + 16 * t, db * 32, lane, (E*)nullptr), pf);
-                    mma(dk[db], tile_frag_tr<QT>(Qs, qb * 32 + 16 * t, db * 32, lane, (E*)nullptr), sf);
+                    mma(dv[db], trd.frag(dOs, qb * 32 + 16 * t, db), pf);
+                    mma(dk[db], trd.frag(Qs, qb * 32 + 16 * t, db), sf);
                 }
             }
         }
@@ -246,8 +260,8 @@ template <class E, int D, int NW, int BC>
 struct DqCfg {
     static constexpr int NT = NW * 64;
     static constexpr int BR = NW * 32;
-    using KTile = DmaTile<E, D, BC, NT>;
-    static constexpr int BUF = 2 * KTile::BYTES;
+    using Tile = DmaTile<E, D, BC, NT>;
+    static constexpr int BUF = 2 * Tile::BYTES;
     static constexpr size_t SMEM = 2 * (size_t)BUF;
 };
 
@@ -255,8 +269,8 @@ template <class E, int D, int NW, int BC, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, sizeof(E) == 2 ? 8 / NW : 1) void bwd_dq_kernel(BwdArgs a)
 {
     using Cfg = DqCfg<E, D, NW, BC>;
-    using KT = typename Cfg::KTile;
-    constexpr int NT = Cfg::NT, BR = Cfg::BR;
+    using Tile = typename Cfg::Tile;
+    constexpr int BR = Cfg::BR;
     constexpr int NKB = BC / 32;
     constexpr int NDB = D / 32;
     constexpr int NKS = D / 16;
@@ -285,8 +299,15 @@ __global__ __launch_bounds__(NW * 64, sizeof(E) == 2 ? 8 / NW : 1) void bwd_dq_k
     const int nkv = (kend + BC - 1) / BC;
     const int nfull = CAUSAL ? (q0 + 1) / BC : a.T / BC;
 
-    KT::load(smem, kh, 0, a.T, tid);
-    KT::load(smem + KT::BYTES, vh, 0, a.T, tid);
+    Tile dma;
+    dma.init(tid);
+    dma.load(smem, kh, 0, a.T, w);
+    dma.load(smem + Tile::BYTES, vh, 0, a.T, w);
+
+    RowReader<Tile, E, D> rrd;  // K and V rows (A of S^T, dP^T)
+    rrd.init(c, g);
+    TrReader<Tile, E, D> trd;   // K^T (A of dQ^T)
+    trd.init(lane);
 
     Frag<E> qf[NKS], of[NKS];
 #pragma unroll
@@ -308,13 +329,14 @@ __global__ __launch_bounds__(NW * 64, sizeof(E) == 2 ? 8 / NW : 1) void bwd_dq_k
     wait_global_loads();
     __syncthreads();
 
-    for (int j = 0; j < nkv; ++j) {
-        const unsigned char* Ks = smem + (j & 1) * Cfg::BUF;
-        const unsigned char* Vs = Ks + KT::BYTES;
+    auto step = [&](auto bufi, int j) {
+        constexpr int BI = decltype(bufi)::value;
+        const unsigned char* Ks = smem + BI * Cfg::BUF;
+        const unsigned char* Vs = Ks + Tile::BYTES;
         if (j + 1 < nkv) {
-            unsigned char* nb = smem + ((j + 1) & 1) * Cfg::BUF;
-            KT::load(nb, kh, (j + 1) * BC, a.T, tid);
-            KT::load(nb + KT::BYTES, vh, (j + 1) * BC, a.T, tid);
+            unsigned char* nb = smem + (1 - BI) * Cfg::BUF;
+            dma.load(nb, kh, (j + 1) * BC, a.T, w);
+            dma.load(nb + Tile::BYTES, vh, (j + 1) * BC, a.T, w);
         }
         const bool need_mask = j >= nfull;
 
@@ -322,11 +344,9 @@ __global__ __launch_bounds__(NW * 64, sizeof(E) == 2 ? 8 / NW : 1) void bwd_dq_k
         for (int kb = 0; kb < NKB; ++kb) {
             f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
-                mma(s, tile_frag<KT>(Ks, kb * 32 + c, 16 * ks + 8 * g, (E*)nullptr), qf[ks]);
+            for (int ks = 0; ks < NKS; ++ks) mma(s, rrd.frag(Ks, kb * 32, ks), qf[ks]);
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
-                mma(dp, tile_frag<KT>(Vs, kb * 32 + c, 16 * ks + 8 * g, (E*)nullptr), of[ks]);
+            for (int ks = 0; ks < NKS; ++ks) mma(dp, rrd.frag(Vs, kb * 32, ks), of[ks]);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 float p = fast_exp2(fmaf(s[r], a.c, -L2));
@@ -341,13 +361,17 @@ __global__ __launch_bounds__(NW * 64, sizeof(E) == 2 ? 8 / NW : 1) void bwd_dq_k
             for (int t = 0; t < 2; ++t) {
                 const Frag<E> sf = acc_frag<E>(dp, t);
 #pragma unroll
-                for (int db = 0; db < NDB; ++db)
-                    mma(dq[db], tile_frag_tr<KT>(Ks, kb * 32 + 16 * t, db * 32, lane, (E*)nullptr), sf);
+                for (int db = 0; db < NDB; ++db) mma(dq[db], trd.frag(Ks, kb * 32 + 16 * t, db), sf);
             }
         }
 
         wait_global_loads();
         __syncthreads();
+    };
+
+    for (int j = 0; j < nkv; j += 2) {
+        step(std::integral_constant<int, 0>{}, j);
+        if (j + 1 < nkv) step(std::integral_constant<int, 1>{}, j + 1);
     }
 
     if (qrow < a.T) {
@@ -391,10 +415,15 @@ hipError_t launch_bwd_pre(const PreArgs& a, int D, int dtype, hipStream_t stream
     return D == 64 ? launch_pre_t<float, 64>(a, stream) : launch_pre_t<float, 128>(a, stream);
 }
 
+// Tile shapes of the backward: dK/dV workgroups own NW*32 keys and stream BQ
+// query rows per step; dQ workgroups own NW*32 queries and stream BC keys.
+constexpr int kDkdvNW = 4, kDkdvBQ = 32;
+constexpr int kDqNW = 4, kDqBC = 64;
+
 template <class E, int D, bool CAUSAL>
 static hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t stream)
 {
-    constexpr int NW = 4, BQ = 32;
+    constexpr int NW = kDkdvNW, BQ = kDkdvBQ;
     using Cfg = DkdvCfg<E, D, NW, BQ>;
     static_assert(Cfg::SMEM <= 160 * 1024, "LDS budget");
     auto kern = bwd_dkdv_kernel<E, D, NW, BQ, CAUSAL>;
@@ -420,7 +449,7 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, int D, int dtype, bool causal, hipS
 template <class E, int D, bool CAUSAL>
 static hipError_t launch_dq_t(const BwdArgs& a, hipStream_t stream)
 {
-    constexpr int NW = 4, BC = 64;
+    constexpr int NW = kDqNW, BC = kDqBC;
     using Cfg = DqCfg<E, D, NW, BC>;
     static_assert(Cfg::SMEM <= 160 * 1024, "LDS budget");
     auto kern = bwd_dq_kernel<E, D, NW, BC, CAUSAL>;
@@ -442,5 +471,20 @@ hipError_t launch_bwd_dq(const BwdArgs& a, int D, int dtype, bool causal, hipStr
     if (D == 64) return causal ? launch_dq_t<float, 64, true>(a, stream) : launch_dq_t<float, 64, false>(a, stream);
     return causal ? launch_dq_t<float, 128, true>(a, stream) : launch_dq_t<float, 128, false>(a, stream);
 }
+
+// Every kernel variant is instantiated explicitly: referencing a kernel
+// template only from a launcher has left some instantiations without their
+// host-side handle.
+#define FA_BWD_INST(E, D)                                                            \
+    template __global__ void bwd_pre_kernel<E, D>(PreArgs);                          \
+    template __global__ void bwd_dkdv_kernel<E, D, kDkdvNW, kDkdvBQ, true>(BwdArgs); \
+    template __global__ void bwd_dkdv_kernel<E, D, kDkdvNW, kDkdvBQ, false>(BwdArgs); \
+    template __global__ void bwd_dq_kernel<E, D, kDqNW, kDqBC, true>(BwdArgs);       \
+    template __global__ void bwd_dq_kernel<E, D, kDqNW, kDqBC, false>(BwdArgs);
+FA_BWD_INST(bf16, 64)
+FA_BWD_INST(bf16, 128)
+FA_BWD_INST(float, 64)
+FA_BWD_INST(float, 128)
+#undef FA_BWD_INST
 
 }  // namespace fa

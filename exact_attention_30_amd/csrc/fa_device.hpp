@@ -36,6 +36,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
+// Word 3 of a raw buffer resource on gfx9-family chips (no swizzle, dword
+// data format); with a zero stride, reads at or past num_records return 0.
+constexpr int kBufferFlags = 0x00020000;
 constexpr float kLn2 = 0.6931471805599453f;
 
 template <class E>
@@ -58,22 +61,6 @@ __device__ __forceinline__ void mma(f32x16& acc, const Frag<float>& a, const Fra
 {
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.v[e], b.v[e], acc, 0, 0, 0);
-}
-
-// 8 contiguous elements from LDS (16-byte aligned).
-__device__ __forceinline__ Frag<bf16> lds_frag(const bf16* p)
-{
-    Frag<bf16> f;
-    f.v = *reinterpret_cast<const bf16x8*>(p);
-    return f;
-}
-__device__ __forceinline__ Frag<float> lds_frag(const float* p)
-{
-    Frag<float> f;
-    const f32x4 lo = *reinterpret_cast<const f32x4*>(p);
-    const f32x4 hi = *reinterpret_cast<const f32x4*>(p + 4);
-    f.v = f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    return f;
 }
 
 // 8 contiguous elements of row `row` of a [nrows][D] global array, or zeros
@@ -169,101 +156,6 @@ __device__ __forceinline__ float pair_sum(float x)
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------------------
-// Tile staging: global [nrows][D] rows row0 .. row0+ROWS-1 -> LDS.
-// Loads go to registers first (issued early), stores to LDS come later, so a
-// tile can be fetched while the previous one is being used.
-//
-// Work unit: 4 consecutive rows x one 16-byte column chunk (CH elements).
-// Both layouts can be written from the same registers:
-//   natural    lds[r][col]          row stride D + CH   (16-byte pad)
-//   transposed lds[col][perm16(r)]  row stride ROWS + CH
-// Rows past the end of the sequence are loaded as zeros.
-// ---------------------------------------------------------------------------
-template <class E, int ROWS, int D, int NT>
-struct TileStage {
-    static constexpr int CH = 16 / (int)sizeof(E);
-    static constexpr int RG = ROWS / 4;  // row groups
-    static constexpr int DG = D / CH;    // column chunks
-    static constexpr int NU = RG * DG;   // units per tile
-    static constexpr int N = (NU + NT - 1) / NT;  // units per thread (last may be idle)
-    static constexpr bool EVEN = (NU % NT) == 0;
-    static constexpr int NSTRIDE = D + CH;
-    static constexpr int TSTRIDE = ROWS + CH;
-
-    u32x4 buf[N][4];
-
-    // unit u -> (row group, column chunk); consecutive threads take
-    // consecutive row groups so that transposed stores of a wave fill whole
-    // LDS rows.
-    __device__ __forceinline__ static void unit(int u, int& rg, int& dg)
-    {
-        rg = u % RG;
-        dg = u / RG;
-    }
-
-    __device__ __forceinline__ void load(const E* head, int row0, int nrows, int tid)
-    {
-#pragma unroll
-        for (int i = 0; i < N; ++i) {
-            if (!EVEN && i * NT + tid >= NU) break;
-            int rg, dg;
-            unit(i * NT + tid, rg, dg);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int row = row0 + 4 * rg + c;
-                if (row < nrows)
-                    buf[i][c] = *reinterpret_cast<const u32x4*>(head + (size_t)row * D + dg * CH);
-                else
-                    buf[i][c] = u32x4{0u, 0u, 0u, 0u};
-            }
-        }
-    }
-
-    __device__ __forceinline__ void store_natural(E* lds, int tid) const
-    {
-#pragma unroll
-        for (int i = 0; i < N; ++i) {
-            if (!EVEN && i * NT + tid >= NU) break;
-            int rg, dg;
-            unit(i * NT + tid, rg, dg);
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-                *reinterpret_cast<u32x4*>(lds + (4 * rg + c) * NSTRIDE + dg * CH) = buf[i][c];
-        }
-    }
-
-    __device__ __forceinline__ void store_transposed(E* lds, int tid) const
-    {
-#pragma unroll
-        for (int i = 0; i < N; ++i) {
-            if (!EVEN && i * NT + tid >= NU) break;
-            int rg, dg;
-            unit(i * NT + tid, rg, dg);
-            const int pos = perm16(4 * rg);  // the 4 rows stay contiguous
-            if constexpr (sizeof(E) == 2) {
-#pragma unroll
-                for (int e = 0; e < CH; ++e) {
-                    // element e of each of the 4 rows: 16-bit halves of dword e/2
-                    const int dw = e >> 1;
-                    const int sh = (e & 1) * 16;
-                    const uint32_t r0 = (buf[i][0][dw] >> sh) & 0xffffu;
-                    const uint32_t r1 = (buf[i][1][dw] >> sh) & 0xffffu;
-                    const uint32_t r2 = (buf[i][2][dw] >> sh) & 0xffffu;
-                    const uint32_t r3 = (buf[i][3][dw] >> sh) & 0xffffu;
-                    *reinterpret_cast<u32x2*>(lds + (dg * CH + e) * TSTRIDE + pos) =
-                        u32x2{r0 | (r1 << 16), r2 | (r3 << 16)};
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < CH; ++e)
-                    *reinterpret_cast<u32x4*>(lds + (dg * CH + e) * TSTRIDE + pos) =
-                        u32x4{buf[i][0][e], buf[i][1][e], buf[i][2][e], buf[i][3][e]};
-            }
-        }
-    }
-};
-
-// ---------------------------------------------------------------------------
 // Tiles loaded straight from global memory into LDS (global_load_lds_dwordx4:
 // each lane of a wave moves one 16-byte chunk; lane L of an instruction lands
 // at byte 16*L of a 1 KiB LDS block whose base the instruction names).  No
@@ -301,98 +193,146 @@ struct DmaTile {
     static constexpr int CPR = F::CPR;
     static constexpr int NCH = ROWS * CPR;  // chunks per tile
     static_assert(NCH % NT == 0, "tile chunks must divide over the threads");
+    static_assert(ROWS % 16 == 0, "tiles hold whole swizzle periods");
     static constexpr int NI = NCH / NT;     // instructions per thread
     static constexpr int BYTES = ROWS * D * (int)sizeof(E);
+    static constexpr int ROWBYTES = CPR * 16;
 
     // Byte offset in the tile of element (row, col).
-    __device__ __forceinline__ static int offset(int row, int col)
+    __device__ __forceinline__ static constexpr int offset(int row, int col)
     {
         const int ch = col / F::CH;
         return (row * CPR + (ch ^ fa::swz<CPR>(row))) * 16 + (col % F::CH) * (int)sizeof(E);
     }
 
-    // Issue the loads of rows row0 .. row0+ROWS-1 of a [nrows][D] array.
-    __device__ __forceinline__ static void load(unsigned char* lds_tile, const E* head, int row0,
-                                                int nrows, int tid)
+    // Per-thread byte offsets (into the global rows of a tile) of the chunks
+    // this thread moves; the same for every tile.
+    uint32_t voff[NI];
+
+    __device__ __forceinline__ void init(int tid)
     {
         const int lane = tid & 63, w = tid >> 6;
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            const int block = i * (NT / 64) + w;  // 64-chunk block of this instruction
-            const int p = block * 64 + lane;      // chunk position in the tile
+            const int p = (i * (NT / 64) + w) * 64 + lane;  // chunk position in the tile
             const int row = p / CPR;
-            const int ch = (p % CPR) ^ fa::swz<CPR>(row);  // global chunk stored there
-            const int grow = min(row0 + row, nrows - 1);
-            const E* src = head + (size_t)grow * D + ch * F::CH;
-            __builtin_amdgcn_global_load_lds(
-                (const void*)src, (__attribute__((address_space(3))) void*)(lds_tile + block * 1024),
-                16, 0, 0);
+            const int ch = (p % CPR) ^ fa::swz<CPR>(row);   // global chunk stored there
+            voff[i] = (uint32_t)((row * D + ch * F::CH) * (int)sizeof(E));
         }
+    }
+
+    // Issue the loads of rows row0 .. row0+ROWS-1 of a [nrows][D] array; rows
+    // past nrows read as zeros (buffer range check).  w: this wave's index
+    // (wave-uniform).
+    __device__ __forceinline__ void load(unsigned char* lds_tile, const E* head, int row0,
+                                         int nrows, int w) const
+    {
+        const int left = nrows - row0;
+        const int bytes = left > 0 ? left * D * (int)sizeof(E) : 0;
+        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(head + (size_t)row0 * D), (short)0, bytes, kBufferFlags);
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc, (__attribute__((address_space(3))) void*)(lds_tile + (i * (NT / 64) + w) * 1024),
+                16, voff[i], 0, 0, 0);
     }
 };
 
 // Wait for this thread's outstanding global loads (including LDS-bound ones).
 __device__ __forceinline__ void wait_global_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// 8 consecutive elements (cols col .. col+7) of one row of a DMA tile.
-template <class Tile>
-__device__ __forceinline__ Frag<bf16> tile_frag(const unsigned char* t, int row, int col, bf16*)
-{
-    Frag<bf16> f;
-    f.v = *reinterpret_cast<const bf16x8*>(t + Tile::offset(row, col));
-    return f;
-}
-template <class Tile>
-__device__ __forceinline__ Frag<float> tile_frag(const unsigned char* t, int row, int col, float*)
-{
-    Frag<float> f;
-    const f32x4 lo = *reinterpret_cast<const f32x4*>(t + Tile::offset(row, col));
-    const f32x4 hi = *reinterpret_cast<const f32x4*>(t + Tile::offset(row, col + 4));
-    f.v = f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    return f;
-}
+// Row-wise fragment reads from a DMA tile: lane (g, c) reads the 8 elements
+// at columns 16ks + 8g .. +7 of row rowbase + rowlane (rowbase a multiple of
+// 16).  The per-lane byte offsets are computed once; in the loop a read is one
+// LDS instruction with a constant offset.
+template <class Tile, class E, int D>
+struct RowReader {
+    static constexpr int NKS = D / 16;
+    static constexpr int NC = 8 * (int)sizeof(E) / 16;  // 16-byte chunks per fragment
+    uint32_t off[NKS][NC];
+
+    __device__ __forceinline__ void init(int rowlane, int g)
+    {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+            for (int h = 0; h < NC; ++h)
+                off[ks][h] = (uint32_t)Tile::offset(rowlane, 16 * ks + 8 * g + 8 * h / NC);
+    }
+
+    __device__ __forceinline__ Frag<E> frag(const unsigned char* tile, int rowbase, int ks) const
+    {
+        const unsigned char* t = tile + rowbase * Tile::ROWBYTES;
+        Frag<E> f;
+        if constexpr (sizeof(E) == 2) {
+            f.v = *reinterpret_cast<const bf16x8*>(t + off[ks][0]);
+        } else {
+            const f32x4 lo = *reinterpret_cast<const f32x4*>(t + off[ks][0]);
+            const f32x4 hi = *reinterpret_cast<const f32x4*>(t + off[ks][1]);
+            f.v = f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+        return f;
+    }
+};
 
 // A-operand fragment of a transposed product, read from a natural tile:
-// lane (g, c) receives element (rows k(e), column col0 + c) for the 8
+// lane (g, c) receives element (rows k(e), column 32db + c) for the 8
 // contraction rows k(e) = rowbase + 8*(e/4) + 4g + e%4, the row order of the
-// accumulator-to-operand reuse described at the top of this file.
+// accumulator-to-operand reuse described at the top of this file (rowbase a
+// multiple of 16).
 //
 // bf16: two ds_read_b64_tr_b16.  Within each group of 16 lanes that
 // instruction hands lane i element (i % 4) of the 8 bytes addressed by lane
 // 4e + i/4 of the group, for e = 0..3.  Lane 16m + j therefore addresses row
-// rowbase + 8h + 4(m/2) + j/4 at column col0 + 16(m%2) + 4(j%4), and the 16
+// rowbase + 8h + 4(m/2) + j/4 at column 32db + 16(m%2) + 4(j%4), and the 16
 // lanes of the group receive 4 rows at 16 consecutive columns.
-template <class Tile>
-__device__ __forceinline__ Frag<bf16> tile_frag_tr(const unsigned char* t, int rowbase, int col0,
-                                                  int lane, bf16*)
-{
-    const int m = lane >> 4, j = lane & 15;
-    const int col = col0 + 16 * (m & 1) + 4 * (j & 3);
-    const int row = rowbase + 4 * (m >> 1) + (j >> 2);
-    // (whole-vector results only: extracting single elements of the
-    // transposed load's result has been miscompiled)
-    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-        (__attribute__((address_space(3))) bf16x4*)(t + Tile::offset(row, col)));
-    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-        (__attribute__((address_space(3))) bf16x4*)(t + Tile::offset(row + 8, col)));
-    Frag<bf16> f;
-    f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    return f;
-}
 // fp32: eight single-element reads.
-template <class Tile>
-__device__ __forceinline__ Frag<float> tile_frag_tr(const unsigned char* t, int rowbase, int col0,
-                                                   int lane, float*)
-{
-    const int g = lane >> 5, c = lane & 31;
-    Frag<float> f;
+template <class Tile, class E, int D>
+struct TrReader {
+    static constexpr int NDB = D / 32;
+    static constexpr int NO = sizeof(E) == 2 ? 2 : 8;
+    uint32_t off[NDB][NO];
+
+    __device__ __forceinline__ void init(int lane)
+    {
+        if constexpr (sizeof(E) == 2) {
+            const int m = lane >> 4, j = lane & 15;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int row = rowbase + 8 * (e >> 2) + 4 * g + (e & 3);
-        f.v[e] = *reinterpret_cast<const float*>(t + Tile::offset(row, col0 + c));
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    off[db][h] = (uint32_t)Tile::offset(8 * h + 4 * (m >> 1) + (j >> 2),
+                                                        db * 32 + 16 * (m & 1) + 4 * (j & 3));
+        } else {
+            const int g = lane >> 5, c = lane & 31;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    off[db][e] = (uint32_t)Tile::offset(8 * (e >> 2) + 4 * g + (e & 3), db * 32 + c);
+        }
     }
-    return f;
-}
+
+    __device__ __forceinline__ Frag<E> frag(const unsigned char* tile, int rowbase, int db) const
+    {
+        const unsigned char* t = tile + rowbase * Tile::ROWBYTES;
+        Frag<E> f;
+        if constexpr (sizeof(E) == 2) {
+            // (whole-vector results only: extracting single elements of the
+            // transposed load's result has been miscompiled)
+            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (__attribute__((address_space(3))) bf16x4*)(t + off[db][0]));
+            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (__attribute__((address_space(3))) bf16x4*)(t + off[db][1]));
+            f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f.v[e] = *reinterpret_cast<const float*>(t + off[db][e]);
+        }
+        return f;
+    }
+};
 
 // ---------------------------------------------------------------------------
 // Work mapping.  Workgroups are dispatched round-robin over the 8 XCDs

@@ -28,6 +28,8 @@
 //     ragged last) tiles take the per-element mask, derived from the lane's
 //     query index and the key index ("Optimización de Flash Attention ...",
 //     «Atención causal» and the K-loop split of «La pila de optimización»).
+#include <type_traits>
+
 #include "fa_device.hpp"
 #include "fa_kernels.hpp"
 
@@ -37,9 +39,8 @@ template <class E, int D, int NW, int BC>
 struct FwdCfg {
     static constexpr int NT = NW * 64;
     static constexpr int BR = NW * 32;
-    using KTile = DmaTile<E, D, BC, NT>;  // read row-wise (K as A operand)
-    using VTile = DmaTile<E, D, BC, NT>;  // read transposed (V^T as A operand)
-    static constexpr int BUF = KTile::BYTES + VTile::BYTES;
+    using Tile = DmaTile<E, D, BC, NT>;  // K (read row-wise) and V (read transposed)
+    static constexpr int BUF = 2 * Tile::BYTES;
     static constexpr size_t SMEM = 2 * (size_t)BUF;
 };
 
@@ -51,9 +52,8 @@ template <class E, int D, int NW, int BC, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, sizeof(E) == 2 ? 8 / NW : 1) void fwd_kernel(FwdArgs a)
 {
     using Cfg = FwdCfg<E, D, NW, BC>;
-    using KT = typename Cfg::KTile;
-    using VT = typename Cfg::VTile;
-    constexpr int NT = Cfg::NT, BR = Cfg::BR;
+    using Tile = typename Cfg::Tile;
+    constexpr int BR = Cfg::BR;
     constexpr int NKB = BC / 32;  // 32-key blocks per tile
     constexpr int NDB = D / 32;   // 32-column blocks of the head dimension
     constexpr int NKS = D / 16;   // 16-deep steps over the head dimension
@@ -82,8 +82,15 @@ __global__ __launch_bounds__(NW * 64, sizeof(E) == 2 ? 8 / NW : 1) void fwd_kern
     const int nkv = (kend + BC - 1) / BC;
     const int nfull = CAUSAL ? (q0 + 1) / BC : a.T / BC;
 
-    KT::load(smem, kh, 0, a.T, tid);
-    VT::load(smem + KT::BYTES, vh, 0, a.T, tid);
+    Tile dma;
+    dma.init(tid);
+    dma.load(smem, kh, 0, a.T, w);
+    dma.load(smem + Tile::BYTES, vh, 0, a.T, w);
+
+    RowReader<Tile, E, D> krd;
+    krd.init(c, g);
+    TrReader<Tile, E, D> vrd;
+    vrd.init(lane);
 
     // B operand of S^T = K Q^T: this lane's query row, 8 columns per step
     Frag<E> qf[NKS];
@@ -99,13 +106,15 @@ __global__ __launch_bounds__(NW * 64, sizeof(E) == 2 ? 8 / NW : 1) void fwd_kern
     wait_global_loads();
     __syncthreads();
 
-    for (int j = 0; j < nkv; ++j) {
-        const unsigned char* Ks = smem + (j & 1) * Cfg::BUF;
-        const unsigned char* Vs = Ks + KT::BYTES;
+    // one key tile; BI (0 or 1) is the LDS buffer it sits in
+    auto step = [&](auto bufi, int j) {
+        constexpr int BI = decltype(bufi)::value;
+        const unsigned char* Ks = smem + BI * Cfg::BUF;
+        const unsigned char* Vs = Ks + Tile::BYTES;
         if (j + 1 < nkv) {
-            unsigned char* nb = smem + ((j + 1) & 1) * Cfg::BUF;
-            KT::load(nb, kh, (j + 1) * BC, a.T, tid);
-            VT::load(nb + KT::BYTES, vh, (j + 1) * BC, a.T, tid);
+            unsigned char* nb = smem + (1 - BI) * Cfg::BUF;
+            dma.load(nb, kh, (j + 1) * BC, a.T, w);
+            dma.load(nb + Tile::BYTES, vh, (j + 1) * BC, a.T, w);
         }
 
         // S^T block kb: rows = keys 32kb.., columns = this wave's 32 queries
@@ -114,8 +123,7 @@ __global__ __launch_bounds__(NW * 64, sizeof(E) == 2 ? 8 / NW : 1) void fwd_kern
         for (int kb = 0; kb < NKB; ++kb) {
             s[kb] = f32x16{};
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
-                mma(s[kb], tile_frag<KT>(Ks, kb * 32 + c, 16 * ks + 8 * g, (E*)nullptr), qf[ks]);
+            for (int ks = 0; ks < NKS; ++ks) mma(s[kb], krd.frag(Ks, kb * 32, ks), qf[ks]);
         }
 
         if (j >= nfull) {  // diagonal or ragged tile: mask from indices
@@ -160,13 +168,17 @@ __global__ __launch_bounds__(NW * 64, sizeof(E) == 2 ? 8 / NW : 1) void fwd_kern
             for (int t = 0; t < 2; ++t) {
                 const Frag<E> pf = acc_frag<E>(s[kb], t);
 #pragma unroll
-                for (int db = 0; db < NDB; ++db)
-                    mma(o[db], tile_frag_tr<VT>(Vs, kb * 32 + 16 * t, db * 32, lane, (E*)nullptr), pf);
+                for (int db = 0; db < NDB; ++db) mma(o[db], vrd.frag(Vs, kb * 32 + 16 * t, db), pf);
             }
         }
 
         wait_global_loads();
         __syncthreads();
+    };
+
+    for (int j = 0; j < nkv; j += 2) {
+        step(std::integral_constant<int, 0>{}, j);
+        if (j + 1 < nkv) step(std::integral_constant<int, 1>{}, j + 1);
     }
 
     // epilogue: divide by l, store O (this lane: query qrow, columns
@@ -197,11 +209,13 @@ __global__ __launch_bounds__(NW * 64, sizeof(E) == 2 ? 8 / NW : 1) void fwd_kern
     }
 }
 
-// Tile configuration per (dtype, D): NW waves of 32 query rows, BC keys per tile.
+// Tile shape of the forward: NW waves of 32 query rows, BC keys per tile.
+constexpr int kFwdNW = 4, kFwdBC = 64;
+
 template <class E, int D, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream)
 {
-    constexpr int NW = 4, BC = 64;
+    constexpr int NW = kFwdNW, BC = kFwdBC;
     using Cfg = FwdCfg<E, D, NW, BC>;
     static_assert(Cfg::SMEM <= 160 * 1024, "LDS budget");
     auto kern = fwd_kernel<E, D, NW, BC, CAUSAL>;
@@ -223,5 +237,19 @@ hipError_t launch_fwd(const FwdArgs& a, int D, int dtype, bool causal, hipStream
     if (D == 64) return causal ? launch_fwd_t<float, 64, true>(a, stream) : launch_fwd_t<float, 64, false>(a, stream);
     return causal ? launch_fwd_t<float, 128, true>(a, stream) : launch_fwd_t<float, 128, false>(a, stream);
 }
+
+// Every kernel variant is instantiated explicitly: referencing a kernel
+// template only from a launcher has left some instantiations without their
+// host-side handle.
+#define FA_FWD_INST(E, D, C) template __global__ void fwd_kernel<E, D, kFwdNW, kFwdBC, C>(FwdArgs);
+FA_FWD_INST(bf16, 64, true)
+FA_FWD_INST(bf16, 64, false)
+FA_FWD_INST(bf16, 128, true)
+FA_FWD_INST(bf16, 128, false)
+FA_FWD_INST(float, 64, true)
+FA_FWD_INST(float, 64, false)
+FA_FWD_INST(float, 128, true)
+FA_FWD_INST(float, 128, false)
+#undef FA_FWD_INST
 
 }  // namespace fa

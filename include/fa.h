@@ -38,8 +38,9 @@
  *
  * Errors.  Arguments are checked on the host before anything is enqueued, in
  * this order, and the first failure is returned:
- *     FA_ERR_SHAPE        B < 0, T < 0, Hq < 1, Hkv < 1, Hq % Hkv != 0, or a
- *                         grid or tensor too large to index;
+ *     FA_ERR_SHAPE        B < 0, T < 0, Hq < 1, Hkv < 1, Hq % Hkv != 0, a
+ *                         grid too large to index, or one head of a tensor
+ *                         (T * D elements) larger than 2^31 - 1 bytes;
  *     FA_ERR_UNSUPPORTED  D not in {64, 128}, unknown dtype, or scale not a
  *                         finite positive number;
  *     FA_ERR_NULL         a required pointer is NULL (pointers are not needed

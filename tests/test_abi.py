@@ -1,0 +1,138 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and rejects bad arguments on the host (before any HIP call)
+with the documented status codes.  CPU only."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_attention_30_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+OK, NULL, SHAPE, UNSUP, ALIGN, HIP = range(6)
+BF16, FP32 = 0, 1
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.LIB_PATH):
+        pytest.fail("libfa.so is not built (run __graft_entry__.build())")
+    return fa.library()
+
+
+def test_library_loads_with_all_symbols_resolved():
+    # RTLD_NOW: every undefined symbol (e.g. a kernel handle) fails the load
+    ctypes.CDLL(fa.LIB_PATH, mode=os.RTLD_NOW | os.RTLD_LOCAL)
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert {"fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/fa.h but not exported"
+    assert set(names) == set(fa.SIGNATURES), "binding signatures and header disagree"
+
+
+def test_status_strings(lib):
+    for s in range(6):
+        assert lib.fa_status_string(s)
+    assert lib.fa_version().decode().count(".") == 2
+
+
+# a fake, 16-byte aligned address that is never dereferenced: every call below
+# must return before touching it
+A = 1 << 20
+
+
+def fwd(lib, q=A, k=A, v=A, o=A, lse=A, B=1, Hq=2, Hkv=1, T=64, D=128, scale=0.1, causal=1,
+        dt=BF16):
+    return lib.fa_fwd(q, k, v, o, lse, B, Hq, Hkv, T, D, scale, causal, dt, None)
+
+
+def bwd(lib, ptrs=None, B=1, Hq=2, Hkv=1, T=64, D=128, scale=0.1, causal=1, dt=BF16):
+    p = ptrs or [A] * 10
+    return lib.fa_bwd(*p, B, Hq, Hkv, T, D, scale, causal, dt, None)
+
+
+def test_shape_errors(lib):
+    assert fwd(lib, Hq=3, Hkv=2) == SHAPE
+    assert fwd(lib, Hkv=0) == SHAPE
+    assert fwd(lib, Hq=0) == SHAPE
+    assert fwd(lib, B=-1) == SHAPE
+    assert fwd(lib, T=-5) == SHAPE
+    # one head beyond the 2^31-byte range of a buffer resource
+    assert fwd(lib, T=(1 << 23) + 1, D=128) == SHAPE
+    assert bwd(lib, Hq=5, Hkv=2) == SHAPE
+
+
+def test_unsupported_errors(lib):
+    assert fwd(lib, D=96) == UNSUP
+    assert fwd(lib, D=32) == UNSUP
+    assert fwd(lib, dt=7) == UNSUP
+    assert fwd(lib, scale=0.0) == UNSUP
+    assert fwd(lib, scale=-0.5) == UNSUP
+    assert fwd(lib, scale=float("inf")) == UNSUP
+    assert fwd(lib, scale=float("nan")) == UNSUP
+    assert bwd(lib, D=80) == UNSUP
+
+
+def test_shape_checked_before_unsupported_and_null(lib):
+    assert fwd(lib, Hq=3, Hkv=2, D=96, q=0) == SHAPE
+    assert fwd(lib, D=96, q=0) == UNSUP
+
+
+def test_null_errors(lib):
+    for name in ("q", "k", "v", "o", "lse"):
+        assert fwd(lib, **{name: 0}) == NULL
+    for i in range(10):
+        p = [A] * 10
+        p[i] = 0
+        assert bwd(lib, p) == NULL
+    assert lib.fa_bwd_preprocess(0, A, A, 1, 2, 64, 128, BF16, None) == NULL
+    assert lib.fa_bwd_dkdv(A, A, A, A, A, A, 0, A, 1, 2, 1, 64, 128, 0.1, 1, BF16, None) == NULL
+    assert lib.fa_bwd_dq(A, A, A, A, A, A, 0, 1, 2, 1, 64, 128, 0.1, 1, BF16, None) == NULL
+
+
+def test_align_errors(lib):
+    assert fwd(lib, q=A + 8) == ALIGN
+    assert fwd(lib, o=A + 2) == ALIGN
+    assert fwd(lib, lse=A + 2) == ALIGN
+    p = [A] * 10
+    p[9] = A + 4  # workspace
+    assert bwd(lib, p) == ALIGN
+
+
+def test_empty_inputs_are_no_ops(lib):
+    # nothing to do: OK without pointers and without touching the GPU
+    assert fwd(lib, q=0, k=0, v=0, o=0, lse=0, T=0) == OK
+    assert fwd(lib, q=0, k=0, v=0, o=0, lse=0, B=0) == OK
+    assert bwd(lib, [0] * 10, T=0) == OK
+    assert lib.fa_bwd_preprocess(0, 0, 0, 0, 2, 64, 128, BF16, None) == OK
+
+
+def test_workspace_bytes(lib):
+    assert lib.fa_bwd_workspace_bytes(1, 32, 8, 16384, 128, BF16) == 32 * 16384 * 4
+    assert lib.fa_bwd_workspace_bytes(2, 3, 1, 5, 64, BF16) == 256  # rounded up
+    assert lib.fa_bwd_workspace_bytes(1, 3, 2, 5, 64, BF16) == 0  # invalid shape
+    assert lib.fa_bwd_workspace_bytes(1, 2, 1, 0, 64, BF16) == 0
+
+
+def test_binding_rejects_bad_tensors():
+    import torch
+
+    q = torch.zeros(1, 2, 8, 64)
+    with pytest.raises(ValueError):
+        fa.fwd(q, q, q)  # not on a GPU
+    with pytest.raises(TypeError):
+        fa.fwd(q.half(), q.half(), q.half())
+    with pytest.raises(ValueError):
+        fa.fwd(q, torch.zeros(1, 2, 9, 64), torch.zeros(1, 2, 9, 64))

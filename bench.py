@@ -53,7 +53,25 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target duration of the oracle sample")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                   help="only run 5 plain device copies of BYTES bytes (a known-size reference "
+                        "for the HBM byte counters) and exit")
     return p.parse_args()
+
+
+def calibrate_copy(nbytes: int):
+    """Five device-to-device copies of nbytes: each reads and writes nbytes, so
+    FETCH_SIZE / WRITE_SIZE of these dispatches calibrate the counters."""
+    import torch
+
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes": nbytes, "copies": 5}), flush=True)
 
 
 def gemm_flop(w, n_gemm):
@@ -143,6 +161,9 @@ def cpu_baseline(w, x, target_s: float):
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "the multi-GPU sharding is described in DESIGN.md but not built.", file=sys.stderr)

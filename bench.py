@@ -166,7 +166,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the multi-GPU sharding is described in DESIGN.md but not built.", file=sys.stderr)
+              "sharding by kv group across GPUs is not built.", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -339,7 +339,6 @@ __global__ __launch_bounds__(NW * 64, sizeof(E) == 2 ? 8 / NW : 1) void bwd_dq_k
             dma.load(nb + Tile::BYTES, vh, (j + 1) * BC, a.T, w);
         }
         const bool need_mask = j >= nfull;
-
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
             f32x16 s = f32x16{}, dp = f32x16{};
@@ -348,15 +347,20 @@ __global__ __launch_bounds__(NW * 64, sizeof(E) == 2 ? 8 / NW : 1) void bwd_dq_k
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) mma(dp, rrd.frag(Vs, kb * 32, ks), of[ks]);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float p = fast_exp2(fmaf(s[r], a.c, -L2));
-                if (need_mask) {
+            for (int r = 0; r < 16; ++r) s[r] = fast_exp2(fmaf(s[r], a.c, -L2));  // P^T
+            if (need_mask) {
+                // a real branch (the empty asm keeps the compiler from turning
+                // it into selects executed on every tile)
+                asm volatile("");
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
                     const int kj = j * BC + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
                     const bool vis = CAUSAL ? (kj <= qrow) : (kj < a.T);
-                    if (!vis) p = 0.f;
+                    s[r] = vis ? s[r] : 0.f;
                 }
-                dp[r] = p * (dp[r] - Dl);  // dS^T
             }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dp[r] = s[r] * (dp[r] - Dl);  // dS^T
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 const Frag<E> sf = acc_frag<E>(dp, t);

@@ -230,10 +230,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream)
 
 hipError_t launch_fwd(const FwdArgs& a, int D, int dtype, bool causal, hipStream_t stream)
 {
-    if (dtype == 0) {
-        if (D == 64) return causal ? launch_fwd_t<bf16, 64, true>(a, stream) : launch_fwd_t<bf16, 64, false>(a, stream);
-        return causal ? launch_fwd_t<bf16, 128, true>(a, stream) : launch_fwd_t<bf16, 128, false>(a, stream);
-    }
+    if (dtype == 0) return launch_fwd_bf16(a, D, causal, stream);
     if (D == 64) return causal ? launch_fwd_t<float, 64, true>(a, stream) : launch_fwd_t<float, 64, false>(a, stream);
     return causal ? launch_fwd_t<float, 128, true>(a, stream) : launch_fwd_t<float, 128, false>(a, stream);
 }
@@ -242,10 +239,6 @@ hipError_t launch_fwd(const FwdArgs& a, int D, int dtype, bool causal, hipStream
 // template only from a launcher has left some instantiations without their
 // host-side handle.
 #define FA_FWD_INST(E, D, C) template __global__ void fwd_kernel<E, D, kFwdNW, kFwdBC, C>(FwdArgs);
-FA_FWD_INST(bf16, 64, true)
-FA_FWD_INST(bf16, 64, false)
-FA_FWD_INST(bf16, 128, true)
-FA_FWD_INST(bf16, 128, false)
 FA_FWD_INST(float, 64, true)
 FA_FWD_INST(float, 64, false)
 FA_FWD_INST(float, 128, true)

@@ -1,0 +1,370 @@
+// bf16 forward kernel: O = softmax(Q K^T * scale [+ causal mask]) V and the
+// row log-sum-exp, without ever writing the T x T scores.
+//
+// Algorithm ("L'attention fusionnée", «Le softmax en ligne»; "FlashAttention:
+// l'attenzione che non spreca memoria", «L'idea: lavorare a tessere»): a
+// workgroup keeps a block of query rows in registers and streams key/value
+// tiles through LDS; per tile it updates a running max m, a running sum l and
+// the output numerator o, rescaling both by exp(m - m') when the max rises;
+// o is divided by l once at the end and L = m + ln l is saved.
+//
+// MI355X mapping.
+//   * Eight waves of 32 query rows.  A wave computes S^T = K Q^T with the
+//     32x32x16 bf16 MFMA, so a lane owns one query column: its row max and sum
+//     are in-lane reductions plus one exchange with lane c ^ 32.  The S^T
+//     accumulator is exponentiated in place (exp2, scale*log2 e folded in) and
+//     fed back as the B operand of O^T += V^T P^T: P never touches LDS.
+//   * Ping-pong.  Waves w and w + 4 share a SIMD.  The two groups of four
+//     waves run the same sequence of steps, one step apart: a matrix step
+//     M(j) = { O += P_{j-1} V_{j-1};  S_j = Q K_j^T } (MFMA work and LDS reads)
+//     and a vector step V(j) = { mask; max; rescale; P_j = exp2(...) } (VALU
+//     work).  In every phase one wave of each SIMD issues MFMAs while its
+//     partner computes exponentials, and a barrier ends the phase; the
+//     matrix-step wave runs at raised priority so its MFMAs issue first.
+//   * K and V tiles move from HBM to LDS by LDS DMA in read order (no bank
+//     conflicts, one address register per operand), three stages deep: stage
+//     j = {K_j, V_{j-1}} is the LDS data of step M(j), issued four phases
+//     before it is needed.
+//   * Lazy rescale: the reference max of a row only moves when the row max
+//     exceeds it by more than 8 (log2 units), so most tiles skip rescaling O
+//     and l; the weights stay below 2^8, and o and l share the reference.
+//   * Causal: tiles wholly in the future of a wave are skipped by that wave;
+//     tiles wholly in its past run without mask code; the remaining tiles take
+//     the per-element mask derived from the lane's query index and the key
+//     index ("Optimización de Flash Attention ...", «Atención causal» and the
+//     K-loop split of «La pila de optimización»).
+#include <type_traits>
+
+#include "fa_device.hpp"
+#include "fa_kernels.hpp"
+#include "fa_pipe.hpp"
+
+namespace fa {
+
+template <int D>
+struct FwdBf16Cfg {
+    static constexpr int NW = 4;             // waves per group
+    static constexpr int NWAVE = 2 * NW;     // waves per workgroup
+    static constexpr int NT = 64 * NWAVE;
+    static constexpr int BR = 32 * NWAVE;    // query rows per workgroup
+    static constexpr int BC = 64;            // keys per tile
+    static constexpr int NSTAGE = 3;
+    using KT = RowFragTile<D, BC>;
+    using VT = TrFragTile<D, BC>;
+    static constexpr int STAGE = KT::BYTES + VT::BYTES;
+    static constexpr int SMEM = NSTAGE * STAGE;
+    static constexpr int KI = KT::NDMA / NWAVE;  // DMA instructions per wave per tile
+    static constexpr int VI = VT::NDMA / NWAVE;
+    static_assert(KT::NDMA % NWAVE == 0 && VT::NDMA % NWAVE == 0, "DMA split");
+};
+
+constexpr float kRescaleThresholdBf16 = 8.0f;
+
+// Scheduling pins for a run of N MFMAs whose A fragments come from LDS, PF
+// fragments ahead: the reads of the first PF fragments, then each MFMA
+// followed by the reads of the fragment PF products later.  Products i < NPV
+// use transposed fragments (two LDS reads), the rest row fragments (one).
+template <int N, int PF, int NPV, int... I>
+__device__ __forceinline__ void pin_mfma_ds_interleave(std::integer_sequence<int, I...>)
+{
+    constexpr int kDsRead = 0x100, kMfma = 0x008;
+    constexpr int pre = (PF >= 1 ? (0 < NPV ? 2 : 1) : 0) + (PF >= 2 ? (1 < NPV ? 2 : 1) : 0) +
+                        (PF >= 3 ? (2 < NPV ? 2 : 1) : 0) + (PF >= 4 ? (3 < NPV ? 2 : 1) : 0);
+    static_assert(PF <= 4, "prefetch depth");
+    __builtin_amdgcn_sched_group_barrier(kDsRead, pre, 0);
+    (
+        [] {
+            __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+            if constexpr (I + PF < N)
+                __builtin_amdgcn_sched_group_barrier(kDsRead, (I + PF < NPV) ? 2 : 1, 0);
+        }(),
+        ...);
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
+{
+    using Cfg = FwdBf16Cfg<D>;
+    using KT = typename Cfg::KT;
+    using VT = typename Cfg::VT;
+    constexpr int BR = Cfg::BR, BC = Cfg::BC, NWAVE = Cfg::NWAVE;
+    constexpr int KI = Cfg::KI, VI = Cfg::VI;
+    constexpr int NKB = BC / 32;  // 32-key blocks per tile
+    constexpr int NDB = D / 32;   // 32-column blocks of the head dimension
+    constexpr int NKS = D / 16;   // 16-deep steps over the head dimension
+
+    extern __shared__ __align__(1024) unsigned char smem[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = w / Cfg::NW;
+    const int g = lane >> 5;
+    const int c = lane & 31;
+
+    const int nqt = (a.T + BR - 1) / BR;
+    const TileId id = map_tile(blockIdx.x, a.B, a.Hq, a.Hkv, a.Hq / a.Hkv, nqt, CAUSAL);
+    const int b = id.b, hq = id.h;
+    const int hk = hq / (a.Hq / a.Hkv);
+    const int q0 = id.tile * BR;
+    const int qw = q0 + 32 * w;   // first query of this wave
+    const int qrow = qw + c;      // the query this lane owns
+
+    const bf16* qh = static_cast<const bf16*>(a.q) + (size_t)(b * a.Hq + hq) * a.T * D;
+    const bf16* kh = static_cast<const bf16*>(a.k) + (size_t)(b * a.Hkv + hk) * a.T * D;
+    const bf16* vh = static_cast<const bf16*>(a.v) + (size_t)(b * a.Hkv + hk) * a.T * D;
+
+    // key tiles visited by the workgroup; per wave, tiles it sees at all
+    // (live) and tiles it sees completely (no mask)
+    const int kend = CAUSAL ? min(q0 + BR, a.T) : a.T;
+    const int nkv = (kend + BC - 1) / BC;
+    const int nfull = CAUSAL ? (qw + 1) / BC : a.T / BC;
+
+    // this thread's DMA source offsets (same for every tile)
+    uint32_t koff[KI], voff[VI];
+#pragma unroll
+    for (int i = 0; i < KI; ++i) koff[i] = KT::dma_off(w + NWAVE * i, lane);
+#pragma unroll
+    for (int i = 0; i < VI; ++i) voff[i] = VT::dma_off(w + NWAVE * i, lane);
+
+    const uint32_t lds0 = lds_addr(smem);
+    // stage s = {K_s (s < nkv), V_{s-1} (s >= 1)} in buffer s % NSTAGE
+    auto load_stage = [&](int s) {
+        const uint32_t base = lds0 + (uint32_t)((s % Cfg::NSTAGE) * Cfg::STAGE);
+        if (s < nkv) {
+            const int row0 = s * BC;
+            const i32x4 r = buffer_rsrc(kh + (size_t)row0 * D, (a.T - row0) * D * 2);
+#pragma unroll
+            for (int i = 0; i < KI; ++i) dma_b128(base + (uint32_t)((w + NWAVE * i) * 1024), r, koff[i]);
+        }
+        if (s >= 1) {
+            const int row0 = (s - 1) * BC;
+            const i32x4 r = buffer_rsrc(vh + (size_t)row0 * D, (a.T - row0) * D * 2);
+#pragma unroll
+            for (int i = 0; i < VI; ++i)
+                dma_b128(base + (uint32_t)(KT::BYTES + (w + NWAVE * i) * 1024), r, voff[i]);
+        }
+    };
+
+    load_stage(0);
+    load_stage(1);  // nkv >= 1, so stage 1 holds at least V_0
+
+    // B operand of S^T = K Q^T: this lane's query row, 8 columns per step
+    Frag<bf16> qf[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qf[ks] = global_frag<bf16>(qh, qrow, a.T, D, 16 * ks + 8 * g);
+
+    f32x16 o[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
+    f32x16 s[NKB];                 // S^T of the current tile (rows = keys)
+    Frag<bf16> pf[NKB][2];         // P of the previous tile (B operands of P V)
+    float mref = -INFINITY;        // reference max, log2 units
+    float l = 0.f;                 // this lane's share of the row sum
+
+    vm_wait<0>();
+    sync_lds();
+
+    // Matrix step M(j): O^T += V_{j-1}^T P_{j-1}^T (PV) and S_j^T = K_j Q^T
+    // (S), from stage j.  The 16 (PV) plus 16 (S) fragment reads run PF
+    // MFMAs ahead of their products.
+    auto matrix_step = [&](int j, auto with_pv, auto with_s) {
+        constexpr bool PV = decltype(with_pv)::value, SS = decltype(with_s)::value;
+        constexpr int NPV = PV ? NKB * 2 * NDB : 0;   // PV products
+        constexpr int NS = SS ? NKS * NKB : 0;        // S products
+        constexpr int N = NPV + NS;
+        constexpr int PF = 3;
+        const unsigned char* st = smem + (j % Cfg::NSTAGE) * Cfg::STAGE;
+        const unsigned char* vl = st + KT::BYTES + 8 * lane;
+        const unsigned char* kl = st + 16 * lane;
+        // product i < NPV: (kb, t, db) = PV block; else (ks, kb) = S block
+        auto read = [&](int i) -> bf16x8 {
+            if (i < NPV) {
+                const int db = i % NDB, t = (i / NDB) % 2, kb = i / (2 * NDB);
+                return VT::read(vl, 2 * kb + t, db);
+            }
+            const int k = i - NPV, kb = k % NKB, ks = k / NKB;
+            return KT::read(kl, kb, ks);
+        };
+        if constexpr (SS) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
+        }
+        bf16x8 fb[PF + 1];
+#pragma unroll
+        for (int i = 0; i < PF; ++i) fb[i] = read(i);
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            if (i + PF < N) fb[(i + PF) % (PF + 1)] = read(i + PF);
+            Frag<bf16> af;
+            af.v = fb[i % (PF + 1)];
+            if (i < NPV) {
+                const int db = i % NDB, t = (i / NDB) % 2, kb = i / (2 * NDB);
+                mma(o[db], af, pf[kb][t]);
+            } else {
+                const int k = i - NPV, kb = k % NKB, ks = k / NKB;
+                mma(s[kb], af, qf[ks]);
+            }
+        }
+        pin_mfma_ds_interleave<N, PF, NPV>(std::make_integer_sequence<int, N>{});
+    };
+
+    // Vector step V(j): mask, lazy reference update (rescaling O and l when it
+    // moves), P_j = exp2(S_j c - mref) with fp32 row sums, rounded for P V.
+    auto vector_step = [&](int j) {
+        if (j >= nfull) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int kj = j * BC + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+                    const bool vis = CAUSAL ? (kj <= qrow) : (kj < a.T);
+                    if (!vis) s[kb][r] = -INFINITY;
+                }
+        }
+        float mt = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) mt = fmaxf(mt, fmaxf(s[kb][r], s[kb][r + 1]));
+        mt = pair_max(mt) * a.c;
+        const bool need = mt > mref + kRescaleThresholdBf16;
+        if (__builtin_amdgcn_ballot_w64(need)) {
+            const float mnew = need ? mt : mref;
+            const float alpha = fast_exp2(mref - mnew);  // 0 on the first visit
+            l *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+            mref = mnew;
+        }
+        const float msub = (mref == -INFINITY) ? 0.f : mref;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                s[kb][r] = fast_exp2(fmaf(s[kb][r], a.c, -msub));
+                l += s[kb][r];
+            }
+#pragma unroll
+            for (int t = 0; t < 2; ++t) pf[kb][t] = acc_frag<bf16>(s[kb], t);
+        }
+    };
+
+    // Phases.  Group 0 runs the sequence M(0) V(0) M(1) V(1) ... V(nkv-1)
+    // M(nkv), one step per phase; group 1 runs it one phase later.  Stage j is
+    // read in phases 2j (group 0) and 2j + 1 (group 1); it is issued at the
+    // start of phase 2j - 4 (stages 0 and 1 before the loop), after the
+    // barrier ending the last phase that read its buffer's previous stage,
+    // and waited for at the end of phase 2j - 1.
+    auto start_even_phase = [&](int k) {  // phase 2k
+        if (k + 2 <= nkv) load_stage(k + 2);
+    };
+    auto end_odd_phase = [&](int k) {     // phase 2k + 1: stage k + 1 must land
+        const int j = k + 1;
+        if (j + 1 < nkv)
+            vm_wait<KI + VI>();
+        else if (j + 1 == nkv)
+            vm_wait<VI>();
+        else
+            vm_wait<0>();
+        sync_lds();
+    };
+    using T0 = std::integral_constant<bool, false>;
+    using T1 = std::integral_constant<bool, true>;
+    if (grp == 0) {
+        start_even_phase(0);
+        __builtin_amdgcn_s_setprio(1);
+        matrix_step(0, T0{}, T1{});
+        __builtin_amdgcn_s_setprio(0);
+        sync_lds();
+        vector_step(0);
+        end_odd_phase(0);
+        for (int k = 1; k < nkv; ++k) {
+            start_even_phase(k);
+            __builtin_amdgcn_s_setprio(1);
+            matrix_step(k, T1{}, T1{});
+            __builtin_amdgcn_s_setprio(0);
+            sync_lds();
+            vector_step(k);
+            end_odd_phase(k);
+        }
+        start_even_phase(nkv);
+        __builtin_amdgcn_s_setprio(1);
+        matrix_step(nkv, T1{}, T0{});
+        __builtin_amdgcn_s_setprio(0);
+        sync_lds();
+        end_odd_phase(nkv);
+    } else {
+        start_even_phase(0);
+        sync_lds();
+        __builtin_amdgcn_s_setprio(1);
+        matrix_step(0, T0{}, T1{});
+        __builtin_amdgcn_s_setprio(0);
+        end_odd_phase(0);
+        for (int k = 1; k < nkv; ++k) {
+            start_even_phase(k);
+            vector_step(k - 1);
+            sync_lds();
+            __builtin_amdgcn_s_setprio(1);
+            matrix_step(k, T1{}, T1{});
+            __builtin_amdgcn_s_setprio(0);
+            end_odd_phase(k);
+        }
+        start_even_phase(nkv);
+        vector_step(nkv - 1);
+        sync_lds();
+        __builtin_amdgcn_s_setprio(1);
+        matrix_step(nkv, T1{}, T0{});
+        __builtin_amdgcn_s_setprio(0);
+        end_odd_phase(nkv);
+    }
+
+    // epilogue: divide by l, store O (this lane: query qrow, columns
+    // 32db + 8rg + 4g + i) and lse
+    const float lt = pair_sum(l);
+    const float inv = 1.f / lt;
+    if (qrow < a.T) {
+        bf16* oh = static_cast<bf16*>(a.o) + ((size_t)(b * a.Hq + hq) * a.T + qrow) * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                bf16x4 x;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) x[i] = (bf16)(o[db][4 * rg + i] * inv);
+                *reinterpret_cast<bf16x4*>(oh + db * 32 + 8 * rg + 4 * g) = x;
+            }
+        if (g == 0) a.lse[(size_t)(b * a.Hq + hq) * a.T + qrow] = (mref + __log2f(lt)) * kLn2;
+    }
+}
+
+template <int D, bool CAUSAL>
+static hipError_t launch_t(const FwdArgs& a, hipStream_t stream)
+{
+    using Cfg = FwdBf16Cfg<D>;
+    static_assert(Cfg::SMEM <= 160 * 1024, "LDS budget");
+    auto kern = fwd_bf16_kernel<D, CAUSAL>;
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::SMEM);
+    if (attr != hipSuccess) return attr;
+    const int nqt = (a.T + Cfg::BR - 1) / Cfg::BR;
+    const long grid = (long)nqt * a.B * a.Hq;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Cfg::NT), Cfg::SMEM, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, int D, bool causal, hipStream_t stream)
+{
+    if (D == 64) return causal ? launch_t<64, true>(a, stream) : launch_t<64, false>(a, stream);
+    return causal ? launch_t<128, true>(a, stream) : launch_t<128, false>(a, stream);
+}
+
+// Every kernel variant is instantiated explicitly: referencing a kernel
+// template only from a launcher has left some instantiations without their
+// host-side handle.
+template __global__ void fwd_bf16_kernel<64, true>(FwdArgs);
+template __global__ void fwd_bf16_kernel<64, false>(FwdArgs);
+template __global__ void fwd_bf16_kernel<128, true>(FwdArgs);
+template __global__ void fwd_bf16_kernel<128, false>(FwdArgs);
+
+}  // namespace fa

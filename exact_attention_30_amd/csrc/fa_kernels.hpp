@@ -41,6 +41,7 @@ struct PreArgs {
 // Each launcher enqueues one kernel on `stream` and returns the launch status.
 // dtype: 0 = bf16, 1 = fp32.  Shapes have been validated by the caller.
 hipError_t launch_fwd(const FwdArgs& a, int D, int dtype, bool causal, hipStream_t stream);
+hipError_t launch_fwd_bf16(const FwdArgs& a, int D, bool causal, hipStream_t stream);
 hipError_t launch_bwd_pre(const PreArgs& a, int D, int dtype, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int D, int dtype, bool causal, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, int D, int dtype, bool causal, hipStream_t stream);

@@ -1,0 +1,149 @@
+// Read-order LDS tiles and explicitly scheduled LDS DMA (gfx950 / CDNA4).
+//
+// A read-order tile stores a block of K or V rows in exactly the order the
+// MFMA operand reads consume it: every read is 64 lanes x 16 bytes (row-wise
+// fragments, ds_read_b128) or 64 lanes x 8 bytes (transposed fragments,
+// ds_read_b64_tr_b16) of contiguous LDS.  Contiguous lane addresses cannot
+// collide on LDS banks, and each read of a tile is one per-lane base register
+// plus a compile-time offset, so the hot loops carry no per-fragment address
+// registers.  The tiles are filled straight from global memory by
+// buffer_load_dwordx4 ... lds: lane L of one such instruction writes bytes
+// 16L .. 16L+15 of a 1 KiB LDS block, so the block order fixes, for every
+// lane, which 16 global bytes it fetches.
+//
+// The DMA is issued through inline assembly.  The compiler then does not
+// treat these loads as LDS stores that every later LDS read might alias (which
+// would make it wait for all outstanding DMA before any LDS read and so stall
+// the prefetch of the next tiles); instead the kernels wait explicitly, with
+// `vm_wait<N>`, for exactly the loads whose data they are about to read, and
+// order LDS accesses around workgroup barriers with `sync_lds`.  Loads return
+// in issue order, so waiting until at most N loads are outstanding completes
+// every load issued before the last N.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_device.hpp"
+
+namespace fa {
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource over `bytes` bytes at `base` (wave-uniform): reads at
+// offsets at or past `bytes` return zeros.
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, int bytes)
+{
+    const uint64_t addr = (uint64_t)(uintptr_t)base;
+    return i32x4{(int32_t)(uint32_t)addr, (int32_t)((addr >> 32) & 0xffff), bytes, kBufferFlags};
+}
+
+// 32-bit LDS address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// One LDS DMA instruction: this lane's 16 bytes at byte `voff` of the buffer
+// land at LDS byte lds + 16 * lane.  `lds` must be wave-uniform.
+__device__ __forceinline__ void dma_b128(uint32_t lds, const i32x4& rsrc, uint32_t voff)
+{
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "{m0}"(lds)
+                 : "memory");
+}
+
+// Wait until at most N of this wave's vector-memory loads are outstanding.
+template <int N>
+__device__ __forceinline__ void vm_wait()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier that also retires this wave's LDS reads (so no read of a
+// buffer is in flight when another wave overwrites it after the barrier) but
+// does not wait for outstanding global loads.  The asm statements are
+// compiler barriers for memory accesses.
+__device__ __forceinline__ void sync_lds()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// ---------------------------------------------------------------------------
+// Row-wise fragments of a ROWS x D bf16 block (A operand of S^T = K Q^T):
+// fragment (kb, ks) gives lane (g, c) row 32kb + c, columns 16ks + 8g .. +7.
+// ---------------------------------------------------------------------------
+template <int D, int ROWS>
+struct RowFragTile {
+    static constexpr int NKS = D / 16;
+    static constexpr int NKB = ROWS / 32;
+    static constexpr int NDMA = NKB * NKS;  // 1 KiB blocks = DMA instructions
+    static constexpr int BYTES = NDMA * 1024;
+
+    __device__ __forceinline__ static constexpr int frag_off(int kb, int ks) { return (kb * NKS + ks) * 1024; }
+
+    // global byte offset (within the block's first row) fetched by `lane` for
+    // DMA instruction f
+    __device__ __forceinline__ static uint32_t dma_off(int f, int lane)
+    {
+        const int kb = f / NKS, ks = f % NKS;
+        const int row = 32 * kb + (lane & 31), col = 16 * ks + 8 * (lane >> 5);
+        return (uint32_t)((row * D + col) * 2);
+    }
+
+    // lane's fragment (kb, ks) of the tile at `tile` (lane offset included by
+    // the caller: tile + 16 * lane)
+    __device__ __forceinline__ static bf16x8 read(const unsigned char* tile_lane, int kb, int ks)
+    {
+        return *reinterpret_cast<const bf16x8*>(tile_lane + frag_off(kb, ks));
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Transposed fragments of a ROWS x D bf16 block (A operand of O^T += V^T P^T):
+// for the 16-row step ts and column block db, lane (g, c) receives elements
+// e = 0..7 = V[16ts + 8(e/4) + 4g + e%4][32db + c], the row order in which the
+// S^T accumulator registers are reused as the B operand.  Each step is two
+// ds_read_b64_tr_b16 (h = e/4), each reading a 512-byte block.  Within 16
+// lanes that instruction gives lane i element i%4 of the 8 bytes addressed by
+// lane 4e + i/4 (e = 0..3); so in block (ts, db, h), lane 16m + a holds the 8
+// bytes V[16ts + 8h + 4(m/2) + a/4][32db + 16(m%2) + 4(a%4) .. +3].
+// ---------------------------------------------------------------------------
+template <int D, int ROWS>
+struct TrFragTile {
+    static constexpr int NTS = ROWS / 16;
+    static constexpr int NDB = D / 32;
+    static constexpr int NDMA = NTS * NDB;  // one 1 KiB block = both halves
+    static constexpr int BYTES = NDMA * 1024;
+
+    __device__ __forceinline__ static constexpr int block_off(int ts, int db, int h)
+    {
+        return ((ts * NDB + db) * 2 + h) * 512;
+    }
+
+    // DMA instruction f = ts * NDB + db: lane L fills bytes 16(L%32) .. +15 of
+    // half h = L/32, i.e. the words of reading lanes 2s and 2s + 1 (s = L%32):
+    // 8 consecutive elements of one row.
+    __device__ __forceinline__ static uint32_t dma_off(int f, int lane)
+    {
+        const int ts = f / NDB, db = f % NDB;
+        const int h = lane >> 5, s = lane & 31;
+        const int row = 16 * ts + 8 * h + 4 * (s >> 4) + ((s & 7) >> 1);
+        const int col = 32 * db + 16 * ((s >> 3) & 1) + 8 * (s & 1);
+        return (uint32_t)((row * D + col) * 2);
+    }
+
+    // lane's fragment for step ts, column block db (tile_lane = tile + 8 * lane)
+    __device__ __forceinline__ static bf16x8 read(const unsigned char* tile_lane, int ts, int db)
+    {
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (__attribute__((address_space(3))) bf16x4*)(tile_lane + block_off(ts, db, 0)));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (__attribute__((address_space(3))) bf16x4*)(tile_lane + block_off(ts, db, 1)));
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+};
+
+}  // namespace fa

@@ -147,3 +147,65 @@ struct TrFragTile {
 };
 
 }  // namespace fa
+
+namespace fa {
+
+// One LDS DMA instruction of 4 bytes per lane: this lane's dword at byte
+// `voff` of the buffer lands at LDS byte lds + 4 * lane.
+__device__ __forceinline__ void dma_b32(uint32_t lds, const i32x4& rsrc, uint32_t voff)
+{
+    asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "{m0}"(lds)
+                 : "memory");
+}
+
+// A ROWS x D bf16 block in natural [row][col] order with the chunk swizzle of
+// DmaTile (row-wise and transposed reads both conflict-free), filled by the
+// explicitly scheduled DMA above; NT threads share the instructions.
+template <int D, int ROWS, int NT>
+struct SwzTile {
+    using Base = DmaTile<bf16, D, ROWS, NT>;
+    static constexpr int NI = Base::NI;
+    static constexpr int BYTES = Base::BYTES;
+    uint32_t voff[NI];
+
+    __device__ __forceinline__ void init(int tid)
+    {
+        Base t;
+        t.init(tid);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) voff[i] = t.voff[i];
+    }
+
+    // rows row0 .. row0 + ROWS - 1 of a [nrows][D] array into the tile at LDS
+    // byte address `lds`; rows past nrows read as zeros.  w: this wave's index.
+    __device__ __forceinline__ void load(uint32_t lds, const bf16* head, int row0, int nrows, int w) const
+    {
+        const int left = nrows - row0;
+        const i32x4 r = buffer_rsrc(head + (size_t)row0 * D, left > 0 ? left * D * 2 : 0);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) dma_b128(lds + (uint32_t)((i * (NT / 64) + w) * 1024), r, voff[i]);
+    }
+};
+
+}  // namespace fa
+
+namespace fa {
+
+// Empty asm through which a value passes: the computation of an input or
+// output cannot move across it, and such statements keep their order among
+// themselves and with scheduling barriers.  Used to place vector work between
+// matrix instructions in a fixed order.
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(uint32_t& x) { asm volatile("" : "+v"(x)); }
+
+// Two floats rounded to nearest even bf16, packed (first in the low half).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
+{
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 v = {(bf16)lo, (bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+}  // namespace fa

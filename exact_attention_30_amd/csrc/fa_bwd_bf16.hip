@@ -5,26 +5,24 @@
 // query row is the precomputed Delta_i = sum_d dO_id O_id:
 //     dV = P^T dO,   dP = dO V^T,   dS = P * (dP - Delta),   dK = dS^T Q * scale.
 //
-// dK/dV kernel.  One workgroup of four waves per (batch, kv head, block of
-// 128 keys), one wave per SIMD; wave w owns 32 keys.  K and V of those keys
-// stay in registers (B operands of S = Q K^T and dP = dO V^T); the dK^T and
-// dV^T accumulators (the MFMA accumulators of dK^T += Q^T dS, dV^T += dO^T P)
-// never leave the matrix-core register file.  Query tiles of 32 rows, of every
-// query head of the kv group, stream through LDS; the group sum of dK and dV
-// therefore stays inside the workgroup and no atomics are needed (the result
-// is bitwise reproducible).
-//
-// Software pipeline.  Per query tile t a wave runs
-//     A(t): S = Q_t K^T, dP = dO_t V^T          (16 MFMAs, row reads of Q_t, dO_t)
-//     B(t): P, mask, dS, bf16 operands          (vector ALU)
-//     C(t): dV^T += dO_t^T P, dK^T += Q_t^T dS  (16 MFMAs, transposed reads)
-// and iteration i issues C(i-1) and A(i+1) on the matrix core interleaved
-// with the vector work of B(i), all three independent, so one wave per SIMD
-// keeps both units busy.  Tiles arrive by LDS DMA four iterations ahead into
-// six stage buffers; the loop is unrolled over the stages so every LDS offset
-// is an immediate.  Causal masking uses, per accumulator register, a
-// workgroup-uniform lane mask: with 32-row query tiles and 32-key waves a tile
-// is wholly visible, wholly invisible or exactly the lower triangle.
+// dK/dV kernel.  One workgroup of eight waves per (batch, kv head, block of
+// 256 keys): two waves per SIMD, so the matrix work of one overlaps the
+// vector work of the other.  Wave w owns 32 keys: K of those keys stays in
+// registers (B operand of S = Q K^T) and the dK^T, dV^T accumulators never
+// leave the register file; V of the workgroup's keys is loaded once into LDS
+// (B operand of dP = dO V^T), which keeps a wave within its 256 registers.
+// Query tiles of 32 rows, of every query head of the kv group, stream through
+// LDS, shared by the eight waves; the group sum of dK and dV therefore stays
+// inside the workgroup and no atomics are needed (the result is bitwise
+// reproducible).  Per query tile a wave runs
+//     S = Q_t K^T, dP = dO_t V^T          (16 MFMAs, row reads of Q_t, dO_t, V)
+//     P, mask, dS, bf16 operands          (vector ALU)
+//     dV^T += dO_t^T P, dK^T += Q_t^T dS  (16 MFMAs, transposed reads)
+// The tiles arrive by explicitly scheduled LDS DMA three tiles ahead in four
+// stage buffers; the loop is unrolled over the stages, so every LDS offset is
+// an immediate.  Tiles wholly visible to a wave carry no mask code; with
+// 32-row query tiles and 32-key waves any other tile is exactly the lower
+// triangle or wholly invisible, handled in a rarely taken branch.
 #include <type_traits>
 #include <utility>
 
@@ -36,18 +34,22 @@ namespace fa {
 
 template <int D>
 struct DkdvBf16Cfg {
-    static constexpr int NW = 4;
+    static constexpr int NW = 8;
     static constexpr int NT = 64 * NW;
     static constexpr int BK = 32 * NW;  // keys per workgroup
     static constexpr int BQ = 32;       // query rows per tile
-    static constexpr int NSTAGE = 6;    // LDS stage buffers (even: register sets alternate)
-    static constexpr int AHEAD = 4;     // tiles in flight ahead of the one entering B
-    using QT = SwzTile<D, BQ, NT>;      // Q and dO tiles
-    using Fmt = DmaTile<bf16, D, BQ, NT>;
-    static constexpr int STATS = 512;   // L*log2(e) (64 floats) and Delta (64 floats)
+    static constexpr int NSTAGE = 4;    // LDS stage buffers
+    static constexpr int AHEAD = 3;     // tiles issued ahead of the one computed
+    // Q and dO tiles: 32 rows; D = 64 needs only four waves to move them
+    static constexpr int QNT = (BQ * D / 8 >= NT) ? NT : BQ * D / 8;
+    using QT = SwzTile<D, BQ, QNT>;
+    using Fmt = DmaTile<bf16, D, BQ, QNT>;
+    using VT = SwzTile<D, BK, NT>;
+    static constexpr int STATS = 512;  // L*log2(e) (64 floats) and Delta (64 floats)
     static constexpr int STAGE = 2 * QT::BYTES + STATS;
-    static constexpr int SMEM = NSTAGE * STAGE;
-    static_assert(AHEAD + 2 <= NSTAGE, "stages in use: t-1, t, t+1 and AHEAD - 1 in flight");
+    static constexpr int SMEM = VT::BYTES + NSTAGE * STAGE;
+    static_assert(AHEAD + 1 <= NSTAGE, "a stage is refilled only after its tile was used");
+    static_assert(QT::NI == 1, "one Q and one dO instruction per loading wave");
 };
 
 // Lane mask of accumulator register r (rows = queries 8(r/4) + 4g + r%4,
@@ -69,18 +71,40 @@ __device__ __forceinline__ void unroll_stages(F& f, int i, std::integer_sequence
     (f(std::integral_constant<int, K>{}, i + K), ...);
 }
 
+// vm_wait<N> for a run-time N that is one of the values a wave can have
+// outstanding here (0 .. 9)
+__device__ __forceinline__ void vm_wait_n(int n)
+{
+    switch (n) {
+    case 0: vm_wait<0>(); break;
+    case 1: vm_wait<1>(); break;
+    case 2: vm_wait<2>(); break;
+    case 3: vm_wait<3>(); break;
+    case 4: vm_wait<4>(); break;
+    case 5: vm_wait<5>(); break;
+    case 6: vm_wait<6>(); break;
+    case 7: vm_wait<7>(); break;
+    case 8: vm_wait<8>(); break;
+    default: vm_wait<9>(); break;
+    }
+}
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(BwdArgs a)
+__global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
 {
     using Cfg = DkdvBf16Cfg<D>;
     using QT = typename Cfg::QT;
     using Fmt = typename Cfg::Fmt;
+    using VT = typename Cfg::VT;
     constexpr int BK = Cfg::BK, BQ = Cfg::BQ, NSTAGE = Cfg::NSTAGE, STAGE = Cfg::STAGE;
     constexpr int AHEAD = Cfg::AHEAD;
     constexpr int NDB = D / 32;
     constexpr int NKS = D / 16;
+    constexpr int QW = Cfg::QNT / 64;  // waves that move Q and dO tiles
 
     extern __shared__ __align__(1024) unsigned char smem[];
+    unsigned char* Vs = smem;
+    unsigned char* stages = smem + VT::BYTES;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -90,7 +114,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(BwdArgs a)
     const int G = a.Hq / a.Hkv;
 
     const int nkt = (a.T + BK - 1) / BK;
-    // causal: the first key tiles see the most query rows
+    // causal: the first key blocks see the most query rows
     const TileId id = map_tile(blockIdx.x, a.B, a.Hq, a.Hkv, 1, nkt, false);
     const int b = id.b, hk = id.h;
     const int key0 = id.tile * BK;
@@ -108,20 +132,21 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(BwdArgs a)
     const int n = G * niq;
     const int npad = (n + NSTAGE - 1) / NSTAGE * NSTAGE;  // padded tiles: all masked
 
+    const uint32_t lds0 = lds_addr(stages);
     QT qt;
-    qt.init(tid);
-    const uint32_t lds0 = lds_addr(smem);
-    // DMA instructions per tile of this wave: Q and dO, plus L (wave 0) or
+    if (w < QW) qt.init(tid);
+    // DMA instructions per tile of this wave: Q and dO, and L (wave 0) or
     // Delta (wave 1)
-    const int vpt = 2 * QT::NI + (w < 2 ? 1 : 0);
-    // DMA cursor: (query head, query tile) of the next tile to issue; the
-    // flattened order runs over the query tiles i0 .. nq-1 of each head
+    const int vpt = (w < QW ? 2 : 0) + (w < 2 ? 1 : 0);
+    // DMA cursor: (query head, query tile) of the next tile to issue
     int dhq = hk * G, dti = i0;
     auto issue = [&](int st) {
-        const size_t qoff = (size_t)(b * a.Hq + dhq) * a.T * D;
         const uint32_t base = lds0 + (uint32_t)(st * STAGE);
-        qt.load(base, static_cast<const bf16*>(a.q) + qoff, dti * BQ, a.T, w);
-        qt.load(base + QT::BYTES, static_cast<const bf16*>(a.dout) + qoff, dti * BQ, a.T, w);
+        if (w < QW) {
+            const size_t qoff = (size_t)(b * a.Hq + dhq) * a.T * D;
+            qt.load(base, static_cast<const bf16*>(a.q) + qoff, dti * BQ, a.T, w);
+            qt.load(base + QT::BYTES, static_cast<const bf16*>(a.dout) + qoff, dti * BQ, a.T, w);
+        }
         if (w < 2) {
             const float* src = (w == 0 ? a.lse : a.delta) + (size_t)(b * a.Hq + dhq) * a.T + dti * BQ;
             const i32x4 r = buffer_rsrc(src, (a.T - dti * BQ) * 4);
@@ -132,216 +157,117 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(BwdArgs a)
             ++dhq;
         }
     };
-    // wait until tile t has landed, given that tiles t+1 .. t+2 may be in flight
+    // wait until tile t has landed while the tiles issued after it
+    // (t + 1 .. t + AHEAD - 1, those that exist) stay in flight
     auto wait_tile = [&](int t) {
-        const int after = (t + 1 < n) + (t + 2 < n);  // tiles issued after t
-        if (vpt == 2 * QT::NI + 1) {
-            if (after == 2) vm_wait<2 * (2 * QT::NI + 1)>();
-            else if (after == 1) vm_wait<2 * QT::NI + 1>();
-            else vm_wait<0>();
-        } else {
-            if (after == 2) vm_wait<2 * (2 * QT::NI)>();
-            else if (after == 1) vm_wait<2 * QT::NI>();
-            else vm_wait<0>();
-        }
+        int after = n - 1 - t;
+        after = after < 0 ? 0 : (after > AHEAD - 1 ? AHEAD - 1 : after);
+        vm_wait_n(after * vpt);
     };
 
-    // Zero every stage first: the first C step and the padded tiles at the end
-    // compute on stages no tile has filled, with all-zero (masked) weights, and
-    // 0 * (uninitialised LDS) could be NaN.
-    for (int off = tid * 16; off < Cfg::SMEM; off += Cfg::NT * 16)
-        *reinterpret_cast<u32x4*>(smem + off) = u32x4{0, 0, 0, 0};
+    // Zero the stages first: the padded tiles at the end compute on stages no
+    // tile has filled, with all-zero (masked) weights, and 0 * (uninitialised
+    // LDS) could be NaN.
+    for (int off = tid * 16; off < NSTAGE * STAGE; off += Cfg::NT * 16)
+        *reinterpret_cast<u32x4*>(stages + off) = u32x4{0, 0, 0, 0};
     sync_lds();
+    {
+        VT vt;
+        vt.init(tid);
+        vt.load(lds_addr(Vs), vh, key0, a.T, w);
+    }
     for (int t = 0; t < AHEAD && t < n; ++t) issue(t);  // stage t
 
-    // B operands of S = Q K^T and dP = dO V^T: this lane's key row, 8 columns
-    // per 16-deep step
-    Frag<bf16> kf[NKS], vf[NKS];
+    // B operand of S = Q K^T: this lane's key row, 8 columns per 16-deep step
+    Frag<bf16> kf[NKS];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-        kf[ks] = global_frag<bf16>(kh, krow, a.T, D, 16 * ks + 8 * g);
-        vf[ks] = global_frag<bf16>(vh, krow, a.T, D, 16 * ks + 8 * g);
-    }
+    for (int ks = 0; ks < NKS; ++ks) kf[ks] = global_frag<bf16>(kh, krow, a.T, D, 16 * ks + 8 * g);
 
-    RowReader<Fmt, bf16, D> qrd;  // Q and dO rows (A of S, dP)
+    // Q, dO rows (A of S, dP) and V rows w*32 + c (B of dP): the V tile has
+    // the same row format, so the same offsets serve
+    RowReader<Fmt, bf16, D> qrd;
     qrd.init(c, g);
-    TrReader<Fmt, bf16, D> trd;   // Q^T and dO^T (A of dK^T, dV^T)
+    TrReader<Fmt, bf16, D> trd;  // Q^T and dO^T (A of dK^T, dV^T)
     trd.init(lane);
 
     f32x16 dk[NDB], dv[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) dk[db] = dv[db] = f32x16{};
-    f32x16 S[2], DP[2];        // scores and dP of tiles of parity 0 / 1
-    // bf16 P and dS of tiles of parity 0 / 1, as B operands of C: 16-deep
-    // step t, packed pairs of elements 2e, 2e + 1
-    uint32_t PW[2][2][4], SW[2][2][4];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) PW[1][t][e] = SW[1][t][e] = 0u;
-    auto frag_of = [](const uint32_t (&wv)[4]) {
-        Frag<bf16> f;
-        f.v = __builtin_bit_cast(bf16x8, u32x4{wv[0], wv[1], wv[2], wv[3]});
-        return f;
-    };
 
-    // L of tile t (natural log) -> L * log2(e), in place, by wave 0
-    auto convert_l = [&](int t) {
+    // L of the tile in stage st (natural log) -> L * log2(e), in place, by
+    // wave 0, whose own DMA moved it
+    auto convert_l = [&](int st) {
         if (w == 0 && lane < BQ) {
-            float* Ls = reinterpret_cast<float*>(smem + (t % NSTAGE) * STAGE + 2 * QT::BYTES);
+            float* Ls = reinterpret_cast<float*>(stages + st * STAGE + 2 * QT::BYTES);
             Ls[lane] *= kLog2e;
         }
     };
 
-    wait_tile(1 < n ? 1 : 0);  // tiles 0 and 1
-    sync_lds();
+    vm_wait<0>();  // V and the first tiles
     convert_l(0);
     sync_lds();
+    int bti = i0;  // query tile of the tile being computed
 
-    int bti = i0;  // query tile of the tile entering B
-    auto tile_q = [&](int st) { return smem + st * STAGE; };
-    auto tile_do = [&](int st) { return smem + st * STAGE + QT::BYTES; };
-
-    // A(t): S = Q_t K^T and dP = dO_t V^T into register set P1
-    auto step_a = [&](auto st_tag, auto par_tag) {
-        constexpr int ST = decltype(st_tag)::value, P1 = decltype(par_tag)::value;
-        S[P1] = f32x16{};
-        DP[P1] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            mma(S[P1], qrd.frag(tile_q(ST), 0, ks), kf[ks]);
-            mma(DP[P1], qrd.frag(tile_do(ST), 0, ks), vf[ks]);
-        }
-    };
-    // C(t): dV^T += dO_t^T P, dK^T += Q_t^T dS from register set P0
-    auto step_c = [&](auto st_tag, auto par_tag) {
-        constexpr int ST = decltype(st_tag)::value, P0 = decltype(par_tag)::value;
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                mma(dv[db], trd.frag(tile_do(ST), 16 * t, db), frag_of(PW[P0][t]));
-                mma(dk[db], trd.frag(tile_q(ST), 16 * t, db), frag_of(SW[P0][t]));
-            }
-    };
-
-    // one iteration: tile i enters B; stage ST = i % NSTAGE (compile time)
     auto body = [&](auto st_tag, int i) {
         constexpr int ST = decltype(st_tag)::value;
-        constexpr int PB = ST & 1, PO = PB ^ 1;
-        constexpr int SPREV = (ST + NSTAGE - 1) % NSTAGE, SNEXT = (ST + 1) % NSTAGE;
+        const unsigned char* Qs = stages + ST * STAGE;
+        const unsigned char* dOs = Qs + QT::BYTES;
+        const float* Ls = reinterpret_cast<const float*>(dOs + QT::BYTES);
+        const float* Ds = Ls + 64;
         if (i + AHEAD < n) issue((ST + AHEAD) % NSTAGE);
-        convert_l(i + 1);
 
-        // Tiles wholly visible to this wave take no mask code.  The others
-        // (causal: the diagonal tile, query rows 0..31 against keys 0..31 of
-        // the wave, and tiles wholly in the past of the wave's keys; the
-        // padding past the last tile) set the invisible scores to -inf in a
-        // branch, so that P = 0 there.
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            mma(s, qrd.frag(Qs, 0, ks), kf[ks]);
+            mma(dp, qrd.frag(dOs, 0, ks), qrd.frag(Vs, 32 * w, ks));
+        }
+        // Tiles wholly visible to this wave take no mask code; the others set
+        // the invisible scores to -inf, so that P = 0 there.
         const bool pad = i >= n;
-        const int qb = bti * BQ;  // first query row of tile i
+        const int qb = bti * BQ;
         if (pad || (CAUSAL && qb <= kw)) {
             asm volatile("");  // keep this a branch
             const bool tri = !pad && qb == kw;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const uint64_t m = tri ? tri_mask(r) : 0ull;
-                S[PB][r] = __builtin_amdgcn_inverse_ballot_w64(m) ? S[PB][r] : -INFINITY;
+                s[r] = __builtin_amdgcn_inverse_ballot_w64(m) ? s[r] : -INFINITY;
             }
         }
         if (++bti == nq) bti = i0;
-
-        // L*log2(e) and Delta of this lane's 16 rows of tile i
-        const float* Ls = reinterpret_cast<const float*>(smem + ST * STAGE + 2 * QT::BYTES);
-        const float* Ds = Ls + 64;
-        f32x4 L4[4], D4[4];
+        // rows of this lane's registers: queries 8*(r/4) + 4g + r%4
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
-            L4[rg] = *reinterpret_cast<const f32x4*>(Ls + 8 * rg + 4 * g);
-            D4[rg] = *reinterpret_cast<const f32x4*>(Ds + 8 * rg + 4 * g);
+            const f32x4 L4 = *reinterpret_cast<const f32x4*>(Ls + 8 * rg + 4 * g);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s[4 * rg + e] = fast_exp2(fmaf(s[4 * rg + e], a.c, -L4[e]));  // P
         }
-
-        // Matrix products of this iteration, in slot order k = 0 .. N-1:
-        //   k < NC : C(i-1), (t, db, which) -> dV^T (which 0) or dK^T (which 1)
-        //   k >= NC: A(i+1), (ks, which)    -> S (which 0) or dP (which 1)
-        constexpr int NC = 2 * 2 * NDB, NA = 2 * NKS, N = NC + NA;
-        constexpr int NCHUNK = 32, CPS = (NCHUNK + N - 1) / N;  // B chunks per slot
-        constexpr int AHD = 4;                                   // reads run AHD products ahead
-        auto frag_for = [&](int k) -> Frag<bf16> {
-            if (k < NC) {
-                const int which = k & 1, db = (k >> 1) % NDB, t = (k >> 1) / NDB;
-                return trd.frag(which ? tile_q(SPREV) : tile_do(SPREV), 16 * t, db);
-            }
-            const int kk = k - NC, which = kk & 1, ks = kk >> 1;
-            return qrd.frag(which ? tile_do(SNEXT) : tile_q(SNEXT), 0, ks);
-        };
-        auto mfma_at = [&](int k, const Frag<bf16>& f) {
-            if (k < NC) {
-                const int which = k & 1, db = (k >> 1) % NDB, t = (k >> 1) / NDB;
-                if (which)
-                    mma(dk[db], f, frag_of(SW[PO][t]));
-                else
-                    mma(dv[db], f, frag_of(PW[PO][t]));
-            } else {
-                const int kk = k - NC, which = kk & 1, ks = kk >> 1;
-                if (which)
-                    mma(DP[PO], f, vf[ks]);
-                else
-                    mma(S[PO], f, kf[ks]);
-            }
-        };
-        // B(i) in 32 chunks, each pinned to its slot by passing its inputs
-        // and outputs through empty asm statements (ordered among themselves
-        // and with the slot barriers): even chunk 2r forms P of register r, odd chunk 2r + 1 its dS and, for odd r, rounds the pair
-        // (r - 1, r) of P and dS into the bf16 operands of C(i).
-        float pv[16], dsv[16];
-        auto b_chunk = [&](int j) {
-            const int r = j >> 1;
-            if (!(j & 1)) {
-                float x = S[PB][r];
-                pin(x);
-                pv[r] = fast_exp2(fmaf(x, a.c, -L4[r >> 2][r & 3]));
-                pin(pv[r]);
-            } else {
-                float y = DP[PB][r];
-                pin(y);
-                dsv[r] = pv[r] * (y - D4[r >> 2][r & 3]);
-                pin(dsv[r]);
-                if (r & 1) {
-                    const int t = (r - 1) >> 3, e = (r - 1) & 7;
-                    uint32_t pp = pack_bf16(pv[r - 1], pv[r]);
-                    uint32_t ss = pack_bf16(dsv[r - 1], dsv[r]);
-                    pin(pp);
-                    pin(ss);
-                    PW[PB][t][e >> 1] = pp;
-                    SW[PB][t][e >> 1] = ss;
-                }
-            }
-        };
-
-        S[PO] = f32x16{};
-        DP[PO] = f32x16{};
-        Frag<bf16> ring[AHD + 1];
 #pragma unroll
-        for (int k = 0; k < AHD; ++k) ring[k] = frag_for(k);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int rg = 0; rg < 4; ++rg) {
+            const f32x4 D4 = *reinterpret_cast<const f32x4*>(Ds + 8 * rg + 4 * g);
 #pragma unroll
-        for (int k = 0; k < N; ++k) {
-#pragma unroll
-            for (int j = k * CPS; j < (k + 1) * CPS && j < NCHUNK; ++j) b_chunk(j);
-            if (k + AHD < N) ring[(k + AHD) % (AHD + 1)] = frag_for(k + AHD);
-            mfma_at(k, ring[k % (AHD + 1)]);
-            __builtin_amdgcn_sched_barrier(0);
+            for (int e = 0; e < 4; ++e) dp[4 * rg + e] = s[4 * rg + e] * (dp[4 * rg + e] - D4[e]);  // dS
         }
-
-        wait_tile(i + 2);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const Frag<bf16> pf = acc_frag<bf16>(s, t);
+            const Frag<bf16> sf = acc_frag<bf16>(dp, t);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                mma(dv[db], trd.frag(dOs, 16 * t, db), pf);
+                mma(dk[db], trd.frag(Qs, 16 * t, db), sf);
+            }
+        }
+        // tile i + 1 must have landed before the barrier that starts the next
+        // iteration; wave 0, which moved its L, converts it before the barrier
+        wait_tile(i + 1);
+        convert_l((ST + 1) % NSTAGE);
         sync_lds();
     };
 
-    step_a(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
     for (int i = 0; i < npad; i += NSTAGE)
         unroll_stages(body, i, std::make_integer_sequence<int, NSTAGE>{});
-    step_c(std::integral_constant<int, NSTAGE - 1>{}, std::integral_constant<int, 1>{});
 
     // this lane: key krow, columns 32db + 8rg + 4g + e
     if (krow < a.T) {

@@ -125,7 +125,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
     const bf16* kh = static_cast<const bf16*>(a.k) + kvoff;
     const bf16* vh = static_cast<const bf16*>(a.v) + kvoff;
 
-    // flattened sequence of (query head, query tile) seeing this key block
+    // the (query head, query tile) pairs that see this key block
     const int nq = (a.T + BQ - 1) / BQ;
     const int i0 = CAUSAL ? key0 / BQ : 0;
     const int niq = nq - i0;
@@ -138,8 +138,12 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
     // DMA instructions per tile of this wave: Q and dO, and L (wave 0) or
     // Delta (wave 1)
     const int vpt = (w < QW ? 2 : 0) + (w < 2 ? 1 : 0);
+    // Tiles are visited from the last query tile down to i0, the G query
+    // heads of the kv group interleaved per tile: every workgroup of the kv
+    // head then reads the same tile at about the same time, so the tiles are
+    // fetched from memory once per L2 rather than once per workgroup.
     // DMA cursor: (query head, query tile) of the next tile to issue
-    int dhq = hk * G, dti = i0;
+    int dhq = hk * G, dti = nq - 1;
     auto issue = [&](int st) {
         const uint32_t base = lds0 + (uint32_t)(st * STAGE);
         if (w < QW) {
@@ -152,9 +156,9 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
             const i32x4 r = buffer_rsrc(src, (a.T - dti * BQ) * 4);
             dma_b32(base + 2 * QT::BYTES + 256 * w, r, (uint32_t)(lane * 4));
         }
-        if (++dti == nq) {
-            dti = i0;
-            ++dhq;
+        if (++dhq == (hk + 1) * G) {
+            dhq = hk * G;
+            --dti;
         }
     };
     // wait until tile t has landed while the tiles issued after it
@@ -206,7 +210,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
     vm_wait<0>();  // V and the first tiles
     convert_l(0);
     sync_lds();
-    int bti = i0;  // query tile of the tile being computed
+    int bti = nq - 1, bh = 0;  // query tile and head (in the group) being computed
 
     auto body = [&](auto st_tag, int i) {
         constexpr int ST = decltype(st_tag)::value;
@@ -235,7 +239,10 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
                 s[r] = __builtin_amdgcn_inverse_ballot_w64(m) ? s[r] : -INFINITY;
             }
         }
-        if (++bti == nq) bti = i0;
+        if (++bh == G) {
+            bh = 0;
+            --bti;
+        }
         // rows of this lane's registers: queries 8*(r/4) + 4g + r%4
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {

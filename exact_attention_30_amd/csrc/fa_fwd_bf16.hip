@@ -14,13 +14,12 @@
 //     are in-lane reductions plus one exchange with lane c ^ 32.  The S^T
 //     accumulator is exponentiated in place (exp2, scale*log2 e folded in) and
 //     fed back as the B operand of O^T += V^T P^T: P never touches LDS.
-//   * Ping-pong.  Waves w and w + 4 share a SIMD.  The two groups of four
-//     waves run the same sequence of steps, one step apart: a matrix step
-//     M(j) = { O += P_{j-1} V_{j-1};  S_j = Q K_j^T } (MFMA work and LDS reads)
-//     and a vector step V(j) = { mask; max; rescale; P_j = exp2(...) } (VALU
-//     work).  In every phase one wave of each SIMD issues MFMAs while its
-//     partner computes exponentials, and a barrier ends the phase; the
-//     matrix-step wave runs at raised priority so its MFMAs issue first.
+//   * Two waves per SIMD (eight per workgroup) run independently between
+//     one barrier per key tile, so the matrix work of one overlaps the vector
+//     work of the other.  Within a wave the matrix step of tile j also issues
+//     the P V product of tile j - 1: M(j) = { O += P_{j-1} V_{j-1};
+//     S_j = Q K_j^T } (MFMAs, LDS reads), then V(j) = { mask; max; rescale;
+//     P_j = exp2(...) } (vector ALU).
 //   * K and V tiles move from HBM to LDS by LDS DMA in read order (no bank
 //     conflicts, one address register per operand), three stages deep: stage
 //     j = {K_j, V_{j-1}} is the LDS data of step M(j), issued four phases
@@ -43,8 +42,7 @@ namespace fa {
 
 template <int D>
 struct FwdBf16Cfg {
-    static constexpr int NW = 4;             // waves per group
-    static constexpr int NWAVE = 2 * NW;     // waves per workgroup
+    static constexpr int NWAVE = 8;          // waves per workgroup (two per SIMD)
     static constexpr int NT = 64 * NWAVE;
     static constexpr int BR = 32 * NWAVE;    // query rows per workgroup
     static constexpr int BC = 64;            // keys per tile
@@ -98,7 +96,6 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int grp = w / Cfg::NW;
     const int g = lane >> 5;
     const int c = lane & 31;
 
@@ -250,20 +247,19 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
         }
     };
 
-    // Phases.  Group 0 runs the sequence M(0) V(0) M(1) V(1) ... V(nkv-1)
-    // M(nkv), one step per phase; group 1 runs it one phase later.  Stage j is
-    // read in phases 2j (group 0) and 2j + 1 (group 1); it is issued at the
-    // start of phase 2j - 4 (stages 0 and 1 before the loop), after the
-    // barrier ending the last phase that read its buffer's previous stage,
-    // and waited for at the end of phase 2j - 1.
-    auto start_even_phase = [&](int k) {  // phase 2k
-        if (k + 2 <= nkv) load_stage(k + 2);
+    // Iteration j: M(j), then V(j).  Stage j is read by M(j) in iteration j
+    // only; stage j + 2 is issued at the start of iteration j into the buffer
+    // of stage j - 1 (read in iteration j - 1, before the barrier that ended
+    // it), and stage j + 1 is waited for at the end of iteration j.  The two
+    // waves of a SIMD run independently between barriers, so the matrix work
+    // of one overlaps the vector work of the other.
+    auto issue_ahead = [&](int j) {
+        if (j + 2 <= nkv) load_stage(j + 2);
     };
-    auto end_odd_phase = [&](int k) {     // phase 2k + 1: stage k + 1 must land
-        const int j = k + 1;
-        if (j + 1 < nkv)
+    auto wait_next = [&](int j) {  // stage j + 1 must land; stage j + 2 may fly
+        if (j + 2 < nkv)
             vm_wait<KI + VI>();
-        else if (j + 1 == nkv)
+        else if (j + 2 == nkv)
             vm_wait<VI>();
         else
             vm_wait<0>();
@@ -271,53 +267,17 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
     };
     using T0 = std::integral_constant<bool, false>;
     using T1 = std::integral_constant<bool, true>;
-    if (grp == 0) {
-        start_even_phase(0);
-        __builtin_amdgcn_s_setprio(1);
-        matrix_step(0, T0{}, T1{});
-        __builtin_amdgcn_s_setprio(0);
-        sync_lds();
-        vector_step(0);
-        end_odd_phase(0);
-        for (int k = 1; k < nkv; ++k) {
-            start_even_phase(k);
-            __builtin_amdgcn_s_setprio(1);
-            matrix_step(k, T1{}, T1{});
-            __builtin_amdgcn_s_setprio(0);
-            sync_lds();
-            vector_step(k);
-            end_odd_phase(k);
-        }
-        start_even_phase(nkv);
-        __builtin_amdgcn_s_setprio(1);
-        matrix_step(nkv, T1{}, T0{});
-        __builtin_amdgcn_s_setprio(0);
-        sync_lds();
-        end_odd_phase(nkv);
-    } else {
-        start_even_phase(0);
-        sync_lds();
-        __builtin_amdgcn_s_setprio(1);
-        matrix_step(0, T0{}, T1{});
-        __builtin_amdgcn_s_setprio(0);
-        end_odd_phase(0);
-        for (int k = 1; k < nkv; ++k) {
-            start_even_phase(k);
-            vector_step(k - 1);
-            sync_lds();
-            __builtin_amdgcn_s_setprio(1);
-            matrix_step(k, T1{}, T1{});
-            __builtin_amdgcn_s_setprio(0);
-            end_odd_phase(k);
-        }
-        start_even_phase(nkv);
-        vector_step(nkv - 1);
-        sync_lds();
-        __builtin_amdgcn_s_setprio(1);
-        matrix_step(nkv, T1{}, T0{});
-        __builtin_amdgcn_s_setprio(0);
-        end_odd_phase(nkv);
+    issue_ahead(0);
+    matrix_step(0, T0{}, T1{});
+    vector_step(0);
+    wait_next(0);
+    for (int j = 1; j < nkv; ++j) {
+        issue_ahead(j);
+        matrix_step(j, T1{}, T1{});
+        vector_step(j);
+        wait_next(j);
     }
+    matrix_step(nkv, T1{}, T0{});
 
     // epilogue: divide by l, store O (this lane: query qrow, columns
     // 32db + 8rg + 4g + i) and lse

@@ -465,10 +465,7 @@ static hipError_t launch_dq_t(const BwdArgs& a, hipStream_t stream)
 
 hipError_t launch_bwd_dq(const BwdArgs& a, int D, int dtype, bool causal, hipStream_t stream)
 {
-    if (dtype == 0) {
-        if (D == 64) return causal ? launch_dq_t<bf16, 64, true>(a, stream) : launch_dq_t<bf16, 64, false>(a, stream);
-        return causal ? launch_dq_t<bf16, 128, true>(a, stream) : launch_dq_t<bf16, 128, false>(a, stream);
-    }
+    if (dtype == 0) return launch_bwd_dq_bf16(a, D, causal, stream);
     if (D == 64) return causal ? launch_dq_t<float, 64, true>(a, stream) : launch_dq_t<float, 64, false>(a, stream);
     return causal ? launch_dq_t<float, 128, true>(a, stream) : launch_dq_t<float, 128, false>(a, stream);
 }
@@ -476,15 +473,14 @@ hipError_t launch_bwd_dq(const BwdArgs& a, int D, int dtype, bool causal, hipStr
 // Every kernel variant is instantiated explicitly: referencing a kernel
 // template only from a launcher has left some instantiations without their
 // host-side handle.
-#define FA_BWD_INST(E, D)                                                      \
-    template __global__ void bwd_pre_kernel<E, D>(PreArgs);                    \
-    template __global__ void bwd_dq_kernel<E, D, kDqNW, kDqBC, true>(BwdArgs); \
-    template __global__ void bwd_dq_kernel<E, D, kDqNW, kDqBC, false>(BwdArgs);
-FA_BWD_INST(bf16, 64)
-FA_BWD_INST(bf16, 128)
-FA_BWD_INST(float, 64)
-FA_BWD_INST(float, 128)
-#undef FA_BWD_INST
+template __global__ void bwd_pre_kernel<bf16, 64>(PreArgs);
+template __global__ void bwd_pre_kernel<bf16, 128>(PreArgs);
+template __global__ void bwd_pre_kernel<float, 64>(PreArgs);
+template __global__ void bwd_pre_kernel<float, 128>(PreArgs);
+template __global__ void bwd_dq_kernel<float, 64, kDqNW, kDqBC, true>(BwdArgs);
+template __global__ void bwd_dq_kernel<float, 64, kDqNW, kDqBC, false>(BwdArgs);
+template __global__ void bwd_dq_kernel<float, 128, kDqNW, kDqBC, true>(BwdArgs);
+template __global__ void bwd_dq_kernel<float, 128, kDqNW, kDqBC, false>(BwdArgs);
 template __global__ void bwd_dkdv_kernel<float, 64, kDkdvNW, kDkdvBQ, true>(BwdArgs);
 template __global__ void bwd_dkdv_kernel<float, 64, kDkdvNW, kDkdvBQ, false>(BwdArgs);
 template __global__ void bwd_dkdv_kernel<float, 128, kDkdvNW, kDkdvBQ, true>(BwdArgs);

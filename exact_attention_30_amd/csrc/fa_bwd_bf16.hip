@@ -297,6 +297,200 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
     }
 }
 
+// ---------------------------------------------------------------------------
+// dQ kernel.  One workgroup of eight waves per (batch, query head, block of
+// 256 query rows), two waves per SIMD; wave w owns 32 queries and keeps Q and
+// dO of them in registers.  Key tiles of 64 rows walk past in the forward's
+// order, K and V by LDS DMA two tiles ahead into three stage buffers.  Per
+// 32-key block a wave forms S^T = K Q^T and dP^T = V dO^T with keys as rows,
+// P^T = exp2(S^T c - L), dS^T = P^T (dP^T - Delta), and accumulates
+// dQ^T += K^T dS^T with dS^T straight from registers; K^T is read transposed
+// from the K tile.  No atomics: each dQ row is owned by one wave.
+// ---------------------------------------------------------------------------
+template <int D>
+struct DqBf16Cfg {
+    static constexpr int NW = 8;
+    static constexpr int NT = 64 * NW;
+    static constexpr int BR = 32 * NW;  // query rows per workgroup
+    static constexpr int BC = 64;       // keys per tile
+    static constexpr int NSTAGE = 3;
+    static constexpr int AHEAD = 2;
+    using KT = SwzTile<D, BC, NT>;  // K (row-wise and transposed) and V (row-wise)
+    using Fmt = DmaTile<bf16, D, BC, NT>;
+    static constexpr int STAGE = 2 * KT::BYTES;
+    static constexpr int SMEM = NSTAGE * STAGE;
+    static_assert(AHEAD + 1 <= NSTAGE, "a stage is refilled only after its tile was used");
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
+{
+    using Cfg = DqBf16Cfg<D>;
+    using KT = typename Cfg::KT;
+    using Fmt = typename Cfg::Fmt;
+    constexpr int BR = Cfg::BR, BC = Cfg::BC, NSTAGE = Cfg::NSTAGE, STAGE = Cfg::STAGE;
+    constexpr int AHEAD = Cfg::AHEAD;
+    constexpr int NKB = BC / 32;
+    constexpr int NDB = D / 32;
+    constexpr int NKS = D / 16;
+    constexpr int VPT = 2 * KT::NI;  // DMA instructions per tile and wave
+
+    extern __shared__ __align__(1024) unsigned char smem[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 5;
+    const int c = lane & 31;
+
+    const int nqt = (a.T + BR - 1) / BR;
+    const TileId id = map_tile(blockIdx.x, a.B, a.Hq, a.Hkv, a.Hq / a.Hkv, nqt, CAUSAL);
+    const int b = id.b, hq = id.h;
+    const int hk = hq / (a.Hq / a.Hkv);
+    const int q0 = id.tile * BR;
+    const int qw = q0 + 32 * w;  // first query of this wave
+    const int qrow = qw + c;     // the query this lane owns
+
+    const size_t qoff = (size_t)(b * a.Hq + hq) * a.T * D;
+    const size_t kvoff = (size_t)(b * a.Hkv + hk) * a.T * D;
+    const bf16* kh = static_cast<const bf16*>(a.k) + kvoff;
+    const bf16* vh = static_cast<const bf16*>(a.v) + kvoff;
+
+    // key tiles visited by the workgroup; tiles below nfull are wholly
+    // visible to this wave
+    const int kend = CAUSAL ? min(q0 + BR, a.T) : a.T;
+    const int nkv = (kend + BC - 1) / BC;
+    const int npad = (nkv + NSTAGE - 1) / NSTAGE * NSTAGE;  // padded tiles: all masked
+    const int nfull = CAUSAL ? (qw + 1) / BC : a.T / BC;
+
+    const uint32_t lds0 = lds_addr(smem);
+    KT kt;
+    kt.init(tid);
+    auto issue = [&](int j, int st) {
+        const uint32_t base = lds0 + (uint32_t)(st * STAGE);
+        kt.load(base, kh, j * BC, a.T, w);
+        kt.load(base + KT::BYTES, vh, j * BC, a.T, w);
+    };
+    // wait until tile j has landed while tiles j + 1 .. j + AHEAD - 1 (those
+    // that exist) stay in flight
+    auto wait_tile = [&](int j) {
+        const int after = nkv - 1 - j;
+        if (after >= 1)
+            vm_wait<VPT>();
+        else
+            vm_wait<0>();
+        static_assert(AHEAD == 2, "wait counts assume one tile in flight after the awaited one");
+    };
+
+    // zero the stages: padded tiles compute on stages no tile has filled
+    for (int off = tid * 16; off < Cfg::SMEM; off += Cfg::NT * 16)
+        *reinterpret_cast<u32x4*>(smem + off) = u32x4{0, 0, 0, 0};
+    sync_lds();
+    for (int j = 0; j < AHEAD && j < nkv; ++j) issue(j, j);
+
+    // B operands of S^T = K Q^T and dP^T = V dO^T: this lane's query row
+    Frag<bf16> qf[NKS], of[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        qf[ks] = global_frag<bf16>(static_cast<const bf16*>(a.q) + qoff, qrow, a.T, D, 16 * ks + 8 * g);
+        of[ks] = global_frag<bf16>(static_cast<const bf16*>(a.dout) + qoff, qrow, a.T, D, 16 * ks + 8 * g);
+    }
+    float L2 = 0.f, Dl = 0.f;
+    if (qrow < a.T) {
+        const size_t r = (size_t)(b * a.Hq + hq) * a.T + qrow;
+        L2 = a.lse[r] * kLog2e;
+        Dl = a.delta[r];
+    }
+
+    RowReader<Fmt, bf16, D> rrd;  // K and V rows (A of S^T, dP^T)
+    rrd.init(c, g);
+    TrReader<Fmt, bf16, D> trd;   // K^T (A of dQ^T)
+    trd.init(lane);
+
+    f32x16 dq[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) dq[db] = f32x16{};
+
+    vm_wait<0>();
+    sync_lds();
+
+    auto body = [&](auto st_tag, int j) {
+        constexpr int ST = decltype(st_tag)::value;
+        const unsigned char* Ks = smem + ST * STAGE;
+        const unsigned char* Vs = Ks + KT::BYTES;
+        if (j + AHEAD < nkv) issue(j + AHEAD, (ST + AHEAD) % NSTAGE);
+        const bool masked = j >= nfull;  // diagonal, future or padded tile
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                mma(s, rrd.frag(Ks, kb * 32, ks), qf[ks]);
+                mma(dp, rrd.frag(Vs, kb * 32, ks), of[ks]);
+            }
+            if (masked) {
+                asm volatile("");  // keep this a branch
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int kj = j * BC + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+                    const bool vis = (j < nkv) && (CAUSAL ? (kj <= qrow) : (kj < a.T));
+                    s[r] = vis ? s[r] : -INFINITY;
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = fast_exp2(fmaf(s[r], a.c, -L2));  // P^T
+                dp[r] = p * (dp[r] - Dl);                         // dS^T
+            }
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const Frag<bf16> sf = acc_frag<bf16>(dp, t);
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) mma(dq[db], trd.frag(Ks, kb * 32 + 16 * t, db), sf);
+            }
+        }
+        wait_tile(j + 1);
+        sync_lds();
+    };
+
+    for (int j = 0; j < npad; j += NSTAGE)
+        unroll_stages(body, j, std::make_integer_sequence<int, NSTAGE>{});
+
+    if (qrow < a.T) {
+        bf16* dqh = static_cast<bf16*>(a.dq) + qoff + (size_t)qrow * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                bf16x4 x;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = (bf16)(dq[db][4 * rg + e] * a.scale);
+                *reinterpret_cast<bf16x4*>(dqh + db * 32 + 8 * rg + 4 * g) = x;
+            }
+    }
+}
+
+template <int D, bool CAUSAL>
+static hipError_t launch_dq(const BwdArgs& a, hipStream_t stream)
+{
+    using Cfg = DqBf16Cfg<D>;
+    static_assert(Cfg::SMEM <= 160 * 1024, "LDS budget");
+    auto kern = dq_bf16_kernel<D, CAUSAL>;
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::SMEM);
+    if (attr != hipSuccess) return attr;
+    const int nqt = (a.T + Cfg::BR - 1) / Cfg::BR;
+    const long grid = (long)nqt * a.B * a.Hq;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Cfg::NT), Cfg::SMEM, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq_bf16(const BwdArgs& a, int D, bool causal, hipStream_t stream)
+{
+    if (D == 64) return causal ? launch_dq<64, true>(a, stream) : launch_dq<64, false>(a, stream);
+    return causal ? launch_dq<128, true>(a, stream) : launch_dq<128, false>(a, stream);
+}
+
 template <int D, bool CAUSAL>
 static hipError_t launch_dkdv(const BwdArgs& a, hipStream_t stream)
 {
@@ -325,5 +519,9 @@ template __global__ void dkdv_bf16_kernel<64, true>(BwdArgs);
 template __global__ void dkdv_bf16_kernel<64, false>(BwdArgs);
 template __global__ void dkdv_bf16_kernel<128, true>(BwdArgs);
 template __global__ void dkdv_bf16_kernel<128, false>(BwdArgs);
+template __global__ void dq_bf16_kernel<64, true>(BwdArgs);
+template __global__ void dq_bf16_kernel<64, false>(BwdArgs);
+template __global__ void dq_bf16_kernel<128, true>(BwdArgs);
+template __global__ void dq_bf16_kernel<128, false>(BwdArgs);
 
 }  // namespace fa

@@ -17,7 +17,9 @@ KERNEL_GEMMS).  The CPU baseline times the fp64 oracle on a bounded sample of
 the same workload (whole kv groups, or a causal prefix of one head).
 
 Prints one JSON line.  Usage: python bench.py [--steps K] [--warmup W]
-[--workload C5] [--no-cpu-baseline]
+[--workload C5] [--no-cpu-baseline]; python bench.py --gemm-reference times a
+large bf16 library GEMM on random data, a reference for the sustained
+matrix-core rate of the chip.
 """
 from __future__ import annotations
 
@@ -53,6 +55,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target duration of the oracle sample")
+    p.add_argument("--gemm-reference", action="store_true",
+                   help="only time a large bf16 library GEMM (torch.matmul, random N(0,1) data) as a "
+                        "reference for the matrix-core throughput reachable on this chip, and exit")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                    help="only run 5 plain device copies of BYTES bytes (a known-size reference "
                         "for the HBM byte counters) and exit")
@@ -74,6 +79,34 @@ def calibrate_copy(nbytes: int):
     print(json.dumps({"calibration_copy_bytes": nbytes, "copies": 5}), flush=True)
 
 
+def gemm_reference():
+    """Time torch.matmul (the vendor GEMM library) on 8192^3 bf16 products of
+    random N(0,1) data: the sustained matrix-core rate a tuned library reaches
+    here, with data-dependent power and clock included."""
+    import torch
+
+    n = 8192
+    g = torch.Generator(device="cuda").manual_seed(7)
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
+    c = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+    for _ in range(5):
+        torch.matmul(a, b, out=c)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 50
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    print(json.dumps({"gemm_reference": f"torch.matmul bf16 {n}x{n}x{n}, random N(0,1)",
+                      "ms": round(ms, 4), "tflops": round(tf, 1),
+                      "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}), flush=True)
+
+
 def gemm_flop(w, n_gemm):
     """FLOP of n_gemm T x T x D products over the visible score entries."""
     pairs = w.B * w.Hq * w.T * w.T * (0.5 if w.causal else 1.0)
@@ -82,7 +115,7 @@ def gemm_flop(w, n_gemm):
 
 def source_hash(kernel_file: str) -> str:
     h = hashlib.sha256()
-    for f in ("fa_device.hpp", kernel_file):
+    for f in ("fa_device.hpp", "fa_pipe.hpp", kernel_file):
         with open(os.path.join(ROOT, "exact_attention_30_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -164,6 +197,9 @@ def main():
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
         return
+    if args.gemm_reference:
+        gemm_reference()
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "sharding by kv group across GPUs is not built.", file=sys.stderr)
@@ -236,11 +272,15 @@ def main():
     pre_bytes = 2 * w.B * w.Hq * w.T * w.D * q.element_size() + 4 * w.B * w.Hq * w.T
 
     dom = max(("fwd", "dkdv", "dq"), key=lambda n: per[n])
-    kfile = {"fwd": "fa_fwd.hip", "dkdv": "fa_bwd.hip", "dq": "fa_bwd.hip"}[dom]
+    bf = w.dtype == torch.bfloat16
+    kfile = {"fwd": "fa_fwd_bf16.hip" if bf else "fa_fwd.hip",
+             "dkdv": "fa_bwd_bf16.hip" if bf else "fa_bwd.hip",
+             "dq": "fa_bwd_bf16.hip" if bf else "fa_bwd.hip"}[dom]
     achieved = gemm_flop(w, KERNEL_GEMMS[dom]) / (per[dom] * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == torch.bfloat16 else PEAK_FP32_TFLOPS
     roofline = {
-        "kernel": {"fwd": "fwd_kernel", "dkdv": "bwd_dkdv_kernel", "dq": "bwd_dq_kernel"}[dom],
+        "kernel": ({"fwd": "fwd_bf16_kernel", "dkdv": "dkdv_bf16_kernel", "dq": "dq_bf16_kernel"} if bf else
+                   {"fwd": "fwd_kernel", "dkdv": "bwd_dkdv_kernel", "dq": "bwd_dq_kernel"})[dom],
         "bound": "mfma",
         "achieved": round(achieved, 2),
         "peak": peak,

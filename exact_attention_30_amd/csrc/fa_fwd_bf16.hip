@@ -42,11 +42,13 @@ namespace fa {
 
 template <int D>
 struct FwdBf16Cfg {
-    static constexpr int NWAVE = 8;          // waves per workgroup (two per SIMD)
+    static constexpr int NW = 4;             // waves per group
+    static constexpr int NWAVE = 2 * NW;     // waves per workgroup (two per SIMD)
     static constexpr int NT = 64 * NWAVE;
     static constexpr int BR = 32 * NWAVE;    // query rows per workgroup
     static constexpr int BC = 64;            // keys per tile
-    static constexpr int NSTAGE = 3;
+    static constexpr int NSTAGE = 4;
+    static constexpr int AHD = 6;            // fragment reads in flight ahead of their MFMA
     using KT = RowFragTile<D, BC>;
     using VT = TrFragTile<D, BC>;
     static constexpr int STAGE = KT::BYTES + VT::BYTES;
@@ -58,23 +60,21 @@ struct FwdBf16Cfg {
 
 constexpr float kRescaleThresholdBf16 = 8.0f;
 
-// Scheduling pins for a run of N MFMAs whose A fragments come from LDS, PF
-// fragments ahead: the reads of the first PF fragments, then each MFMA
-// followed by the reads of the fragment PF products later.  Products i < NPV
-// use transposed fragments (two LDS reads), the rest row fragments (one).
-template <int N, int PF, int NPV, int... I>
-__device__ __forceinline__ void pin_mfma_ds_interleave(std::integer_sequence<int, I...>)
+// Scheduling pins for a run of N MFMAs whose A fragments come from LDS, AHD
+// fragments ahead (the first AHD already in registers): each MFMA is followed
+// by the reads of the fragment AHD products later.  The S products (first)
+// use row fragments (one LDS read), the PV products transposed fragments
+// (two).
+template <int N, int AHD, class TPV, class TS, int... I>
+__device__ __forceinline__ void pin_mfma_ds_interleave(std::integer_sequence<int, I...>, TPV, TS)
 {
     constexpr int kDsRead = 0x100, kMfma = 0x008;
-    constexpr int pre = (PF >= 1 ? (0 < NPV ? 2 : 1) : 0) + (PF >= 2 ? (1 < NPV ? 2 : 1) : 0) +
-                        (PF >= 3 ? (2 < NPV ? 2 : 1) : 0) + (PF >= 4 ? (3 < NPV ? 2 : 1) : 0);
-    static_assert(PF <= 4, "prefetch depth");
-    __builtin_amdgcn_sched_group_barrier(kDsRead, pre, 0);
+    constexpr int NS = TS::value ? (N - (TPV::value ? N / 2 : 0)) : 0;
     (
         [] {
             __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
-            if constexpr (I + PF < N)
-                __builtin_amdgcn_sched_group_barrier(kDsRead, (I + PF < NPV) ? 2 : 1, 0);
+            if constexpr (I + AHD < N)
+                __builtin_amdgcn_sched_group_barrier(kDsRead, (I + AHD < NS) ? 1 : 2, 0);
         }(),
         ...);
 }
@@ -106,6 +106,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
     const int q0 = id.tile * BR;
     const int qw = q0 + 32 * w;   // first query of this wave
     const int qrow = qw + c;      // the query this lane owns
+    const int grp = w / Cfg::NW;  // 0 or 1: phase offset of the ping-pong
 
     const bf16* qh = static_cast<const bf16*>(a.q) + (size_t)(b * a.Hq + hq) * a.T * D;
     const bf16* kh = static_cast<const bf16*>(a.k) + (size_t)(b * a.Hkv + hk) * a.T * D;
@@ -145,6 +146,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
 
     load_stage(0);
     load_stage(1);  // nkv >= 1, so stage 1 holds at least V_0
+    if (nkv >= 2) load_stage(2);
 
     // B operand of S^T = K Q^T: this lane's query row, 8 columns per step
     Frag<bf16> qf[NKS];
@@ -162,54 +164,60 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
     vm_wait<0>();
     sync_lds();
 
-    // Matrix step M(j): O^T += V_{j-1}^T P_{j-1}^T (PV) and S_j^T = K_j Q^T
-    // (S), from stage j.  The 16 (PV) plus 16 (S) fragment reads run PF
-    // MFMAs ahead of their products.
+    // Matrix step M(j): S_j^T = K_j Q^T (S, j < nkv) and O^T += V_{j-1}^T
+    // P_{j-1}^T (PV, j >= 1), all operands from stage j.  Product i reads its
+    // A fragment AHD products ahead into a ring of registers; the first AHD
+    // reads are issued by the preceding vector step of the same wave (its LDS
+    // port is otherwise idle), so the matrix step starts without waiting.
+    constexpr int AHD = Cfg::AHD, RING = AHD + 1;
+    bf16x8 ring[RING];
+    auto frag_read = [&](int j, int i, auto with_pv, auto with_s) -> bf16x8 {
+        constexpr bool PV = decltype(with_pv)::value, SS = decltype(with_s)::value;
+        constexpr int NS = SS ? NKS * NKB : 0;
+        const unsigned char* st = smem + (j % Cfg::NSTAGE) * Cfg::STAGE;
+        if (i < NS) {
+            const int kb = i % NKB, ks = i / NKB;
+            return KT::read(st + 16 * lane, kb, ks);
+        }
+        (void)PV;
+        const int k = i - NS, db = k % NDB, t = (k / NDB) % 2, kb = k / (2 * NDB);
+        return VT::read(st + KT::BYTES + 8 * lane, 2 * kb + t, db);
+    };
+    auto prefetch = [&](int j, auto with_pv, auto with_s) {
+#pragma unroll
+        for (int i = 0; i < AHD; ++i) ring[i] = frag_read(j, i, with_pv, with_s);
+    };
     auto matrix_step = [&](int j, auto with_pv, auto with_s) {
         constexpr bool PV = decltype(with_pv)::value, SS = decltype(with_s)::value;
         constexpr int NPV = PV ? NKB * 2 * NDB : 0;   // PV products
         constexpr int NS = SS ? NKS * NKB : 0;        // S products
         constexpr int N = NPV + NS;
-        constexpr int PF = 3;
-        const unsigned char* st = smem + (j % Cfg::NSTAGE) * Cfg::STAGE;
-        const unsigned char* vl = st + KT::BYTES + 8 * lane;
-        const unsigned char* kl = st + 16 * lane;
-        // product i < NPV: (kb, t, db) = PV block; else (ks, kb) = S block
-        auto read = [&](int i) -> bf16x8 {
-            if (i < NPV) {
-                const int db = i % NDB, t = (i / NDB) % 2, kb = i / (2 * NDB);
-                return VT::read(vl, 2 * kb + t, db);
-            }
-            const int k = i - NPV, kb = k % NKB, ks = k / NKB;
-            return KT::read(kl, kb, ks);
-        };
+        static_assert(N > AHD, "prefetch depth");
         if constexpr (SS) {
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
         }
-        bf16x8 fb[PF + 1];
-#pragma unroll
-        for (int i = 0; i < PF; ++i) fb[i] = read(i);
 #pragma unroll
         for (int i = 0; i < N; ++i) {
-            if (i + PF < N) fb[(i + PF) % (PF + 1)] = read(i + PF);
+            if (i + AHD < N) ring[(i + AHD) % RING] = frag_read(j, i + AHD, with_pv, with_s);
             Frag<bf16> af;
-            af.v = fb[i % (PF + 1)];
-            if (i < NPV) {
-                const int db = i % NDB, t = (i / NDB) % 2, kb = i / (2 * NDB);
-                mma(o[db], af, pf[kb][t]);
-            } else {
-                const int k = i - NPV, kb = k % NKB, ks = k / NKB;
+            af.v = ring[i % RING];
+            if (i < NS) {
+                const int kb = i % NKB, ks = i / NKB;
                 mma(s[kb], af, qf[ks]);
+            } else {
+                const int k = i - NS, db = k % NDB, t = (k / NDB) % 2, kb = k / (2 * NDB);
+                mma(o[db], af, pf[kb][t]);
             }
         }
-        pin_mfma_ds_interleave<N, PF, NPV>(std::make_integer_sequence<int, N>{});
+        pin_mfma_ds_interleave<N, AHD>(std::make_integer_sequence<int, N>{}, with_pv, with_s);
     };
 
     // Vector step V(j): mask, lazy reference update (rescaling O and l when it
     // moves), P_j = exp2(S_j c - mref) with fp32 row sums, rounded for P V.
     auto vector_step = [&](int j) {
         if (j >= nfull) {
+            asm volatile("");  // keep this a branch
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -247,18 +255,24 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
         }
     };
 
-    // Iteration j: M(j), then V(j).  Stage j is read by M(j) in iteration j
-    // only; stage j + 2 is issued at the start of iteration j into the buffer
-    // of stage j - 1 (read in iteration j - 1, before the barrier that ended
-    // it), and stage j + 1 is waited for at the end of iteration j.  The two
-    // waves of a SIMD run independently between barriers, so the matrix work
-    // of one overlaps the vector work of the other.
-    auto issue_ahead = [&](int j) {
-        if (j + 2 <= nkv) load_stage(j + 2);
+    // Lock-step phases (ping-pong).  Group 0 runs the sequence M(0) V(0) M(1)
+    // V(1) ... V(nkv-1) M(nkv), one step per phase; group 1 runs it one phase
+    // later, so in every phase one wave of each SIMD issues MFMAs while its
+    // partner does vector work (one MFMA stream per SIMD at a time runs faster
+    // than two interleaved ones).  V(j) also issues the first fragment reads
+    // of M(j + 1) from stage j + 1.  Stage s is issued at the start of phase
+    // 2s - 6 (stages 0..2 before the loop) into the buffer of stage s - 4,
+    // whose last reader ended with phase 2s - 7; stage j + 1 is waited for at
+    // the end of phase 2j, before the first vector step that prefetches from
+    // it (group 0's V(j), phase 2j + 1).
+    auto issue_ahead = [&](int j) {  // phase 2j
+        if (j + 3 <= nkv) load_stage(j + 3);
     };
-    auto wait_next = [&](int j) {  // stage j + 1 must land; stage j + 2 may fly
-        if (j + 2 < nkv)
-            vm_wait<KI + VI>();
+    auto wait_after_even = [&](int j) {  // end of phase 2j: stage j + 1 must land
+        if (j + 3 < nkv)
+            vm_wait<2 * (KI + VI)>();
+        else if (j + 3 == nkv)
+            vm_wait<(KI + VI) + VI>();
         else if (j + 2 == nkv)
             vm_wait<VI>();
         else
@@ -267,17 +281,46 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
     };
     using T0 = std::integral_constant<bool, false>;
     using T1 = std::integral_constant<bool, true>;
-    issue_ahead(0);
-    matrix_step(0, T0{}, T1{});
-    vector_step(0);
-    wait_next(0);
-    for (int j = 1; j < nkv; ++j) {
-        issue_ahead(j);
-        matrix_step(j, T1{}, T1{});
-        vector_step(j);
-        wait_next(j);
+    prefetch(0, T0{}, T1{});
+    if (grp == 0) {
+        issue_ahead(0);
+        matrix_step(0, T0{}, T1{});
+        wait_after_even(0);
+        for (int j = 0; j + 1 < nkv; ++j) {
+            vector_step(j);
+            prefetch(j + 1, T1{}, T1{});
+            sync_lds();
+            issue_ahead(j + 1);
+            matrix_step(j + 1, T1{}, T1{});
+            wait_after_even(j + 1);
+        }
+        vector_step(nkv - 1);
+        prefetch(nkv, T1{}, T0{});
+        sync_lds();
+        issue_ahead(nkv);
+        matrix_step(nkv, T1{}, T0{});
+        wait_after_even(nkv);
+        sync_lds();
+    } else {
+        issue_ahead(0);
+        wait_after_even(0);
+        matrix_step(0, T0{}, T1{});
+        sync_lds();
+        for (int j = 0; j + 1 < nkv; ++j) {
+            issue_ahead(j + 1);
+            vector_step(j);
+            prefetch(j + 1, T1{}, T1{});
+            wait_after_even(j + 1);
+            matrix_step(j + 1, T1{}, T1{});
+            sync_lds();
+        }
+        issue_ahead(nkv);
+        vector_step(nkv - 1);
+        prefetch(nkv, T1{}, T0{});
+        wait_after_even(nkv);
+        matrix_step(nkv, T1{}, T0{});
+        sync_lds();
     }
-    matrix_step(nkv, T1{}, T0{});
 
     // epilogue: divide by l, store O (this lane: query qrow, columns
     // 32db + 8rg + 4g + i) and lse

@@ -35,7 +35,11 @@ typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ i32x4 buffer_rsrc(const void* base, int bytes)
 {
     const uint64_t addr = (uint64_t)(uintptr_t)base;
-    return i32x4{(int32_t)(uint32_t)addr, (int32_t)((addr >> 32) & 0xffff), bytes, kBufferFlags};
+    // the words must sit in scalar registers; readfirstlane states that they
+    // are uniform where the compiler cannot prove it
+    return i32x4{__builtin_amdgcn_readfirstlane((int32_t)(uint32_t)addr),
+                 __builtin_amdgcn_readfirstlane((int32_t)((addr >> 32) & 0xffff)),
+                 __builtin_amdgcn_readfirstlane(bytes), kBufferFlags};
 }
 
 // 32-bit LDS address of a pointer into a __shared__ array.

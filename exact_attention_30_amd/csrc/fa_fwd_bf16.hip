@@ -14,16 +14,17 @@
 //     are in-lane reductions plus one exchange with lane c ^ 32.  The S^T
 //     accumulator is exponentiated in place (exp2, scale*log2 e folded in) and
 //     fed back as the B operand of O^T += V^T P^T: P never touches LDS.
-//   * Two waves per SIMD (eight per workgroup) run independently between
-//     one barrier per key tile, so the matrix work of one overlaps the vector
-//     work of the other.  Within a wave the matrix step of tile j also issues
-//     the P V product of tile j - 1: M(j) = { O += P_{j-1} V_{j-1};
-//     S_j = Q K_j^T } (MFMAs, LDS reads), then V(j) = { mask; max; rescale;
-//     P_j = exp2(...) } (vector ALU).
+//   * Two waves per SIMD (eight per workgroup) in two groups of four that
+//     run in lock step, one phase apart: in every phase one wave of each SIMD
+//     issues MFMAs while its partner does vector work.  The matrix step of
+//     tile j also issues the P V product of tile j - 1: M(j) = { O += P_{j-1}
+//     V_{j-1}; S_j = Q K_j^T } (MFMAs, LDS reads), then V(j) = { mask; max;
+//     rescale; P_j = exp2(...) } (vector ALU), which also reads the first
+//     operand fragments of M(j + 1).
 //   * K and V tiles move from HBM to LDS by LDS DMA in read order (no bank
-//     conflicts, one address register per operand), three stages deep: stage
-//     j = {K_j, V_{j-1}} is the LDS data of step M(j), issued four phases
-//     before it is needed.
+//     conflicts, one address register per operand) into four stage buffers:
+//     stage j = {K_j, V_{j-1}} is the LDS data of step M(j), issued six
+//     phases before the first read of it.
 //   * Lazy rescale: the reference max of a row only moves when the row max
 //     exceeds it by more than 8 (log2 units), so most tiles skip rescaling O
 //     and l; the weights stay below 2^8, and o and l share the reference.

@@ -9,8 +9,9 @@
 // 256 keys): two waves per SIMD, so the matrix work of one overlaps the
 // vector work of the other.  Wave w owns 32 keys: K of those keys stays in
 // registers (B operand of S = Q K^T) and the dK^T, dV^T accumulators never
-// leave the register file; V of the workgroup's keys is loaded once into LDS
-// (B operand of dP = dO V^T), which keeps a wave within its 256 registers.
+// leave the register file; V of the wave's keys is loaded once into LDS in
+// read order (B operand of dP = dO V^T), which keeps a wave within its 256
+// registers.
 // Query tiles of 32 rows, of every query head of the kv group, stream through
 // LDS, shared by the eight waves; the group sum of dK and dV therefore stays
 // inside the workgroup and no atomics are needed (the result is bitwise
@@ -19,8 +20,9 @@
 //     P, mask, dS, bf16 operands          (vector ALU)
 //     dV^T += dO_t^T P, dK^T += Q_t^T dS  (16 MFMAs, transposed reads)
 // The tiles arrive by explicitly scheduled LDS DMA three tiles ahead in four
-// stage buffers; the loop is unrolled over the stages, so every LDS offset is
-// an immediate.  Tiles wholly visible to a wave carry no mask code; with
+// stage buffers at the bottom of LDS; the loop is unrolled over the stages and
+// the per-lane read addresses carry the LDS base, so every read is one address
+// register plus an immediate offset, with no address arithmetic in the loop.  Tiles wholly visible to a wave carry no mask code; with
 // 32-row query tiles and 32-key waves any other tile is exactly the lower
 // triangle or wholly invisible, handled in a rarely taken branch.
 #include <type_traits>
@@ -44,10 +46,12 @@ struct DkdvBf16Cfg {
     static constexpr int QNT = (BQ * D / 8 >= NT) ? NT : BQ * D / 8;
     using QT = SwzTile<D, BQ, QNT>;
     using Fmt = DmaTile<bf16, D, BQ, QNT>;
-    using VT = SwzTile<D, BK, NT>;
+    using VW = RowFragTile<D, 32>;  // V rows of one wave, in read order
     static constexpr int STATS = 512;  // L*log2(e) (64 floats) and Delta (64 floats)
     static constexpr int STAGE = 2 * QT::BYTES + STATS;
-    static constexpr int SMEM = VT::BYTES + NSTAGE * STAGE;
+    static constexpr int SMEM = NSTAGE * STAGE + NW * VW::BYTES;
+    // every read offset of a stage fits the 16-bit immediate of a DS read
+    static_assert((NSTAGE - 1) * STAGE + QT::BYTES + 16 * Fmt::ROWBYTES < 65536, "LDS immediates");
     static_assert(AHEAD + 1 <= NSTAGE, "a stage is refilled only after its tile was used");
     static_assert(QT::NI == 1, "one Q and one dO instruction per loading wave");
 };
@@ -95,7 +99,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
     using Cfg = DkdvBf16Cfg<D>;
     using QT = typename Cfg::QT;
     using Fmt = typename Cfg::Fmt;
-    using VT = typename Cfg::VT;
+    using VW = typename Cfg::VW;
     constexpr int BK = Cfg::BK, BQ = Cfg::BQ, NSTAGE = Cfg::NSTAGE, STAGE = Cfg::STAGE;
     constexpr int AHEAD = Cfg::AHEAD;
     constexpr int NDB = D / 32;
@@ -103,8 +107,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
     constexpr int QW = Cfg::QNT / 64;  // waves that move Q and dO tiles
 
     extern __shared__ __align__(1024) unsigned char smem[];
-    unsigned char* Vs = smem;
-    unsigned char* stages = smem + VT::BYTES;
+    unsigned char* stages = smem;
+    unsigned char* Vs = smem + NSTAGE * STAGE;  // V rows of wave w at Vs + w * VW::BYTES
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -175,10 +179,12 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
     for (int off = tid * 16; off < NSTAGE * STAGE; off += Cfg::NT * 16)
         *reinterpret_cast<u32x4*>(stages + off) = u32x4{0, 0, 0, 0};
     sync_lds();
-    {
-        VT vt;
-        vt.init(tid);
-        vt.load(lds_addr(Vs), vh, key0, a.T, w);
+    {  // this wave's 32 V rows (rows past T read as zeros)
+        const int left = a.T - kw;
+        const i32x4 r = buffer_rsrc(vh + (size_t)kw * D, left > 0 ? left * D * 2 : 0);
+        const uint32_t vb = lds_addr(Vs) + (uint32_t)(w * VW::BYTES);
+#pragma unroll
+        for (int f = 0; f < VW::NDMA; ++f) dma_b128(vb + (uint32_t)(f * 1024), r, VW::dma_off(f, lane));
     }
     for (int t = 0; t < AHEAD && t < n; ++t) issue(t);  // stage t
 
@@ -187,12 +193,19 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) kf[ks] = global_frag<bf16>(kh, krow, a.T, D, 16 * ks + 8 * g);
 
-    // Q, dO rows (A of S, dP) and V rows w*32 + c (B of dP): the V tile has
-    // the same row format, so the same offsets serve
-    RowReader<Fmt, bf16, D> qrd;
-    qrd.init(c, g);
-    TrReader<Fmt, bf16, D> trd;  // Q^T and dO^T (A of dK^T, dV^T)
-    trd.init(lane);
+    // Q, dO rows (A of S, dP) and Q^T, dO^T (A of dK^T, dV^T) in the
+    // stages; V rows 32w + c (B of dP) in read order
+    SwzRowFrags<Fmt, D> qrd;
+    qrd.init(lds_addr(stages), c, g);
+    SwzTrFrags<Fmt, D> trd;
+    trd.init(lds_addr(stages), lane);
+    uint32_t vrd = lds_addr(Vs) + (uint32_t)(w * VW::BYTES + 16 * lane);
+    asm volatile("" : "+v"(vrd));
+    auto frag = [](bf16x8 v) {
+        Frag<bf16> f;
+        f.v = v;
+        return f;
+    };
 
     f32x16 dk[NDB], dv[NDB];
 #pragma unroll
@@ -208,6 +221,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
     };
 
     vm_wait<0>();  // V and the first tiles
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) settle(kf[ks].v);
     convert_l(0);
     sync_lds();
     int bti = nq - 1, bh = 0;  // query tile and head (in the group) being computed
@@ -220,11 +235,12 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
         const float* Ds = Ls + 64;
         if (i + AHEAD < n) issue((ST + AHEAD) % NSTAGE);
 
+        constexpr uint32_t QI = ST * STAGE, OI = QI + QT::BYTES;  // Q_t, dO_t in the stage
         f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-            mma(s, qrd.frag(Qs, 0, ks), kf[ks]);
-            mma(dp, qrd.frag(dOs, 0, ks), qrd.frag(Vs, 32 * w, ks));
+            mma(s, frag(qrd.read(ks, QI)), kf[ks]);
+            mma(dp, frag(qrd.read(ks, OI)), frag(lds_b128(vrd + (uint32_t)VW::frag_off(0, ks))));
         }
         // Tiles wholly visible to this wave take no mask code; the others set
         // the invisible scores to -inf, so that P = 0 there.
@@ -262,8 +278,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
             const Frag<bf16> sf = acc_frag<bf16>(dp, t);
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                mma(dv[db], trd.frag(dOs, 16 * t, db), pf);
-                mma(dk[db], trd.frag(Qs, 16 * t, db), sf);
+                mma(dv[db], frag(trd.read(db, OI + 16 * t * Fmt::ROWBYTES)), pf);
+                mma(dk[db], frag(trd.read(db, QI + 16 * t * Fmt::ROWBYTES)), sf);
             }
         }
         // tile i + 1 must have landed before the barrier that starts the next
@@ -412,6 +428,13 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
     for (int db = 0; db < NDB; ++db) dq[db] = f32x16{};
 
     vm_wait<0>();
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        settle(qf[ks].v);
+        settle(of[ks].v);
+    }
+    settle(L2);
+    settle(Dl);
     sync_lds();
 
     auto body = [&](auto st_tag, int j) {

@@ -204,6 +204,14 @@ namespace fa {
 __device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void pin(uint32_t& x) { asm volatile("" : "+v"(x)); }
 
+// Empty asm that reads a register value loaded from global memory: the
+// compiler's wait for that load is placed before this point.  Called once
+// before a loop, it keeps the compiler from waiting at the value's first use
+// inside the loop, where its s_waitcnt vmcnt(0) would also drain the
+// explicitly issued LDS DMA of the tiles ahead on every pass.
+__device__ __forceinline__ void settle(const bf16x8& x) { asm volatile("" ::"v"(x)); }
+__device__ __forceinline__ void settle(float x) { asm volatile("" ::"v"(x)); }
+
 // Two floats rounded to nearest even bf16, packed (first in the low half).
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
 {
@@ -211,5 +219,77 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
     const bf16x2 v = {(bf16)lo, (bf16)hi};
     return __builtin_bit_cast(uint32_t, v);
 }
+
+}  // namespace fa
+
+namespace fa {
+
+// Reads at a 32-bit LDS byte address.  A compile-time constant added to the
+// address becomes the instruction's 16-bit immediate offset.
+__device__ __forceinline__ bf16x8 lds_b128(uint32_t addr)
+{
+    return *(const __attribute__((address_space(3))) bf16x8*)addr;
+}
+__device__ __forceinline__ bf16x4 lds_tr_b64(uint32_t addr)
+{
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)addr);
+}
+
+// Operand fragments of bf16 blocks stored in the swizzled row format `Tile`
+// (DmaTile) inside one LDS region.  The region's address is folded into the
+// per-lane addresses once, and an empty asm hides where they came from, so
+// the compiler cannot re-derive them from the LDS symbol at every read (it
+// would add the base again per read); each read is then one address register
+// plus an immediate (block, stage and row offsets, below 64 KiB).
+//
+// SwzRowFrags: fragment ks of rows rowbase + c, columns 16ks + 8g .. +7
+// (A or B operand, one ds_read_b128).
+template <class Tile, int D>
+struct SwzRowFrags {
+    static constexpr int NKS = D / 16;
+    uint32_t addr[NKS];
+
+    __device__ __forceinline__ void init(uint32_t region, int c, int g)
+    {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            addr[ks] = region + (uint32_t)Tile::offset(c, 16 * ks + 8 * g);
+            asm volatile("" : "+v"(addr[ks]));
+        }
+    }
+    // imm: byte offset of the block in the region + rowbase * ROWBYTES
+    // (rowbase a multiple of 16, so the swizzle of row c applies)
+    __device__ __forceinline__ bf16x8 read(int ks, uint32_t imm) const { return lds_b128(addr[ks] + imm); }
+};
+
+// SwzTrFrags: transposed fragment (A operand of a product that contracts over
+// rows): lane (g, c) receives the elements (rowbase + 8(e/4) + 4g + e%4,
+// 32db + c), e = 0..7, as two ds_read_b64_tr_b16 (see TrReader).
+template <class Tile, int D>
+struct SwzTrFrags {
+    static constexpr int NDB = D / 32;
+    uint32_t addr[NDB][2];
+
+    __device__ __forceinline__ void init(uint32_t region, int lane)
+    {
+        const int m = lane >> 4, j = lane & 15;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                addr[db][h] = region + (uint32_t)Tile::offset(8 * h + 4 * (m >> 1) + (j >> 2),
+                                                              db * 32 + 16 * (m & 1) + 4 * (j & 3));
+                asm volatile("" : "+v"(addr[db][h]));
+            }
+    }
+    // imm: byte offset of the block in the region + rowbase * ROWBYTES
+    // (rowbase a multiple of 16)
+    __device__ __forceinline__ bf16x8 read(int db, uint32_t imm) const
+    {
+        const bf16x4 lo = lds_tr_b64(addr[db][0] + imm);
+        const bf16x4 hi = lds_tr_b64(addr[db][1] + imm);
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+};
 
 }  // namespace fa

@@ -317,7 +317,9 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
 // dQ kernel.  One workgroup of eight waves per (batch, query head, block of
 // 256 query rows), two waves per SIMD; wave w owns 32 queries and keeps Q and
 // dO of them in registers.  Key tiles of 64 rows walk past in the forward's
-// order, K and V by LDS DMA two tiles ahead into three stage buffers.  Per
+// order, K and V by LDS DMA two tiles ahead into three stage buffers (K
+// swizzled, read row-wise and transposed; V in read order; every read one
+// address register plus an immediate offset).  Per
 // 32-key block a wave forms S^T = K Q^T and dP^T = V dO^T with keys as rows,
 // P^T = exp2(S^T c - L), dS^T = P^T (dP^T - Delta), and accumulates
 // dQ^T += K^T dS^T with dS^T straight from registers; K^T is read transposed
@@ -331,10 +333,17 @@ struct DqBf16Cfg {
     static constexpr int BC = 64;       // keys per tile
     static constexpr int NSTAGE = 3;
     static constexpr int AHEAD = 2;
-    using KT = SwzTile<D, BC, NT>;  // K (row-wise and transposed) and V (row-wise)
+    using KT = SwzTile<D, BC, NT>;  // K: read row-wise and transposed
     using Fmt = DmaTile<bf16, D, BC, NT>;
-    static constexpr int STAGE = 2 * KT::BYTES;
-    static constexpr int SMEM = NSTAGE * STAGE;
+    using VT = RowFragTile<D, BC>;  // V: read row-wise, stored in read order
+    static constexpr int VI = VT::NDMA / NW;  // V DMA instructions per wave and tile
+    static_assert(VT::NDMA % NW == 0, "V DMA split");
+    // K tiles of all stages first, then the V tiles: every read offset fits
+    // the 16-bit immediate of a DS read
+    static constexpr int VBASE = NSTAGE * KT::BYTES;
+    static constexpr int SMEM = VBASE + NSTAGE * VT::BYTES;
+    static_assert((NSTAGE - 1) * KT::BYTES + BC * Fmt::ROWBYTES < 65536, "LDS immediates");
+    static_assert((NSTAGE - 1) * VT::BYTES + VT::BYTES < 65536, "LDS immediates");
     static_assert(AHEAD + 1 <= NSTAGE, "a stage is refilled only after its tile was used");
 };
 
@@ -344,12 +353,13 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
     using Cfg = DqBf16Cfg<D>;
     using KT = typename Cfg::KT;
     using Fmt = typename Cfg::Fmt;
-    constexpr int BR = Cfg::BR, BC = Cfg::BC, NSTAGE = Cfg::NSTAGE, STAGE = Cfg::STAGE;
+    using VT = typename Cfg::VT;
+    constexpr int BR = Cfg::BR, BC = Cfg::BC, NSTAGE = Cfg::NSTAGE, NWAVE = Cfg::NW;
     constexpr int AHEAD = Cfg::AHEAD;
     constexpr int NKB = BC / 32;
     constexpr int NDB = D / 32;
     constexpr int NKS = D / 16;
-    constexpr int VPT = 2 * KT::NI;  // DMA instructions per tile and wave
+    constexpr int VPT = KT::NI + Cfg::VI;  // DMA instructions per tile and wave
 
     extern __shared__ __align__(1024) unsigned char smem[];
 
@@ -382,10 +392,16 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
     const uint32_t lds0 = lds_addr(smem);
     KT kt;
     kt.init(tid);
-    auto issue = [&](int j, int st) {
-        const uint32_t base = lds0 + (uint32_t)(st * STAGE);
-        kt.load(base, kh, j * BC, a.T, w);
-        kt.load(base + KT::BYTES, vh, j * BC, a.T, w);
+    uint32_t vdma[Cfg::VI];
+#pragma unroll
+    for (int i = 0; i < Cfg::VI; ++i) vdma[i] = VT::dma_off(w + NWAVE * i, lane);
+    auto issue = [&](int j, int st) {  // tile j into stage st
+        kt.load(lds0 + (uint32_t)(st * KT::BYTES), kh, j * BC, a.T, w);
+        const int left = a.T - j * BC;
+        const i32x4 r = buffer_rsrc(vh + (size_t)j * BC * D, left > 0 ? left * D * 2 : 0);
+        const uint32_t vb = lds0 + (uint32_t)(Cfg::VBASE + st * VT::BYTES);
+#pragma unroll
+        for (int i = 0; i < Cfg::VI; ++i) dma_b128(vb + (uint32_t)((w + NWAVE * i) * 1024), r, vdma[i]);
     };
     // wait until tile j has landed while tiles j + 1 .. j + AHEAD - 1 (those
     // that exist) stay in flight
@@ -418,10 +434,17 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
         Dl = a.delta[r];
     }
 
-    RowReader<Fmt, bf16, D> rrd;  // K and V rows (A of S^T, dP^T)
-    rrd.init(c, g);
-    TrReader<Fmt, bf16, D> trd;   // K^T (A of dQ^T)
-    trd.init(lane);
+    SwzRowFrags<Fmt, D> krd;  // K rows (A of S^T)
+    krd.init(lds0, c, g);
+    SwzTrFrags<Fmt, D> ktr;   // K^T (A of dQ^T)
+    ktr.init(lds0, lane);
+    uint32_t vrd = lds0 + (uint32_t)(Cfg::VBASE + 16 * lane);  // V rows (A of dP^T)
+    asm volatile("" : "+v"(vrd));
+    auto frag = [](bf16x8 v) {
+        Frag<bf16> f;
+        f.v = v;
+        return f;
+    };
 
     f32x16 dq[NDB];
 #pragma unroll
@@ -439,8 +462,7 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
 
     auto body = [&](auto st_tag, int j) {
         constexpr int ST = decltype(st_tag)::value;
-        const unsigned char* Ks = smem + ST * STAGE;
-        const unsigned char* Vs = Ks + KT::BYTES;
+        constexpr uint32_t KI = ST * KT::BYTES, VIM = ST * VT::BYTES;  // this stage's tiles
         if (j + AHEAD < nkv) issue(j + AHEAD, (ST + AHEAD) % NSTAGE);
         const bool masked = j >= nfull;  // diagonal, future or padded tile
 #pragma unroll
@@ -448,8 +470,8 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
             f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
-                mma(s, rrd.frag(Ks, kb * 32, ks), qf[ks]);
-                mma(dp, rrd.frag(Vs, kb * 32, ks), of[ks]);
+                mma(s, frag(krd.read(ks, KI + kb * 32 * Fmt::ROWBYTES)), qf[ks]);
+                mma(dp, frag(lds_b128(vrd + VIM + (uint32_t)VT::frag_off(kb, ks))), of[ks]);
             }
             if (masked) {
                 asm volatile("");  // keep this a branch
@@ -469,7 +491,8 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
             for (int t = 0; t < 2; ++t) {
                 const Frag<bf16> sf = acc_frag<bf16>(dp, t);
 #pragma unroll
-                for (int db = 0; db < NDB; ++db) mma(dq[db], trd.frag(Ks, kb * 32 + 16 * t, db), sf);
+                for (int db = 0; db < NDB; ++db)
+                    mma(dq[db], frag(ktr.read(db, KI + (kb * 32 + 16 * t) * Fmt::ROWBYTES)), sf);
             }
         }
         wait_tile(j + 1);

@@ -136,6 +136,58 @@ def traffic_for(kernel: str, kernel_file: str, workload: str):
     return e.get("hbm_bytes_per_launch")
 
 
+def describe(w) -> str:
+    return (f"{w.name}: {'causal' if w.causal else 'non-causal'} {'GQA' if w.Hq != w.Hkv else 'MHA'} "
+            f"attention {'fwd+bwd' if w.backward else 'fwd'}, B={w.B} Hq={w.Hq} Hkv={w.Hkv} "
+            f"T={w.T} D={w.D}, scale={w.scale:.6g}")
+
+
+def forward_only(args, w, x, q, k, v, o, lse):
+    """A forward-only workload: one step is one fa_fwd; the line reports the
+    forward's credited TFLOP/s (no backward exists for it)."""
+    import torch
+
+    import exact_attention_30_amd as fa
+
+    for _ in range(args.warmup):
+        fa.fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse)
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for ev in events:
+        ev[0].record()
+        fa.fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse)
+        ev[1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = sum(ev[0].elapsed_time(ev[1]) for ev in events) / args.steps
+    ms_per_step = max(wall * 1e3 / args.steps, events[0][0].elapsed_time(events[-1][1]) / args.steps)
+    bf = w.dtype == torch.bfloat16
+    peak = PEAK_BF16_TFLOPS if bf else PEAK_FP32_TFLOPS
+    value = w.fwd_flop / (ms_per_step * 1e-3) / 1e12
+    achieved = gemm_flop(w, KERNEL_GEMMS["fwd"]) / (per * 1e-3) / 1e12
+    kfile = "fa_fwd_bf16.hip" if bf else "fa_fwd.hip"
+    out = {
+        "metric": "attention fwd TFLOP/s on 1 MI355X; % of bf16 MFMA peak (forward-only workload)",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if bf else "fp32",
+        "data": "synthetic (seeded N(0,1) inputs of the workload's shape)",
+        "config": {"workload": describe(w), "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "T": w.T, "D": w.D,
+                   "causal": w.causal, "parallelism": "single GPU"},
+        "pct_of_peak": round(100 * value / peak, 2),
+        "roofline": {
+            "kernel": "fwd_bf16_kernel" if bf else "fwd_kernel", "bound": "mfma",
+            "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": traffic_for("fwd", kfile, w.name),
+            "avg_launch_ms": round(per, 4),
+            "algorithmic_flop_per_launch": gemm_flop(w, KERNEL_GEMMS["fwd"]),
+        },
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def cpu_baseline(w, x, target_s: float):
     """Time the oracle's fwd + bwd on a bounded sample of the workload, sized
     to take about target_s seconds: whole kv groups (all their query heads,
@@ -211,18 +263,19 @@ def main():
     from workloads import WORKLOADS, workload_inputs
 
     w = WORKLOADS[args.workload]
-    if not w.backward:
-        raise SystemExit(f"{w.name} is forward-only; the benchmark step needs a backward")
     print(f"[bench] workload {w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} T={w.T} D={w.D} "
           f"causal={w.causal} {w.dtype}", file=sys.stderr, flush=True)
     x = workload_inputs(w)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     d = {k: v.to(dev) for k, v in x.items()}
-    q, k, v, do = d["q"], d["k"], d["v"], d["dout"]
+    q, k, v, do = d["q"], d["k"], d["v"], d.get("dout")
     o = torch.empty_like(q)
     lse = torch.empty(w.B, w.Hq, w.T, dtype=torch.float32, device=dev)
     delta = torch.empty(w.B, w.Hq, w.T, dtype=torch.float32, device=dev)
+    if not w.backward:
+        forward_only(args, w, x, q, k, v, o, lse)
+        return
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
 
     def step(ev=None):
@@ -305,8 +358,7 @@ def main():
         "dtype": "bf16" if w.dtype == torch.bfloat16 else "fp32",
         "data": "synthetic (seeded N(0,1) inputs of the workload's shape)",
         "config": {
-            "workload": f"{w.name}: causal GQA attention fwd+bwd, B={w.B} Hq={w.Hq} Hkv={w.Hkv} "
-                        f"T={w.T} D={w.D}, scale={w.scale:.6g}",
+            "workload": describe(w),
             "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "T": w.T, "D": w.D, "causal": w.causal,
             "parallelism": "single GPU",
         },

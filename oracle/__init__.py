@@ -12,11 +12,14 @@ Pages the oracle follows (cited by title and section):
     GPU is tested against that CPU definition; «La passe arrière» gives
     L = m + ln(l) and the gradient equations.
   * "Optimización de Flash Attention ... NVIDIA CUDA Tile" — «Atención causal»
-    gives the mask (query i sees key j iff i >= j).
+    gives the mask (query i sees key j iff i >= j); the kernel interface of
+    «Parte 1» adds a position offset for it (input_pos): with Tq query rows
+    against Tk keys, query row i stands at position i + q_offset, and the
+    default offset Tk - Tq puts the last query on the last key.
   * "FlashAttention: l'attenzione che non spreca memoria" — «La online softmax,
     con i numeri» gives the safe (max-subtracted) softmax.
 
-All arrays are C-contiguous float64: q [B,Hq,T,D], k/v [B,Hkv,T,D].
+All arrays are C-contiguous float64: q [B,Hq,Tq,D], k/v [B,Hkv,Tk,D].
 """
 from __future__ import annotations
 
@@ -60,13 +63,18 @@ def _idx(idx) -> np.ndarray:
 
 def _shapes(q, k, v, dout=None):
     if q.ndim != 4 or k.ndim != 4 or v.shape != k.shape:
-        raise ValueError("q must be [B,Hq,T,D], k and v [B,Hkv,T,D]")
-    B, Hq, T, D = q.shape
-    if k.shape[0] != B or k.shape[2] != T or k.shape[3] != D or Hq % k.shape[1] != 0:
+        raise ValueError("q must be [B,Hq,Tq,D], k and v [B,Hkv,Tk,D]")
+    B, Hq, Tq, D = q.shape
+    if k.shape[0] != B or k.shape[3] != D or Hq % k.shape[1] != 0:
         raise ValueError(f"incompatible shapes q{q.shape} k{k.shape}")
     if dout is not None and dout.shape != q.shape:
         raise ValueError("dout must have the shape of q")
-    return B, Hq, k.shape[1], T, D
+    return B, Hq, k.shape[1], Tq, k.shape[2], D
+
+
+def _offset(Tq: int, Tk: int, q_offset) -> int:
+    """Position of query row 0 among the keys: Tk - Tq unless given."""
+    return int(Tk - Tq if q_offset is None else q_offset)
 
 
 def _check(rc: int):
@@ -81,11 +89,12 @@ class Oracle:
         lib = ctypes.CDLL(lib_path)
         i, d, l = ctypes.c_int, ctypes.c_double, ctypes.c_long
         dp, ip = _dp, _ip
-        lib.oracle_fwd.argtypes = [dp, dp, dp, dp, dp, dp, i, i, i, i, i, d, i]
-        lib.oracle_bwd.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, i, i, i, i, i, d, i]
-        lib.oracle_fwd_rows.argtypes = [dp, dp, dp, ip, l, dp, dp, i, i, i, i, i, d, i]
-        lib.oracle_dq_rows.argtypes = [dp, dp, dp, dp, ip, l, dp, i, i, i, i, i, d, i]
-        lib.oracle_dkdv_rows.argtypes = [dp, dp, dp, dp, ip, l, dp, dp, i, i, i, i, i, d, i]
+        shp = [i, i, i, i, i, i, d, i, i]  # B, Hq, Hkv, Tq, Tk, D, scale, causal, offset
+        lib.oracle_fwd.argtypes = [dp, dp, dp, dp, dp, dp] + shp
+        lib.oracle_bwd.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp] + shp
+        lib.oracle_fwd_rows.argtypes = [dp, dp, dp, ip, l, dp, dp] + shp
+        lib.oracle_dq_rows.argtypes = [dp, dp, dp, dp, ip, l, dp] + shp
+        lib.oracle_dkdv_rows.argtypes = [dp, dp, dp, dp, ip, l, dp, dp] + shp
         for f in (lib.oracle_fwd, lib.oracle_bwd, lib.oracle_fwd_rows, lib.oracle_dq_rows,
                   lib.oracle_dkdv_rows):
             f.restype = ctypes.c_int
@@ -97,36 +106,37 @@ class Oracle:
         """OpenMP threads the oracle's parallel loops use."""
         return int(self.lib.oracle_threads())
 
-    def fwd(self, q, k, v, scale: float, causal: bool, return_mag: bool = False):
-        """Return (o [B,Hq,T,D], lse [B,Hq,T]) in float64; with return_mag also
-        o_mag, the per-element sum of absolute terms sum_j |P_ij v_jd|."""
+    def fwd(self, q, k, v, scale: float, causal: bool, return_mag: bool = False, q_offset=None):
+        """Return (o [B,Hq,Tq,D], lse [B,Hq,Tq]) in float64; with return_mag also
+        o_mag, the per-element sum of absolute terms sum_j |P_ij v_jd|.
+        q_offset: position of query row 0 among the keys (default Tk - Tq)."""
         q, k, v = _f64(q), _f64(k), _f64(v)
-        B, Hq, Hkv, T, D = _shapes(q, k, v)
-        o = np.zeros((B, Hq, T, D))
-        lse = np.zeros((B, Hq, T))
-        om = np.zeros((B, Hq, T, D)) if return_mag else None
+        B, Hq, Hkv, Tq, Tk, D = _shapes(q, k, v)
+        o = np.zeros((B, Hq, Tq, D))
+        lse = np.zeros((B, Hq, Tq))
+        om = np.zeros((B, Hq, Tq, D)) if return_mag else None
         _check(self.lib.oracle_fwd(_p(q), _p(k), _p(v), _p(o), _p(lse),
-                                   _p(om) if return_mag else None, B, Hq, Hkv, T, D,
-                                   float(scale), int(bool(causal))))
+                                   _p(om) if return_mag else None, B, Hq, Hkv, Tq, Tk, D,
+                                   float(scale), int(bool(causal)), _offset(Tq, Tk, q_offset)))
         return (o, lse, om) if return_mag else (o, lse)
 
     def bwd(self, q, k, v, dout, scale: float, causal: bool, return_jac: bool = False,
-            return_mag: bool = False):
+            return_mag: bool = False, q_offset=None):
         """Return (dq, dk, dv) of the loss sum(O * dout); with return_jac also
-        the per-row Jacobian term c_i = sum_j P_ij dP_ij ([B,Hq,T]); with
+        the per-row Jacobian term c_i = sum_j P_ij dP_ij ([B,Hq,Tq]); with
         return_mag also (dq_mag, dk_mag, dv_mag), the per-element sums of the
-        absolute values of the terms."""
+        absolute values of the terms.  q_offset as in fwd."""
         q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
-        B, Hq, Hkv, T, D = _shapes(q, k, v, dout)
+        B, Hq, Hkv, Tq, Tk, D = _shapes(q, k, v, dout)
         dq = np.zeros_like(q)
         dk = np.zeros_like(k)
         dv = np.zeros_like(v)
-        jac = np.zeros((B, Hq, T))
+        jac = np.zeros((B, Hq, Tq))
         mags = (np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)) if return_mag else None
         mp = [_p(m) for m in mags] if return_mag else [None, None, None]
         _check(self.lib.oracle_bwd(_p(q), _p(k), _p(v), _p(dout), _p(dq), _p(dk), _p(dv),
-                                   _p(jac), *mp, B, Hq, Hkv, T, D, float(scale),
-                                   int(bool(causal))))
+                                   _p(jac), *mp, B, Hq, Hkv, Tq, Tk, D, float(scale),
+                                   int(bool(causal)), _offset(Tq, Tk, q_offset)))
         out = (dq, dk, dv)
         if return_jac:
             out = out + (jac,)
@@ -134,39 +144,40 @@ class Oracle:
             out = out + (mags,)
         return out
 
-    def fwd_rows(self, q, k, v, idx, scale: float, causal: bool):
+    def fwd_rows(self, q, k, v, idx, scale: float, causal: bool, q_offset=None):
         """Output rows for query rows idx = [(b, h, i), ...]: (o [n,D], lse [n])."""
         q, k, v = _f64(q), _f64(k), _f64(v)
-        B, Hq, Hkv, T, D = _shapes(q, k, v)
+        B, Hq, Hkv, Tq, Tk, D = _shapes(q, k, v)
         ix = _idx(idx)
         o = np.zeros((len(ix), D))
         lse = np.zeros(len(ix))
         _check(self.lib.oracle_fwd_rows(_p(q), _p(k), _p(v), ix.ctypes.data_as(_ip), len(ix),
-                                        _p(o), _p(lse), B, Hq, Hkv, T, D, float(scale),
-                                        int(bool(causal))))
+                                        _p(o), _p(lse), B, Hq, Hkv, Tq, Tk, D, float(scale),
+                                        int(bool(causal)), _offset(Tq, Tk, q_offset)))
         return o, lse
 
-    def dq_rows(self, q, k, v, dout, idx, scale: float, causal: bool):
+    def dq_rows(self, q, k, v, dout, idx, scale: float, causal: bool, q_offset=None):
         """dq rows for query rows idx = [(b, h, i), ...]: [n, D]."""
         q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
-        B, Hq, Hkv, T, D = _shapes(q, k, v, dout)
+        B, Hq, Hkv, Tq, Tk, D = _shapes(q, k, v, dout)
         ix = _idx(idx)
         dq = np.zeros((len(ix), D))
         _check(self.lib.oracle_dq_rows(_p(q), _p(k), _p(v), _p(dout), ix.ctypes.data_as(_ip),
-                                       len(ix), _p(dq), B, Hq, Hkv, T, D, float(scale),
-                                       int(bool(causal))))
+                                       len(ix), _p(dq), B, Hq, Hkv, Tq, Tk, D, float(scale),
+                                       int(bool(causal)), _offset(Tq, Tk, q_offset)))
         return dq
 
-    def dkdv_rows(self, q, k, v, dout, idx, scale: float, causal: bool):
+    def dkdv_rows(self, q, k, v, dout, idx, scale: float, causal: bool, q_offset=None):
         """dk and dv rows for key rows idx = [(b, hkv, j), ...]: ([n, D], [n, D])."""
         q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
-        B, Hq, Hkv, T, D = _shapes(q, k, v, dout)
+        B, Hq, Hkv, Tq, Tk, D = _shapes(q, k, v, dout)
         ix = _idx(idx)
         dk = np.zeros((len(ix), D))
         dv = np.zeros((len(ix), D))
         _check(self.lib.oracle_dkdv_rows(_p(q), _p(k), _p(v), _p(dout), ix.ctypes.data_as(_ip),
-                                         len(ix), _p(dk), _p(dv), B, Hq, Hkv, T, D,
-                                         float(scale), int(bool(causal))))
+                                         len(ix), _p(dk), _p(dv), B, Hq, Hkv, Tq, Tk, D,
+                                         float(scale), int(bool(causal)),
+                                         _offset(Tq, Tk, q_offset)))
         return dk, dv
 
 
@@ -184,22 +195,22 @@ def default() -> Oracle:
     return _default
 
 
-def fwd(q, k, v, scale: float, causal: bool, return_mag: bool = False):
-    return default().fwd(q, k, v, scale, causal, return_mag)
+def fwd(q, k, v, scale: float, causal: bool, return_mag: bool = False, q_offset=None):
+    return default().fwd(q, k, v, scale, causal, return_mag, q_offset)
 
 
 def bwd(q, k, v, dout, scale: float, causal: bool, return_jac: bool = False,
-        return_mag: bool = False):
-    return default().bwd(q, k, v, dout, scale, causal, return_jac, return_mag)
+        return_mag: bool = False, q_offset=None):
+    return default().bwd(q, k, v, dout, scale, causal, return_jac, return_mag, q_offset)
 
 
-def fwd_rows(q, k, v, idx, scale: float, causal: bool):
-    return default().fwd_rows(q, k, v, idx, scale, causal)
+def fwd_rows(q, k, v, idx, scale: float, causal: bool, q_offset=None):
+    return default().fwd_rows(q, k, v, idx, scale, causal, q_offset)
 
 
-def dq_rows(q, k, v, dout, idx, scale: float, causal: bool):
-    return default().dq_rows(q, k, v, dout, idx, scale, causal)
+def dq_rows(q, k, v, dout, idx, scale: float, causal: bool, q_offset=None):
+    return default().dq_rows(q, k, v, dout, idx, scale, causal, q_offset)
 
 
-def dkdv_rows(q, k, v, dout, idx, scale: float, causal: bool):
-    return default().dkdv_rows(q, k, v, dout, idx, scale, causal)
+def dkdv_rows(q, k, v, dout, idx, scale: float, causal: bool, q_offset=None):
+    return default().dkdv_rows(q, k, v, dout, idx, scale, causal, q_offset)

@@ -406,3 +406,160 @@ def test_kdk_equals_dqq():
         lhs = np.einsum("bhtd,bhte->bhde", k, dk)
         rhs = np.einsum("bhgtd,bhgte->bhde", dq.reshape(B, Hkv, 2, T, D), q.reshape(B, Hkv, 2, T, D))
         np.testing.assert_allclose(lhs, rhs, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Query rows against a longer (or shorter) key sequence, causal offset
+# ("Optimización de Flash Attention ...", «Parte 1»: the kernel takes a
+# position offset for the causal mask, input_pos; "L'attention fusionnée",
+# «Un premier kernel plus lent»: one query against 70 positions, as in
+# generation).  Query row i stands at position i + q_offset among the keys and
+# sees key j iff j <= i + q_offset; the default offset is Tk - Tq.
+# ---------------------------------------------------------------------------
+
+def sdpa_masked(q, k, v, do, scale, causal, off):
+    """PyTorch float64 SDPA with an explicit boolean mask, and autograd."""
+    G = q.shape[1] // k.shape[1]
+    Tq, Tk = q.shape[2], k.shape[2]
+    qt, kt, vt = (torch.from_numpy(x).clone().requires_grad_(True) for x in (q, k, v))
+    mask = None
+    if causal:
+        i = torch.arange(Tq)[:, None]
+        j = torch.arange(Tk)[None, :]
+        mask = j <= i + off
+    ot = torch.nn.functional.scaled_dot_product_attention(
+        qt, kt.repeat_interleave(G, dim=1), vt.repeat_interleave(G, dim=1), attn_mask=mask,
+        scale=scale)
+    (ot * torch.from_numpy(do)).sum().backward()
+    return ot.detach().numpy(), qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy()
+
+
+@pytest.mark.parametrize("D", [5, 3])
+def test_single_query_against_70_keys(D):
+    """One query against 70 positions (the page's generation-shaped test, with
+    its head sizes 5 and 3): with the default offset the query stands after
+    every key, so causal and non-causal attention agree, and both match
+    PyTorch's float64 SDPA over all keys."""
+    q, k, v, do = rnd((1, 1, 1, D), 40), rnd((1, 1, 70, D), 41), rnd((1, 1, 70, D), 42), rnd((1, 1, 1, D), 43)
+    oc, lc = oracle.fwd(q, k, v, 0.5, True)
+    on, ln = oracle.fwd(q, k, v, 0.5, False)
+    np.testing.assert_array_equal(oc, on)
+    np.testing.assert_array_equal(lc, ln)
+    ot, dqt, dkt, dvt = sdpa_masked(q, k, v, do, 0.5, False, 0)
+    np.testing.assert_allclose(oc, ot, atol=1e-12)
+    dq, dk, dv = oracle.bwd(q, k, v, do, 0.5, True)
+    np.testing.assert_allclose(dq, dqt, atol=1e-12)
+    np.testing.assert_allclose(dk, dkt, atol=1e-12)
+    np.testing.assert_allclose(dv, dvt, atol=1e-12)
+    # with offset 0 the single query sees key 0 only: o = v_0 exactly
+    o0, l0 = oracle.fwd(q, k, v, 0.5, True, q_offset=0)
+    np.testing.assert_array_equal(o0[0, 0, 0], v[0, 0, 0])
+    assert abs(l0[0, 0, 0] - 0.5 * float(np.dot(q[0, 0, 0], k[0, 0, 0]))) < 1e-15
+
+
+@pytest.mark.parametrize("Tq,Tk", [(3, 8), (5, 5), (1, 9), (7, 20)])
+def test_bottom_right_rows_are_the_last_rows_of_the_square_problem(Tq, Tk):
+    """With the default offset the Tq query rows are the last Tq rows of the
+    square causal problem over the same keys: o, lse and dq equal those rows,
+    and dk, dv equal the square problem's with dO = 0 on its first Tk - Tq rows
+    (rows that then add nothing to any gradient)."""
+    B, Hq, Hkv, D = 1, 4, 2, 6
+    qs, k, v, dos = rnd((B, Hq, Tk, D), 44), rnd((B, Hkv, Tk, D), 45), rnd((B, Hkv, Tk, D), 46), rnd((B, Hq, Tk, D), 47)
+    dos[:, :, :Tk - Tq] = 0.0
+    o_sq, lse_sq = oracle.fwd(qs, k, v, 0.45, True)
+    dq_sq, dk_sq, dv_sq = oracle.bwd(qs, k, v, dos, 0.45, True)
+    q, do = qs[:, :, Tk - Tq:].copy(), dos[:, :, Tk - Tq:].copy()
+    o, lse = oracle.fwd(q, k, v, 0.45, True)
+    dq, dk, dv = oracle.bwd(q, k, v, do, 0.45, True)
+    np.testing.assert_allclose(o, o_sq[:, :, Tk - Tq:], atol=1e-14)
+    np.testing.assert_allclose(lse, lse_sq[:, :, Tk - Tq:], atol=1e-14)
+    np.testing.assert_allclose(dq, dq_sq[:, :, Tk - Tq:], atol=1e-13)
+    np.testing.assert_allclose(dk, dk_sq, atol=1e-13)
+    np.testing.assert_allclose(dv, dv_sq, atol=1e-13)
+
+
+@pytest.mark.parametrize("case", [
+    dict(B=1, Hq=2, Hkv=1, Tq=4, Tk=9, off=None, causal=True),
+    dict(B=1, Hq=1, Hkv=1, Tq=4, Tk=9, off=1, causal=True),
+    dict(B=2, Hq=2, Hkv=2, Tq=6, Tk=3, off=0, causal=True),
+    dict(B=1, Hq=2, Hkv=1, Tq=5, Tk=7, off=None, causal=False),
+])
+def test_kv_gradients_match_finite_differences(case):
+    """Brute force with Tq != Tk and several offsets: central differences of
+    sum(O * dO) in every input element."""
+    B, Hq, Hkv, Tq, Tk = (case[x] for x in ("B", "Hq", "Hkv", "Tq", "Tk"))
+    D, scale, causal, off = 3, 0.8, case["causal"], case["off"]
+    q, k, v, do = rnd((B, Hq, Tq, D), 48), rnd((B, Hkv, Tk, D), 49), rnd((B, Hkv, Tk, D), 50), rnd((B, Hq, Tq, D), 51)
+    grads = oracle.bwd(q, k, v, do, scale, causal, q_offset=off)
+
+    def loss(*a):
+        return float(np.sum(oracle.fwd(*a, scale, causal, q_offset=off)[0] * do))
+
+    h = 1e-6
+    for which, x in enumerate((q, k, v)):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            args_p, args_m = [q, k, v], [q, k, v]
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p[which], args_m[which] = xp, xm
+            fd[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        err = np.max(np.abs(fd - grads[which]) / np.maximum(1.0, np.abs(grads[which])))
+        assert err < 1e-7, (which, err)
+
+
+@pytest.mark.parametrize("case", [
+    dict(Hq=4, Hkv=2, Tq=33, Tk=70, D=5, off=None),
+    dict(Hq=3, Hkv=1, Tq=70, Tk=70, D=3, off=0),
+    dict(Hq=2, Hkv=2, Tq=20, Tk=50, D=8, off=7),
+    dict(Hq=2, Hkv=1, Tq=40, Tk=25, D=4, off=3),
+])
+def test_kv_matches_torch_sdpa_with_explicit_mask(case):
+    """PyTorch's float64 SDPA with the mask j <= i + offset written out as a
+    boolean matrix, with autograd for the gradients."""
+    Hq, Hkv, Tq, Tk, D, off = (case[x] for x in ("Hq", "Hkv", "Tq", "Tk", "D", "off"))
+    q, k, v, do = rnd((1, Hq, Tq, D), 52), rnd((1, Hkv, Tk, D), 53), rnd((1, Hkv, Tk, D), 54), rnd((1, Hq, Tq, D), 55)
+    o, lse = oracle.fwd(q, k, v, 0.6, True, q_offset=off)
+    dq, dk, dv = oracle.bwd(q, k, v, do, 0.6, True, q_offset=off)
+    ot, dqt, dkt, dvt = sdpa_masked(q, k, v, do, 0.6, True, Tk - Tq if off is None else off)
+    np.testing.assert_allclose(o, ot, atol=1e-12)
+    np.testing.assert_allclose(dq, dqt, atol=1e-12)
+    np.testing.assert_allclose(dk, dkt, atol=1e-12)
+    np.testing.assert_allclose(dv, dvt, atol=1e-12)
+
+
+def test_rows_without_a_visible_key():
+    """A negative offset leaves the first rows without any visible key: the
+    oracle defines their output as 0 and their lse as -inf, and they add
+    nothing to any gradient; the other rows are unaffected."""
+    q, k, v, do = rnd((1, 1, 6, 4), 56), rnd((1, 1, 6, 4), 57), rnd((1, 1, 6, 4), 58), rnd((1, 1, 6, 4), 59)
+    o, lse = oracle.fwd(q, k, v, 0.5, True, q_offset=-2)
+    assert np.all(o[0, 0, :2] == 0.0) and np.all(np.isneginf(lse[0, 0, :2]))
+    dq, dk, dv = oracle.bwd(q, k, v, do, 0.5, True, q_offset=-2)
+    assert np.all(dq[0, 0, :2] == 0.0)
+    ot, dqt, dkt, dvt = sdpa_masked(q[:, :, 2:].copy(), k, v, do[:, :, 2:].copy(), 0.5, True, 0)
+    np.testing.assert_allclose(o[:, :, 2:], ot, atol=1e-12)
+    np.testing.assert_allclose(dq[:, :, 2:], dqt, atol=1e-12)
+    np.testing.assert_allclose(dk, dkt, atol=1e-12)
+    np.testing.assert_allclose(dv, dvt, atol=1e-12)
+
+
+def test_kv_row_entry_points_match_full():
+    """The per-row entry points with Tq != Tk and an explicit offset."""
+    B, Hq, Hkv, Tq, Tk, D, off = 1, 4, 2, 23, 57, 7, 20
+    q, k, v, do = rnd((B, Hq, Tq, D), 60), rnd((B, Hkv, Tk, D), 61), rnd((B, Hkv, Tk, D), 62), rnd((B, Hq, Tq, D), 63)
+    o, lse = oracle.fwd(q, k, v, 0.5, True, q_offset=off)
+    dq, dk, dv = oracle.bwd(q, k, v, do, 0.5, True, q_offset=off)
+    qi = [(0, 0, 0), (0, 3, 22), (0, 2, 9)]
+    oo, ll = oracle.fwd_rows(q, k, v, qi, 0.5, True, q_offset=off)
+    dqr = oracle.dq_rows(q, k, v, do, qi, 0.5, True, q_offset=off)
+    for n, (b, h, i) in enumerate(qi):
+        np.testing.assert_allclose(oo[n], o[b, h, i], atol=1e-14)
+        assert abs(ll[n] - lse[b, h, i]) < 1e-14
+        np.testing.assert_allclose(dqr[n], dq[b, h, i], atol=1e-14)
+    ki = [(0, 0, 0), (0, 1, 56), (0, 1, 30)]
+    dkr, dvr = oracle.dkdv_rows(q, k, v, do, ki, 0.5, True, q_offset=off)
+    for n, (b, hk, j) in enumerate(ki):
+        np.testing.assert_allclose(dkr[n], dk[b, hk, j], atol=1e-13)
+        np.testing.assert_allclose(dvr[n], dv[b, hk, j], atol=1e-13)

@@ -16,16 +16,22 @@ import oracle
 from tests.conftest import read_golden
 
 MUTANTS = {
-    "mask_off_by_one": [("return s->causal ? (j <= i) : 1;", "return s->causal ? (j < i) : 1;")],
-    "mask_reversed": [("return s->causal ? (j <= i) : 1;", "return s->causal ? (j >= i) : 1;")],
+    "mask_off_by_one": [("return s->causal ? ((long)j <= (long)i + s->off) : 1;",
+                         "return s->causal ? ((long)j < (long)i + s->off) : 1;")],
+    "mask_reversed": [("return s->causal ? ((long)j <= (long)i + s->off) : 1;",
+                       "return s->causal ? ((long)j >= (long)i + s->off) : 1;")],
+    "offset_ignored": [("return s->causal ? ((long)j <= (long)i + s->off) : 1;",
+                        "return s->causal ? ((long)j <= (long)i) : 1;")],
+    "offset_sign": [("return s->causal ? ((long)j <= (long)i + s->off) : 1;",
+                     "return s->causal ? ((long)j <= (long)i - s->off) : 1;")],
     "lse_sign": [("m + log(l)", "m - log(l)")],
     "no_normalisation": [("for (int j = 0; j < T; ++j) p[j] /= l;", "")],
     "scores_unscaled": [("s->scale * dot(q_i", "dot(q_i")],
-    "gqa_modulo_map": [("const int G = s->Hq / s->Hkv, hk = h / G, D = s->D, T = s->T;\n"
+    "gqa_modulo_map": [("const int G = s->Hq / s->Hkv, hk = h / G, D = s->D, T = s->Tk;\n"
                         "    const double* k_head = kvrow(k, s, b, hk, 0);\n"
                         "    const double* v_head = kvrow(v, s, b, hk, 0);\n"
                         "    double m, l;",
-                        "const int hk = h % s->Hkv, D = s->D, T = s->T;\n"
+                        "const int hk = h % s->Hkv, D = s->D, T = s->Tk;\n"
                         "    const double* k_head = kvrow(k, s, b, hk, 0);\n"
                         "    const double* v_head = kvrow(v, s, b, hk, 0);\n"
                         "    double m, l;")],
@@ -116,6 +122,17 @@ def battery(orc) -> dict:
         o, _ = orc.fwd(q.numpy(), k.numpy(), v.numpy(), 0.5, causal)
         ok &= bool(np.allclose(o, ot.numpy(), atol=1e-10))
     res["sdpa"] = ok
+
+    # bottom-right alignment: Tq queries against Tk keys with the default
+    # offset Tk - Tq are the last Tq rows of the square causal problem
+    # ("Optimización de Flash Attention ...", input_pos of «Parte 1»)
+    Tq, Tk, D = 3, 8, 4
+    kk, vv = rnd((1, 1, Tk, D), 14), rnd((1, 1, Tk, D), 15)
+    qs = rnd((1, 1, Tk, D), 16)
+    o_sq, lse_sq = orc.fwd(qs, kk, vv, 0.7, True)
+    o_kv, lse_kv = orc.fwd(qs[:, :, Tk - Tq:], kk, vv, 0.7, True)
+    res["kv_offset"] = (np.allclose(o_kv, o_sq[:, :, Tk - Tq:], atol=1e-14) and
+                        np.allclose(lse_kv, lse_sq[:, :, Tk - Tq:], atol=1e-14))
     return res
 
 

@@ -108,9 +108,8 @@ def gemm_reference():
 
 
 def gemm_flop(w, n_gemm):
-    """FLOP of n_gemm T x T x D products over the visible score entries."""
-    pairs = w.B * w.Hq * w.T * w.T * (0.5 if w.causal else 1.0)
-    return 2.0 * n_gemm * pairs * w.D
+    """FLOP of n_gemm Tq x Tk x D products over the visible score entries."""
+    return 2.0 * n_gemm * w.B * w.Hq * w.pairs * w.D
 
 
 def source_hash(kernel_file: str) -> str:
@@ -137,9 +136,10 @@ def traffic_for(kernel: str, kernel_file: str, workload: str):
 
 
 def describe(w) -> str:
+    rows = f"T={w.T}" if w.Tkv == w.T else f"Tq={w.T} Tk={w.Tkv} q_offset={w.q_offset}"
     return (f"{w.name}: {'causal' if w.causal else 'non-causal'} {'GQA' if w.Hq != w.Hkv else 'MHA'} "
             f"attention {'fwd+bwd' if w.backward else 'fwd'}, B={w.B} Hq={w.Hq} Hkv={w.Hkv} "
-            f"T={w.T} D={w.D}, scale={w.scale:.6g}")
+            f"{rows} D={w.D}, scale={w.scale:.6g}")
 
 
 def forward_only(args, w, x, q, k, v, o, lse):
@@ -174,7 +174,8 @@ def forward_only(args, w, x, q, k, v, o, lse):
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if bf else "fp32",
         "data": "synthetic (seeded N(0,1) inputs of the workload's shape)",
         "config": {"workload": describe(w), "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "T": w.T, "D": w.D,
-                   "causal": w.causal, "parallelism": "single GPU"},
+                   "causal": w.causal, "parallelism": "single GPU",
+                   **({"Tk": w.Tkv, "q_offset": w.q_offset} if w.Tkv != w.T else {})},
         "pct_of_peak": round(100 * value / peak, 2),
         "roofline": {
             "kernel": "fwd_bf16_kernel" if bf else "fwd_kernel", "bound": "mfma",
@@ -361,6 +362,7 @@ def main():
             "workload": describe(w),
             "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "T": w.T, "D": w.D, "causal": w.causal,
             "parallelism": "single GPU",
+            **({"Tk": w.Tkv, "q_offset": w.q_offset} if w.Tkv != w.T else {}),
         },
         "pct_of_peak": round(100 * value / peak, 2),
         "breakdown": {
@@ -373,7 +375,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and w.Tkv == w.T:  # the sample takes prefixes of one sequence
         print("[bench] timing the oracle on a bounded sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
     print(json.dumps(out), flush=True)

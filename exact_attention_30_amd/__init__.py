@@ -11,9 +11,11 @@ raises if it is missing.
     o, lse = fwd(q, k, v, scale=None, causal=True)
     dq, dk, dv = bwd(q, k, v, o, dout, lse, scale=None, causal=True)
 
-q, o, dout: [B, Hq, T, D]; k, v: [B, Hkv, T, D]; contiguous, on the same GPU,
-all bfloat16 or all float32; lse: [B, Hq, T] float32.  `scale` defaults to
-1/sqrt(D).
+q, o, dout: [B, Hq, Tq, D]; k, v: [B, Hkv, Tk, D]; contiguous, on the same GPU,
+all bfloat16 or all float32; lse: [B, Hq, Tq] float32.  `scale` defaults to
+1/sqrt(D).  With causal=True, query row i sees keys j <= i + q_offset;
+q_offset defaults to Tk - Tq (the last query row on the last key; 0 when
+Tq == Tk).
 """
 from __future__ import annotations
 
@@ -43,6 +45,14 @@ SIGNATURES = {
                      _vp], ctypes.c_int),
     "fa_bwd_dq": ([_vp, _vp, _vp, _vp, _fp, _fp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _vp],
                   ctypes.c_int),
+    "fa_fwd_kv": ([_vp, _vp, _vp, _vp, _fp, _i, _i, _i, _i, _i, _i, _f, _i, _i, _i, _vp],
+                  ctypes.c_int),
+    "fa_bwd_kv": ([_vp, _vp, _vp, _vp, _vp, _fp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f,
+                   _i, _i, _i, _vp], ctypes.c_int),
+    "fa_bwd_dkdv_kv": ([_vp, _vp, _vp, _vp, _fp, _fp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i,
+                        _i, _i, _vp], ctypes.c_int),
+    "fa_bwd_dq_kv": ([_vp, _vp, _vp, _vp, _fp, _fp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _i, _i,
+                      _vp], ctypes.c_int),
     "fa_status_string": ([_i], ctypes.c_char_p),
     "fa_version": ([], ctypes.c_char_p),
 }
@@ -86,13 +96,18 @@ def _stream(t: torch.Tensor) -> int:
 
 
 def _dims(q, k, v):
+    """(B, Hq, Hkv, Tq, Tk, D) of q [B,Hq,Tq,D] and k, v [B,Hkv,Tk,D]."""
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
-        raise ValueError("q must be [B,Hq,T,D]; k and v [B,Hkv,T,D]")
-    B, Hq, T, D = q.shape
-    Hkv = k.shape[1]
-    if k.shape[0] != B or k.shape[2] != T or k.shape[3] != D:
+        raise ValueError("q must be [B,Hq,Tq,D]; k and v [B,Hkv,Tk,D]")
+    B, Hq, Tq, D = q.shape
+    Hkv, Tk = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != D:
         raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)}")
-    return B, Hq, Hkv, T, D
+    return B, Hq, Hkv, Tq, Tk, D
+
+
+def _offset(Tq, Tk, q_offset) -> int:
+    return Tk - Tq if q_offset is None else int(q_offset)
 
 
 def _dtype_code(*ts) -> int:
@@ -113,15 +128,23 @@ def _scale(scale, D) -> float:
     return 1.0 / math.sqrt(D) if scale is None else float(scale)
 
 
-def fwd(q, k, v, scale=None, causal: bool = True, out=None, lse=None):
-    """Forward pass; returns (o, lse).  `out`/`lse` may be preallocated."""
-    B, Hq, Hkv, T, D = _dims(q, k, v)
+def fwd(q, k, v, scale=None, causal: bool = True, out=None, lse=None, q_offset=None):
+    """Forward pass; returns (o, lse).  `out`/`lse` may be preallocated.
+    Calls fa_fwd when Tq == Tk and the offset is 0, else fa_fwd_kv."""
+    B, Hq, Hkv, Tq, Tk, D = _dims(q, k, v)
     dt = _dtype_code(q, k, v)
+    off = _offset(Tq, Tk, q_offset)
     o = torch.empty_like(q) if out is None else out
-    l = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device) if lse is None else lse
-    _check(library().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(),
-                            B, Hq, Hkv, T, D, _scale(scale, D), int(bool(causal)), dt,
-                            _stream(q)), "fa_fwd")
+    l = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device) if lse is None else lse
+    lib = library()
+    if Tq == Tk and (off == 0 or not causal):
+        _check(lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(),
+                          B, Hq, Hkv, Tq, D, _scale(scale, D), int(bool(causal)), dt,
+                          _stream(q)), "fa_fwd")
+    else:
+        _check(lib.fa_fwd_kv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(),
+                             B, Hq, Hkv, Tq, Tk, D, _scale(scale, D), int(bool(causal)), off, dt,
+                             _stream(q)), "fa_fwd_kv")
     return o, l
 
 
@@ -129,25 +152,33 @@ def bwd_workspace_bytes(B, Hq, Hkv, T, D, dtype=torch.bfloat16) -> int:
     return int(library().fa_bwd_workspace_bytes(B, Hq, Hkv, T, D, _DTYPES[dtype]))
 
 
-def bwd(q, k, v, o, dout, lse, scale=None, causal: bool = True, workspace=None, grads=None):
+def bwd(q, k, v, o, dout, lse, scale=None, causal: bool = True, workspace=None, grads=None,
+        q_offset=None):
     """Backward pass; returns (dq, dk, dv).  `grads` = (dq, dk, dv) may be
     preallocated; `workspace` is a uint8 device tensor of at least
-    bwd_workspace_bytes(...) bytes."""
-    B, Hq, Hkv, T, D = _dims(q, k, v)
+    bwd_workspace_bytes(...) bytes.  Calls fa_bwd when Tq == Tk and the
+    offset is 0, else fa_bwd_kv (same q_offset as the forward)."""
+    B, Hq, Hkv, Tq, Tk, D = _dims(q, k, v)
     dt = _dtype_code(q, k, v, o, dout)
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, T):
-        raise ValueError("lse must be float32 [B,Hq,T]")
+    off = _offset(Tq, Tk, q_offset)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Tq):
+        raise ValueError("lse must be float32 [B,Hq,Tq]")
     dq, dk, dv = grads if grads is not None else (torch.empty_like(q), torch.empty_like(k),
                                                   torch.empty_like(v))
-    ws_bytes = bwd_workspace_bytes(B, Hq, Hkv, T, D, q.dtype)
+    ws_bytes = bwd_workspace_bytes(B, Hq, Hkv, Tq, D, q.dtype)
     ws = workspace if workspace is not None else torch.empty(max(ws_bytes, 16), dtype=torch.uint8,
                                                              device=q.device)
     if ws.numel() * ws.element_size() < ws_bytes:
         raise ValueError("workspace too small")
-    _check(library().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                            dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
-                            dv.data_ptr(), ws.data_ptr(), B, Hq, Hkv, T, D, _scale(scale, D),
-                            int(bool(causal)), dt, _stream(q)), "fa_bwd")
+    lib = library()
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr())
+    if Tq == Tk and (off == 0 or not causal):
+        _check(lib.fa_bwd(*ptrs, B, Hq, Hkv, Tq, D, _scale(scale, D), int(bool(causal)), dt,
+                          _stream(q)), "fa_bwd")
+    else:
+        _check(lib.fa_bwd_kv(*ptrs, B, Hq, Hkv, Tq, Tk, D, _scale(scale, D), int(bool(causal)), off,
+                             dt, _stream(q)), "fa_bwd_kv")
     return dq, dk, dv
 
 
@@ -161,23 +192,37 @@ def bwd_preprocess(o, dout, delta=None):
     return d
 
 
-def bwd_dkdv(q, k, v, dout, lse, delta, scale=None, causal: bool = True, dk=None, dv=None):
-    B, Hq, Hkv, T, D = _dims(q, k, v)
+def bwd_dkdv(q, k, v, dout, lse, delta, scale=None, causal: bool = True, dk=None, dv=None,
+             q_offset=None):
+    B, Hq, Hkv, Tq, Tk, D = _dims(q, k, v)
     dt = _dtype_code(q, k, v, dout)
+    off = _offset(Tq, Tk, q_offset)
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    _check(library().fa_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
-                                 lse.data_ptr(), delta.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                                 B, Hq, Hkv, T, D, _scale(scale, D), int(bool(causal)), dt,
-                                 _stream(q)), "fa_bwd_dkdv")
+    lib = library()
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+            delta.data_ptr(), dk.data_ptr(), dv.data_ptr())
+    if Tq == Tk and (off == 0 or not causal):
+        _check(lib.fa_bwd_dkdv(*ptrs, B, Hq, Hkv, Tq, D, _scale(scale, D), int(bool(causal)), dt,
+                               _stream(q)), "fa_bwd_dkdv")
+    else:
+        _check(lib.fa_bwd_dkdv_kv(*ptrs, B, Hq, Hkv, Tq, Tk, D, _scale(scale, D), int(bool(causal)),
+                                  off, dt, _stream(q)), "fa_bwd_dkdv_kv")
     return dk, dv
 
 
-def bwd_dq(q, k, v, dout, lse, delta, scale=None, causal: bool = True, dq=None):
-    B, Hq, Hkv, T, D = _dims(q, k, v)
+def bwd_dq(q, k, v, dout, lse, delta, scale=None, causal: bool = True, dq=None, q_offset=None):
+    B, Hq, Hkv, Tq, Tk, D = _dims(q, k, v)
     dt = _dtype_code(q, k, v, dout)
+    off = _offset(Tq, Tk, q_offset)
     dq = torch.empty_like(q) if dq is None else dq
-    _check(library().fa_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
-                               lse.data_ptr(), delta.data_ptr(), dq.data_ptr(), B, Hq, Hkv, T, D,
-                               _scale(scale, D), int(bool(causal)), dt, _stream(q)), "fa_bwd_dq")
+    lib = library()
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+            delta.data_ptr(), dq.data_ptr())
+    if Tq == Tk and (off == 0 or not causal):
+        _check(lib.fa_bwd_dq(*ptrs, B, Hq, Hkv, Tq, D, _scale(scale, D), int(bool(causal)), dt,
+                             _stream(q)), "fa_bwd_dq")
+    else:
+        _check(lib.fa_bwd_dq_kv(*ptrs, B, Hq, Hkv, Tq, Tk, D, _scale(scale, D), int(bool(causal)),
+                                off, dt, _stream(q)), "fa_bwd_dq_kv")
     return dq

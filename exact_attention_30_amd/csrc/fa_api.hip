@@ -14,20 +14,27 @@ constexpr float kLog2e = 1.4426950408889634f;
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // Shape and option checks shared by every entry point; `D`/`dt` may be
-// ignored by passing D = 64, dt = FA_BF16.
-fa_status check_common(int B, int Hq, int Hkv, int T, int D, fa_dtype dt)
+// ignored by passing D = 64, dt = FA_BF16.  Tq query rows against Tk key rows;
+// `off` (causal only) places query row i at key position i + off.
+fa_status check_kv(int B, int Hq, int Hkv, int Tq, int Tk, int D, fa_dtype dt, bool causal, int off)
 {
-    if (B < 0 || T < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return FA_ERR_SHAPE;
+    if (B < 0 || Tq < 0 || Tk < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return FA_ERR_SHAPE;
+    // query rows need at least one key
+    if ((long long)B * Tq > 0 && Tk == 0) return FA_ERR_SHAPE;
+    // every row sees key 0, and every key index a kernel forms fits an int
+    if (causal && (off < 0 || (long long)off + Tq > 0x7fffffffLL - 4096)) return FA_ERR_SHAPE;
     // every tensor index must fit the 64-bit offsets and every grid the
-    // 32-bit workgroup count: B*Hq*ceil(T/32) workgroups at most
-    const long long rows = (long long)B * Hq * (((long long)T + 31) / 32);
-    if (rows > 0x7fffffffLL) return FA_ERR_SHAPE;
+    // 32-bit workgroup count: B*H*ceil(T/32) workgroups at most
+    const long long qrows = (long long)B * Hq * (((long long)Tq + 31) / 32);
+    const long long krows = (long long)B * Hkv * (((long long)Tk + 31) / 32);
+    if (qrows > 0x7fffffffLL || krows > 0x7fffffffLL) return FA_ERR_SHAPE;
     if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
     if (dt != FA_BF16 && dt != FA_FP32) return FA_ERR_UNSUPPORTED;
     // one head of one tensor is addressed through a buffer resource whose
     // byte range is a signed 32-bit count
-    const long long head_bytes = (long long)T * D * (dt == FA_BF16 ? 2 : 4);
-    if (head_bytes > 0x7fffffffLL) return FA_ERR_SHAPE;
+    const long long esz = dt == FA_BF16 ? 2 : 4;
+    if ((long long)Tq * D * esz > 0x7fffffffLL || (long long)Tk * D * esz > 0x7fffffffLL)
+        return FA_ERR_SHAPE;
     return FA_OK;
 }
 
@@ -40,11 +47,32 @@ fa_status from_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; 
 
 int dtype_code(fa_dtype dt) { return dt == FA_BF16 ? 0 : 1; }
 
+void fill_bwd(fa::BwdArgs& a, const void* q, const void* k, const void* v, const void* dout,
+              const float* lse, const float* delta, int B, int Hq, int Hkv, int Tq, int Tk,
+              int off, float scale)
+{
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.dout = dout;
+    a.lse = lse;
+    a.delta = delta;
+    a.dq = a.dk = a.dv = nullptr;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.Tq = Tq;
+    a.Tk = Tk;
+    a.off = off;
+    a.c = scale * kLog2e;
+    a.scale = scale;
+}
+
 }  // namespace
 
 extern "C" {
 
-const char* fa_version(void) { return "0.1.0"; }
+const char* fa_version(void) { return "0.2.0"; }
 
 const char* fa_status_string(fa_status s)
 {
@@ -59,13 +87,15 @@ const char* fa_status_string(fa_status s)
     return "unknown status";
 }
 
-fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
-                 int Hkv, int T, int D, float scale, int causal, fa_dtype dt, void* stream)
+fa_status fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                    int Hkv, int Tq, int Tk, int D, float scale, int causal, int q_offset,
+                    fa_dtype dt, void* stream)
 {
-    fa_status st = check_common(B, Hq, Hkv, T, D, dt);
+    const int off = causal ? q_offset : 0;
+    fa_status st = check_kv(B, Hq, Hkv, Tq, Tk, D, dt, causal != 0, off);
     if (st != FA_OK) return st;
     if ((st = check_scale(scale)) != FA_OK) return st;
-    if ((long long)B * T == 0) return FA_OK;
+    if ((long long)B * Tq == 0) return FA_OK;
     if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
         return FA_ERR_ALIGN;
@@ -78,15 +108,23 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
     a.B = B;
     a.Hq = Hq;
     a.Hkv = Hkv;
-    a.T = T;
+    a.Tq = Tq;
+    a.Tk = Tk;
+    a.off = off;
     a.c = scale * kLog2e;
     a.scale = scale;
     return from_hip(fa::launch_fwd(a, D, dtype_code(dt), causal != 0, static_cast<hipStream_t>(stream)));
 }
 
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                 int Hkv, int T, int D, float scale, int causal, fa_dtype dt, void* stream)
+{
+    return fa_fwd_kv(q, k, v, o, lse, B, Hq, Hkv, T, T, D, scale, causal, 0, dt, stream);
+}
+
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int T, int D, fa_dtype dt)
 {
-    if (check_common(B, Hq, Hkv, T, D, dt) != FA_OK) return 0;
+    if (check_kv(B, Hq, Hkv, T, T, D, dt, false, 0) != FA_OK) return 0;
     const size_t bytes = (size_t)B * (size_t)Hq * (size_t)T * sizeof(float);
     return (bytes + 255) / 256 * 256;
 }
@@ -94,7 +132,7 @@ size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int T, int D, fa_dtype dt)
 fa_status fa_bwd_preprocess(const void* o, const void* dout, float* delta, int B, int Hq, int T,
                             int D, fa_dtype dt, void* stream)
 {
-    fa_status st = check_common(B, Hq, 1, T, D, dt);
+    fa_status st = check_kv(B, Hq, 1, T, T, D, dt, false, 0);
     if (st != FA_OK) return st;
     if ((long long)B * T == 0) return FA_OK;
     if (!o || !dout || !delta) return FA_ERR_NULL;
@@ -107,84 +145,115 @@ fa_status fa_bwd_preprocess(const void* o, const void* dout, float* delta, int B
     return from_hip(fa::launch_bwd_pre(a, D, dtype_code(dt), static_cast<hipStream_t>(stream)));
 }
 
-static fa_status bwd_args(const void* q, const void* k, const void* v, const void* dout,
-                          const float* lse, const float* delta, int B, int Hq, int Hkv, int T,
-                          int D, float scale, fa_dtype dt, fa::BwdArgs& a, bool& empty)
+// Checks shared by the two backward kernels' entry points.  `skip` is set
+// when there is nothing to enqueue.
+static fa_status bwd_check(const void* q, const void* k, const void* v, const void* dout,
+                           const float* lse, const float* delta, int B, int Hq, int Hkv, int Tq,
+                           int Tk, int D, float scale, int causal, int off, fa_dtype dt, bool& skip)
 {
-    fa_status st = check_common(B, Hq, Hkv, T, D, dt);
+    fa_status st = check_kv(B, Hq, Hkv, Tq, Tk, D, dt, causal != 0, off);
     if (st != FA_OK) return st;
     if ((st = check_scale(scale)) != FA_OK) return st;
-    empty = (long long)B * T == 0;
-    if (empty) return FA_OK;
-    if (!q || !k || !v || !dout || !lse || !delta) return FA_ERR_NULL;
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) ||
-        !aligned(lse, 4) || !aligned(delta, 4))
-        return FA_ERR_ALIGN;
-    a.q = q;
-    a.k = k;
-    a.v = v;
-    a.dout = dout;
-    a.lse = lse;
-    a.delta = delta;
-    a.dq = a.dk = a.dv = nullptr;
-    a.B = B;
-    a.Hq = Hq;
-    a.Hkv = Hkv;
-    a.T = T;
-    a.c = scale * kLog2e;
-    a.scale = scale;
+    skip = (long long)B * Tk == 0;
+    if (skip) return FA_OK;
+    // with no query row the key-side gradients are zero: only pointers to
+    // them (and k, v) are needed
+    if (Tq > 0) {
+        if (!q || !dout || !lse || !delta) return FA_ERR_NULL;
+        if (!aligned(q, 16) || !aligned(dout, 16) || !aligned(lse, 4) || !aligned(delta, 4))
+            return FA_ERR_ALIGN;
+    }
+    if (!k || !v) return FA_ERR_NULL;
+    if (!aligned(k, 16) || !aligned(v, 16)) return FA_ERR_ALIGN;
     return FA_OK;
+}
+
+fa_status fa_bwd_dkdv_kv(const void* q, const void* k, const void* v, const void* dout,
+                         const float* lse, const float* delta, void* dk, void* dv, int B, int Hq,
+                         int Hkv, int Tq, int Tk, int D, float scale, int causal, int q_offset,
+                         fa_dtype dt, void* stream)
+{
+    const int off = causal ? q_offset : 0;
+    bool skip = false;
+    fa_status st = bwd_check(q, k, v, dout, lse, delta, B, Hq, Hkv, Tq, Tk, D, scale, causal, off,
+                             dt, skip);
+    if (st != FA_OK || skip) return st;
+    if (!dk || !dv) return FA_ERR_NULL;
+    if (!aligned(dk, 16) || !aligned(dv, 16)) return FA_ERR_ALIGN;
+    fa::BwdArgs a;
+    fill_bwd(a, q, k, v, dout, lse, delta, B, Hq, Hkv, Tq, Tk, off, scale);
+    a.dk = dk;
+    a.dv = dv;
+    return from_hip(fa::launch_bwd_dkdv(a, D, dtype_code(dt), causal != 0, static_cast<hipStream_t>(stream)));
+}
+
+fa_status fa_bwd_dq_kv(const void* q, const void* k, const void* v, const void* dout,
+                       const float* lse, const float* delta, void* dq, int B, int Hq, int Hkv,
+                       int Tq, int Tk, int D, float scale, int causal, int q_offset, fa_dtype dt,
+                       void* stream)
+{
+    const int off = causal ? q_offset : 0;
+    bool skip = false;
+    fa_status st = bwd_check(q, k, v, dout, lse, delta, B, Hq, Hkv, Tq, Tk, D, scale, causal, off,
+                             dt, skip);
+    if (st != FA_OK || skip || Tq == 0) return st;
+    if (!dq) return FA_ERR_NULL;
+    if (!aligned(dq, 16)) return FA_ERR_ALIGN;
+    fa::BwdArgs a;
+    fill_bwd(a, q, k, v, dout, lse, delta, B, Hq, Hkv, Tq, Tk, off, scale);
+    a.dq = dq;
+    return from_hip(fa::launch_bwd_dq(a, D, dtype_code(dt), causal != 0, static_cast<hipStream_t>(stream)));
 }
 
 fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
                       const float* lse, const float* delta, void* dk, void* dv, int B, int Hq,
                       int Hkv, int T, int D, float scale, int causal, fa_dtype dt, void* stream)
 {
-    fa::BwdArgs a;
-    bool empty = false;
-    fa_status st = bwd_args(q, k, v, dout, lse, delta, B, Hq, Hkv, T, D, scale, dt, a, empty);
-    if (st != FA_OK || empty) return st;
-    if (!dk || !dv) return FA_ERR_NULL;
-    if (!aligned(dk, 16) || !aligned(dv, 16)) return FA_ERR_ALIGN;
-    a.dk = dk;
-    a.dv = dv;
-    return from_hip(fa::launch_bwd_dkdv(a, D, dtype_code(dt), causal != 0, static_cast<hipStream_t>(stream)));
+    return fa_bwd_dkdv_kv(q, k, v, dout, lse, delta, dk, dv, B, Hq, Hkv, T, T, D, scale, causal, 0,
+                          dt, stream);
 }
 
 fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
                     const float* lse, const float* delta, void* dq, int B, int Hq, int Hkv, int T,
                     int D, float scale, int causal, fa_dtype dt, void* stream)
 {
-    fa::BwdArgs a;
-    bool empty = false;
-    fa_status st = bwd_args(q, k, v, dout, lse, delta, B, Hq, Hkv, T, D, scale, dt, a, empty);
-    if (st != FA_OK || empty) return st;
-    if (!dq) return FA_ERR_NULL;
-    if (!aligned(dq, 16)) return FA_ERR_ALIGN;
-    a.dq = dq;
-    return from_hip(fa::launch_bwd_dq(a, D, dtype_code(dt), causal != 0, static_cast<hipStream_t>(stream)));
+    return fa_bwd_dq_kv(q, k, v, dout, lse, delta, dq, B, Hq, Hkv, T, T, D, scale, causal, 0, dt,
+                        stream);
+}
+
+fa_status fa_bwd_kv(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, void* dq, void* dk, void* dv, void* workspace, int B, int Hq,
+                    int Hkv, int Tq, int Tk, int D, float scale, int causal, int q_offset,
+                    fa_dtype dt, void* stream)
+{
+    // validate everything before enqueuing anything
+    const int off = causal ? q_offset : 0;
+    fa_status st = check_kv(B, Hq, Hkv, Tq, Tk, D, dt, causal != 0, off);
+    if (st != FA_OK) return st;
+    if ((st = check_scale(scale)) != FA_OK) return st;
+    if ((long long)B * Tk == 0) return FA_OK;
+    const bool rows = Tq > 0;
+    if (!k || !v || !dk || !dv) return FA_ERR_NULL;
+    if (rows && (!q || !o || !dout || !lse || !dq || !workspace)) return FA_ERR_NULL;
+    if (!aligned(k, 16) || !aligned(v, 16) || !aligned(dk, 16) || !aligned(dv, 16)) return FA_ERR_ALIGN;
+    if (rows && (!aligned(q, 16) || !aligned(o, 16) || !aligned(dout, 16) || !aligned(lse, 4) ||
+                 !aligned(dq, 16) || !aligned(workspace, 16)))
+        return FA_ERR_ALIGN;
+    float* delta = static_cast<float*>(workspace);
+    if (rows && (st = fa_bwd_preprocess(o, dout, delta, B, Hq, Tq, D, dt, stream)) != FA_OK) return st;
+    if ((st = fa_bwd_dkdv_kv(q, k, v, dout, lse, delta, dk, dv, B, Hq, Hkv, Tq, Tk, D, scale, causal,
+                             q_offset, dt, stream)) != FA_OK)
+        return st;
+    return fa_bwd_dq_kv(q, k, v, dout, lse, delta, dq, B, Hq, Hkv, Tq, Tk, D, scale, causal,
+                        q_offset, dt, stream);
 }
 
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                  const float* lse, void* dq, void* dk, void* dv, void* workspace, int B, int Hq,
                  int Hkv, int T, int D, float scale, int causal, fa_dtype dt, void* stream)
 {
-    // validate everything before enqueuing anything
-    fa_status st = check_common(B, Hq, Hkv, T, D, dt);
-    if (st != FA_OK) return st;
-    if ((st = check_scale(scale)) != FA_OK) return st;
-    if ((long long)B * T == 0) return FA_OK;
-    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) return FA_ERR_NULL;
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
-        !aligned(dout, 16) || !aligned(lse, 4) || !aligned(dq, 16) || !aligned(dk, 16) ||
-        !aligned(dv, 16) || !aligned(workspace, 16))
-        return FA_ERR_ALIGN;
-    float* delta = static_cast<float*>(workspace);
-    if ((st = fa_bwd_preprocess(o, dout, delta, B, Hq, T, D, dt, stream)) != FA_OK) return st;
-    if ((st = fa_bwd_dkdv(q, k, v, dout, lse, delta, dk, dv, B, Hq, Hkv, T, D, scale, causal, dt,
-                          stream)) != FA_OK)
-        return st;
-    return fa_bwd_dq(q, k, v, dout, lse, delta, dq, B, Hq, Hkv, T, D, scale, causal, dt, stream);
+    return fa_bwd_kv(q, k, v, o, dout, lse, dq, dk, dv, workspace, B, Hq, Hkv, T, T, D, scale,
+                     causal, 0, dt, stream);
 }
 
 }  // extern "C"

@@ -100,21 +100,22 @@ __global__ __launch_bounds__(NW * 64, sizeof(E) == 2 ? 8 / NW : 1) void bwd_dkdv
     const int c = lane & 31;
     const int G = a.Hq / a.Hkv;
 
-    const int nkt = (a.T + BK - 1) / BK;
+    const int nkt = (a.Tk + BK - 1) / BK;
     // causal: the first key tiles see the most query rows
     const TileId id = map_tile(blockIdx.x, a.B, a.Hq, a.Hkv, 1, nkt, false);
     const int b = id.b, hk = id.h;
     const int key0 = id.tile * BK;
     const int krow = key0 + w * 32 + c;  // the key this lane owns
 
-    const size_t kvoff = (size_t)(b * a.Hkv + hk) * a.T * D;
+    const size_t kvoff = (size_t)(b * a.Hkv + hk) * a.Tk * D;
     const E* kh = static_cast<const E*>(a.k) + kvoff;
     const E* vh = static_cast<const E*>(a.v) + kvoff;
 
-    // query tiles that see this key tile, for each of the G query heads
-    const int nq = (a.T + BQ - 1) / BQ;
-    const int i0 = CAUSAL ? key0 / BQ : 0;
-    const int niq = nq - i0;
+    // query tiles that see this key tile (query row i sees keys j <= i + off
+    // when causal), for each of the G query heads
+    const int nq = (a.Tq + BQ - 1) / BQ;
+    const int i0 = CAUSAL ? max(key0 - a.off, 0) / BQ : 0;
+    const int niq = max(nq - i0, 0);
     const int nit = G * niq;
 
     QT qdma;
@@ -123,12 +124,12 @@ __global__ __launch_bounds__(NW * 64, sizeof(E) == 2 ? 8 / NW : 1) void bwd_dkdv
     // the L / Delta row of this thread (if any) goes to a register
     auto issue = [&](int it, unsigned char* buf, float& stat) {
         const int hq = hk * G + it / niq, i = i0 + it % niq;
-        const size_t qoff = (size_t)(b * a.Hq + hq) * a.T * D;
-        qdma.load(buf, static_cast<const E*>(a.q) + qoff, i * BQ, a.T, w);
-        qdma.load(buf + QT::BYTES, static_cast<const E*>(a.dout) + qoff, i * BQ, a.T, w);
+        const size_t qoff = (size_t)(b * a.Hq + hq) * a.Tq * D;
+        qdma.load(buf, static_cast<const E*>(a.q) + qoff, i * BQ, a.Tq, w);
+        qdma.load(buf + QT::BYTES, static_cast<const E*>(a.dout) + qoff, i * BQ, a.Tq, w);
         if (tid < 2 * BQ) {
-            const int qi = min(i * BQ + (tid % BQ), a.T - 1);
-            const size_t off = (size_t)(b * a.Hq + hq) * a.T + qi;
+            const int qi = min(i * BQ + (tid % BQ), a.Tq - 1);
+            const size_t off = (size_t)(b * a.Hq + hq) * a.Tq + qi;
             stat = tid < BQ ? a.lse[off] * kLog2e : a.delta[off];
         }
     };
@@ -136,14 +137,14 @@ __global__ __launch_bounds__(NW * 64, sizeof(E) == 2 ? 8 / NW : 1) void bwd_dkdv
     {
         VT vdma;
         vdma.init(tid);
-        vdma.load(Vs, vh, key0, a.T, w);
+        vdma.load(Vs, vh, key0, a.Tk, w);
     }
     float stat = 0.f;
-    issue(0, qbuf, stat);
+    if (nit > 0) issue(0, qbuf, stat);  // no query row may see this key block
 
     Frag<E> kf[NKS];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) kf[ks] = global_frag<E>(kh, krow, a.T, D, 16 * ks + 8 * g);
+    for (int ks = 0; ks < NKS; ++ks) kf[ks] = global_frag<E>(kh, krow, a.Tk, D, 16 * ks + 8 * g);
 
     // Q and dO rows (A of S, dP); the V tile has the same row format, so the
     // same offsets read V rows w*32 + c (B of dP)
@@ -172,7 +173,7 @@ __global__ __launch_bounds__(NW * 64, sizeof(E) == 2 ? 8 / NW : 1) void bwd_dkdv
         if (more) issue(it + 1, nb, stat);
 
         const int qbase = (i0 + it % niq) * BQ;
-        const bool need_mask = (CAUSAL && qbase < key0 + BK - 1) || (qbase + BQ > a.T);
+        const bool need_mask = (CAUSAL && qbase + a.off < key0 + BK - 1) || (qbase + BQ > a.Tq);
 
 #pragma unroll
         for (int qb = 0; qb < NQB; ++qb) {
@@ -193,7 +194,7 @@ __global__ __launch_bounds__(NW * 64, sizeof(E) == 2 ? 8 / NW : 1) void bwd_dkdv
                     float p = fast_exp2(fmaf(s[r], a.c, -L4[e]));
                     if (need_mask) {
                         const int qi = qbase + q + e;
-                        const bool vis = (qi < a.T) && (!CAUSAL || krow <= qi);
+                        const bool vis = (qi < a.Tq) && (!CAUSAL || krow <= qi + a.off);
                         if (!vis) p = 0.f;
                     }
                     s[r] = p;                     // P
@@ -218,7 +219,7 @@ __global__ __launch_bounds__(NW * 64, sizeof(E) == 2 ? 8 / NW : 1) void bwd_dkdv
     }
 
     // this lane: key krow, columns 32db + 8rg + 4g + e
-    if (krow < a.T) {
+    if (krow < a.Tk) {
         E* dkh = static_cast<E*>(a.dk) + kvoff + (size_t)krow * D;
         E* dvh = static_cast<E*>(a.dv) + kvoff + (size_t)krow * D;
 #pragma unroll
@@ -283,26 +284,27 @@ __global__ __launch_bounds__(NW * 64, sizeof(E) == 2 ? 8 / NW : 1) void bwd_dq_k
     const int g = lane >> 5;
     const int c = lane & 31;
 
-    const int nqt = (a.T + BR - 1) / BR;
+    const int nqt = (a.Tq + BR - 1) / BR;
     const TileId id = map_tile(blockIdx.x, a.B, a.Hq, a.Hkv, a.Hq / a.Hkv, nqt, CAUSAL);
     const int b = id.b, hq = id.h;
     const int hk = hq / (a.Hq / a.Hkv);
     const int q0 = id.tile * BR;
     const int qrow = q0 + w * 32 + c;
 
-    const size_t qoff = (size_t)(b * a.Hq + hq) * a.T * D;
-    const size_t kvoff = (size_t)(b * a.Hkv + hk) * a.T * D;
+    const size_t qoff = (size_t)(b * a.Hq + hq) * a.Tq * D;
+    const size_t kvoff = (size_t)(b * a.Hkv + hk) * a.Tk * D;
     const E* kh = static_cast<const E*>(a.k) + kvoff;
     const E* vh = static_cast<const E*>(a.v) + kvoff;
 
-    const int kend = CAUSAL ? min(q0 + BR, a.T) : a.T;
+    // key tiles visited (query row i sees keys j <= i + off when causal)
+    const int kend = CAUSAL ? min(q0 + BR + a.off, a.Tk) : a.Tk;
     const int nkv = (kend + BC - 1) / BC;
-    const int nfull = CAUSAL ? (q0 + 1) / BC : a.T / BC;
+    const int nfull = CAUSAL ? min((q0 + a.off + 1) / BC, a.Tk / BC) : a.Tk / BC;
 
     Tile dma;
     dma.init(tid);
-    dma.load(smem, kh, 0, a.T, w);
-    dma.load(smem + Tile::BYTES, vh, 0, a.T, w);
+    dma.load(smem, kh, 0, a.Tk, w);
+    dma.load(smem + Tile::BYTES, vh, 0, a.Tk, w);
 
     RowReader<Tile, E, D> rrd;  // K and V rows (A of S^T, dP^T)
     rrd.init(c, g);
@@ -312,12 +314,12 @@ __global__ __launch_bounds__(NW * 64, sizeof(E) == 2 ? 8 / NW : 1) void bwd_dq_k
     Frag<E> qf[NKS], of[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-        qf[ks] = global_frag<E>(static_cast<const E*>(a.q) + qoff, qrow, a.T, D, 16 * ks + 8 * g);
-        of[ks] = global_frag<E>(static_cast<const E*>(a.dout) + qoff, qrow, a.T, D, 16 * ks + 8 * g);
+        qf[ks] = global_frag<E>(static_cast<const E*>(a.q) + qoff, qrow, a.Tq, D, 16 * ks + 8 * g);
+        of[ks] = global_frag<E>(static_cast<const E*>(a.dout) + qoff, qrow, a.Tq, D, 16 * ks + 8 * g);
     }
     float L2 = 0.f, Dl = 0.f;
-    if (qrow < a.T) {
-        const size_t r = (size_t)(b * a.Hq + hq) * a.T + qrow;
+    if (qrow < a.Tq) {
+        const size_t r = (size_t)(b * a.Hq + hq) * a.Tq + qrow;
         L2 = a.lse[r] * kLog2e;
         Dl = a.delta[r];
     }
@@ -335,8 +337,8 @@ __global__ __launch_bounds__(NW * 64, sizeof(E) == 2 ? 8 / NW : 1) void bwd_dq_k
         const unsigned char* Vs = Ks + Tile::BYTES;
         if (j + 1 < nkv) {
             unsigned char* nb = smem + (1 - BI) * Cfg::BUF;
-            dma.load(nb, kh, (j + 1) * BC, a.T, w);
-            dma.load(nb + Tile::BYTES, vh, (j + 1) * BC, a.T, w);
+            dma.load(nb, kh, (j + 1) * BC, a.Tk, w);
+            dma.load(nb + Tile::BYTES, vh, (j + 1) * BC, a.Tk, w);
         }
         const bool need_mask = j >= nfull;
 #pragma unroll
@@ -355,7 +357,7 @@ __global__ __launch_bounds__(NW * 64, sizeof(E) == 2 ? 8 / NW : 1) void bwd_dq_k
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int kj = j * BC + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-                    const bool vis = CAUSAL ? (kj <= qrow) : (kj < a.T);
+                    const bool vis = kj < a.Tk && (!CAUSAL || kj <= qrow + a.off);
                     s[r] = vis ? s[r] : 0.f;
                 }
             }
@@ -378,7 +380,7 @@ __global__ __launch_bounds__(NW * 64, sizeof(E) == 2 ? 8 / NW : 1) void bwd_dq_k
         if (j + 1 < nkv) step(std::integral_constant<int, 1>{}, j + 1);
     }
 
-    if (qrow < a.T) {
+    if (qrow < a.Tq) {
         E* dqh = static_cast<E*>(a.dq) + qoff + (size_t)qrow * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
@@ -434,7 +436,7 @@ static hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t stream)
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cfg::SMEM);
     if (attr != hipSuccess) return attr;
-    const int nkt = (a.T + Cfg::BK - 1) / Cfg::BK;
+    const int nkt = (a.Tk + Cfg::BK - 1) / Cfg::BK;
     const long grid = (long)nkt * a.B * a.Hkv;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Cfg::NT), Cfg::SMEM, stream, a);
     return hipGetLastError();
@@ -457,7 +459,7 @@ static hipError_t launch_dq_t(const BwdArgs& a, hipStream_t stream)
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cfg::SMEM);
     if (attr != hipSuccess) return attr;
-    const int nqt = (a.T + Cfg::BR - 1) / Cfg::BR;
+    const int nqt = (a.Tq + Cfg::BR - 1) / Cfg::BR;
     const long grid = (long)nqt * a.B * a.Hq;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Cfg::NT), Cfg::SMEM, stream, a);
     return hipGetLastError();

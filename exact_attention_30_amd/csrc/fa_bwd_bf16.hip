@@ -22,9 +22,10 @@
 // The tiles arrive by explicitly scheduled LDS DMA three tiles ahead in four
 // stage buffers at the bottom of LDS; the loop is unrolled over the stages and
 // the per-lane read addresses carry the LDS base, so every read is one address
-// register plus an immediate offset, with no address arithmetic in the loop.  Tiles wholly visible to a wave carry no mask code; with
-// 32-row query tiles and 32-key waves any other tile is exactly the lower
-// triangle or wholly invisible, handled in a rarely taken branch.
+// register plus an immediate offset, with no address arithmetic in the loop.
+// Tiles wholly visible to a wave carry no mask code; the few others (near the
+// diagonal j = i + off of the causal mask, or padding) take a per-element mask
+// in a rarely taken branch.
 #include <type_traits>
 #include <utility>
 
@@ -55,18 +56,6 @@ struct DkdvBf16Cfg {
     static_assert(AHEAD + 1 <= NSTAGE, "a stage is refilled only after its tile was used");
     static_assert(QT::NI == 1, "one Q and one dO instruction per loading wave");
 };
-
-// Lane mask of accumulator register r (rows = queries 8(r/4) + 4g + r%4,
-// columns = keys c) for a query tile that starts at the wave's first key:
-// query row >= key.
-__host__ __device__ constexpr uint64_t tri_mask(int r)
-{
-    const int q0 = 8 * (r / 4) + r % 4;  // row of lane group g = 0
-    const int q1 = q0 + 4;               // row of lane group g = 1
-    const uint64_t lo = (q0 + 1 >= 32) ? 0xffffffffull : ((1ull << (q0 + 1)) - 1);
-    const uint64_t hi = (q1 + 1 >= 32) ? 0xffffffffull : ((1ull << (q1 + 1)) - 1);
-    return lo | (hi << 32);
-}
 
 // f(stage, i + K) for K = 0 .. N-1, with the stage as a compile-time constant
 template <class F, int... K>
@@ -117,7 +106,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
     const int c = lane & 31;
     const int G = a.Hq / a.Hkv;
 
-    const int nkt = (a.T + BK - 1) / BK;
+    const int nkt = (a.Tk + BK - 1) / BK;
     // causal: the first key blocks see the most query rows
     const TileId id = map_tile(blockIdx.x, a.B, a.Hq, a.Hkv, 1, nkt, false);
     const int b = id.b, hk = id.h;
@@ -125,14 +114,15 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
     const int kw = key0 + 32 * w;  // first key of this wave
     const int krow = kw + c;       // the key this lane owns
 
-    const size_t kvoff = (size_t)(b * a.Hkv + hk) * a.T * D;
+    const size_t kvoff = (size_t)(b * a.Hkv + hk) * a.Tk * D;
     const bf16* kh = static_cast<const bf16*>(a.k) + kvoff;
     const bf16* vh = static_cast<const bf16*>(a.v) + kvoff;
 
-    // the (query head, query tile) pairs that see this key block
-    const int nq = (a.T + BQ - 1) / BQ;
-    const int i0 = CAUSAL ? key0 / BQ : 0;
-    const int niq = nq - i0;
+    // the (query head, query tile) pairs that see this key block (query row i
+    // sees keys j <= i + off when causal)
+    const int nq = (a.Tq + BQ - 1) / BQ;
+    const int i0 = CAUSAL ? max(key0 - a.off, 0) / BQ : 0;
+    const int niq = max(nq - i0, 0);
     const int n = G * niq;
     const int npad = (n + NSTAGE - 1) / NSTAGE * NSTAGE;  // padded tiles: all masked
 
@@ -151,13 +141,13 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
     auto issue = [&](int st) {
         const uint32_t base = lds0 + (uint32_t)(st * STAGE);
         if (w < QW) {
-            const size_t qoff = (size_t)(b * a.Hq + dhq) * a.T * D;
-            qt.load(base, static_cast<const bf16*>(a.q) + qoff, dti * BQ, a.T, w);
-            qt.load(base + QT::BYTES, static_cast<const bf16*>(a.dout) + qoff, dti * BQ, a.T, w);
+            const size_t qoff = (size_t)(b * a.Hq + dhq) * a.Tq * D;
+            qt.load(base, static_cast<const bf16*>(a.q) + qoff, dti * BQ, a.Tq, w);
+            qt.load(base + QT::BYTES, static_cast<const bf16*>(a.dout) + qoff, dti * BQ, a.Tq, w);
         }
         if (w < 2) {
-            const float* src = (w == 0 ? a.lse : a.delta) + (size_t)(b * a.Hq + dhq) * a.T + dti * BQ;
-            const i32x4 r = buffer_rsrc(src, (a.T - dti * BQ) * 4);
+            const float* src = (w == 0 ? a.lse : a.delta) + (size_t)(b * a.Hq + dhq) * a.Tq + dti * BQ;
+            const i32x4 r = buffer_rsrc(src, (a.Tq - dti * BQ) * 4);
             dma_b32(base + 2 * QT::BYTES + 256 * w, r, (uint32_t)(lane * 4));
         }
         if (++dhq == (hk + 1) * G) {
@@ -180,7 +170,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
         *reinterpret_cast<u32x4*>(stages + off) = u32x4{0, 0, 0, 0};
     sync_lds();
     {  // this wave's 32 V rows (rows past T read as zeros)
-        const int left = a.T - kw;
+        const int left = a.Tk - kw;
         const i32x4 r = buffer_rsrc(vh + (size_t)kw * D, left > 0 ? left * D * 2 : 0);
         const uint32_t vb = lds_addr(Vs) + (uint32_t)(w * VW::BYTES);
 #pragma unroll
@@ -191,7 +181,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
     // B operand of S = Q K^T: this lane's key row, 8 columns per 16-deep step
     Frag<bf16> kf[NKS];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) kf[ks] = global_frag<bf16>(kh, krow, a.T, D, 16 * ks + 8 * g);
+    for (int ks = 0; ks < NKS; ++ks) kf[ks] = global_frag<bf16>(kh, krow, a.Tk, D, 16 * ks + 8 * g);
 
     // Q, dO rows (A of S, dP) and Q^T, dO^T (A of dK^T, dV^T) in the
     // stages; V rows 32w + c (B of dP) in read order
@@ -243,16 +233,17 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
             mma(dp, frag(qrd.read(ks, OI)), frag(lds_b128(vrd + (uint32_t)VW::frag_off(0, ks))));
         }
         // Tiles wholly visible to this wave take no mask code; the others set
-        // the invisible scores to -inf, so that P = 0 there.
+        // the invisible scores to -inf, so that P = 0 there.  Lane c's key
+        // kw + c is visible to query qb + row iff c <= qb + off - kw + row.
         const bool pad = i >= n;
         const int qb = bti * BQ;
-        if (pad || (CAUSAL && qb <= kw)) {
+        if (pad || (CAUSAL && qb + a.off < kw + 31)) {
             asm volatile("");  // keep this a branch
-            const bool tri = !pad && qb == kw;
+            const int dlt = pad ? -64 : max(qb + a.off - kw, -64);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const uint64_t m = tri ? tri_mask(r) : 0ull;
-                s[r] = __builtin_amdgcn_inverse_ballot_w64(m) ? s[r] : -INFINITY;
+                const int row = 8 * (r >> 2) + 4 * g + (r & 3);
+                s[r] = c <= dlt + row ? s[r] : -INFINITY;
             }
         }
         if (++bh == G) {
@@ -293,7 +284,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
         unroll_stages(body, i, std::make_integer_sequence<int, NSTAGE>{});
 
     // this lane: key krow, columns 32db + 8rg + 4g + e
-    if (krow < a.T) {
+    if (krow < a.Tk) {
         bf16* dkh = static_cast<bf16*>(a.dk) + kvoff + (size_t)krow * D;
         bf16* dvh = static_cast<bf16*>(a.dv) + kvoff + (size_t)krow * D;
 #pragma unroll
@@ -369,7 +360,7 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
     const int g = lane >> 5;
     const int c = lane & 31;
 
-    const int nqt = (a.T + BR - 1) / BR;
+    const int nqt = (a.Tq + BR - 1) / BR;
     const TileId id = map_tile(blockIdx.x, a.B, a.Hq, a.Hkv, a.Hq / a.Hkv, nqt, CAUSAL);
     const int b = id.b, hq = id.h;
     const int hk = hq / (a.Hq / a.Hkv);
@@ -377,17 +368,17 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
     const int qw = q0 + 32 * w;  // first query of this wave
     const int qrow = qw + c;     // the query this lane owns
 
-    const size_t qoff = (size_t)(b * a.Hq + hq) * a.T * D;
-    const size_t kvoff = (size_t)(b * a.Hkv + hk) * a.T * D;
+    const size_t qoff = (size_t)(b * a.Hq + hq) * a.Tq * D;
+    const size_t kvoff = (size_t)(b * a.Hkv + hk) * a.Tk * D;
     const bf16* kh = static_cast<const bf16*>(a.k) + kvoff;
     const bf16* vh = static_cast<const bf16*>(a.v) + kvoff;
 
-    // key tiles visited by the workgroup; tiles below nfull are wholly
-    // visible to this wave
-    const int kend = CAUSAL ? min(q0 + BR, a.T) : a.T;
+    // key tiles visited by the workgroup (query row i sees keys j <= i + off
+    // when causal); tiles below nfull are wholly visible to this wave
+    const int kend = CAUSAL ? min(q0 + BR + a.off, a.Tk) : a.Tk;
     const int nkv = (kend + BC - 1) / BC;
     const int npad = (nkv + NSTAGE - 1) / NSTAGE * NSTAGE;  // padded tiles: all masked
-    const int nfull = CAUSAL ? (qw + 1) / BC : a.T / BC;
+    const int nfull = CAUSAL ? min((qw + a.off + 1) / BC, a.Tk / BC) : a.Tk / BC;
 
     const uint32_t lds0 = lds_addr(smem);
     KT kt;
@@ -396,8 +387,8 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
 #pragma unroll
     for (int i = 0; i < Cfg::VI; ++i) vdma[i] = VT::dma_off(w + NWAVE * i, lane);
     auto issue = [&](int j, int st) {  // tile j into stage st
-        kt.load(lds0 + (uint32_t)(st * KT::BYTES), kh, j * BC, a.T, w);
-        const int left = a.T - j * BC;
+        kt.load(lds0 + (uint32_t)(st * KT::BYTES), kh, j * BC, a.Tk, w);
+        const int left = a.Tk - j * BC;
         const i32x4 r = buffer_rsrc(vh + (size_t)j * BC * D, left > 0 ? left * D * 2 : 0);
         const uint32_t vb = lds0 + (uint32_t)(Cfg::VBASE + st * VT::BYTES);
 #pragma unroll
@@ -424,12 +415,12 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
     Frag<bf16> qf[NKS], of[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-        qf[ks] = global_frag<bf16>(static_cast<const bf16*>(a.q) + qoff, qrow, a.T, D, 16 * ks + 8 * g);
-        of[ks] = global_frag<bf16>(static_cast<const bf16*>(a.dout) + qoff, qrow, a.T, D, 16 * ks + 8 * g);
+        qf[ks] = global_frag<bf16>(static_cast<const bf16*>(a.q) + qoff, qrow, a.Tq, D, 16 * ks + 8 * g);
+        of[ks] = global_frag<bf16>(static_cast<const bf16*>(a.dout) + qoff, qrow, a.Tq, D, 16 * ks + 8 * g);
     }
     float L2 = 0.f, Dl = 0.f;
-    if (qrow < a.T) {
-        const size_t r = (size_t)(b * a.Hq + hq) * a.T + qrow;
+    if (qrow < a.Tq) {
+        const size_t r = (size_t)(b * a.Hq + hq) * a.Tq + qrow;
         L2 = a.lse[r] * kLog2e;
         Dl = a.delta[r];
     }
@@ -478,7 +469,7 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int kj = j * BC + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-                    const bool vis = (j < nkv) && (CAUSAL ? (kj <= qrow) : (kj < a.T));
+                    const bool vis = (j < nkv) && kj < a.Tk && (!CAUSAL || kj <= qrow + a.off);
                     s[r] = vis ? s[r] : -INFINITY;
                 }
             }
@@ -502,7 +493,7 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
     for (int j = 0; j < npad; j += NSTAGE)
         unroll_stages(body, j, std::make_integer_sequence<int, NSTAGE>{});
 
-    if (qrow < a.T) {
+    if (qrow < a.Tq) {
         bf16* dqh = static_cast<bf16*>(a.dq) + qoff + (size_t)qrow * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
@@ -525,7 +516,7 @@ static hipError_t launch_dq(const BwdArgs& a, hipStream_t stream)
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::SMEM);
     if (attr != hipSuccess) return attr;
-    const int nqt = (a.T + Cfg::BR - 1) / Cfg::BR;
+    const int nqt = (a.Tq + Cfg::BR - 1) / Cfg::BR;
     const long grid = (long)nqt * a.B * a.Hq;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Cfg::NT), Cfg::SMEM, stream, a);
     return hipGetLastError();
@@ -546,7 +537,7 @@ static hipError_t launch_dkdv(const BwdArgs& a, hipStream_t stream)
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::SMEM);
     if (attr != hipSuccess) return attr;
-    const int nkt = (a.T + Cfg::BK - 1) / Cfg::BK;
+    const int nkt = (a.Tk + Cfg::BK - 1) / Cfg::BK;
     const long grid = (long)nkt * a.B * a.Hkv;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Cfg::NT), Cfg::SMEM, stream, a);
     return hipGetLastError();

@@ -66,26 +66,27 @@ __global__ __launch_bounds__(NW * 64, sizeof(E) == 2 ? 8 / NW : 1) void fwd_kern
     const int g = lane >> 5;
     const int c = lane & 31;
 
-    const int nqt = (a.T + BR - 1) / BR;
+    const int nqt = (a.Tq + BR - 1) / BR;
     const TileId id = map_tile(blockIdx.x, a.B, a.Hq, a.Hkv, a.Hq / a.Hkv, nqt, CAUSAL);
     const int b = id.b, hq = id.h;
     const int hk = hq / (a.Hq / a.Hkv);
     const int q0 = id.tile * BR;
     const int qrow = q0 + w * 32 + c;  // the query this lane owns
 
-    const E* qh = static_cast<const E*>(a.q) + (size_t)(b * a.Hq + hq) * a.T * D;
-    const E* kh = static_cast<const E*>(a.k) + (size_t)(b * a.Hkv + hk) * a.T * D;
-    const E* vh = static_cast<const E*>(a.v) + (size_t)(b * a.Hkv + hk) * a.T * D;
+    const E* qh = static_cast<const E*>(a.q) + (size_t)(b * a.Hq + hq) * a.Tq * D;
+    const E* kh = static_cast<const E*>(a.k) + (size_t)(b * a.Hkv + hk) * a.Tk * D;
+    const E* vh = static_cast<const E*>(a.v) + (size_t)(b * a.Hkv + hk) * a.Tk * D;
 
-    // key tiles to visit, and how many of them need no mask
-    const int kend = CAUSAL ? min(q0 + BR, a.T) : a.T;
+    // key tiles to visit (query row i sees keys j <= i + off when causal), and
+    // how many of them need no mask
+    const int kend = CAUSAL ? min(q0 + BR + a.off, a.Tk) : a.Tk;
     const int nkv = (kend + BC - 1) / BC;
-    const int nfull = CAUSAL ? (q0 + 1) / BC : a.T / BC;
+    const int nfull = CAUSAL ? min((q0 + a.off + 1) / BC, a.Tk / BC) : a.Tk / BC;
 
     Tile dma;
     dma.init(tid);
-    dma.load(smem, kh, 0, a.T, w);
-    dma.load(smem + Tile::BYTES, vh, 0, a.T, w);
+    dma.load(smem, kh, 0, a.Tk, w);
+    dma.load(smem + Tile::BYTES, vh, 0, a.Tk, w);
 
     RowReader<Tile, E, D> krd;
     krd.init(c, g);
@@ -95,7 +96,7 @@ __global__ __launch_bounds__(NW * 64, sizeof(E) == 2 ? 8 / NW : 1) void fwd_kern
     // B operand of S^T = K Q^T: this lane's query row, 8 columns per step
     Frag<E> qf[NKS];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) qf[ks] = global_frag<E>(qh, qrow, a.T, D, 16 * ks + 8 * g);
+    for (int ks = 0; ks < NKS; ++ks) qf[ks] = global_frag<E>(qh, qrow, a.Tq, D, 16 * ks + 8 * g);
 
     f32x16 o[NDB];
 #pragma unroll
@@ -113,8 +114,8 @@ __global__ __launch_bounds__(NW * 64, sizeof(E) == 2 ? 8 / NW : 1) void fwd_kern
         const unsigned char* Vs = Ks + Tile::BYTES;
         if (j + 1 < nkv) {
             unsigned char* nb = smem + (1 - BI) * Cfg::BUF;
-            dma.load(nb, kh, (j + 1) * BC, a.T, w);
-            dma.load(nb + Tile::BYTES, vh, (j + 1) * BC, a.T, w);
+            dma.load(nb, kh, (j + 1) * BC, a.Tk, w);
+            dma.load(nb + Tile::BYTES, vh, (j + 1) * BC, a.Tk, w);
         }
 
         // S^T block kb: rows = keys 32kb.., columns = this wave's 32 queries
@@ -132,7 +133,7 @@ __global__ __launch_bounds__(NW * 64, sizeof(E) == 2 ? 8 / NW : 1) void fwd_kern
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int kj = j * BC + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-                    const bool vis = CAUSAL ? (kj <= qrow) : (kj < a.T);
+                    const bool vis = kj < a.Tk && (!CAUSAL || kj <= qrow + a.off);
                     if (!vis) s[kb][r] = -INFINITY;
                 }
         }
@@ -185,8 +186,8 @@ __global__ __launch_bounds__(NW * 64, sizeof(E) == 2 ? 8 / NW : 1) void fwd_kern
     // 32db + 8rg + 4g + i) and lse
     const float lt = pair_sum(l);
     const float inv = 1.f / lt;
-    if (qrow < a.T) {
-        E* oh = static_cast<E*>(a.o) + ((size_t)(b * a.Hq + hq) * a.T + qrow) * D;
+    if (qrow < a.Tq) {
+        E* oh = static_cast<E*>(a.o) + ((size_t)(b * a.Hq + hq) * a.Tq + qrow) * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -205,7 +206,7 @@ __global__ __launch_bounds__(NW * 64, sizeof(E) == 2 ? 8 / NW : 1) void fwd_kern
                 }
             }
         if (g == 0)
-            a.lse[(size_t)(b * a.Hq + hq) * a.T + qrow] = (mref + __log2f(lt)) * kLn2;
+            a.lse[(size_t)(b * a.Hq + hq) * a.Tq + qrow] = (mref + __log2f(lt)) * kLn2;
     }
 }
 
@@ -222,7 +223,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream)
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cfg::SMEM);
     if (attr != hipSuccess) return attr;
-    const int nqt = (a.T + Cfg::BR - 1) / Cfg::BR;
+    const int nqt = (a.Tq + Cfg::BR - 1) / Cfg::BR;
     const long grid = (long)nqt * a.B * a.Hq;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Cfg::NT), Cfg::SMEM, stream, a);
     return hipGetLastError();

@@ -28,11 +28,14 @@
 //   * Lazy rescale: the reference max of a row only moves when the row max
 //     exceeds it by more than 8 (log2 units), so most tiles skip rescaling O
 //     and l; the weights stay below 2^8, and o and l share the reference.
-//   * Causal: tiles wholly in the future of a wave are skipped by that wave;
-//     tiles wholly in its past run without mask code; the remaining tiles take
-//     the per-element mask derived from the lane's query index and the key
-//     index ("Optimización de Flash Attention ...", «Atención causal» and the
-//     K-loop split of «La pila de optimización»).
+//   * Causal: query row i sees key j iff j <= i + off, where off places the
+//     query rows among the keys (0 when both are the same sequence; the
+//     cuTile kernel's input_pos, «Parte 1»).  Key tiles past the workgroup's
+//     last visible key are not visited; tiles wholly visible to a wave run
+//     without mask code; the others take the per-element mask derived from the
+//     lane's query index and the key index ("Optimización de Flash Attention
+//     ...", «Atención causal» and the K-loop split of «La pila de
+//     optimización»).
 #include <type_traits>
 
 #include "fa_device.hpp"
@@ -100,7 +103,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
     const int g = lane >> 5;
     const int c = lane & 31;
 
-    const int nqt = (a.T + BR - 1) / BR;
+    const int nqt = (a.Tq + BR - 1) / BR;
     const TileId id = map_tile(blockIdx.x, a.B, a.Hq, a.Hkv, a.Hq / a.Hkv, nqt, CAUSAL);
     const int b = id.b, hq = id.h;
     const int hk = hq / (a.Hq / a.Hkv);
@@ -109,15 +112,15 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
     const int qrow = qw + c;      // the query this lane owns
     const int grp = w / Cfg::NW;  // 0 or 1: phase offset of the ping-pong
 
-    const bf16* qh = static_cast<const bf16*>(a.q) + (size_t)(b * a.Hq + hq) * a.T * D;
-    const bf16* kh = static_cast<const bf16*>(a.k) + (size_t)(b * a.Hkv + hk) * a.T * D;
-    const bf16* vh = static_cast<const bf16*>(a.v) + (size_t)(b * a.Hkv + hk) * a.T * D;
+    const bf16* qh = static_cast<const bf16*>(a.q) + (size_t)(b * a.Hq + hq) * a.Tq * D;
+    const bf16* kh = static_cast<const bf16*>(a.k) + (size_t)(b * a.Hkv + hk) * a.Tk * D;
+    const bf16* vh = static_cast<const bf16*>(a.v) + (size_t)(b * a.Hkv + hk) * a.Tk * D;
 
-    // key tiles visited by the workgroup; per wave, tiles it sees at all
-    // (live) and tiles it sees completely (no mask)
-    const int kend = CAUSAL ? min(q0 + BR, a.T) : a.T;
+    // key tiles visited by the workgroup (query row i sees keys j <= i + off
+    // when causal); per wave, the tiles it sees completely (no mask)
+    const int kend = CAUSAL ? min(q0 + BR + a.off, a.Tk) : a.Tk;
     const int nkv = (kend + BC - 1) / BC;
-    const int nfull = CAUSAL ? (qw + 1) / BC : a.T / BC;
+    const int nfull = CAUSAL ? min((qw + a.off + 1) / BC, a.Tk / BC) : a.Tk / BC;
 
     // this thread's DMA source offsets (same for every tile)
     uint32_t koff[KI], voff[VI];
@@ -132,13 +135,13 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
         const uint32_t base = lds0 + (uint32_t)((s % Cfg::NSTAGE) * Cfg::STAGE);
         if (s < nkv) {
             const int row0 = s * BC;
-            const i32x4 r = buffer_rsrc(kh + (size_t)row0 * D, (a.T - row0) * D * 2);
+            const i32x4 r = buffer_rsrc(kh + (size_t)row0 * D, (a.Tk - row0) * D * 2);
 #pragma unroll
             for (int i = 0; i < KI; ++i) dma_b128(base + (uint32_t)((w + NWAVE * i) * 1024), r, koff[i]);
         }
         if (s >= 1) {
             const int row0 = (s - 1) * BC;
-            const i32x4 r = buffer_rsrc(vh + (size_t)row0 * D, (a.T - row0) * D * 2);
+            const i32x4 r = buffer_rsrc(vh + (size_t)row0 * D, (a.Tk - row0) * D * 2);
 #pragma unroll
             for (int i = 0; i < VI; ++i)
                 dma_b128(base + (uint32_t)(KT::BYTES + (w + NWAVE * i) * 1024), r, voff[i]);
@@ -152,7 +155,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
     // B operand of S^T = K Q^T: this lane's query row, 8 columns per step
     Frag<bf16> qf[NKS];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) qf[ks] = global_frag<bf16>(qh, qrow, a.T, D, 16 * ks + 8 * g);
+    for (int ks = 0; ks < NKS; ++ks) qf[ks] = global_frag<bf16>(qh, qrow, a.Tq, D, 16 * ks + 8 * g);
 
     f32x16 o[NDB];
 #pragma unroll
@@ -224,7 +227,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int kj = j * BC + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-                    const bool vis = CAUSAL ? (kj <= qrow) : (kj < a.T);
+                    const bool vis = kj < a.Tk && (!CAUSAL || kj <= qrow + a.off);
                     if (!vis) s[kb][r] = -INFINITY;
                 }
         }
@@ -327,8 +330,8 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
     // 32db + 8rg + 4g + i) and lse
     const float lt = pair_sum(l);
     const float inv = 1.f / lt;
-    if (qrow < a.T) {
-        bf16* oh = static_cast<bf16*>(a.o) + ((size_t)(b * a.Hq + hq) * a.T + qrow) * D;
+    if (qrow < a.Tq) {
+        bf16* oh = static_cast<bf16*>(a.o) + ((size_t)(b * a.Hq + hq) * a.Tq + qrow) * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -338,7 +341,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
                 for (int i = 0; i < 4; ++i) x[i] = (bf16)(o[db][4 * rg + i] * inv);
                 *reinterpret_cast<bf16x4*>(oh + db * 32 + 8 * rg + 4 * g) = x;
             }
-        if (g == 0) a.lse[(size_t)(b * a.Hq + hq) * a.T + qrow] = (mref + __log2f(lt)) * kLn2;
+        if (g == 0) a.lse[(size_t)(b * a.Hq + hq) * a.Tq + qrow] = (mref + __log2f(lt)) * kLn2;
     }
 }
 
@@ -351,7 +354,7 @@ static hipError_t launch_t(const FwdArgs& a, hipStream_t stream)
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::SMEM);
     if (attr != hipSuccess) return attr;
-    const int nqt = (a.T + Cfg::BR - 1) / Cfg::BR;
+    const int nqt = (a.Tq + Cfg::BR - 1) / Cfg::BR;
     const long grid = (long)nqt * a.B * a.Hq;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Cfg::NT), Cfg::SMEM, stream, a);
     return hipGetLastError();

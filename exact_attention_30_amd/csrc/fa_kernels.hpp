@@ -11,7 +11,9 @@ struct FwdArgs {
     const void* v;
     void* o;
     float* lse;
-    int B, Hq, Hkv, T;
+    int B, Hq, Hkv;
+    int Tq, Tk;   // query rows, key rows
+    int off;      // causal: query row i sees key j iff j <= i + off (off >= 0)
     float c;      // scale * log2(e): scores are exponentiated in base 2
     float scale;  // for the natural-log lse
 };
@@ -26,8 +28,10 @@ struct BwdArgs {
     void* dq;
     void* dk;
     void* dv;
-    int B, Hq, Hkv, T;
-    float c;      // scale * log2(e)
+    int B, Hq, Hkv;
+    int Tq, Tk;  // query rows, key rows
+    int off;     // causal: query row i sees key j iff j <= i + off (off >= 0)
+    float c;     // scale * log2(e)
     float scale;
 };
 

@@ -10,9 +10,12 @@
  *
  *     O = softmax(Q K^T * scale + mask) V
  *
- * where the causal mask lets query i see key j iff i >= j ("Optimización de
- * Flash Attention ...", «Atención causal»).  The T x T score and weight
- * matrices are never written to memory: the forward walks key tiles with the
+ * where the causal mask lets query i see key j iff j <= i + q_offset
+ * ("Optimización de Flash Attention ...", «Atención causal»; the offset is the
+ * position of query row 0 among the keys, the input_pos argument of the
+ * cuTile kernel in «Parte 1»; it is 0 when queries and keys are one
+ * sequence).  The Tq x Tk score and weight matrices are never written to
+ * memory: the forward walks key tiles with the
  * online softmax (running max m, sum l, rescale by exp(m - m')), as in
  * "L'attention fusionnée", «Le softmax en ligne», and stores per query row the
  * log-sum-exp L = m + ln(l).  The backward recomputes P = exp(S - L) tile by
@@ -23,11 +26,11 @@
  *     dK = dS^T Q * scale.
  *
  * Layouts.  All tensors are contiguous, row-major, element type `dt`:
- *     q, o, dout, dq : [B][Hq][T][D]
- *     k, v, dk, dv   : [B][Hkv][T][D]
- *     lse            : [B][Hq][T] float32, natural log, in units of the scaled
+ *     q, o, dout, dq : [B][Hq][Tq][D]
+ *     k, v, dk, dv   : [B][Hkv][Tk][D]
+ *     lse            : [B][Hq][Tq] float32, natural log, in units of the scaled
  *                      scores (lse_i = log sum_j exp(scale * q_i . k_j)).
- * Query and key sequences have the same length T.
+ * The calls without a _kv suffix take one length T = Tq = Tk and offset 0.
  *
  * Ownership and execution.  The caller owns every buffer; the library never
  * allocates device memory and keeps no pointer after a call returns.  Each call
@@ -38,13 +41,19 @@
  *
  * Errors.  Arguments are checked on the host before anything is enqueued, in
  * this order, and the first failure is returned:
- *     FA_ERR_SHAPE        B < 0, T < 0, Hq < 1, Hkv < 1, Hq % Hkv != 0, a
- *                         grid too large to index, or one head of a tensor
- *                         (T * D elements) larger than 2^31 - 1 bytes;
+ *     FA_ERR_SHAPE        B < 0, Tq < 0, Tk < 0, Hq < 1, Hkv < 1,
+ *                         Hq % Hkv != 0, query rows without keys (B*Tq > 0
+ *                         and Tk == 0), causal with q_offset < 0 or
+ *                         q_offset + Tq > 2^31 - 4097, a grid too large to
+ *                         index, or one head of a tensor (T * D elements)
+ *                         larger than 2^31 - 1 bytes;
  *     FA_ERR_UNSUPPORTED  D not in {64, 128}, unknown dtype, or scale not a
  *                         finite positive number;
  *     FA_ERR_NULL         a required pointer is NULL (pointers are not needed
- *                         when B * T == 0, which is a valid no-op);
+ *                         when there is nothing to compute: B * Tq == 0 for
+ *                         the forward, B * Tk == 0 for the backward; with
+ *                         Tq == 0 the backward only needs k, v, dk, dv, and
+ *                         sets dk = dv = 0);
  *     FA_ERR_ALIGN        a tensor pointer is not 16-byte aligned (lse and the
  *                         workspace: 4-byte and 16-byte);
  *     FA_ERR_HIP          the HIP runtime reported an error while launching.
@@ -90,8 +99,21 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  int Hkv, int T, int D, float scale, int causal, fa_dtype dt, void* stream);
 
 /*
+ * Forward pass of Tq query rows against Tk key rows: as fa_fwd, with
+ *   q, o [B,Hq,Tq,D], k/v [B,Hkv,Tk,D], lse [B,Hq,Tq];
+ *   q_offset (causal only, >= 0): query row i sees keys j <= i + q_offset.
+ *   Tk - Tq aligns the last query with the last key (a block of new queries
+ *   against cached keys; a single query against Tk keys sees all of them, as
+ *   in "L'attention fusionnée", «Un premier kernel plus lent»).
+ */
+fa_status fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                    int Hkv, int Tq, int Tk, int D, float scale, int causal, int q_offset,
+                    fa_dtype dt, void* stream);
+
+/*
  * Bytes of device workspace fa_bwd needs: one float32 Delta per query row,
- * B * Hq * T * 4, rounded up to 256.  Returns 0 for invalid or empty shapes.
+ * B * Hq * T * 4, rounded up to 256 (T = Tq for fa_bwd_kv).  Returns 0 for
+ * invalid or empty shapes.
  */
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int T, int D, fa_dtype dt);
 
@@ -113,9 +135,20 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  int Hkv, int T, int D, float scale, int causal, fa_dtype dt, void* stream);
 
 /*
+ * Backward pass of fa_fwd_kv: as fa_bwd, with dq [B,Hq,Tq,D], dk/dv
+ * [B,Hkv,Tk,D] and the same q_offset as the forward.  Keys that no query row
+ * sees get dk = dv = 0.
+ */
+fa_status fa_bwd_kv(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, void* dq, void* dk, void* dv, void* workspace, int B, int Hq,
+                    int Hkv, int Tq, int Tk, int D, float scale, int causal, int q_offset,
+                    fa_dtype dt, void* stream);
+
+/*
  * The three stages of fa_bwd, for callers that schedule or time them
  * separately.  `delta` is a [B,Hq,T] float32 device buffer (for instance the
- * start of the fa_bwd workspace).
+ * start of the fa_bwd workspace).  The _kv forms take Tq, Tk and q_offset as
+ * fa_bwd_kv does (delta [B,Hq,Tq]: fa_bwd_preprocess with T = Tq).
  *   fa_bwd_preprocess: delta_i = sum_d dout_id * o_id ("L'attention
  *       fusionnée", «La passe arrière», the row reduction run before the rest).
  *   fa_bwd_dkdv: dk, dv for every key row (per key tile, summed over the query
@@ -130,11 +163,19 @@ fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* d
 fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
                     const float* lse, const float* delta, void* dq, int B, int Hq, int Hkv, int T,
                     int D, float scale, int causal, fa_dtype dt, void* stream);
+fa_status fa_bwd_dkdv_kv(const void* q, const void* k, const void* v, const void* dout,
+                         const float* lse, const float* delta, void* dk, void* dv, int B, int Hq,
+                         int Hkv, int Tq, int Tk, int D, float scale, int causal, int q_offset,
+                         fa_dtype dt, void* stream);
+fa_status fa_bwd_dq_kv(const void* q, const void* k, const void* v, const void* dout,
+                       const float* lse, const float* delta, void* dq, int B, int Hq, int Hkv,
+                       int Tq, int Tk, int D, float scale, int causal, int q_offset, fa_dtype dt,
+                       void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* fa_status_string(fa_status s);
 
-/* Library version string, e.g. "0.1.0". */
+/* Library version string, e.g. "0.2.0". */
 const char* fa_version(void);
 
 #ifdef __cplusplus

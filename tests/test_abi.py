@@ -135,4 +135,55 @@ def test_binding_rejects_bad_tensors():
     with pytest.raises(TypeError):
         fa.fwd(q.half(), q.half(), q.half())
     with pytest.raises(ValueError):
-        fa.fwd(q, torch.zeros(1, 2, 9, 64), torch.zeros(1, 2, 9, 64))
+        fa.fwd(q, torch.zeros(1, 2, 9, 32), torch.zeros(1, 2, 9, 32))  # head sizes differ
+
+
+def fwd_kv(lib, q=A, k=A, v=A, o=A, lse=A, B=1, Hq=2, Hkv=1, Tq=64, Tk=100, D=128, scale=0.1,
+           causal=1, off=36, dt=BF16):
+    return lib.fa_fwd_kv(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, D, scale, causal, off, dt, None)
+
+
+def bwd_kv(lib, ptrs=None, B=1, Hq=2, Hkv=1, Tq=64, Tk=100, D=128, scale=0.1, causal=1, off=36,
+           dt=BF16):
+    p = ptrs or [A] * 10
+    return lib.fa_bwd_kv(*p, B, Hq, Hkv, Tq, Tk, D, scale, causal, off, dt, None)
+
+
+def test_kv_shape_errors(lib):
+    assert fwd_kv(lib, off=-1) == SHAPE                    # a row would see no key
+    assert fwd_kv(lib, Tk=0) == SHAPE                      # query rows without keys
+    assert fwd_kv(lib, Tq=-1) == SHAPE
+    assert fwd_kv(lib, Tk=-3) == SHAPE
+    assert fwd_kv(lib, off=(1 << 31) - 100, Tq=64) == SHAPE  # key positions overflow
+    assert fwd_kv(lib, Tk=(1 << 23) + 1) == SHAPE          # one K head beyond 2^31 bytes
+    assert bwd_kv(lib, off=-5) == SHAPE
+    assert bwd_kv(lib, Tk=0) == SHAPE
+    assert fwd_kv(lib, off=-1, D=96) == SHAPE              # shape before unsupported
+    assert fwd_kv(lib, D=96) == UNSUP
+    for fn in (lib.fa_bwd_dkdv_kv, lib.fa_bwd_dq_kv):
+        n = 8 if fn is lib.fa_bwd_dkdv_kv else 7
+        assert fn(*([A] * n), 1, 2, 1, 64, 100, 128, 0.1, 1, -2, BF16, None) == SHAPE
+
+
+def test_kv_null_and_align_errors(lib):
+    for name in ("q", "k", "v", "o", "lse"):
+        assert fwd_kv(lib, **{name: 0}) == NULL
+    assert fwd_kv(lib, k=A + 4) == ALIGN
+    for i in range(10):
+        p = [A] * 10
+        p[i] = 0
+        assert bwd_kv(lib, p) == NULL
+    # without query rows only k, v, dk, dv are needed, and they are checked
+    p = [0] * 10
+    p[1] = p[2] = p[8] = A  # k, v, dv; dk (index 7) missing
+    assert bwd_kv(lib, p, Tq=0) == NULL
+    p = [A] * 10
+    p[2] = A + 8
+    assert bwd_kv(lib, p) == ALIGN
+
+
+def test_kv_empty_inputs_are_no_ops(lib):
+    assert fwd_kv(lib, q=0, k=0, v=0, o=0, lse=0, Tq=0) == OK
+    assert fwd_kv(lib, q=0, k=0, v=0, o=0, lse=0, B=0) == OK
+    assert bwd_kv(lib, [0] * 10, Tq=0, Tk=0) == OK
+    assert bwd_kv(lib, [0] * 10, B=0) == OK

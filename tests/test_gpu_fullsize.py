@@ -1,5 +1,7 @@
 """GPU parity at the full workload sizes, in the launch configuration the
-benchmark times (the library's default tiles, one fa_fwd and one fa_bwd call).
+benchmark times (the library's default tiles, one fa_fwd and one fa_bwd call;
+C5-prefill: 4096 query rows against 16384 keys with the default causal
+offset, through fa_fwd_kv and fa_bwd_kv).
 
 The oracle cannot redo these in full, so it checks sampled rows it can afford
 one by one: query rows (O, lse, dQ) spread over heads and positions, and key
@@ -31,7 +33,8 @@ def run(name):
     w = WORKLOADS[name]
     x = workload_inputs(w)
     d = {k: v.cuda() for k, v in x.items()}
-    say(f"full-size {name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} T={w.T} D={w.D} causal={w.causal}")
+    say(f"full-size {name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} Tq={w.T} Tk={w.Tkv} D={w.D} "
+        f"causal={w.causal}")
     o, lse = fa.fwd(d["q"], d["k"], d["v"], scale=w.scale, causal=w.causal)
     out = {"o": o, "lse": lse}
     if w.backward:
@@ -58,7 +61,7 @@ def head_slice(x, b, h0, h1):
     return x[b:b + 1, h0:h1].double().numpy()
 
 
-@pytest.mark.parametrize("name", ["C3", "C4", "C5"])
+@pytest.mark.parametrize("name", ["C3", "C4", "C5", "C5-prefill"])
 def test_forward_sampled_rows(name):
     w, x, out = run(name)
     G = w.Hq // w.Hkv
@@ -75,7 +78,7 @@ def test_forward_sampled_rows(name):
     assert_lse_close(np.array(got_l), np.array(ref_l), w.dtype)
 
 
-@pytest.mark.parametrize("name", ["C3", "C5"])
+@pytest.mark.parametrize("name", ["C3", "C5", "C5-prefill"])
 def test_dq_sampled_rows(name):
     w, x, out = run(name)
     G = w.Hq // w.Hkv
@@ -90,11 +93,11 @@ def test_dq_sampled_rows(name):
     assert_close("dQ rows", np.array(got), np.array(ref), w.dtype)
 
 
-@pytest.mark.parametrize("name", ["C3", "C5"])
+@pytest.mark.parametrize("name", ["C3", "C5", "C5-prefill"])
 def test_dkdv_sampled_rows(name):
     w, x, out = run(name)
     G = w.Hq // w.Hkv
-    T = w.T
+    T = w.Tkv
     keys = [T - 1, T - 2, T - 33, T - 64, T - 65, T - 100, T - 128]
     if name == "C3":  # short enough for early keys too
         keys += [0, 1, 63, 64, 1000]
@@ -114,7 +117,7 @@ def test_dkdv_sampled_rows(name):
     assert_close("dV rows", np.array(got_v), np.array(ref_v), w.dtype)
 
 
-@pytest.mark.parametrize("name", ["C3", "C5"])
+@pytest.mark.parametrize("name", ["C3", "C5", "C5-prefill"])
 def test_gradient_identities_all_rows(name):
     w, x, out = run(name)
     G = w.Hq // w.Hkv
@@ -124,7 +127,8 @@ def test_gradient_identities_all_rows(name):
     q = x["q"].double()
     k = x["k"].double()
     do = x["dout"].double()
-    B, Hkv, T, D = dk.shape
+    B, Hkv, _, D = dk.shape
+    T = w.T  # query rows
     # sum_j dK_j = 0, relative to the size of dK's columns
     s = dk.sum(dim=2)
     col = dk.norm(dim=2)

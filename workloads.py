@@ -20,6 +20,9 @@ Workloads (layout [B, H, T, D], contiguous):
   C5  bf16, B=1, Hq=32, Hkv=8, T=16384, D=128, causal, scale 1/sqrt(128)
   C5-share  one kv group of C5 (B=1, Hq=4, Hkv=1), the part of C5 one GPU
       would own if C5 were split by kv group.
+  C5-prefill  C5's heads with 4096 new query rows against 16384 keys (the
+      last 4096 positions: causal offset Tk - Tq = 12288), a prefill step
+      against cached keys.
 """
 from __future__ import annotations
 
@@ -43,12 +46,37 @@ class Workload:
     seed: int
     input_scale: float = 1.0
     backward: bool = True
+    Tk: int = 0  # key rows; 0: the same as T (the query rows)
+
+    @property
+    def Tkv(self) -> int:
+        return self.Tk or self.T
+
+    @property
+    def q_offset(self) -> int:
+        """Position of query row 0 among the keys (last query on the last key)."""
+        return self.Tkv - self.T
+
+    @property
+    def pairs(self) -> float:
+        """(query, key) pairs of one head that the mask lets through; for
+        T = Tk and causal, T^2/2 (the credited convention, not T(T+1)/2)."""
+        if not self.causal:
+            return float(self.T) * self.Tkv
+        if self.Tkv == self.T:
+            return self.T * self.T / 2.0
+        # row i sees min(Tk, i + off + 1) keys (off >= 0: every row sees key 0)
+        off, T, Tk = self.q_offset, self.T, self.Tkv
+        assert off >= 0, "causal workloads have at least as many keys as query rows"
+        full = max(0, min(T, T - (Tk - off - 1)))  # rows that see every key
+        part = T - full
+        return float(full) * Tk + part * (off + 1) + part * (part - 1) / 2.0
 
     @property
     def fwd_flop(self) -> float:
-        """Credited forward FLOP: 4*B*Hq*T^2*D, halved when causal."""
-        f = 4.0 * self.B * self.Hq * self.T * self.T * self.D
-        return f / 2 if self.causal else f
+        """Credited forward FLOP: 4*B*Hq*D per visible pair (4*B*Hq*T^2*D,
+        halved when causal, for one sequence)."""
+        return 4.0 * self.B * self.Hq * self.D * self.pairs
 
     @property
     def bwd_flop(self) -> float:
@@ -65,20 +93,25 @@ WORKLOADS = {
     "C5": Workload("C5", torch.bfloat16, 1, 32, 8, 16384, 128, True, 1 / math.sqrt(128), 5000),
     "C5-share": Workload("C5-share", torch.bfloat16, 1, 4, 1, 16384, 128, True,
                          1 / math.sqrt(128), 5500),
+    "C5-prefill": Workload("C5-prefill", torch.bfloat16, 1, 32, 8, 4096, 128, True,
+                           1 / math.sqrt(128), 5700, Tk=16384),
 }
 
 
 def make_inputs(B: int, Hq: int, Hkv: int, T: int, D: int, dtype: torch.dtype, seed: int,
-                input_scale: float = 1.0, with_dout: bool = True) -> dict:
-    """Return CPU tensors q [B,Hq,T,D], k and v [B,Hkv,T,D] and (optionally)
-    dout [B,Hq,T,D], drawn as described in the module docstring."""
+                input_scale: float = 1.0, with_dout: bool = True, Tk: int | None = None) -> dict:
+    """Return CPU tensors q [B,Hq,T,D], k and v [B,Hkv,Tk,D] (Tk = T unless
+    given) and (optionally) dout [B,Hq,T,D], drawn as described in the module
+    docstring."""
     g = torch.Generator(device="cpu")
     g.manual_seed(int(seed))
+    Tk = T if Tk is None else Tk
     out = {}
     for name, h in (("q", Hq), ("k", Hkv), ("v", Hkv), ("dout", Hq)):
         if name == "dout" and not with_dout:
             break
-        x = torch.randn((B, h, T, D), generator=g, dtype=torch.float32)
+        rows = T if name in ("q", "dout") else Tk
+        x = torch.randn((B, h, rows, D), generator=g, dtype=torch.float32)
         if input_scale != 1.0:
             x = x * input_scale
         out[name] = x.to(dtype).contiguous()
@@ -86,4 +119,5 @@ def make_inputs(B: int, Hq: int, Hkv: int, T: int, D: int, dtype: torch.dtype, s
 
 
 def workload_inputs(w: Workload) -> dict:
-    return make_inputs(w.B, w.Hq, w.Hkv, w.T, w.D, w.dtype, w.seed, w.input_scale, w.backward)
+    return make_inputs(w.B, w.Hq, w.Hkv, w.T, w.D, w.dtype, w.seed, w.input_scale, w.backward,
+                       Tk=w.Tkv)

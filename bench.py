@@ -278,6 +278,9 @@ def main():
         forward_only(args, w, x, q, k, v, o, lse)
         return
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    # scratch of the dK/dV stage when the shapes split its query side (as in fa_bwd)
+    part = torch.empty(max(fa.dkdv_split_bytes(w.B, w.Hq, w.Hkv, w.T, w.Tkv, w.D, w.dtype), 16),
+                       dtype=torch.uint8, device=dev)
 
     def step(ev=None):
         if ev:
@@ -288,7 +291,8 @@ def main():
         fa.bwd_preprocess(o, do, delta)
         if ev:
             ev[2].record()
-        fa.bwd_dkdv(q, k, v, do, lse, delta, scale=w.scale, causal=w.causal, dk=dk, dv=dv)
+        fa.bwd_dkdv(q, k, v, do, lse, delta, scale=w.scale, causal=w.causal, dk=dk, dv=dv,
+                    partial=part)
         if ev:
             ev[3].record()
         fa.bwd_dq(q, k, v, do, lse, delta, scale=w.scale, causal=w.causal, dq=dq)

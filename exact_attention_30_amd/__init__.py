@@ -26,7 +26,7 @@ import os
 import torch
 
 __all__ = ["fwd", "bwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "bwd_workspace_bytes",
-           "FAError", "library", "LIB_PATH", "version"]
+           "dkdv_split_bytes", "FAError", "library", "LIB_PATH", "version"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
@@ -53,6 +53,10 @@ SIGNATURES = {
                         _i, _i, _vp], ctypes.c_int),
     "fa_bwd_dq_kv": ([_vp, _vp, _vp, _vp, _fp, _fp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _i, _i,
                       _vp], ctypes.c_int),
+    "fa_bwd_kv_workspace_bytes": ([_i, _i, _i, _i, _i, _i, _i], ctypes.c_size_t),
+    "fa_bwd_dkdv_split_bytes": ([_i, _i, _i, _i, _i, _i, _i], ctypes.c_size_t),
+    "fa_bwd_dkdv_split": ([_vp, _vp, _vp, _vp, _fp, _fp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f,
+                           _i, _i, _i, _vp], ctypes.c_int),
     "fa_status_string": ([_i], ctypes.c_char_p),
     "fa_version": ([], ctypes.c_char_p),
 }
@@ -148,8 +152,16 @@ def fwd(q, k, v, scale=None, causal: bool = True, out=None, lse=None, q_offset=N
     return o, l
 
 
-def bwd_workspace_bytes(B, Hq, Hkv, T, D, dtype=torch.bfloat16) -> int:
-    return int(library().fa_bwd_workspace_bytes(B, Hq, Hkv, T, D, _DTYPES[dtype]))
+def bwd_workspace_bytes(B, Hq, Hkv, T, D, dtype=torch.bfloat16, Tk=None) -> int:
+    """Workspace bytes of bwd for T query rows (against Tk keys, default T)."""
+    Tk = T if Tk is None else Tk
+    return int(library().fa_bwd_kv_workspace_bytes(B, Hq, Hkv, T, Tk, D, _DTYPES[dtype]))
+
+
+def dkdv_split_bytes(B, Hq, Hkv, Tq, Tk, D, dtype=torch.bfloat16) -> int:
+    """Bytes of the partial-sum buffer bwd_dkdv uses to split its query side
+    (0: these shapes do not split)."""
+    return int(library().fa_bwd_dkdv_split_bytes(B, Hq, Hkv, Tq, Tk, D, _DTYPES[dtype]))
 
 
 def bwd(q, k, v, o, dout, lse, scale=None, causal: bool = True, workspace=None, grads=None,
@@ -165,7 +177,7 @@ def bwd(q, k, v, o, dout, lse, scale=None, causal: bool = True, workspace=None, 
         raise ValueError("lse must be float32 [B,Hq,Tq]")
     dq, dk, dv = grads if grads is not None else (torch.empty_like(q), torch.empty_like(k),
                                                   torch.empty_like(v))
-    ws_bytes = bwd_workspace_bytes(B, Hq, Hkv, Tq, D, q.dtype)
+    ws_bytes = bwd_workspace_bytes(B, Hq, Hkv, Tq, D, q.dtype, Tk=Tk)
     ws = workspace if workspace is not None else torch.empty(max(ws_bytes, 16), dtype=torch.uint8,
                                                              device=q.device)
     if ws.numel() * ws.element_size() < ws_bytes:
@@ -193,7 +205,10 @@ def bwd_preprocess(o, dout, delta=None):
 
 
 def bwd_dkdv(q, k, v, dout, lse, delta, scale=None, causal: bool = True, dk=None, dv=None,
-             q_offset=None):
+             q_offset=None, partial=None):
+    """dK, dV; with `partial` (a device tensor of at least dkdv_split_bytes(...)
+    bytes) the query side is split over more workgroups when the shapes call
+    for it (fa_bwd_dkdv_split)."""
     B, Hq, Hkv, Tq, Tk, D = _dims(q, k, v)
     dt = _dtype_code(q, k, v, dout)
     off = _offset(Tq, Tk, q_offset)
@@ -202,7 +217,14 @@ def bwd_dkdv(q, k, v, dout, lse, delta, scale=None, causal: bool = True, dk=None
     lib = library()
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), lse.data_ptr(),
             delta.data_ptr(), dk.data_ptr(), dv.data_ptr())
-    if Tq == Tk and (off == 0 or not causal):
+    if partial is not None:
+        need = dkdv_split_bytes(B, Hq, Hkv, Tq, Tk, D, q.dtype)
+        if partial.numel() * partial.element_size() < need:
+            raise ValueError("partial buffer too small")
+        _check(lib.fa_bwd_dkdv_split(*ptrs, partial.data_ptr() if need else None, B, Hq, Hkv, Tq,
+                                     Tk, D, _scale(scale, D), int(bool(causal)), off, dt,
+                                     _stream(q)), "fa_bwd_dkdv_split")
+    elif Tq == Tk and (off == 0 or not causal):
         _check(lib.fa_bwd_dkdv(*ptrs, B, Hq, Hkv, Tq, D, _scale(scale, D), int(bool(causal)), dt,
                                _stream(q)), "fa_bwd_dkdv")
     else:

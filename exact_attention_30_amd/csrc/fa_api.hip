@@ -66,6 +66,19 @@ void fill_bwd(fa::BwdArgs& a, const void* q, const void* k, const void* v, const
     a.off = off;
     a.c = scale * kLog2e;
     a.scale = scale;
+    a.part = nullptr;
+    a.nsplit = 1;
+}
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// bytes of fp32 dK/dV partial sums the split dK/dV stage uses (0: no split)
+size_t split_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int D, fa_dtype dt)
+{
+    if (dt != FA_BF16 || (long long)B * Tk == 0) return 0;
+    const int S = fa::dkdv_nsplit(B, Hq, Hkv, Tq, Tk, D);
+    if (S <= 1) return 0;
+    return align256((size_t)2 * S * (size_t)B * Hkv * (size_t)Tk * D * sizeof(float));
 }
 
 }  // namespace
@@ -122,11 +135,22 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
     return fa_fwd_kv(q, k, v, o, lse, B, Hq, Hkv, T, T, D, scale, causal, 0, dt, stream);
 }
 
+size_t fa_bwd_kv_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int D, fa_dtype dt)
+{
+    if (check_kv(B, Hq, Hkv, Tq, Tk, D, dt, false, 0) != FA_OK) return 0;
+    return align256((size_t)B * (size_t)Hq * (size_t)Tq * sizeof(float)) +
+           split_bytes(B, Hq, Hkv, Tq, Tk, D, dt);
+}
+
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int T, int D, fa_dtype dt)
 {
-    if (check_kv(B, Hq, Hkv, T, T, D, dt, false, 0) != FA_OK) return 0;
-    const size_t bytes = (size_t)B * (size_t)Hq * (size_t)T * sizeof(float);
-    return (bytes + 255) / 256 * 256;
+    return fa_bwd_kv_workspace_bytes(B, Hq, Hkv, T, T, D, dt);
+}
+
+size_t fa_bwd_dkdv_split_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int D, fa_dtype dt)
+{
+    if (check_kv(B, Hq, Hkv, Tq, Tk, D, dt, false, 0) != FA_OK) return 0;
+    return split_bytes(B, Hq, Hkv, Tq, Tk, D, dt);
 }
 
 fa_status fa_bwd_preprocess(const void* o, const void* dout, float* delta, int B, int Hq, int T,
@@ -168,10 +192,10 @@ static fa_status bwd_check(const void* q, const void* k, const void* v, const vo
     return FA_OK;
 }
 
-fa_status fa_bwd_dkdv_kv(const void* q, const void* k, const void* v, const void* dout,
-                         const float* lse, const float* delta, void* dk, void* dv, int B, int Hq,
-                         int Hkv, int Tq, int Tk, int D, float scale, int causal, int q_offset,
-                         fa_dtype dt, void* stream)
+fa_status fa_bwd_dkdv_split(const void* q, const void* k, const void* v, const void* dout,
+                            const float* lse, const float* delta, void* dk, void* dv, void* partial,
+                            int B, int Hq, int Hkv, int Tq, int Tk, int D, float scale, int causal,
+                            int q_offset, fa_dtype dt, void* stream)
 {
     const int off = causal ? q_offset : 0;
     bool skip = false;
@@ -179,12 +203,25 @@ fa_status fa_bwd_dkdv_kv(const void* q, const void* k, const void* v, const void
                              dt, skip);
     if (st != FA_OK || skip) return st;
     if (!dk || !dv) return FA_ERR_NULL;
-    if (!aligned(dk, 16) || !aligned(dv, 16)) return FA_ERR_ALIGN;
+    if (!aligned(dk, 16) || !aligned(dv, 16) || !aligned(partial, 16)) return FA_ERR_ALIGN;
     fa::BwdArgs a;
     fill_bwd(a, q, k, v, dout, lse, delta, B, Hq, Hkv, Tq, Tk, off, scale);
     a.dk = dk;
     a.dv = dv;
+    if (partial && split_bytes(B, Hq, Hkv, Tq, Tk, D, dt) > 0) {
+        a.part = static_cast<float*>(partial);
+        a.nsplit = fa::dkdv_nsplit(B, Hq, Hkv, Tq, Tk, D);
+    }
     return from_hip(fa::launch_bwd_dkdv(a, D, dtype_code(dt), causal != 0, static_cast<hipStream_t>(stream)));
+}
+
+fa_status fa_bwd_dkdv_kv(const void* q, const void* k, const void* v, const void* dout,
+                         const float* lse, const float* delta, void* dk, void* dv, int B, int Hq,
+                         int Hkv, int Tq, int Tk, int D, float scale, int causal, int q_offset,
+                         fa_dtype dt, void* stream)
+{
+    return fa_bwd_dkdv_split(q, k, v, dout, lse, delta, dk, dv, nullptr, B, Hq, Hkv, Tq, Tk, D,
+                             scale, causal, q_offset, dt, stream);
 }
 
 fa_status fa_bwd_dq_kv(const void* q, const void* k, const void* v, const void* dout,
@@ -239,10 +276,16 @@ fa_status fa_bwd_kv(const void* q, const void* k, const void* v, const void* o, 
     if (rows && (!aligned(q, 16) || !aligned(o, 16) || !aligned(dout, 16) || !aligned(lse, 4) ||
                  !aligned(dq, 16) || !aligned(workspace, 16)))
         return FA_ERR_ALIGN;
+    // workspace: Delta, then the dK/dV partial sums (when the shapes split)
     float* delta = static_cast<float*>(workspace);
+    void* partial = split_bytes(B, Hq, Hkv, Tq, Tk, D, dt) > 0
+                        ? static_cast<char*>(workspace) +
+                              align256((size_t)B * (size_t)Hq * (size_t)Tq * sizeof(float))
+                        : nullptr;
+    if (!workspace) partial = nullptr;
     if (rows && (st = fa_bwd_preprocess(o, dout, delta, B, Hq, Tq, D, dt, stream)) != FA_OK) return st;
-    if ((st = fa_bwd_dkdv_kv(q, k, v, dout, lse, delta, dk, dv, B, Hq, Hkv, Tq, Tk, D, scale, causal,
-                             q_offset, dt, stream)) != FA_OK)
+    if ((st = fa_bwd_dkdv_split(q, k, v, dout, lse, delta, dk, dv, partial, B, Hq, Hkv, Tq, Tk, D,
+                                scale, causal, q_offset, dt, stream)) != FA_OK)
         return st;
     return fa_bwd_dq_kv(q, k, v, dout, lse, delta, dq, B, Hq, Hkv, Tq, Tk, D, scale, causal,
                         q_offset, dt, stream);

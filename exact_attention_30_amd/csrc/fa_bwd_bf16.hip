@@ -107,9 +107,11 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
     const int G = a.Hq / a.Hkv;
 
     const int nkt = (a.Tk + BK - 1) / BK;
-    // causal: the first key blocks see the most query rows
-    const TileId id = map_tile(blockIdx.x, a.B, a.Hq, a.Hkv, 1, nkt, false);
-    const int b = id.b, hk = id.h;
+    // causal: the first key blocks see the most query rows; the nsplit chunks
+    // of one key block are neighbours (and share an XCD where possible)
+    const int S = a.nsplit;
+    const TileId id = map_tile(blockIdx.x, a.B, a.Hq, a.Hkv, S, nkt, false);
+    const int b = id.b, hk = id.h / S, split = id.h % S;
     const int key0 = id.tile * BK;
     const int kw = key0 + 32 * w;  // first key of this wave
     const int krow = kw + c;       // the key this lane owns
@@ -119,11 +121,14 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
     const bf16* vh = static_cast<const bf16*>(a.v) + kvoff;
 
     // the (query head, query tile) pairs that see this key block (query row i
-    // sees keys j <= i + off when causal)
+    // sees keys j <= i + off when causal), in visiting order; this workgroup
+    // takes the contiguous chunk [p0, p0 + n) of them
     const int nq = (a.Tq + BQ - 1) / BQ;
     const int i0 = CAUSAL ? max(key0 - a.off, 0) / BQ : 0;
     const int niq = max(nq - i0, 0);
-    const int n = G * niq;
+    const long npair = (long)G * niq;
+    const int p0 = (int)(npair * split / S);
+    const int n = (int)(npair * (split + 1) / S) - p0;
     const int npad = (n + NSTAGE - 1) / NSTAGE * NSTAGE;  // padded tiles: all masked
 
     const uint32_t lds0 = lds_addr(stages);
@@ -137,7 +142,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
     // head then reads the same tile at about the same time, so the tiles are
     // fetched from memory once per L2 rather than once per workgroup.
     // DMA cursor: (query head, query tile) of the next tile to issue
-    int dhq = hk * G, dti = nq - 1;
+    int dhq = hk * G + p0 % G, dti = nq - 1 - p0 / G;
     auto issue = [&](int st) {
         const uint32_t base = lds0 + (uint32_t)(st * STAGE);
         if (w < QW) {
@@ -215,7 +220,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
     for (int ks = 0; ks < NKS; ++ks) settle(kf[ks].v);
     convert_l(0);
     sync_lds();
-    int bti = nq - 1, bh = 0;  // query tile and head (in the group) being computed
+    int bti = nq - 1 - p0 / G, bh = p0 % G;  // query tile and head (in the group) being computed
 
     auto body = [&](auto st_tag, int i) {
         constexpr int ST = decltype(st_tag)::value;
@@ -285,23 +290,73 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
 
     // this lane: key krow, columns 32db + 8rg + 4g + e
     if (krow < a.Tk) {
-        bf16* dkh = static_cast<bf16*>(a.dk) + kvoff + (size_t)krow * D;
-        bf16* dvh = static_cast<bf16*>(a.dv) + kvoff + (size_t)krow * D;
+        if (S == 1) {
+            bf16* dkh = static_cast<bf16*>(a.dk) + kvoff + (size_t)krow * D;
+            bf16* dvh = static_cast<bf16*>(a.dv) + kvoff + (size_t)krow * D;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+            for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-                const int col = db * 32 + 8 * rg + 4 * g;
-                bf16x4 x, y;
+                for (int rg = 0; rg < 4; ++rg) {
+                    const int col = db * 32 + 8 * rg + 4 * g;
+                    bf16x4 x, y;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    x[e] = (bf16)(dk[db][4 * rg + e] * a.scale);
-                    y[e] = (bf16)dv[db][4 * rg + e];
+                    for (int e = 0; e < 4; ++e) {
+                        x[e] = (bf16)(dk[db][4 * rg + e] * a.scale);
+                        y[e] = (bf16)dv[db][4 * rg + e];
+                    }
+                    *reinterpret_cast<bf16x4*>(dkh + col) = x;
+                    *reinterpret_cast<bf16x4*>(dvh + col) = y;
                 }
-                *reinterpret_cast<bf16x4*>(dkh + col) = x;
-                *reinterpret_cast<bf16x4*>(dvh + col) = y;
-            }
+        } else {
+            // fp32 partial sums of this chunk (dK unscaled)
+            const size_t plane = (size_t)a.B * a.Hkv * a.Tk * D;
+            float* pk = a.part + (size_t)split * plane + kvoff + (size_t)krow * D;
+            float* pv = pk + (size_t)S * plane;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg) {
+                    const int col = db * 32 + 8 * rg + 4 * g;
+                    f32x4 x, y;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        x[e] = dk[db][4 * rg + e];
+                        y[e] = dv[db][4 * rg + e];
+                    }
+                    *reinterpret_cast<f32x4*>(pk + col) = x;
+                    *reinterpret_cast<f32x4*>(pv + col) = y;
+                }
+        }
     }
+}
+
+// Sum of the nsplit fp32 partials of dK and dV, in chunk order (so the result
+// does not depend on scheduling), scaled (dK) and rounded to bf16.  One thread
+// per 8 consecutive elements.
+__global__ __launch_bounds__(256) void dkdv_reduce_kernel(const float* part, bf16* dk, bf16* dv,
+                                                          long n8, long plane, int S, float scale)
+{
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n8) return;
+    f32x4 k0 = {}, k1 = {}, v0 = {}, v1 = {};
+    for (int s = 0; s < S; ++s) {
+        const f32x4* pk = reinterpret_cast<const f32x4*>(part + (size_t)s * plane) + 2 * i;
+        const f32x4* pv = reinterpret_cast<const f32x4*>(part + (size_t)(S + s) * plane) + 2 * i;
+        k0 += pk[0];
+        k1 += pk[1];
+        v0 += pv[0];
+        v1 += pv[1];
+    }
+    bf16x8 x, y;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        x[e] = (bf16)(k0[e] * scale);
+        x[4 + e] = (bf16)(k1[e] * scale);
+        y[e] = (bf16)v0[e];
+        y[4 + e] = (bf16)v1[e];
+    }
+    reinterpret_cast<bf16x8*>(dk)[i] = x;
+    reinterpret_cast<bf16x8*>(dv)[i] = y;
 }
 
 // ---------------------------------------------------------------------------
@@ -538,9 +593,34 @@ static hipError_t launch_dkdv(const BwdArgs& a, hipStream_t stream)
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::SMEM);
     if (attr != hipSuccess) return attr;
     const int nkt = (a.Tk + Cfg::BK - 1) / Cfg::BK;
-    const long grid = (long)nkt * a.B * a.Hkv;
+    const long grid = (long)nkt * a.B * a.Hkv * a.nsplit;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Cfg::NT), Cfg::SMEM, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.nsplit == 1) return e;
+    const long plane = (long)a.B * a.Hkv * a.Tk * D;
+    const long n8 = plane / 8;
+    hipLaunchKernelGGL(dkdv_reduce_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream,
+                       a.part, static_cast<bf16*>(a.dk), static_cast<bf16*>(a.dv), n8, plane,
+                       a.nsplit, a.scale);
     return hipGetLastError();
+}
+
+// Chunks per key block for the bf16 dK/dV kernel: enough workgroups for about
+// two per compute unit when the key blocks alone are too few (few kv heads,
+// short keys), at most 8, and at least 8 (query head, query tile) pairs per
+// chunk.  Independent of the query offset, so a caller can size the
+// workspace from the shapes alone.
+int dkdv_nsplit(int B, int Hq, int Hkv, int Tq, int Tk, int D)
+{
+    (void)D;
+    constexpr long kTarget = 512;
+    const long wgs = (long)((Tk + 255) / 256) * B * Hkv;
+    if (wgs <= 0 || wgs >= kTarget) return 1;
+    long s = (kTarget + wgs - 1) / wgs;
+    s = s < 8 ? s : 8;
+    const long pairs = (long)(Hq / Hkv) * ((Tq + 31) / 32);
+    const long cap = pairs / 8 > 1 ? pairs / 8 : 1;
+    return (int)(s < cap ? s : cap);
 }
 
 hipError_t launch_bwd_dkdv_bf16(const BwdArgs& a, int D, bool causal, hipStream_t stream)

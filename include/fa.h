@@ -111,11 +111,13 @@ fa_status fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float*
                     fa_dtype dt, void* stream);
 
 /*
- * Bytes of device workspace fa_bwd needs: one float32 Delta per query row,
- * B * Hq * T * 4, rounded up to 256 (T = Tq for fa_bwd_kv).  Returns 0 for
- * invalid or empty shapes.
+ * Bytes of device workspace fa_bwd (fa_bwd_kv) needs: one float32 Delta per
+ * query row, B * Hq * Tq * 4 rounded up to 256, followed by the dK/dV partial
+ * sums of fa_bwd_dkdv_split_bytes when the shapes leave the dK/dV kernel too
+ * few workgroups.  Returns 0 for invalid or empty shapes.
  */
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int T, int D, fa_dtype dt);
+size_t fa_bwd_kv_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int D, fa_dtype dt);
 
 /*
  * Backward pass of fa_fwd for the upstream gradient dout: writes dq, dk, dv.
@@ -171,6 +173,30 @@ fa_status fa_bwd_dq_kv(const void* q, const void* k, const void* v, const void* 
                        const float* lse, const float* delta, void* dq, int B, int Hq, int Hkv,
                        int Tq, int Tk, int D, float scale, int causal, int q_offset, fa_dtype dt,
                        void* stream);
+
+/*
+ * The dK/dV stage with its query side split, for shapes whose key blocks
+ * alone give the GPU too few workgroups (few kv heads, short key sequences;
+ * bf16 only).  Each key block's (query head, query tile) pairs are cut into
+ * up to 8 contiguous chunks; every chunk writes fp32 partial sums of dK and dV
+ * into `partial`, and a second kernel adds the chunks in chunk order, scales
+ * dK and rounds both to bf16, so the result is the same on every run.  This is
+ * the split of the dK/dV work of "L'attention fusionnée", «La passe arrière»,
+ * over more workgroups; the terms themselves are those of fa_bwd_dkdv.
+ *   fa_bwd_dkdv_split_bytes: bytes of `partial` for these shapes (0: the
+ *       shapes do not split; the 256-byte rounded size of
+ *       2 * chunks * B * Hkv * Tk * D float32 otherwise).
+ *   fa_bwd_dkdv_split: as fa_bwd_dkdv_kv, plus `partial` (device scratch of
+ *       fa_bwd_dkdv_split_bytes bytes, 16-byte aligned, contents on return
+ *       unspecified).  With partial == NULL, or when the shapes do not split,
+ *       it is fa_bwd_dkdv_kv.  fa_bwd and fa_bwd_kv use it with the part of
+ *       their workspace after Delta.
+ */
+size_t fa_bwd_dkdv_split_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int D, fa_dtype dt);
+fa_status fa_bwd_dkdv_split(const void* q, const void* k, const void* v, const void* dout,
+                            const float* lse, const float* delta, void* dk, void* dv, void* partial,
+                            int B, int Hq, int Hkv, int Tq, int Tk, int D, float scale, int causal,
+                            int q_offset, fa_dtype dt, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* fa_status_string(fa_status s);

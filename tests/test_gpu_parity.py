@@ -249,9 +249,41 @@ def test_stage_entry_points_equal_fa_bwd():
     o, l = fa.fwd(x["q"], x["k"], x["v"], causal=True)
     dq, dk, dv = fa.bwd(x["q"], x["k"], x["v"], o, x["dout"], l, causal=True)
     delta = fa.bwd_preprocess(o, x["dout"])
-    dk2, dv2 = fa.bwd_dkdv(x["q"], x["k"], x["v"], x["dout"], l, delta, causal=True)
+    part = torch.empty(max(fa.dkdv_split_bytes(2, 4, 4, 333, 333, 64), 16), dtype=torch.uint8,
+                       device="cuda")
+    dk2, dv2 = fa.bwd_dkdv(x["q"], x["k"], x["v"], x["dout"], l, delta, causal=True, partial=part)
     dq2 = fa.bwd_dq(x["q"], x["k"], x["v"], x["dout"], l, delta, causal=True)
     assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+
+
+@pytest.mark.parametrize("shape", [(1, 4, 1, 1000, 128), (1, 8, 2, 700, 64), (2, 2, 1, 513, 128)])
+def test_split_dkdv(shape):
+    """Few kv heads leave the dK/dV kernel few workgroups, so its query side
+    is split into chunks whose fp32 partial sums are added in chunk order: the
+    result is bitwise reproducible, within one bf16 rounding of the unsplit
+    kernel's, and within the tolerance of the oracle."""
+    B, Hq, Hkv, T, D = shape
+    nbytes = fa.dkdv_split_bytes(B, Hq, Hkv, T, T, D)
+    assert nbytes > 0, "shape expected to split"
+    x = to_dev(make_inputs(B, Hq, Hkv, T, D, bf16, seed=12 + T))
+    say(f"split dK/dV B={B} Hq={Hq} Hkv={Hkv} T={T} D={D}")
+    o, l = fa.fwd(x["q"], x["k"], x["v"], causal=True)
+    delta = fa.bwd_preprocess(o, x["dout"])
+    part = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    args = (x["q"], x["k"], x["v"], x["dout"], l, delta)
+    dk1, dv1 = fa.bwd_dkdv(*args, causal=True, partial=part)
+    dk2, dv2 = fa.bwd_dkdv(*args, causal=True, partial=part)
+    dk0, dv0 = fa.bwd_dkdv(*args, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dk1, dk2) and torch.equal(dv1, dv2)
+    for split, whole in ((dk1, dk0), (dv1, dv0)):
+        a, b = f64(split), f64(whole)
+        # the two fp32 sums differ in order only: at most one bf16 step apart
+        assert np.all(np.abs(a - b) <= 2.0 ** -7 * np.maximum(np.abs(b), 1e-30) + 1e-6)
+    q, k, v, do = (x[n].double().cpu().numpy() for n in ("q", "k", "v", "dout"))
+    _, rdk, rdv, mags = oracle.bwd(q, k, v, do, 1 / math.sqrt(D), True, return_mag=True)
+    assert_close("dK split", f64(dk1), rdk, bf16, mags[1])
+    assert_close("dV split", f64(dv1), rdv, bf16, mags[2])
 
 
 def test_no_device_allocation_by_the_library():

@@ -279,7 +279,8 @@ def main():
         return
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     # scratch of the dK/dV stage when the shapes split its query side (as in fa_bwd)
-    part = torch.empty(max(fa.dkdv_split_bytes(w.B, w.Hq, w.Hkv, w.T, w.Tkv, w.D, w.dtype), 16),
+    part = torch.empty(max(fa.dkdv_split_bytes(w.B, w.Hq, w.Hkv, w.T, w.Tkv, w.D, w.dtype),
+                           fa.dq_split_bytes(w.B, w.Hq, w.Hkv, w.T, w.Tkv, w.D, w.dtype), 16),
                        dtype=torch.uint8, device=dev)
 
     def step(ev=None):
@@ -295,7 +296,7 @@ def main():
                     partial=part)
         if ev:
             ev[3].record()
-        fa.bwd_dq(q, k, v, do, lse, delta, scale=w.scale, causal=w.causal, dq=dq)
+        fa.bwd_dq(q, k, v, do, lse, delta, scale=w.scale, causal=w.causal, dq=dq, partial=part)
         if ev:
             ev[4].record()
 

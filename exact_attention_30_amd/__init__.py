@@ -26,7 +26,7 @@ import os
 import torch
 
 __all__ = ["fwd", "bwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "bwd_workspace_bytes",
-           "dkdv_split_bytes", "FAError", "library", "LIB_PATH", "version"]
+           "dkdv_split_bytes", "dq_split_bytes", "FAError", "library", "LIB_PATH", "version"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
@@ -57,6 +57,9 @@ SIGNATURES = {
     "fa_bwd_dkdv_split_bytes": ([_i, _i, _i, _i, _i, _i, _i], ctypes.c_size_t),
     "fa_bwd_dkdv_split": ([_vp, _vp, _vp, _vp, _fp, _fp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f,
                            _i, _i, _i, _vp], ctypes.c_int),
+    "fa_bwd_dq_split_bytes": ([_i, _i, _i, _i, _i, _i, _i], ctypes.c_size_t),
+    "fa_bwd_dq_split": ([_vp, _vp, _vp, _vp, _fp, _fp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i,
+                         _i, _i, _vp], ctypes.c_int),
     "fa_status_string": ([_i], ctypes.c_char_p),
     "fa_version": ([], ctypes.c_char_p),
 }
@@ -158,6 +161,12 @@ def bwd_workspace_bytes(B, Hq, Hkv, T, D, dtype=torch.bfloat16, Tk=None) -> int:
     return int(library().fa_bwd_kv_workspace_bytes(B, Hq, Hkv, T, Tk, D, _DTYPES[dtype]))
 
 
+def dq_split_bytes(B, Hq, Hkv, Tq, Tk, D, dtype=torch.bfloat16) -> int:
+    """Bytes of the partial-sum buffer bwd_dq uses to split its key range
+    (0: these shapes do not split)."""
+    return int(library().fa_bwd_dq_split_bytes(B, Hq, Hkv, Tq, Tk, D, _DTYPES[dtype]))
+
+
 def dkdv_split_bytes(B, Hq, Hkv, Tq, Tk, D, dtype=torch.bfloat16) -> int:
     """Bytes of the partial-sum buffer bwd_dkdv uses to split its query side
     (0: these shapes do not split)."""
@@ -233,7 +242,10 @@ def bwd_dkdv(q, k, v, dout, lse, delta, scale=None, causal: bool = True, dk=None
     return dk, dv
 
 
-def bwd_dq(q, k, v, dout, lse, delta, scale=None, causal: bool = True, dq=None, q_offset=None):
+def bwd_dq(q, k, v, dout, lse, delta, scale=None, causal: bool = True, dq=None, q_offset=None,
+           partial=None):
+    """dQ; with `partial` (at least dq_split_bytes(...) bytes) the key range is
+    split over more workgroups when the shapes call for it (fa_bwd_dq_split)."""
     B, Hq, Hkv, Tq, Tk, D = _dims(q, k, v)
     dt = _dtype_code(q, k, v, dout)
     off = _offset(Tq, Tk, q_offset)
@@ -241,7 +253,14 @@ def bwd_dq(q, k, v, dout, lse, delta, scale=None, causal: bool = True, dq=None, 
     lib = library()
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), lse.data_ptr(),
             delta.data_ptr(), dq.data_ptr())
-    if Tq == Tk and (off == 0 or not causal):
+    if partial is not None:
+        need = dq_split_bytes(B, Hq, Hkv, Tq, Tk, D, q.dtype)
+        if partial.numel() * partial.element_size() < need:
+            raise ValueError("partial buffer too small")
+        _check(lib.fa_bwd_dq_split(*ptrs, partial.data_ptr() if need else None, B, Hq, Hkv, Tq, Tk,
+                                   D, _scale(scale, D), int(bool(causal)), off, dt, _stream(q)),
+               "fa_bwd_dq_split")
+    elif Tq == Tk and (off == 0 or not causal):
         _check(lib.fa_bwd_dq(*ptrs, B, Hq, Hkv, Tq, D, _scale(scale, D), int(bool(causal)), dt,
                              _stream(q)), "fa_bwd_dq")
     else:

@@ -72,13 +72,31 @@ void fill_bwd(fa::BwdArgs& a, const void* q, const void* k, const void* v, const
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-// bytes of fp32 dK/dV partial sums the split dK/dV stage uses (0: no split)
+// bytes of fp32 partial sums the split dK/dV stage uses (0: no split)
 size_t split_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int D, fa_dtype dt)
 {
     if (dt != FA_BF16 || (long long)B * Tk == 0) return 0;
     const int S = fa::dkdv_nsplit(B, Hq, Hkv, Tq, Tk, D);
     if (S <= 1) return 0;
     return align256((size_t)2 * S * (size_t)B * Hkv * (size_t)Tk * D * sizeof(float));
+}
+
+// bytes of fp32 partial sums the split dQ stage uses (0: no split)
+size_t dq_split_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int D, fa_dtype dt)
+{
+    if (dt != FA_BF16 || (long long)B * Tq == 0) return 0;
+    const int S = fa::dq_nsplit(B, Hq, Hkv, Tq, Tk, D);
+    if (S <= 1) return 0;
+    return align256((size_t)S * (size_t)B * Hq * (size_t)Tq * D * sizeof(float));
+}
+
+// the split stages of one backward run one after the other: they share one
+// partial-sum region of the larger size
+size_t shared_split_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int D, fa_dtype dt)
+{
+    const size_t a = split_bytes(B, Hq, Hkv, Tq, Tk, D, dt);
+    const size_t b = dq_split_bytes(B, Hq, Hkv, Tq, Tk, D, dt);
+    return a > b ? a : b;
 }
 
 }  // namespace
@@ -139,7 +157,7 @@ size_t fa_bwd_kv_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int D, 
 {
     if (check_kv(B, Hq, Hkv, Tq, Tk, D, dt, false, 0) != FA_OK) return 0;
     return align256((size_t)B * (size_t)Hq * (size_t)Tq * sizeof(float)) +
-           split_bytes(B, Hq, Hkv, Tq, Tk, D, dt);
+           shared_split_bytes(B, Hq, Hkv, Tq, Tk, D, dt);
 }
 
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int T, int D, fa_dtype dt)
@@ -151,6 +169,12 @@ size_t fa_bwd_dkdv_split_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int D, fa
 {
     if (check_kv(B, Hq, Hkv, Tq, Tk, D, dt, false, 0) != FA_OK) return 0;
     return split_bytes(B, Hq, Hkv, Tq, Tk, D, dt);
+}
+
+size_t fa_bwd_dq_split_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int D, fa_dtype dt)
+{
+    if (check_kv(B, Hq, Hkv, Tq, Tk, D, dt, false, 0) != FA_OK) return 0;
+    return dq_split_bytes(B, Hq, Hkv, Tq, Tk, D, dt);
 }
 
 fa_status fa_bwd_preprocess(const void* o, const void* dout, float* delta, int B, int Hq, int T,
@@ -224,10 +248,10 @@ fa_status fa_bwd_dkdv_kv(const void* q, const void* k, const void* v, const void
                              scale, causal, q_offset, dt, stream);
 }
 
-fa_status fa_bwd_dq_kv(const void* q, const void* k, const void* v, const void* dout,
-                       const float* lse, const float* delta, void* dq, int B, int Hq, int Hkv,
-                       int Tq, int Tk, int D, float scale, int causal, int q_offset, fa_dtype dt,
-                       void* stream)
+fa_status fa_bwd_dq_split(const void* q, const void* k, const void* v, const void* dout,
+                          const float* lse, const float* delta, void* dq, void* partial, int B,
+                          int Hq, int Hkv, int Tq, int Tk, int D, float scale, int causal,
+                          int q_offset, fa_dtype dt, void* stream)
 {
     const int off = causal ? q_offset : 0;
     bool skip = false;
@@ -235,11 +259,24 @@ fa_status fa_bwd_dq_kv(const void* q, const void* k, const void* v, const void* 
                              dt, skip);
     if (st != FA_OK || skip || Tq == 0) return st;
     if (!dq) return FA_ERR_NULL;
-    if (!aligned(dq, 16)) return FA_ERR_ALIGN;
+    if (!aligned(dq, 16) || !aligned(partial, 16)) return FA_ERR_ALIGN;
     fa::BwdArgs a;
     fill_bwd(a, q, k, v, dout, lse, delta, B, Hq, Hkv, Tq, Tk, off, scale);
     a.dq = dq;
+    if (partial && dq_split_bytes(B, Hq, Hkv, Tq, Tk, D, dt) > 0) {
+        a.part = static_cast<float*>(partial);
+        a.nsplit = fa::dq_nsplit(B, Hq, Hkv, Tq, Tk, D);
+    }
     return from_hip(fa::launch_bwd_dq(a, D, dtype_code(dt), causal != 0, static_cast<hipStream_t>(stream)));
+}
+
+fa_status fa_bwd_dq_kv(const void* q, const void* k, const void* v, const void* dout,
+                       const float* lse, const float* delta, void* dq, int B, int Hq, int Hkv,
+                       int Tq, int Tk, int D, float scale, int causal, int q_offset, fa_dtype dt,
+                       void* stream)
+{
+    return fa_bwd_dq_split(q, k, v, dout, lse, delta, dq, nullptr, B, Hq, Hkv, Tq, Tk, D, scale,
+                           causal, q_offset, dt, stream);
 }
 
 fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
@@ -276,9 +313,10 @@ fa_status fa_bwd_kv(const void* q, const void* k, const void* v, const void* o, 
     if (rows && (!aligned(q, 16) || !aligned(o, 16) || !aligned(dout, 16) || !aligned(lse, 4) ||
                  !aligned(dq, 16) || !aligned(workspace, 16)))
         return FA_ERR_ALIGN;
-    // workspace: Delta, then the dK/dV partial sums (when the shapes split)
+    // workspace: Delta, then the partial sums of the split stages (when the
+    // shapes split; the dK/dV and dQ stages take turns with one region)
     float* delta = static_cast<float*>(workspace);
-    void* partial = split_bytes(B, Hq, Hkv, Tq, Tk, D, dt) > 0
+    void* partial = shared_split_bytes(B, Hq, Hkv, Tq, Tk, D, dt) > 0
                         ? static_cast<char*>(workspace) +
                               align256((size_t)B * (size_t)Hq * (size_t)Tq * sizeof(float))
                         : nullptr;
@@ -287,8 +325,8 @@ fa_status fa_bwd_kv(const void* q, const void* k, const void* v, const void* o, 
     if ((st = fa_bwd_dkdv_split(q, k, v, dout, lse, delta, dk, dv, partial, B, Hq, Hkv, Tq, Tk, D,
                                 scale, causal, q_offset, dt, stream)) != FA_OK)
         return st;
-    return fa_bwd_dq_kv(q, k, v, dout, lse, delta, dq, B, Hq, Hkv, Tq, Tk, D, scale, causal,
-                        q_offset, dt, stream);
+    return fa_bwd_dq_split(q, k, v, dout, lse, delta, dq, partial, B, Hq, Hkv, Tq, Tk, D, scale,
+                           causal, q_offset, dt, stream);
 }
 
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,

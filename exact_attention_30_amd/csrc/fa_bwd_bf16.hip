@@ -330,33 +330,36 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
     }
 }
 
-// Sum of the nsplit fp32 partials of dK and dV, in chunk order (so the result
-// does not depend on scheduling), scaled (dK) and rounded to bf16.  One thread
-// per 8 consecutive elements.
-__global__ __launch_bounds__(256) void dkdv_reduce_kernel(const float* part, bf16* dk, bf16* dv,
-                                                          long n8, long plane, int S, float scale)
+// out = scale * (sum of the S fp32 partials part[s * plane + .]), added in
+// chunk order (so the result does not depend on scheduling), rounded to
+// bf16.  One thread per 8 consecutive elements; n8 = plane / 8.
+__global__ __launch_bounds__(256) void sum_partials_kernel(const float* part, bf16* out, long n8,
+                                                           long plane, int S, float scale)
 {
     const long i = (long)blockIdx.x * 256 + threadIdx.x;
     if (i >= n8) return;
-    f32x4 k0 = {}, k1 = {}, v0 = {}, v1 = {};
+    f32x4 lo = {}, hi = {};
     for (int s = 0; s < S; ++s) {
-        const f32x4* pk = reinterpret_cast<const f32x4*>(part + (size_t)s * plane) + 2 * i;
-        const f32x4* pv = reinterpret_cast<const f32x4*>(part + (size_t)(S + s) * plane) + 2 * i;
-        k0 += pk[0];
-        k1 += pk[1];
-        v0 += pv[0];
-        v1 += pv[1];
+        const f32x4* p = reinterpret_cast<const f32x4*>(part + (size_t)s * plane) + 2 * i;
+        lo += p[0];
+        hi += p[1];
     }
-    bf16x8 x, y;
+    bf16x8 x;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        x[e] = (bf16)(k0[e] * scale);
-        x[4 + e] = (bf16)(k1[e] * scale);
-        y[e] = (bf16)v0[e];
-        y[4 + e] = (bf16)v1[e];
+        x[e] = (bf16)(lo[e] * scale);
+        x[4 + e] = (bf16)(hi[e] * scale);
     }
-    reinterpret_cast<bf16x8*>(dk)[i] = x;
-    reinterpret_cast<bf16x8*>(dv)[i] = y;
+    reinterpret_cast<bf16x8*>(out)[i] = x;
+}
+
+static hipError_t sum_partials(const float* part, void* out, long plane, int S, float scale,
+                               hipStream_t stream)
+{
+    const long n8 = plane / 8;
+    hipLaunchKernelGGL(sum_partials_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream,
+                       part, static_cast<bf16*>(out), n8, plane, S, scale);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -416,8 +419,10 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
     const int c = lane & 31;
 
     const int nqt = (a.Tq + BR - 1) / BR;
-    const TileId id = map_tile(blockIdx.x, a.B, a.Hq, a.Hkv, a.Hq / a.Hkv, nqt, CAUSAL);
-    const int b = id.b, hq = id.h;
+    // the nsplit chunks of one query block are neighbours
+    const int S = a.nsplit;
+    const TileId id = map_tile(blockIdx.x, a.B, a.Hq, a.Hkv, (a.Hq / a.Hkv) * S, nqt, CAUSAL);
+    const int b = id.b, hq = id.h / S, split = id.h % S;
     const int hk = hq / (a.Hq / a.Hkv);
     const int q0 = id.tile * BR;
     const int qw = q0 + 32 * w;  // first query of this wave
@@ -429,9 +434,12 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
     const bf16* vh = static_cast<const bf16*>(a.v) + kvoff;
 
     // key tiles visited by the workgroup (query row i sees keys j <= i + off
-    // when causal); tiles below nfull are wholly visible to this wave
+    // when causal), of which this workgroup takes the chunk [j0, j0 + nkv);
+    // tiles below nfull are wholly visible to this wave
     const int kend = CAUSAL ? min(q0 + BR + a.off, a.Tk) : a.Tk;
-    const int nkv = (kend + BC - 1) / BC;
+    const int nall = (kend + BC - 1) / BC;
+    const int j0 = nall * split / S;
+    const int nkv = nall * (split + 1) / S - j0;
     const int npad = (nkv + NSTAGE - 1) / NSTAGE * NSTAGE;  // padded tiles: all masked
     const int nfull = CAUSAL ? min((qw + a.off + 1) / BC, a.Tk / BC) : a.Tk / BC;
 
@@ -441,7 +449,8 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
     uint32_t vdma[Cfg::VI];
 #pragma unroll
     for (int i = 0; i < Cfg::VI; ++i) vdma[i] = VT::dma_off(w + NWAVE * i, lane);
-    auto issue = [&](int j, int st) {  // tile j into stage st
+    auto issue = [&](int t, int st) {  // tile j0 + t into stage st
+        const int j = j0 + t;
         kt.load(lds0 + (uint32_t)(st * KT::BYTES), kh, j * BC, a.Tk, w);
         const int left = a.Tk - j * BC;
         const i32x4 r = buffer_rsrc(vh + (size_t)j * BC * D, left > 0 ? left * D * 2 : 0);
@@ -449,10 +458,10 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
 #pragma unroll
         for (int i = 0; i < Cfg::VI; ++i) dma_b128(vb + (uint32_t)((w + NWAVE * i) * 1024), r, vdma[i]);
     };
-    // wait until tile j has landed while tiles j + 1 .. j + AHEAD - 1 (those
-    // that exist) stay in flight
-    auto wait_tile = [&](int j) {
-        const int after = nkv - 1 - j;
+    // wait until chunk tile t has landed while tiles t + 1 .. t + AHEAD - 1
+    // (those that exist) stay in flight
+    auto wait_tile = [&](int t) {
+        const int after = nkv - 1 - t;
         if (after >= 1)
             vm_wait<VPT>();
         else
@@ -464,7 +473,7 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
     for (int off = tid * 16; off < Cfg::SMEM; off += Cfg::NT * 16)
         *reinterpret_cast<u32x4*>(smem + off) = u32x4{0, 0, 0, 0};
     sync_lds();
-    for (int j = 0; j < AHEAD && j < nkv; ++j) issue(j, j);
+    for (int t = 0; t < AHEAD && t < nkv; ++t) issue(t, t);
 
     // B operands of S^T = K Q^T and dP^T = V dO^T: this lane's query row
     Frag<bf16> qf[NKS], of[NKS];
@@ -506,11 +515,12 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
     settle(Dl);
     sync_lds();
 
-    auto body = [&](auto st_tag, int j) {
+    auto body = [&](auto st_tag, int t) {  // chunk tile t = key tile j0 + t
         constexpr int ST = decltype(st_tag)::value;
         constexpr uint32_t KI = ST * KT::BYTES, VIM = ST * VT::BYTES;  // this stage's tiles
-        if (j + AHEAD < nkv) issue(j + AHEAD, (ST + AHEAD) % NSTAGE);
-        const bool masked = j >= nfull;  // diagonal, future or padded tile
+        if (t + AHEAD < nkv) issue(t + AHEAD, (ST + AHEAD) % NSTAGE);
+        const int j = j0 + t;
+        const bool masked = j >= nfull || t >= nkv;  // diagonal, future or padded tile
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
             f32x16 s = f32x16{}, dp = f32x16{};
@@ -524,7 +534,7 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int kj = j * BC + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-                    const bool vis = (j < nkv) && kj < a.Tk && (!CAUSAL || kj <= qrow + a.off);
+                    const bool vis = (t < nkv) && kj < a.Tk && (!CAUSAL || kj <= qrow + a.off);
                     s[r] = vis ? s[r] : -INFINITY;
                 }
             }
@@ -541,24 +551,37 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
                     mma(dq[db], frag(ktr.read(db, KI + (kb * 32 + 16 * t) * Fmt::ROWBYTES)), sf);
             }
         }
-        wait_tile(j + 1);
+        wait_tile(t + 1);
         sync_lds();
     };
 
-    for (int j = 0; j < npad; j += NSTAGE)
-        unroll_stages(body, j, std::make_integer_sequence<int, NSTAGE>{});
+    for (int t = 0; t < npad; t += NSTAGE)
+        unroll_stages(body, t, std::make_integer_sequence<int, NSTAGE>{});
 
     if (qrow < a.Tq) {
-        bf16* dqh = static_cast<bf16*>(a.dq) + qoff + (size_t)qrow * D;
+        if (S == 1) {
+            bf16* dqh = static_cast<bf16*>(a.dq) + qoff + (size_t)qrow * D;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+            for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-                bf16x4 x;
+                for (int rg = 0; rg < 4; ++rg) {
+                    bf16x4 x;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) x[e] = (bf16)(dq[db][4 * rg + e] * a.scale);
-                *reinterpret_cast<bf16x4*>(dqh + db * 32 + 8 * rg + 4 * g) = x;
-            }
+                    for (int e = 0; e < 4; ++e) x[e] = (bf16)(dq[db][4 * rg + e] * a.scale);
+                    *reinterpret_cast<bf16x4*>(dqh + db * 32 + 8 * rg + 4 * g) = x;
+                }
+        } else {  // fp32 partial sums of this chunk (unscaled)
+            float* ph = a.part + (size_t)split * a.B * a.Hq * a.Tq * D + qoff + (size_t)qrow * D;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg) {
+                    f32x4 x;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) x[e] = dq[db][4 * rg + e];
+                    *reinterpret_cast<f32x4*>(ph + db * 32 + 8 * rg + 4 * g) = x;
+                }
+        }
     }
 }
 
@@ -572,9 +595,11 @@ static hipError_t launch_dq(const BwdArgs& a, hipStream_t stream)
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::SMEM);
     if (attr != hipSuccess) return attr;
     const int nqt = (a.Tq + Cfg::BR - 1) / Cfg::BR;
-    const long grid = (long)nqt * a.B * a.Hq;
+    const long grid = (long)nqt * a.B * a.Hq * a.nsplit;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Cfg::NT), Cfg::SMEM, stream, a);
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.nsplit == 1) return e;
+    return sum_partials(a.part, a.dq, (long)a.B * a.Hq * a.Tq * D, a.nsplit, a.scale, stream);
 }
 
 hipError_t launch_bwd_dq_bf16(const BwdArgs& a, int D, bool causal, hipStream_t stream)
@@ -598,11 +623,8 @@ static hipError_t launch_dkdv(const BwdArgs& a, hipStream_t stream)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1) return e;
     const long plane = (long)a.B * a.Hkv * a.Tk * D;
-    const long n8 = plane / 8;
-    hipLaunchKernelGGL(dkdv_reduce_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream,
-                       a.part, static_cast<bf16*>(a.dk), static_cast<bf16*>(a.dv), n8, plane,
-                       a.nsplit, a.scale);
-    return hipGetLastError();
+    if ((e = sum_partials(a.part, a.dk, plane, a.nsplit, a.scale, stream)) != hipSuccess) return e;
+    return sum_partials(a.part + (size_t)a.nsplit * plane, a.dv, plane, a.nsplit, 1.f, stream);
 }
 
 // Chunks per key block for the bf16 dK/dV kernel: enough workgroups for about
@@ -620,6 +642,23 @@ int dkdv_nsplit(int B, int Hq, int Hkv, int Tq, int Tk, int D)
     s = s < 8 ? s : 8;
     const long pairs = (long)(Hq / Hkv) * ((Tq + 31) / 32);
     const long cap = pairs / 8 > 1 ? pairs / 8 : 1;
+    return (int)(s < cap ? s : cap);
+}
+
+// Chunks of the key range per query block for the bf16 dQ kernel: about two
+// workgroups per compute unit when the query blocks alone are too few, at
+// most 8, and at least 4 key tiles per chunk.
+int dq_nsplit(int B, int Hq, int Hkv, int Tq, int Tk, int D)
+{
+    (void)Hkv;
+    (void)D;
+    constexpr long kTarget = 512;
+    const long wgs = (long)((Tq + 255) / 256) * B * Hq;
+    if (wgs <= 0 || wgs >= kTarget) return 1;
+    long s = (kTarget + wgs - 1) / wgs;
+    s = s < 8 ? s : 8;
+    const long tiles = (Tk + 63) / 64;
+    const long cap = tiles / 4 > 1 ? tiles / 4 : 1;
     return (int)(s < cap ? s : cap);
 }
 

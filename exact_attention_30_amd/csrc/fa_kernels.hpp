@@ -33,9 +33,10 @@ struct BwdArgs {
     int off;     // causal: query row i sees key j iff j <= i + off (off >= 0)
     float c;     // scale * log2(e)
     float scale;
-    // dK/dV split over the query side: with nsplit > 1, workgroup chunk s of a
-    // key block writes its fp32 partial sums to part (dK^T unscaled at
-    // [s][B][Hkv][Tk][D], dV after all of them) and a reduction adds them
+    // Split work: with nsplit > 1, chunk s of a key block (dK/dV kernel:
+    // dK unscaled at part[s][B][Hkv][Tk][D], dV after all of them) or of a
+    // query block's key range (dQ kernel: dQ unscaled at part[s][B][Hq][Tq][D])
+    // writes fp32 partial sums, and a reduction adds them
     float* part;
     int nsplit;
 };
@@ -53,8 +54,10 @@ hipError_t launch_fwd(const FwdArgs& a, int D, int dtype, bool causal, hipStream
 hipError_t launch_fwd_bf16(const FwdArgs& a, int D, bool causal, hipStream_t stream);
 hipError_t launch_bwd_pre(const PreArgs& a, int D, int dtype, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int D, int dtype, bool causal, hipStream_t stream);
-// chunks the bf16 dK/dV kernel splits each key block into (1: no split)
+// chunks the bf16 dK/dV kernel splits each key block into, and the bf16 dQ
+// kernel the key range of each query block into (1: no split)
 int dkdv_nsplit(int B, int Hq, int Hkv, int Tq, int Tk, int D);
+int dq_nsplit(int B, int Hq, int Hkv, int Tq, int Tk, int D);
 hipError_t launch_bwd_dkdv_bf16(const BwdArgs& a, int D, bool causal, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, int D, int dtype, bool causal, hipStream_t stream);
 hipError_t launch_bwd_dq_bf16(const BwdArgs& a, int D, bool causal, hipStream_t stream);

@@ -112,9 +112,10 @@ fa_status fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float*
 
 /*
  * Bytes of device workspace fa_bwd (fa_bwd_kv) needs: one float32 Delta per
- * query row, B * Hq * Tq * 4 rounded up to 256, followed by the dK/dV partial
- * sums of fa_bwd_dkdv_split_bytes when the shapes leave the dK/dV kernel too
- * few workgroups.  Returns 0 for invalid or empty shapes.
+ * query row, B * Hq * Tq * 4 rounded up to 256, followed by one region for the
+ * partial sums of the split stages, of the larger of fa_bwd_dkdv_split_bytes
+ * and fa_bwd_dq_split_bytes (0 when neither stage splits).  Returns 0 for
+ * invalid or empty shapes.
  */
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int T, int D, fa_dtype dt);
 size_t fa_bwd_kv_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int D, fa_dtype dt);
@@ -197,6 +198,23 @@ fa_status fa_bwd_dkdv_split(const void* q, const void* k, const void* v, const v
                             const float* lse, const float* delta, void* dk, void* dv, void* partial,
                             int B, int Hq, int Hkv, int Tq, int Tk, int D, float scale, int causal,
                             int q_offset, fa_dtype dt, void* stream);
+
+/*
+ * The dQ stage with its key range split the same way, for shapes whose query
+ * blocks alone give the GPU too few workgroups: up to 8 contiguous chunks of
+ * each query block's key tiles, fp32 partial sums of dQ in `partial`, added in
+ * chunk order, scaled and rounded to bf16 by a second kernel (bf16 only).
+ *   fa_bwd_dq_split_bytes: bytes of `partial` (0: no split; the 256-byte
+ *       rounded size of chunks * B * Hq * Tq * D float32 otherwise).
+ *   fa_bwd_dq_split: as fa_bwd_dq_kv, plus `partial` (NULL or no split: it is
+ *       fa_bwd_dq_kv).  fa_bwd and fa_bwd_kv give both split stages the part
+ *       of their workspace after Delta, one after the other.
+ */
+size_t fa_bwd_dq_split_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int D, fa_dtype dt);
+fa_status fa_bwd_dq_split(const void* q, const void* k, const void* v, const void* dout,
+                          const float* lse, const float* delta, void* dq, void* partial, int B,
+                          int Hq, int Hkv, int Tq, int Tk, int D, float scale, int causal,
+                          int q_offset, fa_dtype dt, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* fa_status_string(fa_status s);

@@ -94,15 +94,16 @@ def test_bottom_right_rows_equal_the_square_problems_rows(Tq, Tk, D):
     """With the default offset, o, lse and dq of the Tq query rows are, bit for
     bit, the last Tq rows of the square causal problem over the same keys: each
     row walks the same key tiles in the same order (tiles past its last key
-    add exact zeros)."""
+    add exact zeros).  dq comes from the unsplit dQ stage here (a split cuts a
+    row's key range at boundaries that depend on its query block)."""
     x = to_dev(make_inputs(1, 4, 2, Tk, D, bf16, seed=9100 + Tq))
     q, k, v, do = x["q"], x["k"], x["v"], x["dout"]
     qt, dot = q[:, :, Tk - Tq:].contiguous(), do[:, :, Tk - Tq:].contiguous()
     say(f"bottom-right rows Tq={Tq} Tk={Tk} D={D}")
     o_sq, lse_sq = fa.fwd(q, k, v, causal=True)
     o_kv, lse_kv = fa.fwd(qt, k, v, causal=True)
-    dq_sq, _, _ = fa.bwd(q, k, v, o_sq, do, lse_sq, causal=True)
-    dq_kv, _, _ = fa.bwd(qt, k, v, o_kv, dot, lse_kv, causal=True)
+    dq_sq = fa.bwd_dq(q, k, v, do, lse_sq, fa.bwd_preprocess(o_sq, do), causal=True)
+    dq_kv = fa.bwd_dq(qt, k, v, dot, lse_kv, fa.bwd_preprocess(o_kv, dot), causal=True)
     torch.cuda.synchronize()
     assert torch.equal(o_kv, o_sq[:, :, Tk - Tq:])
     assert torch.equal(lse_kv, lse_sq[:, :, Tk - Tq:])

@@ -249,10 +249,11 @@ def test_stage_entry_points_equal_fa_bwd():
     o, l = fa.fwd(x["q"], x["k"], x["v"], causal=True)
     dq, dk, dv = fa.bwd(x["q"], x["k"], x["v"], o, x["dout"], l, causal=True)
     delta = fa.bwd_preprocess(o, x["dout"])
-    part = torch.empty(max(fa.dkdv_split_bytes(2, 4, 4, 333, 333, 64), 16), dtype=torch.uint8,
+    part = torch.empty(max(fa.dkdv_split_bytes(2, 4, 4, 333, 333, 64),
+                           fa.dq_split_bytes(2, 4, 4, 333, 333, 64), 16), dtype=torch.uint8,
                        device="cuda")
     dk2, dv2 = fa.bwd_dkdv(x["q"], x["k"], x["v"], x["dout"], l, delta, causal=True, partial=part)
-    dq2 = fa.bwd_dq(x["q"], x["k"], x["v"], x["dout"], l, delta, causal=True)
+    dq2 = fa.bwd_dq(x["q"], x["k"], x["v"], x["dout"], l, delta, causal=True, partial=part)
     assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
 
 
@@ -308,3 +309,29 @@ def test_no_device_allocation_by_the_library():
     free1, _ = torch.cuda.mem_get_info()
     assert torch.cuda.memory_allocated() == alloc0
     assert abs(free1 - free0) < (1 << 20)
+
+
+@pytest.mark.parametrize("shape", [(1, 4, 1, 2048, 128), (1, 2, 2, 1500, 64), (2, 1, 1, 700, 128)])
+def test_split_dq(shape):
+    """Few query blocks: dQ's key range is split into chunks whose fp32
+    partial sums are added in chunk order; bitwise reproducible, within one
+    bf16 rounding of the unsplit kernel, within the tolerance of the oracle."""
+    B, Hq, Hkv, T, D = shape
+    nbytes = fa.dq_split_bytes(B, Hq, Hkv, T, T, D)
+    assert nbytes > 0, "shape expected to split"
+    x = to_dev(make_inputs(B, Hq, Hkv, T, D, bf16, seed=13 + T))
+    say(f"split dQ B={B} Hq={Hq} Hkv={Hkv} T={T} D={D}")
+    o, l = fa.fwd(x["q"], x["k"], x["v"], causal=True)
+    delta = fa.bwd_preprocess(o, x["dout"])
+    part = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    args = (x["q"], x["k"], x["v"], x["dout"], l, delta)
+    dq1 = fa.bwd_dq(*args, causal=True, partial=part)
+    dq2 = fa.bwd_dq(*args, causal=True, partial=part)
+    dq0 = fa.bwd_dq(*args, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dq1, dq2)
+    a, b = f64(dq1), f64(dq0)
+    assert np.all(np.abs(a - b) <= 2.0 ** -7 * np.abs(b) + 1e-6)
+    q, k, v, do = (x[n].double().cpu().numpy() for n in ("q", "k", "v", "dout"))
+    rdq, _, _, mags = oracle.bwd(q, k, v, do, 1 / math.sqrt(D), True, return_mag=True)
+    assert_close("dQ split", a, rdq, bf16, mags[0])

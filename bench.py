@@ -283,10 +283,13 @@ def main():
                            fa.dq_split_bytes(w.B, w.Hq, w.Hkv, w.T, w.Tkv, w.D, w.dtype), 16),
                        dtype=torch.uint8, device=dev)
 
+    fpart = torch.empty(max(fa.fwd_split_bytes(w.B, w.Hq, w.Hkv, w.T, w.Tkv, w.D, w.dtype), 16),
+                        dtype=torch.uint8, device=dev)
+
     def step(ev=None):
         if ev:
             ev[0].record()
-        fa.fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse)
+        fa.fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse, partial=fpart)
         if ev:
             ev[1].record()
         fa.bwd_preprocess(o, do, delta)

@@ -26,7 +26,8 @@ import os
 import torch
 
 __all__ = ["fwd", "bwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "bwd_workspace_bytes",
-           "dkdv_split_bytes", "dq_split_bytes", "FAError", "library", "LIB_PATH", "version"]
+           "dkdv_split_bytes", "dq_split_bytes", "fwd_split_bytes", "FAError", "library",
+           "LIB_PATH", "version"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
@@ -60,6 +61,9 @@ SIGNATURES = {
     "fa_bwd_dq_split_bytes": ([_i, _i, _i, _i, _i, _i, _i], ctypes.c_size_t),
     "fa_bwd_dq_split": ([_vp, _vp, _vp, _vp, _fp, _fp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i,
                          _i, _i, _vp], ctypes.c_int),
+    "fa_fwd_split_bytes": ([_i, _i, _i, _i, _i, _i, _i], ctypes.c_size_t),
+    "fa_fwd_split": ([_vp, _vp, _vp, _vp, _fp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _i, _i, _vp],
+                     ctypes.c_int),
     "fa_status_string": ([_i], ctypes.c_char_p),
     "fa_version": ([], ctypes.c_char_p),
 }
@@ -135,16 +139,33 @@ def _scale(scale, D) -> float:
     return 1.0 / math.sqrt(D) if scale is None else float(scale)
 
 
-def fwd(q, k, v, scale=None, causal: bool = True, out=None, lse=None, q_offset=None):
+def fwd_split_bytes(B, Hq, Hkv, Tq, Tk, D, dtype=torch.bfloat16) -> int:
+    """Bytes of the chunk-partial buffer fwd uses to split key ranges (0: these
+    shapes do not split)."""
+    return int(library().fa_fwd_split_bytes(B, Hq, Hkv, Tq, Tk, D, _DTYPES[dtype]))
+
+
+def fwd(q, k, v, scale=None, causal: bool = True, out=None, lse=None, q_offset=None,
+        partial=None):
     """Forward pass; returns (o, lse).  `out`/`lse` may be preallocated.
-    Calls fa_fwd when Tq == Tk and the offset is 0, else fa_fwd_kv."""
+    Calls fa_fwd when Tq == Tk and the offset is 0, else fa_fwd_kv; with
+    `partial` (a device tensor of at least fwd_split_bytes(...) bytes) calls
+    fa_fwd_split, which splits key ranges when the shapes call for it."""
     B, Hq, Hkv, Tq, Tk, D = _dims(q, k, v)
     dt = _dtype_code(q, k, v)
     off = _offset(Tq, Tk, q_offset)
     o = torch.empty_like(q) if out is None else out
     l = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device) if lse is None else lse
     lib = library()
-    if Tq == Tk and (off == 0 or not causal):
+    if partial is not None:
+        need = fwd_split_bytes(B, Hq, Hkv, Tq, Tk, D, q.dtype)
+        if partial.numel() * partial.element_size() < need:
+            raise ValueError("partial buffer too small")
+        _check(lib.fa_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                l.data_ptr(), partial.data_ptr() if need else None, B, Hq, Hkv, Tq,
+                                Tk, D, _scale(scale, D), int(bool(causal)), off, dt, _stream(q)),
+               "fa_fwd_split")
+    elif Tq == Tk and (off == 0 or not causal):
         _check(lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(),
                           B, Hq, Hkv, Tq, D, _scale(scale, D), int(bool(causal)), dt,
                           _stream(q)), "fa_fwd")

@@ -118,9 +118,19 @@ const char* fa_status_string(fa_status s)
     return "unknown status";
 }
 
-fa_status fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
-                    int Hkv, int Tq, int Tk, int D, float scale, int causal, int q_offset,
-                    fa_dtype dt, void* stream)
+// bytes of the forward's chunk partials: numerators, then (max, sum) pairs
+size_t fwd_split_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int D, fa_dtype dt)
+{
+    if (dt != FA_BF16 || (long long)B * Tq == 0) return 0;
+    const int S = fa::fwd_nsplit(B, Hq, Hkv, Tq, Tk, D);
+    if (S <= 1) return 0;
+    const size_t rows = (size_t)S * B * Hq * Tq;
+    return align256(rows * D * sizeof(float)) + align256(rows * 2 * sizeof(float));
+}
+
+fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                       void* partial, int B, int Hq, int Hkv, int Tq, int Tk, int D, float scale,
+                       int causal, int q_offset, fa_dtype dt, void* stream)
 {
     const int off = causal ? q_offset : 0;
     fa_status st = check_kv(B, Hq, Hkv, Tq, Tk, D, dt, causal != 0, off);
@@ -128,7 +138,8 @@ fa_status fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float*
     if ((st = check_scale(scale)) != FA_OK) return st;
     if ((long long)B * Tq == 0) return FA_OK;
     if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
+        !aligned(partial, 16))
         return FA_ERR_ALIGN;
     fa::FwdArgs a;
     a.q = q;
@@ -144,7 +155,29 @@ fa_status fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float*
     a.off = off;
     a.c = scale * kLog2e;
     a.scale = scale;
+    a.opart = a.ml = nullptr;
+    a.nsplit = 1;
+    if (partial && fwd_split_bytes(B, Hq, Hkv, Tq, Tk, D, dt) > 0) {
+        a.nsplit = fa::fwd_nsplit(B, Hq, Hkv, Tq, Tk, D);
+        const size_t rows = (size_t)a.nsplit * B * Hq * Tq;
+        a.opart = static_cast<float*>(partial);
+        a.ml = reinterpret_cast<float*>(static_cast<char*>(partial) + align256(rows * D * sizeof(float)));
+    }
     return from_hip(fa::launch_fwd(a, D, dtype_code(dt), causal != 0, static_cast<hipStream_t>(stream)));
+}
+
+size_t fa_fwd_split_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int D, fa_dtype dt)
+{
+    if (check_kv(B, Hq, Hkv, Tq, Tk, D, dt, false, 0) != FA_OK) return 0;
+    return fwd_split_bytes(B, Hq, Hkv, Tq, Tk, D, dt);
+}
+
+fa_status fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                    int Hkv, int Tq, int Tk, int D, float scale, int causal, int q_offset,
+                    fa_dtype dt, void* stream)
+{
+    return fa_fwd_split(q, k, v, o, lse, nullptr, B, Hq, Hkv, Tq, Tk, D, scale, causal, q_offset,
+                        dt, stream);
 }
 
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,

@@ -148,7 +148,8 @@ __global__ __launch_bounds__(NW * 64, sizeof(E) == 2 ? 8 / NW : 1) void fwd_kern
         const bool need = mt > mref + kRescaleThreshold;
         if (__builtin_amdgcn_ballot_w64(need)) {
             const float mnew = need ? mt : mref;
-            const float alpha = fast_exp2(mref - mnew);  // 0 on the first visit
+            // 0 on a row's first visible key; 1 for rows that keep their reference
+            const float alpha = need ? fast_exp2(mref - mnew) : 1.f;
             l *= alpha;
 #pragma unroll
             for (int db = 0; db < NDB; ++db) o[db] *= alpha;

@@ -104,8 +104,10 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
     const int c = lane & 31;
 
     const int nqt = (a.Tq + BR - 1) / BR;
-    const TileId id = map_tile(blockIdx.x, a.B, a.Hq, a.Hkv, a.Hq / a.Hkv, nqt, CAUSAL);
-    const int b = id.b, hq = id.h;
+    // the nsplit chunks of one query block are neighbours
+    const int S = a.nsplit;
+    const TileId id = map_tile(blockIdx.x, a.B, a.Hq, a.Hkv, (a.Hq / a.Hkv) * S, nqt, CAUSAL);
+    const int b = id.b, hq = id.h / S, split = id.h % S;
     const int hk = hq / (a.Hq / a.Hkv);
     const int q0 = id.tile * BR;
     const int qw = q0 + 32 * w;   // first query of this wave
@@ -117,10 +119,24 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
     const bf16* vh = static_cast<const bf16*>(a.v) + (size_t)(b * a.Hkv + hk) * a.Tk * D;
 
     // key tiles visited by the workgroup (query row i sees keys j <= i + off
-    // when causal); per wave, the tiles it sees completely (no mask)
+    // when causal), of which this workgroup takes the chunk [j0, j0 + nkv);
+    // per wave, the tiles it sees completely (no mask)
     const int kend = CAUSAL ? min(q0 + BR + a.off, a.Tk) : a.Tk;
-    const int nkv = (kend + BC - 1) / BC;
+    const int nall = (kend + BC - 1) / BC;
+    const int j0 = nall * split / S;
+    const int nkv = nall * (split + 1) / S - j0;
     const int nfull = CAUSAL ? min((qw + a.off + 1) / BC, a.Tk / BC) : a.Tk / BC;
+    const size_t rowidx = (size_t)(b * a.Hq + hq) * a.Tq + qrow;  // this lane's query row
+    if (nkv == 0) {  // an empty chunk (uniform over the workgroup): nothing seen
+        if (qrow < a.Tq && g == 0) {
+            const size_t plane = (size_t)a.B * a.Hq * a.Tq;
+            float* op = a.opart + ((size_t)split * plane + rowidx) * D;
+            for (int d = 0; d < D; ++d) op[d] = 0.f;
+            a.ml[2 * ((size_t)split * plane + rowidx)] = -INFINITY;
+            a.ml[2 * ((size_t)split * plane + rowidx) + 1] = 0.f;
+        }
+        return;
+    }
 
     // this thread's DMA source offsets (same for every tile)
     uint32_t koff[KI], voff[VI];
@@ -134,13 +150,13 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
     auto load_stage = [&](int s) {
         const uint32_t base = lds0 + (uint32_t)((s % Cfg::NSTAGE) * Cfg::STAGE);
         if (s < nkv) {
-            const int row0 = s * BC;
+            const int row0 = (j0 + s) * BC;
             const i32x4 r = buffer_rsrc(kh + (size_t)row0 * D, (a.Tk - row0) * D * 2);
 #pragma unroll
             for (int i = 0; i < KI; ++i) dma_b128(base + (uint32_t)((w + NWAVE * i) * 1024), r, koff[i]);
         }
         if (s >= 1) {
-            const int row0 = (s - 1) * BC;
+            const int row0 = (j0 + s - 1) * BC;
             const i32x4 r = buffer_rsrc(vh + (size_t)row0 * D, (a.Tk - row0) * D * 2);
 #pragma unroll
             for (int i = 0; i < VI; ++i)
@@ -219,7 +235,8 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
 
     // Vector step V(j): mask, lazy reference update (rescaling O and l when it
     // moves), P_j = exp2(S_j c - mref) with fp32 row sums, rounded for P V.
-    auto vector_step = [&](int j) {
+    auto vector_step = [&](int jl) {
+        const int j = j0 + jl;  // key tile
         if (j >= nfull) {
             asm volatile("");  // keep this a branch
 #pragma unroll
@@ -240,7 +257,9 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
         const bool need = mt > mref + kRescaleThresholdBf16;
         if (__builtin_amdgcn_ballot_w64(need)) {
             const float mnew = need ? mt : mref;
-            const float alpha = fast_exp2(mref - mnew);  // 0 on the first visit
+            // 0 on a row's first visible key; 1 for rows that keep their
+            // reference (also those that have seen no key yet: -inf - -inf)
+            const float alpha = need ? fast_exp2(mref - mnew) : 1.f;
             l *= alpha;
 #pragma unroll
             for (int db = 0; db < NDB; ++db) o[db] *= alpha;
@@ -329,6 +348,26 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
     // epilogue: divide by l, store O (this lane: query qrow, columns
     // 32db + 8rg + 4g + i) and lse
     const float lt = pair_sum(l);
+    if (S > 1) {  // this chunk's unnormalised numerator, reference max and sum
+        if (qrow < a.Tq) {
+            const size_t plane = (size_t)a.B * a.Hq * a.Tq;
+            float* op = a.opart + ((size_t)split * plane + rowidx) * D;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg) {
+                    f32x4 x;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) x[i] = o[db][4 * rg + i];
+                    *reinterpret_cast<f32x4*>(op + db * 32 + 8 * rg + 4 * g) = x;
+                }
+            if (g == 0) {
+                a.ml[2 * ((size_t)split * plane + rowidx)] = mref;
+                a.ml[2 * ((size_t)split * plane + rowidx) + 1] = lt;
+            }
+        }
+        return;
+    }
     const float inv = 1.f / lt;
     if (qrow < a.Tq) {
         bf16* oh = static_cast<bf16*>(a.o) + ((size_t)(b * a.Hq + hq) * a.Tq + qrow) * D;
@@ -345,6 +384,46 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
     }
 }
 
+// Merge of the key-range chunks of every query row, the rule by which block
+// results combine ("FlashAttention" note, «Blockergebnisse…»; "L'attention
+// fusionnée", «Le softmax en ligne»): with chunk s holding the numerator o_s
+// and sum l_s relative to its reference max m_s (base 2),
+//     M = max_s m_s,  w_s = 2^(m_s - M),  O = sum_s w_s o_s / sum_s w_s l_s,
+//     lse = ln 2 * (M + log2 sum_s w_s l_s).
+// A chunk that saw no key has m_s = -inf and weight 0; chunk 0 always holds
+// key 0, which every row sees, so M is finite.  One thread per 8 consecutive
+// elements of a row.
+template <int D>
+__global__ __launch_bounds__(256) void merge_chunks_kernel(const float* opart, const float* ml,
+                                                           bf16* o, float* lse, long rows, int S)
+{
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= rows * (D / 8)) return;
+    const long row = i / (D / 8);
+    const int c8 = (int)(i % (D / 8)) * 8;
+    float M = -INFINITY;
+    for (int s = 0; s < S; ++s) M = fmaxf(M, ml[2 * (s * rows + row)]);
+    float L = 0.f;
+    f32x4 lo = {}, hi = {};
+    for (int s = 0; s < S; ++s) {
+        const float m = ml[2 * (s * rows + row)];
+        const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
+        L += w * ml[2 * (s * rows + row) + 1];
+        const f32x4* p = reinterpret_cast<const f32x4*>(opart + ((size_t)s * rows + row) * D + c8);
+        lo += w * p[0];
+        hi += w * p[1];
+    }
+    const float inv = 1.f / L;
+    bf16x8 x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        x[e] = (bf16)(lo[e] * inv);
+        x[4 + e] = (bf16)(hi[e] * inv);
+    }
+    *reinterpret_cast<bf16x8*>(o + row * D + c8) = x;
+    if (c8 == 0) lse[row] = (M + log2f(L)) * kLn2;
+}
+
 template <int D, bool CAUSAL>
 static hipError_t launch_t(const FwdArgs& a, hipStream_t stream)
 {
@@ -355,9 +434,32 @@ static hipError_t launch_t(const FwdArgs& a, hipStream_t stream)
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::SMEM);
     if (attr != hipSuccess) return attr;
     const int nqt = (a.Tq + Cfg::BR - 1) / Cfg::BR;
-    const long grid = (long)nqt * a.B * a.Hq;
+    const long grid = (long)nqt * a.B * a.Hq * a.nsplit;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Cfg::NT), Cfg::SMEM, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.nsplit == 1) return e;
+    const long rows = (long)a.B * a.Hq * a.Tq;
+    const long n8 = rows * (D / 8);
+    hipLaunchKernelGGL(merge_chunks_kernel<D>, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0,
+                       stream, a.opart, a.ml, static_cast<bf16*>(a.o), a.lse, rows, a.nsplit);
     return hipGetLastError();
+}
+
+// Chunks of the key range per query block: about two workgroups per compute
+// unit when the query blocks alone are too few, at most 8, and at least 4 key
+// tiles per chunk.
+int fwd_nsplit(int B, int Hq, int Hkv, int Tq, int Tk, int D)
+{
+    (void)Hkv;
+    (void)D;
+    constexpr long kTarget = 512;
+    const long wgs = (long)((Tq + 255) / 256) * B * Hq;
+    if (wgs <= 0 || wgs >= kTarget) return 1;
+    long s = (kTarget + wgs - 1) / wgs;
+    s = s < 8 ? s : 8;
+    const long tiles = (Tk + 63) / 64;
+    const long cap = tiles / 4 > 1 ? tiles / 4 : 1;
+    return (int)(s < cap ? s : cap);
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, int D, bool causal, hipStream_t stream)

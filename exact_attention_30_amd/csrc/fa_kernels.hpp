@@ -16,6 +16,13 @@ struct FwdArgs {
     int off;      // causal: query row i sees key j iff j <= i + off (off >= 0)
     float c;      // scale * log2(e): scores are exponentiated in base 2
     float scale;  // for the natural-log lse
+    // Split key range: with nsplit > 1, chunk s of a query block's key tiles
+    // writes its unnormalised numerator o (fp32, opart[s][B][Hq][Tq][D]) and
+    // its reference max and sum (ml[s][B][Hq][Tq][2], base-2 units), and a
+    // merge kernel combines the chunks
+    float* opart;
+    float* ml;
+    int nsplit;
 };
 
 struct BwdArgs {
@@ -58,6 +65,8 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, int D, int dtype, bool causal, hipS
 // kernel the key range of each query block into (1: no split)
 int dkdv_nsplit(int B, int Hq, int Hkv, int Tq, int Tk, int D);
 int dq_nsplit(int B, int Hq, int Hkv, int Tq, int Tk, int D);
+// chunks the bf16 forward splits each query block's key range into
+int fwd_nsplit(int B, int Hq, int Hkv, int Tq, int Tk, int D);
 hipError_t launch_bwd_dkdv_bf16(const BwdArgs& a, int D, bool causal, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, int D, int dtype, bool causal, hipStream_t stream);
 hipError_t launch_bwd_dq_bf16(const BwdArgs& a, int D, bool causal, hipStream_t stream);

@@ -111,6 +111,25 @@ fa_status fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float*
                     fa_dtype dt, void* stream);
 
 /*
+ * The forward with each query block's key range split into up to 8 chunks,
+ * for shapes whose query blocks alone give the GPU too few workgroups (few
+ * query heads, short query sequences; bf16 only).  Each chunk runs the online
+ * softmax over its key tiles and writes its unnormalised numerator, reference
+ * max and sum (fp32) to `partial`; a second kernel merges the chunks with the
+ * rule by which block results combine ("FlashAttention" note,
+ * «Blockergebnisse…»; "L'attention fusionnée", «Le softmax en ligne»):
+ * M = max m_s, O = sum 2^(m_s-M) o_s / sum 2^(m_s-M) l_s.
+ *   fa_fwd_split_bytes: bytes of `partial` (0: these shapes do not split).
+ *   fa_fwd_split: as fa_fwd_kv plus `partial` (device scratch, 16-byte
+ *       aligned, contents on return unspecified); NULL or no split: it is
+ *       fa_fwd_kv.  O and lse agree with the unsplit forward to rounding.
+ */
+size_t fa_fwd_split_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int D, fa_dtype dt);
+fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                       void* partial, int B, int Hq, int Hkv, int Tq, int Tk, int D, float scale,
+                       int causal, int q_offset, fa_dtype dt, void* stream);
+
+/*
  * Bytes of device workspace fa_bwd (fa_bwd_kv) needs: one float32 Delta per
  * query row, B * Hq * Tq * 4 rounded up to 256, followed by one region for the
  * partial sums of the split stages, of the larger of fa_bwd_dkdv_split_bytes

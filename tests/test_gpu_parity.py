@@ -335,3 +335,31 @@ def test_split_dq(shape):
     q, k, v, do = (x[n].double().cpu().numpy() for n in ("q", "k", "v", "dout"))
     rdq, _, _, mags = oracle.bwd(q, k, v, do, 1 / math.sqrt(D), True, return_mag=True)
     assert_close("dQ split", a, rdq, bf16, mags[0])
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1, 2048, 2048, 128), (1, 4, 2, 700, 700, 64),
+                                   (2, 2, 1, 300, 2000, 128)])
+def test_split_forward(shape):
+    """Few query blocks: the forward splits each block's key range into
+    chunks and merges their (numerator, reference max, sum) with the block
+    merge rule.  O and lse match the oracle, agree with the unsplit forward to
+    rounding, and are bitwise reproducible; chunks without keys (a query block
+    with fewer key tiles than chunks) contribute nothing."""
+    B, Hq, Hkv, Tq, Tk, D = shape
+    nbytes = fa.fwd_split_bytes(B, Hq, Hkv, Tq, Tk, D)
+    assert nbytes > 0, "shape expected to split"
+    x = to_dev(make_inputs(B, Hq, Hkv, Tq, D, bf16, seed=14 + Tq, Tk=Tk))
+    say(f"split forward B={B} Hq={Hq} Hkv={Hkv} Tq={Tq} Tk={Tk} D={D}")
+    part = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    o1, l1 = fa.fwd(x["q"], x["k"], x["v"], causal=True, partial=part)
+    o2, l2 = fa.fwd(x["q"], x["k"], x["v"], causal=True, partial=part)
+    o0, l0 = fa.fwd(x["q"], x["k"], x["v"], causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert float((l1 - l0).abs().max()) < 1e-4
+    a, b = f64(o1), f64(o0)
+    assert np.all(np.abs(a - b) <= 2.0 ** -7 * np.abs(b) + 1e-3)
+    q, k, v = (x[n].double().cpu().numpy() for n in ("q", "k", "v"))
+    ro, rl, om = oracle.fwd(q, k, v, 1 / math.sqrt(D), True, return_mag=True)
+    assert_close("O split", a, ro, bf16, om)
+    assert_lse_close(f64(l1), rl, bf16)

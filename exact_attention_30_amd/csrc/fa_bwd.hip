@@ -24,17 +24,27 @@ namespace fa {
 // Delta_i = sum_d dO_id * O_id.  HBM-bound: each row is read once, 16 bytes per
 // lane, and reduced over the lanes of the row in a fixed order.
 // ---------------------------------------------------------------------------
+// lanes per row of the preprocess: 16 bytes each, rounded up to a power of
+// two so the row reduction is a butterfly
+template <class E, int D>
+__host__ __device__ constexpr int pre_lanes()
+{
+    int n = D / (16 / (int)sizeof(E)), p = 1;
+    while (p < n) p *= 2;
+    return p;
+}
+
 template <class E, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(PreArgs a)
 {
     constexpr int CH = 16 / (int)sizeof(E);
-    constexpr int LPR = D / CH;      // lanes per row (8 or 16 or 32)
-    constexpr int RPB = 256 / LPR;   // rows per workgroup
+    constexpr int LPR = pre_lanes<E, D>();  // lanes per row (a power of two)
+    constexpr int RPB = 256 / LPR;          // rows per workgroup
     const int tid = threadIdx.x;
     const long row = (long)blockIdx.x * RPB + tid / LPR;
     const int col = (tid % LPR) * CH;
     float acc = 0.f;
-    if (row < a.rows) {
+    if (row < a.rows && col < D) {  // lanes past the end of a row add nothing
         const E* o = static_cast<const E*>(a.o) + row * D + col;
         const E* d = static_cast<const E*>(a.dout) + row * D + col;
         if constexpr (sizeof(E) == 2) {
@@ -408,7 +418,7 @@ __global__ __launch_bounds__(NW * 64, sizeof(E) == 2 ? 8 / NW : 1) void bwd_dq_k
 template <class E, int D>
 static hipError_t launch_pre_t(const PreArgs& a, hipStream_t stream)
 {
-    constexpr int LPR = D / (16 / (int)sizeof(E));
+    constexpr int LPR = pre_lanes<E, D>();
     constexpr int RPB = 256 / LPR;
     const long grid = (a.rows + RPB - 1) / RPB;
     hipLaunchKernelGGL((bwd_pre_kernel<E, D>), dim3((unsigned)grid), dim3(256), 0, stream, a);
@@ -417,7 +427,10 @@ static hipError_t launch_pre_t(const PreArgs& a, hipStream_t stream)
 
 hipError_t launch_bwd_pre(const PreArgs& a, int D, int dtype, hipStream_t stream)
 {
-    if (dtype == 0) return D == 64 ? launch_pre_t<bf16, 64>(a, stream) : launch_pre_t<bf16, 128>(a, stream);
+    if (dtype == 0) {
+        if (D == 96) return launch_pre_t<bf16, 96>(a, stream);
+        return D == 64 ? launch_pre_t<bf16, 64>(a, stream) : launch_pre_t<bf16, 128>(a, stream);
+    }
     return D == 64 ? launch_pre_t<float, 64>(a, stream) : launch_pre_t<float, 128>(a, stream);
 }
 
@@ -476,6 +489,7 @@ hipError_t launch_bwd_dq(const BwdArgs& a, int D, int dtype, bool causal, hipStr
 // template only from a launcher has left some instantiations without their
 // host-side handle.
 template __global__ void bwd_pre_kernel<bf16, 64>(PreArgs);
+template __global__ void bwd_pre_kernel<bf16, 96>(PreArgs);
 template __global__ void bwd_pre_kernel<bf16, 128>(PreArgs);
 template __global__ void bwd_pre_kernel<float, 64>(PreArgs);
 template __global__ void bwd_pre_kernel<float, 128>(PreArgs);

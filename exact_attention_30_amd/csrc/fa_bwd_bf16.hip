@@ -35,8 +35,9 @@
 
 namespace fa {
 
-template <int D>
+template <int D>  // head size of the tensors in memory
 struct DkdvBf16Cfg {
+    static constexpr int DT = tile_dim(D);  // head size of the tiles and products
     static constexpr int NW = 8;
     static constexpr int NT = 64 * NW;
     static constexpr int BK = 32 * NW;  // keys per workgroup
@@ -44,10 +45,10 @@ struct DkdvBf16Cfg {
     static constexpr int NSTAGE = 4;    // LDS stage buffers
     static constexpr int AHEAD = 3;     // tiles issued ahead of the one computed
     // Q and dO tiles: 32 rows; D = 64 needs only four waves to move them
-    static constexpr int QNT = (BQ * D / 8 >= NT) ? NT : BQ * D / 8;
-    using QT = SwzTile<D, BQ, QNT>;
-    using Fmt = DmaTile<bf16, D, BQ, QNT>;
-    using VW = RowFragTile<D, 32>;  // V rows of one wave, in read order
+    static constexpr int QNT = (BQ * DT / 8 >= NT) ? NT : BQ * DT / 8;
+    using QT = SwzTile<DT, BQ, QNT, D>;
+    using Fmt = DmaTile<bf16, DT, BQ, QNT>;
+    using VW = RowFragTile<DT, 32, D>;  // V rows of one wave, in read order
     static constexpr int STATS = 512;  // L*log2(e) (64 floats) and Delta (64 floats)
     static constexpr int STAGE = 2 * QT::BYTES + STATS;
     static constexpr int SMEM = NSTAGE * STAGE + NW * VW::BYTES;
@@ -91,8 +92,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
     using VW = typename Cfg::VW;
     constexpr int BK = Cfg::BK, BQ = Cfg::BQ, NSTAGE = Cfg::NSTAGE, STAGE = Cfg::STAGE;
     constexpr int AHEAD = Cfg::AHEAD;
-    constexpr int NDB = D / 32;
-    constexpr int NKS = D / 16;
+    constexpr int NDB = Cfg::DT / 32;  // tile head size (D in memory; padding columns are zeros)
+    constexpr int NKS = Cfg::DT / 16;
     constexpr int QW = Cfg::QNT / 64;  // waves that move Q and dO tiles
 
     extern __shared__ __align__(1024) unsigned char smem[];
@@ -190,9 +191,9 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
 
     // Q, dO rows (A of S, dP) and Q^T, dO^T (A of dK^T, dV^T) in the
     // stages; V rows 32w + c (B of dP) in read order
-    SwzRowFrags<Fmt, D> qrd;
+    SwzRowFrags<Fmt, Cfg::DT> qrd;
     qrd.init(lds_addr(stages), c, g);
-    SwzTrFrags<Fmt, D> trd;
+    SwzTrFrags<Fmt, Cfg::DT> trd;
     trd.init(lds_addr(stages), lane);
     uint32_t vrd = lds_addr(Vs) + (uint32_t)(w * VW::BYTES + 16 * lane);
     asm volatile("" : "+v"(vrd));
@@ -298,6 +299,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
 #pragma unroll
                 for (int rg = 0; rg < 4; ++rg) {
                     const int col = db * 32 + 8 * rg + 4 * g;
+                    if (col >= D) continue;  // padding columns
                     bf16x4 x, y;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -317,6 +319,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
 #pragma unroll
                 for (int rg = 0; rg < 4; ++rg) {
                     const int col = db * 32 + 8 * rg + 4 * g;
+                    if (col >= D) continue;  // padding columns
                     f32x4 x, y;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -374,17 +377,18 @@ static hipError_t sum_partials(const float* part, void* out, long plane, int S, 
 // dQ^T += K^T dS^T with dS^T straight from registers; K^T is read transposed
 // from the K tile.  No atomics: each dQ row is owned by one wave.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D>  // head size of the tensors in memory
 struct DqBf16Cfg {
+    static constexpr int DT = tile_dim(D);  // head size of the tiles and products
     static constexpr int NW = 8;
     static constexpr int NT = 64 * NW;
     static constexpr int BR = 32 * NW;  // query rows per workgroup
     static constexpr int BC = 64;       // keys per tile
     static constexpr int NSTAGE = 3;
     static constexpr int AHEAD = 2;
-    using KT = SwzTile<D, BC, NT>;  // K: read row-wise and transposed
-    using Fmt = DmaTile<bf16, D, BC, NT>;
-    using VT = RowFragTile<D, BC>;  // V: read row-wise, stored in read order
+    using KT = SwzTile<DT, BC, NT, D>;  // K: read row-wise and transposed
+    using Fmt = DmaTile<bf16, DT, BC, NT>;
+    using VT = RowFragTile<DT, BC, D>;  // V: read row-wise, stored in read order
     static constexpr int VI = VT::NDMA / NW;  // V DMA instructions per wave and tile
     static_assert(VT::NDMA % NW == 0, "V DMA split");
     // K tiles of all stages first, then the V tiles: every read offset fits
@@ -406,8 +410,8 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
     constexpr int BR = Cfg::BR, BC = Cfg::BC, NSTAGE = Cfg::NSTAGE, NWAVE = Cfg::NW;
     constexpr int AHEAD = Cfg::AHEAD;
     constexpr int NKB = BC / 32;
-    constexpr int NDB = D / 32;
-    constexpr int NKS = D / 16;
+    constexpr int NDB = Cfg::DT / 32;  // tile head size (D in memory; padding columns are zeros)
+    constexpr int NKS = Cfg::DT / 16;
     constexpr int VPT = KT::NI + Cfg::VI;  // DMA instructions per tile and wave
 
     extern __shared__ __align__(1024) unsigned char smem[];
@@ -489,9 +493,9 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
         Dl = a.delta[r];
     }
 
-    SwzRowFrags<Fmt, D> krd;  // K rows (A of S^T)
+    SwzRowFrags<Fmt, Cfg::DT> krd;  // K rows (A of S^T)
     krd.init(lds0, c, g);
-    SwzTrFrags<Fmt, D> ktr;   // K^T (A of dQ^T)
+    SwzTrFrags<Fmt, Cfg::DT> ktr;   // K^T (A of dQ^T)
     ktr.init(lds0, lane);
     uint32_t vrd = lds0 + (uint32_t)(Cfg::VBASE + 16 * lane);  // V rows (A of dP^T)
     asm volatile("" : "+v"(vrd));
@@ -565,6 +569,7 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
                 for (int rg = 0; rg < 4; ++rg) {
+                    if (db * 32 + 8 * rg + 4 * g >= D) continue;  // padding columns
                     bf16x4 x;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) x[e] = (bf16)(dq[db][4 * rg + e] * a.scale);
@@ -576,6 +581,7 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
                 for (int rg = 0; rg < 4; ++rg) {
+                    if (db * 32 + 8 * rg + 4 * g >= D) continue;  // padding columns
                     f32x4 x;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) x[e] = dq[db][4 * rg + e];
@@ -605,6 +611,7 @@ static hipError_t launch_dq(const BwdArgs& a, hipStream_t stream)
 hipError_t launch_bwd_dq_bf16(const BwdArgs& a, int D, bool causal, hipStream_t stream)
 {
     if (D == 64) return causal ? launch_dq<64, true>(a, stream) : launch_dq<64, false>(a, stream);
+    if (D == 96) return causal ? launch_dq<96, true>(a, stream) : launch_dq<96, false>(a, stream);
     return causal ? launch_dq<128, true>(a, stream) : launch_dq<128, false>(a, stream);
 }
 
@@ -665,6 +672,7 @@ int dq_nsplit(int B, int Hq, int Hkv, int Tq, int Tk, int D)
 hipError_t launch_bwd_dkdv_bf16(const BwdArgs& a, int D, bool causal, hipStream_t stream)
 {
     if (D == 64) return causal ? launch_dkdv<64, true>(a, stream) : launch_dkdv<64, false>(a, stream);
+    if (D == 96) return causal ? launch_dkdv<96, true>(a, stream) : launch_dkdv<96, false>(a, stream);
     return causal ? launch_dkdv<128, true>(a, stream) : launch_dkdv<128, false>(a, stream);
 }
 
@@ -673,10 +681,14 @@ hipError_t launch_bwd_dkdv_bf16(const BwdArgs& a, int D, bool causal, hipStream_
 // host-side handle.
 template __global__ void dkdv_bf16_kernel<64, true>(BwdArgs);
 template __global__ void dkdv_bf16_kernel<64, false>(BwdArgs);
+template __global__ void dkdv_bf16_kernel<96, true>(BwdArgs);
+template __global__ void dkdv_bf16_kernel<96, false>(BwdArgs);
 template __global__ void dkdv_bf16_kernel<128, true>(BwdArgs);
 template __global__ void dkdv_bf16_kernel<128, false>(BwdArgs);
 template __global__ void dq_bf16_kernel<64, true>(BwdArgs);
 template __global__ void dq_bf16_kernel<64, false>(BwdArgs);
+template __global__ void dq_bf16_kernel<96, true>(BwdArgs);
+template __global__ void dq_bf16_kernel<96, false>(BwdArgs);
 template __global__ void dq_bf16_kernel<128, true>(BwdArgs);
 template __global__ void dq_bf16_kernel<128, false>(BwdArgs);
 

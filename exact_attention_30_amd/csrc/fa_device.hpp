@@ -69,7 +69,7 @@ template <class E>
 __device__ __forceinline__ Frag<E> global_frag(const E* base, int row, int nrows, int D, int col)
 {
     Frag<E> f;
-    if (row < nrows) {
+    if (row < nrows && col < D) {  // rows past nrows and padding columns read as zeros
         const E* p = base + (size_t)row * D + col;
         if constexpr (sizeof(E) == 2) {
             f.v = *reinterpret_cast<const bf16x8*>(p);

@@ -44,8 +44,9 @@
 
 namespace fa {
 
-template <int D>
+template <int D>  // head size of the tensors in memory
 struct FwdBf16Cfg {
+    static constexpr int DT = tile_dim(D);   // head size of the tiles and products
     static constexpr int NW = 4;             // waves per group
     static constexpr int NWAVE = 2 * NW;     // waves per workgroup (two per SIMD)
     static constexpr int NT = 64 * NWAVE;
@@ -53,8 +54,8 @@ struct FwdBf16Cfg {
     static constexpr int BC = 64;            // keys per tile
     static constexpr int NSTAGE = 4;
     static constexpr int AHD = 6;            // fragment reads in flight ahead of their MFMA
-    using KT = RowFragTile<D, BC>;
-    using VT = TrFragTile<D, BC>;
+    using KT = RowFragTile<DT, BC, D>;
+    using VT = TrFragTile<DT, BC, D>;
     static constexpr int STAGE = KT::BYTES + VT::BYTES;
     static constexpr int SMEM = NSTAGE * STAGE;
     static constexpr int KI = KT::NDMA / NWAVE;  // DMA instructions per wave per tile
@@ -91,9 +92,10 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
     using VT = typename Cfg::VT;
     constexpr int BR = Cfg::BR, BC = Cfg::BC, NWAVE = Cfg::NWAVE;
     constexpr int KI = Cfg::KI, VI = Cfg::VI;
+    constexpr int DT = Cfg::DT;   // tile head size (D in memory; padding columns are zeros)
     constexpr int NKB = BC / 32;  // 32-key blocks per tile
-    constexpr int NDB = D / 32;   // 32-column blocks of the head dimension
-    constexpr int NKS = D / 16;   // 16-deep steps over the head dimension
+    constexpr int NDB = DT / 32;  // 32-column blocks of the head dimension
+    constexpr int NKS = DT / 16;  // 16-deep steps over the head dimension
 
     extern __shared__ __align__(1024) unsigned char smem[];
 
@@ -356,6 +358,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
                 for (int rg = 0; rg < 4; ++rg) {
+                    if (db * 32 + 8 * rg + 4 * g >= D) continue;  // padding columns
                     f32x4 x;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) x[i] = o[db][4 * rg + i];
@@ -375,6 +378,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
+                if (db * 32 + 8 * rg + 4 * g >= D) continue;  // padding columns
                 bf16x4 x;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) x[i] = (bf16)(o[db][4 * rg + i] * inv);
@@ -465,6 +469,7 @@ int fwd_nsplit(int B, int Hq, int Hkv, int Tq, int Tk, int D)
 hipError_t launch_fwd_bf16(const FwdArgs& a, int D, bool causal, hipStream_t stream)
 {
     if (D == 64) return causal ? launch_t<64, true>(a, stream) : launch_t<64, false>(a, stream);
+    if (D == 96) return causal ? launch_t<96, true>(a, stream) : launch_t<96, false>(a, stream);
     return causal ? launch_t<128, true>(a, stream) : launch_t<128, false>(a, stream);
 }
 
@@ -473,6 +478,8 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, int D, bool causal, hipStream_t str
 // host-side handle.
 template __global__ void fwd_bf16_kernel<64, true>(FwdArgs);
 template __global__ void fwd_bf16_kernel<64, false>(FwdArgs);
+template __global__ void fwd_bf16_kernel<96, true>(FwdArgs);
+template __global__ void fwd_bf16_kernel<96, false>(FwdArgs);
 template __global__ void fwd_bf16_kernel<128, true>(FwdArgs);
 template __global__ void fwd_bf16_kernel<128, false>(FwdArgs);
 

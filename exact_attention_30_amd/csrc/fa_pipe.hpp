@@ -42,6 +42,20 @@ __device__ __forceinline__ i32x4 buffer_rsrc(const void* base, int bytes)
                  __builtin_amdgcn_readfirstlane(bytes), kBufferFlags};
 }
 
+// Head sizes whose rows are not a power-of-two number of 16-byte chunks run
+// on the tiles of the next supported size: columns D .. tile_dim(D) - 1 are
+// zeros in every tile (they add nothing to any product) and are never stored.
+__host__ __device__ constexpr int tile_dim(int D) { return D == 96 ? 128 : D; }
+
+// Byte offset fetched for element (row, col) of a [rows][DS] bf16 array: a
+// padding column (col >= DS) gets an offset past any buffer range, so the
+// buffer load returns zeros there.
+constexpr uint32_t kPastEnd = 0x80000000u;
+__device__ __forceinline__ constexpr uint32_t elem_off(int row, int col, int ds)
+{
+    return col < ds ? (uint32_t)((row * ds + col) * 2) : kPastEnd;
+}
+
 // 32-bit LDS address of a pointer into a __shared__ array.
 __device__ __forceinline__ uint32_t lds_addr(const void* p)
 {
@@ -79,7 +93,7 @@ __device__ __forceinline__ void sync_lds()
 // Row-wise fragments of a ROWS x D bf16 block (A operand of S^T = K Q^T):
 // fragment (kb, ks) gives lane (g, c) row 32kb + c, columns 16ks + 8g .. +7.
 // ---------------------------------------------------------------------------
-template <int D, int ROWS>
+template <int D, int ROWS, int DS = D>
 struct RowFragTile {
     static constexpr int NKS = D / 16;
     static constexpr int NKB = ROWS / 32;
@@ -94,7 +108,7 @@ struct RowFragTile {
     {
         const int kb = f / NKS, ks = f % NKS;
         const int row = 32 * kb + (lane & 31), col = 16 * ks + 8 * (lane >> 5);
-        return (uint32_t)((row * D + col) * 2);
+        return elem_off(row, col, DS);
     }
 
     // lane's fragment (kb, ks) of the tile at `tile` (lane offset included by
@@ -115,7 +129,7 @@ struct RowFragTile {
 // lane 4e + i/4 (e = 0..3); so in block (ts, db, h), lane 16m + a holds the 8
 // bytes V[16ts + 8h + 4(m/2) + a/4][32db + 16(m%2) + 4(a%4) .. +3].
 // ---------------------------------------------------------------------------
-template <int D, int ROWS>
+template <int D, int ROWS, int DS = D>
 struct TrFragTile {
     static constexpr int NTS = ROWS / 16;
     static constexpr int NDB = D / 32;
@@ -136,7 +150,7 @@ struct TrFragTile {
         const int h = lane >> 5, s = lane & 31;
         const int row = 16 * ts + 8 * h + 4 * (s >> 4) + ((s & 7) >> 1);
         const int col = 32 * db + 16 * ((s >> 3) & 1) + 8 * (s & 1);
-        return (uint32_t)((row * D + col) * 2);
+        return elem_off(row, col, DS);
     }
 
     // lane's fragment for step ts, column block db (tile_lane = tile + 8 * lane)
@@ -166,28 +180,36 @@ __device__ __forceinline__ void dma_b32(uint32_t lds, const i32x4& rsrc, uint32_
 
 // A ROWS x D bf16 block in natural [row][col] order with the chunk swizzle of
 // DmaTile (row-wise and transposed reads both conflict-free), filled by the
-// explicitly scheduled DMA above; NT threads share the instructions.
-template <int D, int ROWS, int NT>
+// explicitly scheduled DMA above; NT threads share the instructions.  The
+// rows come from a [nrows][DS] array (DS <= D; columns DS .. D-1 are zeros).
+template <int D, int ROWS, int NT, int DS = D>
 struct SwzTile {
     using Base = DmaTile<bf16, D, ROWS, NT>;
     static constexpr int NI = Base::NI;
     static constexpr int BYTES = Base::BYTES;
+    static constexpr int CPR = Base::CPR;  // 16-byte chunks per tile row
     uint32_t voff[NI];
 
+    // the chunk stored at each of this thread's DMA positions (the swizzle of
+    // DmaTile) and the global bytes it comes from
     __device__ __forceinline__ void init(int tid)
     {
-        Base t;
-        t.init(tid);
+        const int lane = tid & 63, w = tid >> 6;
 #pragma unroll
-        for (int i = 0; i < NI; ++i) voff[i] = t.voff[i];
+        for (int i = 0; i < NI; ++i) {
+            const int p = (i * (NT / 64) + w) * 64 + lane;  // chunk position in the tile
+            const int row = p / CPR;
+            const int ch = (p % CPR) ^ fa::swz<CPR>(row);
+            voff[i] = elem_off(row, ch * 8, DS);
+        }
     }
 
-    // rows row0 .. row0 + ROWS - 1 of a [nrows][D] array into the tile at LDS
+    // rows row0 .. row0 + ROWS - 1 of a [nrows][DS] array into the tile at LDS
     // byte address `lds`; rows past nrows read as zeros.  w: this wave's index.
     __device__ __forceinline__ void load(uint32_t lds, const bf16* head, int row0, int nrows, int w) const
     {
         const int left = nrows - row0;
-        const i32x4 r = buffer_rsrc(head + (size_t)row0 * D, left > 0 ? left * D * 2 : 0);
+        const i32x4 r = buffer_rsrc(head + (size_t)row0 * DS, left > 0 ? left * DS * 2 : 0);
 #pragma unroll
         for (int i = 0; i < NI; ++i) dma_b128(lds + (uint32_t)((i * (NT / 64) + w) * 1024), r, voff[i]);
     }

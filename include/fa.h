@@ -25,6 +25,11 @@
  *     dV = P^T dO,  dS = P * (dO V^T - Delta),  dQ = dS K * scale,
  *     dK = dS^T Q * scale.
  *
+ * Head dimensions.  D = 64 and 128 in both element types; D = 96 in bf16 (the
+ * 96-component queries and keys that "L'attention fusionnée", «Ce qui reste»,
+ * names as the case its kernels could not reach), computed with the 128-wide
+ * tiles and the last 32 columns taken as zero.
+ *
  * Layouts.  All tensors are contiguous, row-major, element type `dt`:
  *     q, o, dout, dq : [B][Hq][Tq][D]
  *     k, v, dk, dv   : [B][Hkv][Tk][D]
@@ -47,8 +52,8 @@
  *                         q_offset + Tq > 2^31 - 4097, a grid too large to
  *                         index, or one head of a tensor (T * D elements)
  *                         larger than 2^31 - 1 bytes;
- *     FA_ERR_UNSUPPORTED  D not in {64, 128}, unknown dtype, or scale not a
- *                         finite positive number;
+ *     FA_ERR_UNSUPPORTED  unknown dtype, D not in {64, 128} (bf16: also 96),
+ *                         or scale not a finite positive number;
  *     FA_ERR_NULL         a required pointer is NULL (pointers are not needed
  *                         when there is nothing to compute: B * Tq == 0 for
  *                         the forward, B * Tk == 0 for the backward; with

@@ -75,7 +75,9 @@ def test_shape_errors(lib):
 
 
 def test_unsupported_errors(lib):
-    assert fwd(lib, D=96) == UNSUP
+    assert fwd(lib, D=96, dt=FP32) == UNSUP
+    assert bwd(lib, D=96, dt=FP32) == UNSUP
+    assert lib.fa_bwd_preprocess(A, A, A, 1, 2, 64, 96, FP32, None) == UNSUP
     assert fwd(lib, D=32) == UNSUP
     assert fwd(lib, dt=7) == UNSUP
     assert fwd(lib, scale=0.0) == UNSUP
@@ -86,8 +88,17 @@ def test_unsupported_errors(lib):
 
 
 def test_shape_checked_before_unsupported_and_null(lib):
-    assert fwd(lib, Hq=3, Hkv=2, D=96, q=0) == SHAPE
-    assert fwd(lib, D=96, q=0) == UNSUP
+    assert fwd(lib, Hq=3, Hkv=2, D=80, q=0) == SHAPE
+    assert fwd(lib, D=80, q=0) == UNSUP
+
+
+def test_head_dim_96_accepted_in_bf16(lib):
+    # D = 96 passes the dimension check in bf16 and stops at the null pointer
+    assert fwd(lib, D=96, q=0) == NULL
+    p = [A] * 10
+    p[0] = 0
+    assert bwd(lib, p, D=96) == NULL
+    assert lib.fa_bwd_preprocess(0, A, A, 1, 2, 64, 96, BF16, None) == NULL
 
 
 def test_null_errors(lib):
@@ -158,8 +169,8 @@ def test_kv_shape_errors(lib):
     assert fwd_kv(lib, Tk=(1 << 23) + 1) == SHAPE          # one K head beyond 2^31 bytes
     assert bwd_kv(lib, off=-5) == SHAPE
     assert bwd_kv(lib, Tk=0) == SHAPE
-    assert fwd_kv(lib, off=-1, D=96) == SHAPE              # shape before unsupported
-    assert fwd_kv(lib, D=96) == UNSUP
+    assert fwd_kv(lib, off=-1, D=80) == SHAPE              # shape before unsupported
+    assert fwd_kv(lib, D=80) == UNSUP
     for fn in (lib.fa_bwd_dkdv_kv, lib.fa_bwd_dq_kv):
         n = 8 if fn is lib.fa_bwd_dkdv_kv else 7
         assert fn(*([A] * n), 1, 2, 1, 64, 100, 128, 0.1, 1, -2, BF16, None) == SHAPE

@@ -61,7 +61,7 @@ def head_slice(x, b, h0, h1):
     return x[b:b + 1, h0:h1].double().numpy()
 
 
-@pytest.mark.parametrize("name", ["C3", "C4", "C5", "C5-prefill"])
+@pytest.mark.parametrize("name", ["C3", "C4", "C5", "C5-prefill", "C5-d96"])
 def test_forward_sampled_rows(name):
     w, x, out = run(name)
     G = w.Hq // w.Hkv
@@ -78,7 +78,7 @@ def test_forward_sampled_rows(name):
     assert_lse_close(np.array(got_l), np.array(ref_l), w.dtype)
 
 
-@pytest.mark.parametrize("name", ["C3", "C5", "C5-prefill"])
+@pytest.mark.parametrize("name", ["C3", "C5", "C5-prefill", "C5-d96"])
 def test_dq_sampled_rows(name):
     w, x, out = run(name)
     G = w.Hq // w.Hkv
@@ -93,7 +93,7 @@ def test_dq_sampled_rows(name):
     assert_close("dQ rows", np.array(got), np.array(ref), w.dtype)
 
 
-@pytest.mark.parametrize("name", ["C3", "C5", "C5-prefill"])
+@pytest.mark.parametrize("name", ["C3", "C5", "C5-prefill", "C5-d96"])
 def test_dkdv_sampled_rows(name):
     w, x, out = run(name)
     G = w.Hq // w.Hkv
@@ -117,7 +117,7 @@ def test_dkdv_sampled_rows(name):
     assert_close("dV rows", np.array(got_v), np.array(ref_v), w.dtype)
 
 
-@pytest.mark.parametrize("name", ["C3", "C5", "C5-prefill"])
+@pytest.mark.parametrize("name", ["C3", "C5", "C5-prefill", "C5-d96"])
 def test_gradient_identities_all_rows(name):
     w, x, out = run(name)
     G = w.Hq // w.Hkv

@@ -34,6 +34,9 @@ CASES = {
     "q300_k200_d128_off0": (2, 2, 1, 300, 200, 128, bf16, True, 0, S128),
     "q257_k513_d128_cross": (1, 4, 4, 257, 513, 128, bf16, False, None, S128),
     "q64_k2048_d128_gqa4": (1, 8, 2, 64, 2048, 128, bf16, True, None, S128),
+    "q1_k300_d96": (1, 2, 1, 1, 300, 96, bf16, True, None, 1 / math.sqrt(96)),
+    "q300_k900_d96_off250_gqa": (1, 4, 2, 300, 900, 96, bf16, True, 250, 1 / math.sqrt(96)),
+    "q257_k513_d96_cross": (1, 2, 2, 257, 513, 96, bf16, False, None, 1 / math.sqrt(96)),
     "fp32_q70_k200_d64_off40": (1, 2, 2, 70, 200, 64, fp32, True, 40, 1 / 8),
     "fp32_q129_k70_d128_cross": (1, 2, 1, 129, 70, 128, fp32, False, None, S128),
 }

@@ -31,6 +31,9 @@ CASES = {
     "t333_d128_full_gqa": (1, 8, 2, 333, 128, bf16, False, 1 / math.sqrt(128)),
     "t777_d64_causal_gqa": (1, 6, 3, 777, 64, bf16, True, 0.15),
     "t1000_d128_causal_gqa4": (1, 4, 1, 1000, 128, bf16, True, 1 / math.sqrt(128)),
+    "t70_d96_causal": (1, 2, 2, 70, 96, bf16, True, 1 / math.sqrt(96)),
+    "t333_d96_full_gqa": (1, 4, 2, 333, 96, bf16, False, 1 / math.sqrt(96)),
+    "t1000_d96_causal_gqa4": (1, 4, 1, 1000, 96, bf16, True, 1 / math.sqrt(96)),
     "fp32_t200_d128": (1, 2, 1, 200, 128, fp32, True, 1 / math.sqrt(128)),
     "fp32_t70_d64_full": (1, 2, 2, 70, 64, fp32, False, 1 / 8),
 }
@@ -84,8 +87,7 @@ def test_backward_matches_oracle(name):
     assert_close("dV", f64(dv), rdv, dt, mv)
 
 
-@pytest.mark.parametrize("dt", [bf16, fp32])
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dt,D", [(bf16, 64), (bf16, 96), (bf16, 128), (fp32, 64), (fp32, 128)])
 def test_preprocess_matches_jacobian_term(dt, D):
     """Delta = rowsum(dO * O) ("L'attention fusionnée", «La passe arrière»):
     exact (fp32 rounding) on the kernel's own inputs, and equal to the
@@ -257,7 +259,8 @@ def test_stage_entry_points_equal_fa_bwd():
     assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
 
 
-@pytest.mark.parametrize("shape", [(1, 4, 1, 1000, 128), (1, 8, 2, 700, 64), (2, 2, 1, 513, 128)])
+@pytest.mark.parametrize("shape", [(1, 4, 1, 1000, 128), (1, 8, 2, 700, 64), (2, 2, 1, 513, 128),
+                                   (1, 4, 1, 900, 96)])
 def test_split_dkdv(shape):
     """Few kv heads leave the dK/dV kernel few workgroups, so its query side
     is split into chunks whose fp32 partial sums are added in chunk order: the
@@ -311,7 +314,8 @@ def test_no_device_allocation_by_the_library():
     assert abs(free1 - free0) < (1 << 20)
 
 
-@pytest.mark.parametrize("shape", [(1, 4, 1, 2048, 128), (1, 2, 2, 1500, 64), (2, 1, 1, 700, 128)])
+@pytest.mark.parametrize("shape", [(1, 4, 1, 2048, 128), (1, 2, 2, 1500, 64), (2, 1, 1, 700, 128),
+                                   (1, 2, 1, 1500, 96)])
 def test_split_dq(shape):
     """Few query blocks: dQ's key range is split into chunks whose fp32
     partial sums are added in chunk order; bitwise reproducible, within one
@@ -338,7 +342,7 @@ def test_split_dq(shape):
 
 
 @pytest.mark.parametrize("shape", [(1, 1, 1, 2048, 2048, 128), (1, 4, 2, 700, 700, 64),
-                                   (2, 2, 1, 300, 2000, 128)])
+                                   (2, 2, 1, 300, 2000, 128), (1, 2, 1, 600, 1800, 96)])
 def test_split_forward(shape):
     """Few query blocks: the forward splits each block's key range into
     chunks and merges their (numerator, reference max, sum) with the block

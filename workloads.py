@@ -23,6 +23,8 @@ Workloads (layout [B, H, T, D], contiguous):
   C5-prefill  C5's heads with 4096 new query rows against 16384 keys (the
       last 4096 positions: causal offset Tk - Tq = 12288), a prefill step
       against cached keys.
+  C5-d96  C5's shape with head dimension 96 (scale 1/sqrt(96)); the credited
+      FLOP count uses D = 96.
 """
 from __future__ import annotations
 
@@ -95,6 +97,7 @@ WORKLOADS = {
                          1 / math.sqrt(128), 5500),
     "C5-prefill": Workload("C5-prefill", torch.bfloat16, 1, 32, 8, 4096, 128, True,
                            1 / math.sqrt(128), 5700, Tk=16384),
+    "C5-d96": Workload("C5-d96", torch.bfloat16, 1, 32, 8, 16384, 96, True, 1 / math.sqrt(96), 5900),
 }
 
 

@@ -9,25 +9,29 @@
 // o is divided by l once at the end and L = m + ln l is saved.
 //
 // MI355X mapping.
-//   * Eight waves of 32 query rows.  A wave computes S^T = K Q^T with the
-//     32x32x16 bf16 MFMA, so a lane owns one query column: its row max and sum
-//     are in-lane reductions plus one exchange with lane c ^ 32.  The S^T
-//     accumulator is exponentiated in place (exp2, scale*log2 e folded in) and
-//     fed back as the B operand of O^T += V^T P^T: P never touches LDS.
-//   * Two waves per SIMD (eight per workgroup) in two groups of four that
-//     run in lock step, one phase apart: in every phase one wave of each SIMD
-//     issues MFMAs while its partner does vector work.  The matrix step of
-//     tile j also issues the P V product of tile j - 1: M(j) = { O += P_{j-1}
-//     V_{j-1}; S_j = Q K_j^T } (MFMAs, LDS reads), then V(j) = { mask; max;
-//     rescale; P_j = exp2(...) } (vector ALU), which also reads the first
-//     operand fragments of M(j + 1).
+//   * Eight waves of 32 query rows, two per SIMD, each running on its own
+//     (one barrier per tile for the shared LDS stages).  A wave computes
+//     S^T = K Q^T with the 32x32x16 bf16 MFMA, so a lane owns one query
+//     column and its row reductions are in-lane plus one exchange with lane
+//     c ^ 32.  The weights are formed from the S^T registers and fed back as
+//     the B operand of O^T += V^T P^T: P never touches LDS.
+//   * Software pipeline per wave: iteration i issues the products S_i and
+//     P_{i-2} V_{i-2}, which do not depend on each other or on the softmax,
+//     interleaved one by one with the vector work of tile i - 1 (exp2 of the
+//     scores, row sums, bf16 packing).  On gfx950 vector instructions cost
+//     MFMA time unless each wave slots them between its own independent
+//     MFMAs (measured: about 90 % MFMA occupancy interleaved, 69 % when one
+//     wave of a SIMD does the MFMAs and the other the vector work).
 //   * K and V tiles move from HBM to LDS by LDS DMA in read order (no bank
 //     conflicts, one address register per operand) into four stage buffers:
-//     stage j = {K_j, V_{j-1}} is the LDS data of step M(j), issued six
-//     phases before the first read of it.
+//     stage t = {K_t, V_{t-2}}, all that iteration t reads, issued three
+//     iterations ahead.
 //   * Lazy rescale: the reference max of a row only moves when the row max
 //     exceeds it by more than 8 (log2 units), so most tiles skip rescaling O
 //     and l; the weights stay below 2^8, and o and l share the reference.
+//     The weights are first formed with the current reference and the row
+//     max is taken only when some lane's share of the tile sum exceeds 2^8
+//     (implied whenever a weight does), so most tiles skip the max as well.
 //   * Causal: query row i sees key j iff j <= i + off, where off places the
 //     query rows among the keys (0 when both are the same sequence; the
 //     cuTile kernel's input_pos, «Parte 1»).  Key tiles past the workgroup's
@@ -47,13 +51,12 @@ namespace fa {
 template <int D>  // head size of the tensors in memory
 struct FwdBf16Cfg {
     static constexpr int DT = tile_dim(D);   // head size of the tiles and products
-    static constexpr int NW = 4;             // waves per group
-    static constexpr int NWAVE = 2 * NW;     // waves per workgroup (two per SIMD)
+    static constexpr int NWAVE = 8;          // waves per workgroup (two per SIMD)
     static constexpr int NT = 64 * NWAVE;
     static constexpr int BR = 32 * NWAVE;    // query rows per workgroup
     static constexpr int BC = 64;            // keys per tile
     static constexpr int NSTAGE = 4;
-    static constexpr int AHD = 6;            // fragment reads in flight ahead of their MFMA
+    static constexpr int AHD = 4;            // fragment reads in flight ahead of their MFMA
     using KT = RowFragTile<DT, BC, D>;
     using VT = TrFragTile<DT, BC, D>;
     static constexpr int STAGE = KT::BYTES + VT::BYTES;
@@ -63,26 +66,10 @@ struct FwdBf16Cfg {
     static_assert(KT::NDMA % NWAVE == 0 && VT::NDMA % NWAVE == 0, "DMA split");
 };
 
+// The reference max of a row moves only when a weight 2^(s c - mref) of the
+// tile would exceed 2^8.
 constexpr float kRescaleThresholdBf16 = 8.0f;
-
-// Scheduling pins for a run of N MFMAs whose A fragments come from LDS, AHD
-// fragments ahead (the first AHD already in registers): each MFMA is followed
-// by the reads of the fragment AHD products later.  The S products (first)
-// use row fragments (one LDS read), the PV products transposed fragments
-// (two).
-template <int N, int AHD, class TPV, class TS, int... I>
-__device__ __forceinline__ void pin_mfma_ds_interleave(std::integer_sequence<int, I...>, TPV, TS)
-{
-    constexpr int kDsRead = 0x100, kMfma = 0x008;
-    constexpr int NS = TS::value ? (N - (TPV::value ? N / 2 : 0)) : 0;
-    (
-        [] {
-            __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
-            if constexpr (I + AHD < N)
-                __builtin_amdgcn_sched_group_barrier(kDsRead, (I + AHD < NS) ? 1 : 2, 0);
-        }(),
-        ...);
-}
+constexpr float kMaxWeightBf16 = 256.0f;  // 2^kRescaleThresholdBf16
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
@@ -96,6 +83,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
     constexpr int NKB = BC / 32;  // 32-key blocks per tile
     constexpr int NDB = DT / 32;  // 32-column blocks of the head dimension
     constexpr int NKS = DT / 16;  // 16-deep steps over the head dimension
+    constexpr int AHD = Cfg::AHD, RING = AHD + 1;
 
     extern __shared__ __align__(1024) unsigned char smem[];
 
@@ -114,7 +102,6 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
     const int q0 = id.tile * BR;
     const int qw = q0 + 32 * w;   // first query of this wave
     const int qrow = qw + c;      // the query this lane owns
-    const int grp = w / Cfg::NW;  // 0 or 1: phase offset of the ping-pong
 
     const bf16* qh = static_cast<const bf16*>(a.q) + (size_t)(b * a.Hq + hq) * a.Tq * D;
     const bf16* kh = static_cast<const bf16*>(a.k) + (size_t)(b * a.Hkv + hk) * a.Tk * D;
@@ -147,28 +134,33 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
 #pragma unroll
     for (int i = 0; i < VI; ++i) voff[i] = VT::dma_off(w + NWAVE * i, lane);
 
+    // Stage t = {K_t (t < nkv), V_{t-2} (2 <= t <= nkv + 1)} in buffer
+    // t % NSTAGE: everything iteration t reads from LDS.
     const uint32_t lds0 = lds_addr(smem);
-    // stage s = {K_s (s < nkv), V_{s-1} (s >= 1)} in buffer s % NSTAGE
-    auto load_stage = [&](int s) {
-        const uint32_t base = lds0 + (uint32_t)((s % Cfg::NSTAGE) * Cfg::STAGE);
-        if (s < nkv) {
-            const int row0 = (j0 + s) * BC;
+    auto load_stage = [&](int t) {
+        const uint32_t base = lds0 + (uint32_t)((t % Cfg::NSTAGE) * Cfg::STAGE);
+        if (t < nkv) {
+            const int row0 = (j0 + t) * BC;
             const i32x4 r = buffer_rsrc(kh + (size_t)row0 * D, (a.Tk - row0) * D * 2);
 #pragma unroll
             for (int i = 0; i < KI; ++i) dma_b128(base + (uint32_t)((w + NWAVE * i) * 1024), r, koff[i]);
         }
-        if (s >= 1) {
-            const int row0 = (j0 + s - 1) * BC;
+        if (t >= 2 && t <= nkv + 1) {
+            const int row0 = (j0 + t - 2) * BC;
             const i32x4 r = buffer_rsrc(vh + (size_t)row0 * D, (a.Tk - row0) * D * 2);
 #pragma unroll
             for (int i = 0; i < VI; ++i)
                 dma_b128(base + (uint32_t)(KT::BYTES + (w + NWAVE * i) * 1024), r, voff[i]);
         }
     };
+    // DMA instructions of stage t issued by this wave
+    auto stage_ops = [&](int t) {
+        return t > nkv + 1 ? 0 : (t < nkv ? KI : 0) + (t >= 2 ? VI : 0);
+    };
 
     load_stage(0);
-    load_stage(1);  // nkv >= 1, so stage 1 holds at least V_0
-    if (nkv >= 2) load_stage(2);
+    load_stage(1);
+    load_stage(2);
 
     // B operand of S^T = K Q^T: this lane's query row, 8 columns per step
     Frag<bf16> qf[NKS];
@@ -178,173 +170,212 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
     f32x16 o[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) o[db] = f32x16{};
-    f32x16 s[NKB];                 // S^T of the current tile (rows = keys)
-    Frag<bf16> pf[NKB][2];         // P of the previous tile (B operands of P V)
-    float mref = -INFINITY;        // reference max, log2 units
-    float l = 0.f;                 // this lane's share of the row sum
+    f32x16 s[2][NKB];          // S^T of tile i (being computed) and of tile i - 1
+    u32x4 pf[2][NKB][2];       // P of tile i - 1 (being formed) and of tile i - 2 (B of P V),
+                               // bf16 pairs
+    float mref = -INFINITY;    // reference max, log2 units
+    float l = 0.f;             // this lane's share of the row sum
 
-    vm_wait<0>();
-    sync_lds();
-
-    // Matrix step M(j): S_j^T = K_j Q^T (S, j < nkv) and O^T += V_{j-1}^T
-    // P_{j-1}^T (PV, j >= 1), all operands from stage j.  Product i reads its
-    // A fragment AHD products ahead into a ring of registers; the first AHD
-    // reads are issued by the preceding vector step of the same wave (its LDS
-    // port is otherwise idle), so the matrix step starts without waiting.
-    constexpr int AHD = Cfg::AHD, RING = AHD + 1;
-    bf16x8 ring[RING];
-    auto frag_read = [&](int j, int i, auto with_pv, auto with_s) -> bf16x8 {
-        constexpr bool PV = decltype(with_pv)::value, SS = decltype(with_s)::value;
-        constexpr int NS = SS ? NKS * NKB : 0;
-        const unsigned char* st = smem + (j % Cfg::NSTAGE) * Cfg::STAGE;
-        if (i < NS) {
-            const int kb = i % NKB, ks = i / NKB;
+    // fragment k of iteration t: score products first, then P V products
+    auto frag_read = [&](int t, int k, auto ns) -> bf16x8 {
+        constexpr int NS = decltype(ns)::value;
+        const unsigned char* st = smem + (t % Cfg::NSTAGE) * Cfg::STAGE;
+        if (k < NS) {
+            const int kb = k % NKB, ks = k / NKB;
             return KT::read(st + 16 * lane, kb, ks);
         }
-        (void)PV;
-        const int k = i - NS, db = k % NDB, t = (k / NDB) % 2, kb = k / (2 * NDB);
-        return VT::read(st + KT::BYTES + 8 * lane, 2 * kb + t, db);
-    };
-    auto prefetch = [&](int j, auto with_pv, auto with_s) {
-#pragma unroll
-        for (int i = 0; i < AHD; ++i) ring[i] = frag_read(j, i, with_pv, with_s);
-    };
-    auto matrix_step = [&](int j, auto with_pv, auto with_s) {
-        constexpr bool PV = decltype(with_pv)::value, SS = decltype(with_s)::value;
-        constexpr int NPV = PV ? NKB * 2 * NDB : 0;   // PV products
-        constexpr int NS = SS ? NKS * NKB : 0;        // S products
-        constexpr int N = NPV + NS;
-        static_assert(N > AHD, "prefetch depth");
-        if constexpr (SS) {
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
-        }
-#pragma unroll
-        for (int i = 0; i < N; ++i) {
-            if (i + AHD < N) ring[(i + AHD) % RING] = frag_read(j, i + AHD, with_pv, with_s);
-            Frag<bf16> af;
-            af.v = ring[i % RING];
-            if (i < NS) {
-                const int kb = i % NKB, ks = i / NKB;
-                mma(s[kb], af, qf[ks]);
-            } else {
-                const int k = i - NS, db = k % NDB, t = (k / NDB) % 2, kb = k / (2 * NDB);
-                mma(o[db], af, pf[kb][t]);
-            }
-        }
-        pin_mfma_ds_interleave<N, AHD>(std::make_integer_sequence<int, N>{}, with_pv, with_s);
+        const int m = k - NS, db = m % NDB, u = (m / NDB) % 2, kb = m / (2 * NDB);
+        return VT::read(st + KT::BYTES + 8 * lane, 2 * kb + u, db);
     };
 
-    // Vector step V(j): mask, lazy reference update (rescaling O and l when it
-    // moves), P_j = exp2(S_j c - mref) with fp32 row sums, rounded for P V.
-    auto vector_step = [&](int jl) {
-        const int j = j0 + jl;  // key tile
-        if (j >= nfull) {
-            asm volatile("");  // keep this a branch
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int kj = j * BC + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-                    const bool vis = kj < a.Tk && (!CAUSAL || kj <= qrow + a.off);
-                    if (!vis) s[kb][r] = -INFINITY;
-                }
-        }
-        float mt = -INFINITY;
+    // Mask of tile jl (chunk-local index) for this lane's query: keys past Tk
+    // and, when causal, past qrow + off get -inf.
+    auto mask_tile = [&](f32x16 (&st)[NKB], int jl) __attribute__((always_inline)) {
+        const int j = j0 + jl;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; r += 2) mt = fmaxf(mt, fmaxf(s[kb][r], s[kb][r + 1]));
-        mt = pair_max(mt) * a.c;
-        const bool need = mt > mref + kRescaleThresholdBf16;
-        if (__builtin_amdgcn_ballot_w64(need)) {
-            const float mnew = need ? mt : mref;
-            // 0 on a row's first visible key; 1 for rows that keep their
-            // reference (also those that have seen no key yet: -inf - -inf)
-            const float alpha = need ? fast_exp2(mref - mnew) : 1.f;
-            l *= alpha;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) o[db] *= alpha;
-            mref = mnew;
-        }
-        const float msub = (mref == -INFINITY) ? 0.f : mref;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
             for (int r = 0; r < 16; ++r) {
-                s[kb][r] = fast_exp2(fmaf(s[kb][r], a.c, -msub));
-                l += s[kb][r];
+                const int kj = j * BC + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+                const bool vis = kj < a.Tk && (!CAUSAL || kj <= qrow + a.off);
+                if (!vis) st[kb][r] = -INFINITY;
             }
-#pragma unroll
-            for (int t = 0; t < 2; ++t) pf[kb][t] = acc_frag<bf16>(s[kb], t);
-        }
     };
 
-    // Lock-step phases (ping-pong).  Group 0 runs the sequence M(0) V(0) M(1)
-    // V(1) ... V(nkv-1) M(nkv), one step per phase; group 1 runs it one phase
-    // later, so in every phase one wave of each SIMD issues MFMAs while its
-    // partner does vector work (one MFMA stream per SIMD at a time runs faster
-    // than two interleaved ones).  V(j) also issues the first fragment reads
-    // of M(j + 1) from stage j + 1.  Stage s is issued at the start of phase
-    // 2s - 6 (stages 0..2 before the loop) into the buffer of stage s - 4,
-    // whose last reader ended with phase 2s - 7; stage j + 1 is waited for at
-    // the end of phase 2j, before the first vector step that prefetches from
-    // it (group 0's V(j), phase 2j + 1).
-    auto issue_ahead = [&](int j) {  // phase 2j
-        if (j + 3 <= nkv) load_stage(j + 3);
+    // Weights P = 2^(S c - mref) of one tile into bf16 B fragments; returns
+    // this lane's share of their sum.
+    auto weights = [&](const f32x16 (&st)[NKB], u32x4 (&pt)[NKB][2], float msub)
+        __attribute__((always_inline)) -> float {
+        float sum[NKB];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            float p[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) p[r] = fast_exp2(fmaf(st[kb][r], a.c, -msub));
+            sum[kb] = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sum[kb] += p[r];
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) pt[kb][r / 8][(r % 8) / 2] = pack_bf16(p[r], p[r + 1]);
+        }
+        float t = sum[0];
+#pragma unroll
+        for (int kb = 1; kb < NKB; ++kb) t += sum[kb];
+        return t;
     };
-    auto wait_after_even = [&](int j) {  // end of phase 2j: stage j + 1 must land
-        if (j + 3 < nkv)
+
+    // Iteration i (parity P of i): S_i = Q K_i^T into s[P] (HS: i < nkv),
+    // O^T += V_{i-2}^T P_{i-2}^T from pf[P] (HPV: i >= 2), and the weights of
+    // tile i - 1 from s[P ^ 1] into pf[P ^ 1] (HW: 1 <= i <= nkv), the three
+    // interleaved in one instruction stream.  The weights use the current
+    // reference; when some weight of a lane may exceed 2^8 (its share of the
+    // tile sum does), or a row has no reference yet, the tile takes the
+    // reference update of the online softmax («Le softmax en ligne»): row max,
+    // a new reference where it rose by more than 8, O and l rescaled, weights
+    // recomputed.  O then includes P_{i-2} V_{i-2}, formed with the old
+    // reference, so the rescale applies to it too.
+    auto iteration = [&](int i, auto par, auto hs, auto hw, auto hpv) __attribute__((always_inline)) {
+        constexpr int P = decltype(par)::value;
+        constexpr bool HS = decltype(hs)::value, HW = decltype(hw)::value, HPV = decltype(hpv)::value;
+        constexpr int NS = HS ? NKS * NKB : 0;         // score products
+        constexpr int NPV = HPV ? NKB * 2 * NDB : 0;   // P V products
+        constexpr int N = NS + NPV;
+
+        // stage i has landed (this wave's DMA and, after the barrier, every
+        // wave's); every wave has left iteration i - 1, whose buffer takes
+        // stage i + 3
+        const int ahead = stage_ops(i + 1) + stage_ops(i + 2);
+        if (ahead == 2 * (KI + VI))
             vm_wait<2 * (KI + VI)>();
-        else if (j + 3 == nkv)
+        else if (ahead == (KI + VI) + VI)
             vm_wait<(KI + VI) + VI>();
-        else if (j + 2 == nkv)
+        else if (ahead == 2 * VI)
+            vm_wait<2 * VI>();
+        else if (ahead == VI)
             vm_wait<VI>();
         else
             vm_wait<0>();
         sync_lds();
+        load_stage(i + 3);
+
+        if constexpr (HW) {
+            if (j0 + i - 1 >= nfull) {
+                asm volatile("");  // keep this a branch
+                mask_tile(s[P ^ 1], i - 1);
+            }
+        }
+        const float msub = (mref == -INFINITY) ? 0.f : mref;
+
+        // One group per product: the MFMA, the fragment read of the product
+        // AHD later, and a share of the weights, which move through four
+        // steps per element e (fma at step e, exp2 at e + 1, sum at e + 2,
+        // bf16 pair at e + 3) so few temporaries are live; groups are fenced
+        // so the compiler keeps this order.  With both kinds of products
+        // they alternate (score, P V, ...), which also spaces the dependent
+        // products of one accumulator.
+        constexpr int NE = HW ? 16 * NKB : 0;  // weight elements of this lane
+        constexpr int NSTEP = HW ? NE + 3 : 0;
+        auto product = [](int k) {  // k-th product: score product index, or NS + P V index
+            if (NS == 0 || NPV == 0) return k;
+            return (k % 2 == 0) ? k / 2 : NS + k / 2;
+        };
+        bf16x8 ring[RING];
+        using NSc = std::integral_constant<int, NS>;
+#pragma unroll
+        for (int k = 0; k < AHD && k < N; ++k) ring[k] = frag_read(i, product(k), NSc{});
+        const f32x16(&sw)[NKB] = s[P ^ 1];
+        u32x4(&pw)[NKB][2] = pf[P ^ 1];
+        float fx[NE > 0 ? NE : 1], px[NE > 0 ? NE : 1];
+        float lt = 0.f;
+        auto step = [&](int t) __attribute__((always_inline)) {
+            if (t < NE) fx[t] = fmaf(sw[t / 16][t % 16], a.c, -msub);
+            if (t >= 1 && t - 1 < NE) px[t - 1] = fast_exp2(fx[t - 1]);
+            if (t >= 2 && t - 2 < NE) lt += px[t - 2];
+            if (t >= 3 && (t - 3) % 2 == 0 && t - 2 < NE) {
+                // the pair is formed here (the empty asm keeps the compiler
+                // from sinking it, with both weights live, to the end)
+                const int e = t - 3, kb = e / 16, r = e % 16;
+                uint32_t pr = pack_bf16(px[e], px[e + 1]);
+                asm volatile("" : "+v"(pr));
+                pw[kb][r / 8][(r % 8) / 2] = pr;
+            }
+        };
+        if constexpr (N == 0) {
+#pragma unroll
+            for (int t = 0; t < NSTEP; ++t) step(t);
+        }
+#pragma unroll
+        for (int k = 0; k < N; ++k) {
+            if (k + AHD < N) ring[(k + AHD) % RING] = frag_read(i, product(k + AHD), NSc{});
+            Frag<bf16> af;
+            af.v = ring[k % RING];
+            const int pk = product(k);
+            if (pk < NS) {
+                const int kb = pk % NKB, ks = pk / NKB;
+                if (ks == 0)
+                    s[P][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af.v, qf[0].v, f32x16{}, 0, 0, 0);
+                else
+                    mma(s[P][kb], af, qf[ks]);
+            } else {
+                const int m = pk - NS, db = m % NDB, u = (m / NDB) % 2, kb = m / (2 * NDB);
+                Frag<bf16> bf;
+                bf.v = __builtin_bit_cast(bf16x8, pf[P][kb][u]);
+                mma(o[db], af, bf);
+            }
+#pragma unroll
+            for (int t = k * NSTEP / (N > 0 ? N : 1); t < (k + 1) * NSTEP / (N > 0 ? N : 1); ++t) step(t);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+        if constexpr (HW) {
+            if (__builtin_amdgcn_ballot_w64(lt > kMaxWeightBf16 || mref == -INFINITY)) {
+                float mt = -INFINITY;
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; r += 2) mt = fmaxf(mt, fmaxf(s[P ^ 1][kb][r], s[P ^ 1][kb][r + 1]));
+                mt = pair_max(mt) * a.c;
+                const bool need = mt > mref + kRescaleThresholdBf16;
+                if (__builtin_amdgcn_ballot_w64(need)) {
+                    const float mnew = need ? mt : mref;
+                    // 0 on a row's first visible key; 1 for rows that keep
+                    // their reference (also those that have seen no key yet)
+                    const float alpha = need ? fast_exp2(mref - mnew) : 1.f;
+                    l *= alpha;
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+                    mref = mnew;
+                    lt = weights(s[P ^ 1], pf[P ^ 1], (mref == -INFINITY) ? 0.f : mref);
+                }
+            }
+            l += lt;
+        }
     };
-    using T0 = std::integral_constant<bool, false>;
-    using T1 = std::integral_constant<bool, true>;
-    prefetch(0, T0{}, T1{});
-    if (grp == 0) {
-        issue_ahead(0);
-        matrix_step(0, T0{}, T1{});
-        wait_after_even(0);
-        for (int j = 0; j + 1 < nkv; ++j) {
-            vector_step(j);
-            prefetch(j + 1, T1{}, T1{});
-            sync_lds();
-            issue_ahead(j + 1);
-            matrix_step(j + 1, T1{}, T1{});
-            wait_after_even(j + 1);
-        }
-        vector_step(nkv - 1);
-        prefetch(nkv, T1{}, T0{});
-        sync_lds();
-        issue_ahead(nkv);
-        matrix_step(nkv, T1{}, T0{});
-        wait_after_even(nkv);
-        sync_lds();
+
+    using F = std::false_type;
+    using T = std::true_type;
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    iteration(0, P0{}, T{}, F{}, F{});
+    if (nkv == 1) {
+        iteration(1, P1{}, F{}, T{}, F{});
+        iteration(2, P0{}, F{}, F{}, T{});
     } else {
-        issue_ahead(0);
-        wait_after_even(0);
-        matrix_step(0, T0{}, T1{});
-        sync_lds();
-        for (int j = 0; j + 1 < nkv; ++j) {
-            issue_ahead(j + 1);
-            vector_step(j);
-            prefetch(j + 1, T1{}, T1{});
-            wait_after_even(j + 1);
-            matrix_step(j + 1, T1{}, T1{});
-            sync_lds();
+        iteration(1, P1{}, T{}, T{}, F{});
+        int i = 2;
+        for (; i + 1 < nkv; i += 2) {
+            iteration(i, P0{}, T{}, T{}, T{});
+            iteration(i + 1, P1{}, T{}, T{}, T{});
         }
-        issue_ahead(nkv);
-        vector_step(nkv - 1);
-        prefetch(nkv, T1{}, T0{});
-        wait_after_even(nkv);
-        matrix_step(nkv, T1{}, T0{});
-        sync_lds();
+        if (i < nkv) iteration(i++, P0{}, T{}, T{}, T{});
+        // i == nkv
+        if ((nkv & 1) == 0) {
+            iteration(nkv, P0{}, F{}, T{}, T{});
+            iteration(nkv + 1, P1{}, F{}, F{}, T{});
+        } else {
+            iteration(nkv, P1{}, F{}, T{}, T{});
+            iteration(nkv + 1, P0{}, F{}, F{}, T{});
+        }
     }
 
     // epilogue: divide by l, store O (this lane: query qrow, columns
@@ -361,7 +392,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
                     if (db * 32 + 8 * rg + 4 * g >= D) continue;  // padding columns
                     f32x4 x;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) x[i] = o[db][4 * rg + i];
+                    for (int e = 0; e < 4; ++e) x[e] = o[db][4 * rg + e];
                     *reinterpret_cast<f32x4*>(op + db * 32 + 8 * rg + 4 * g) = x;
                 }
             if (g == 0) {
@@ -381,7 +412,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
                 if (db * 32 + 8 * rg + 4 * g >= D) continue;  // padding columns
                 bf16x4 x;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) x[i] = (bf16)(o[db][4 * rg + i] * inv);
+                for (int e = 0; e < 4; ++e) x[e] = (bf16)(o[db][4 * rg + e] * inv);
                 *reinterpret_cast<bf16x4*>(oh + db * 32 + 8 * rg + 4 * g) = x;
             }
         if (g == 0) a.lse[(size_t)(b * a.Hq + hq) * a.Tq + qrow] = (mref + __log2f(lt)) * kLn2;

@@ -356,26 +356,34 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
     using T = std::true_type;
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
+    // Iterations 0 and 1 are the same for every nkv (with nkv = 1, the
+    // product S_1 of iteration 1 reads a stage no tile filled and is never
+    // used): no register state then lives across the branch below.
     iteration(0, P0{}, T{}, F{}, F{});
+    iteration(1, P1{}, T{}, T{}, F{});
     if (nkv == 1) {
-        iteration(1, P1{}, F{}, T{}, F{});
         iteration(2, P0{}, F{}, F{}, T{});
     } else {
-        iteration(1, P1{}, T{}, T{}, F{});
         int i = 2;
         for (; i + 1 < nkv; i += 2) {
             iteration(i, P0{}, T{}, T{}, T{});
             iteration(i + 1, P1{}, T{}, T{}, T{});
         }
         if (i < nkv) iteration(i++, P0{}, T{}, T{}, T{});
-        // i == nkv
-        if ((nkv & 1) == 0) {
-            iteration(nkv, P0{}, F{}, T{}, T{});
-            iteration(nkv + 1, P1{}, F{}, F{}, T{});
-        } else {
-            iteration(nkv, P1{}, F{}, T{}, T{});
-            iteration(nkv + 1, P0{}, F{}, F{}, T{});
+        // i == nkv.  The last two iterations exist in one parity only: with
+        // nkv odd, S_{nkv-1} and P_{nkv-2} move to the registers that parity
+        // expects (a copy once per workgroup instead of a second version of
+        // the code, across which the compiler spills).
+        if (nkv & 1) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                s[1][kb] = s[0][kb];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) pf[0][kb][u] = pf[1][kb][u];
+            }
         }
+        iteration(nkv, P0{}, F{}, T{}, T{});
+        iteration(nkv + 1, P1{}, F{}, F{}, T{});
     }
 
     // epilogue: divide by l, store O (this lane: query qrow, columns

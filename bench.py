@@ -36,6 +36,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_FP32_TFLOPS = 157.3    # MI355X dense fp32 MFMA, published
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, published
 METRIC = "causal attention fwd+bwd TFLOP/s on 1 MI355X; % of bf16 MFMA peak"
 
 # GEMMs each kernel performs, in units of one T x T x D product over the
@@ -189,6 +190,67 @@ def forward_only(args, w, x, q, k, v, o, lse):
     print(json.dumps(out), flush=True)
 
 
+def forward_only_fp8(args, w, q, k, v, lse):
+    """The e4m3 forward-only workload: one step is one fa_fwd_fp8 (the V
+    transpose pre-pass and the forward); the roofline is the forward kernel
+    alone (fa_fwd_fp8_vt, timed by its own events) against the dense fp8 MFMA
+    peak."""
+    import torch
+
+    import exact_attention_30_amd as fa
+
+    ds = 1.0 / w.input_scale
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    ws = torch.empty(max(fa.fwd_fp8_workspace_bytes(w.B, w.Hkv, w.Tkv, w.D), 16), dtype=torch.uint8,
+                     device=q.device)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        fa.fp8_transpose_v(v, ws)
+        if ev:
+            ev[1].record()
+        fa.fwd_fp8_vt(q, k, ws, v.shape, ds, ds, ds, scale=w.scale, causal=w.causal, out=o, lse=lse)
+        if ev:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for ev in events:
+        step(ev)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    vt_ms = sum(ev[0].elapsed_time(ev[1]) for ev in events) / args.steps
+    per = sum(ev[1].elapsed_time(ev[2]) for ev in events) / args.steps
+    ms_per_step = max(wall * 1e3 / args.steps, events[0][0].elapsed_time(events[-1][2]) / args.steps)
+    value = w.fwd_flop / (ms_per_step * 1e-3) / 1e12
+    achieved = gemm_flop(w, KERNEL_GEMMS["fwd"]) / (per * 1e-3) / 1e12
+    out = {
+        "metric": "attention fwd TFLOP/s on 1 MI355X; % of fp8 MFMA peak (forward-only e4m3 workload)",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8",
+        "data": "synthetic (seeded N(0,1) inputs of the workload's shape, x16 and rounded to e4m3, "
+                "descale 1/16)",
+        "config": {"workload": describe(w), "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "T": w.T, "D": w.D,
+                   "causal": w.causal, "parallelism": "single GPU"},
+        "pct_of_peak": round(100 * value / PEAK_FP8_TFLOPS, 2),
+        "breakdown": {"transpose_v_ms": round(vt_ms, 4), "fwd_ms": round(per, 4)},
+        "roofline": {
+            "kernel": "fwd_fp8_kernel", "bound": "mfma", "achieved": round(achieved, 2),
+            "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
+            "traffic": traffic_for("fwd_fp8", "fa_fwd_fp8.hip", w.name),
+            "avg_launch_ms": round(per, 4),
+            "algorithmic_flop_per_launch": gemm_flop(w, KERNEL_GEMMS["fwd"]),
+        },
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def cpu_baseline(w, x, target_s: float):
     """Time the oracle's fwd + bwd on a bounded sample of the workload, sized
     to take about target_s seconds: whole kv groups (all their query heads,
@@ -271,6 +333,10 @@ def main():
     torch.cuda.set_device(dev)
     d = {k: v.to(dev) for k, v in x.items()}
     q, k, v, do = d["q"], d["k"], d["v"], d.get("dout")
+    if w.dtype == torch.float8_e4m3fn:
+        forward_only_fp8(args, w, q, k, v,
+                         torch.empty(w.B, w.Hq, w.T, dtype=torch.float32, device=dev))
+        return
     o = torch.empty_like(q)
     lse = torch.empty(w.B, w.Hq, w.T, dtype=torch.float32, device=dev)
     delta = torch.empty(w.B, w.Hq, w.T, dtype=torch.float32, device=dev)

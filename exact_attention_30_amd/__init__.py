@@ -64,6 +64,12 @@ SIGNATURES = {
     "fa_fwd_split_bytes": ([_i, _i, _i, _i, _i, _i, _i], ctypes.c_size_t),
     "fa_fwd_split": ([_vp, _vp, _vp, _vp, _fp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _i, _i, _vp],
                      ctypes.c_int),
+    "fa_fwd_fp8_workspace_bytes": ([_i, _i, _i, _i], ctypes.c_size_t),
+    "fa_fwd_fp8": ([_vp, _vp, _vp, _f, _f, _f, _vp, _fp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _i,
+                    _vp], ctypes.c_int),
+    "fa_fp8_transpose_v": ([_vp, _vp, _i, _i, _i, _i, _vp], ctypes.c_int),
+    "fa_fwd_fp8_vt": ([_vp, _vp, _vp, _f, _f, _f, _vp, _fp, _i, _i, _i, _i, _i, _i, _f, _i, _i,
+                       _vp], ctypes.c_int),
     "fa_status_string": ([_i], ctypes.c_char_p),
     "fa_version": ([], ctypes.c_char_p),
 }
@@ -173,6 +179,76 @@ def fwd(q, k, v, scale=None, causal: bool = True, out=None, lse=None, q_offset=N
         _check(lib.fa_fwd_kv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(),
                              B, Hq, Hkv, Tq, Tk, D, _scale(scale, D), int(bool(causal)), off, dt,
                              _stream(q)), "fa_fwd_kv")
+    return o, l
+
+
+def fwd_fp8_workspace_bytes(B, Hkv, Tk, D) -> int:
+    """Workspace bytes of fwd_fp8 (V transposed tile by tile)."""
+    return int(library().fa_fwd_fp8_workspace_bytes(B, Hkv, Tk, D))
+
+
+def _fp8_check(*ts):
+    for t in ts:
+        if t.dtype != torch.float8_e4m3fn:
+            raise TypeError("the fp8 calls take torch.float8_e4m3fn tensors")
+        if not t.is_cuda or t.device != ts[0].device or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous tensors on one GPU")
+
+
+def fp8_transpose_v(v, vt=None):
+    """V (float8_e4m3fn [B,Hkv,Tk,D]) transposed as fwd_fp8_vt reads it, into a
+    uint8 device tensor of fwd_fp8_workspace_bytes(...) bytes (fa_fp8_transpose_v)."""
+    _fp8_check(v)
+    B, Hkv, Tk, D = v.shape
+    need = fwd_fp8_workspace_bytes(B, Hkv, Tk, D)
+    if vt is None:
+        vt = torch.empty(max(need, 16), dtype=torch.uint8, device=v.device)
+    elif vt.numel() * vt.element_size() < need:
+        raise ValueError("vt too small")
+    _check(library().fa_fp8_transpose_v(v.data_ptr(), vt.data_ptr(), B, Hkv, Tk, D, _stream(v)),
+           "fa_fp8_transpose_v")
+    return vt
+
+
+def fwd_fp8_vt(q, k, vt, v_shape, q_descale, k_descale, v_descale, scale=None,
+               causal: bool = True, out=None, lse=None, q_offset=None):
+    """fwd_fp8 with V already transposed by fp8_transpose_v (fa_fwd_fp8_vt);
+    v_shape is the shape of the V it came from."""
+    _fp8_check(q, k)
+    B, Hq, Tq, D = q.shape
+    Hkv, Tk = k.shape[1], k.shape[2]
+    if tuple(k.shape) != tuple(v_shape) or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("shape mismatch")
+    off = _offset(Tq, Tk, q_offset)
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device) if out is None else out
+    l = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check(library().fa_fwd_fp8_vt(q.data_ptr(), k.data_ptr(), vt.data_ptr(), float(q_descale),
+                                   float(k_descale), float(v_descale), o.data_ptr(), l.data_ptr(),
+                                   B, Hq, Hkv, Tq, Tk, D, _scale(scale, D), int(bool(causal)), off,
+                                   _stream(q)), "fa_fwd_fp8_vt")
+    return o, l
+
+
+def fwd_fp8(q, k, v, q_descale, k_descale, v_descale, scale=None, causal: bool = True,
+            out=None, lse=None, q_offset=None, workspace=None):
+    """FP8 forward: q, k, v are torch.float8_e4m3fn codes whose real values are
+    the codes times q_descale, k_descale, v_descale.  Returns (o bf16, lse
+    float32); calls fa_fwd_fp8.  `workspace` (uint8 device tensor of at least
+    fwd_fp8_workspace_bytes(...) bytes) is allocated when not given."""
+    B, Hq, Hkv, Tq, Tk, D = _dims(q, k, v)
+    _fp8_check(q, k, v)
+    off = _offset(Tq, Tk, q_offset)
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device) if out is None else out
+    l = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device) if lse is None else lse
+    need = fwd_fp8_workspace_bytes(B, Hkv, Tk, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise ValueError("workspace too small")
+    _check(library().fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), float(q_descale),
+                                float(k_descale), float(v_descale), o.data_ptr(), l.data_ptr(),
+                                workspace.data_ptr(), B, Hq, Hkv, Tq, Tk, D, _scale(scale, D),
+                                int(bool(causal)), off, _stream(q)), "fa_fwd_fp8")
     return o, l
 
 

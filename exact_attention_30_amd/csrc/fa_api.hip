@@ -105,7 +105,7 @@ size_t shared_split_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int D, fa_dtyp
 
 extern "C" {
 
-const char* fa_version(void) { return "0.2.0"; }
+const char* fa_version(void) { return "0.3.0"; }
 
 const char* fa_status_string(fa_status s)
 {
@@ -159,6 +159,7 @@ fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, flo
     a.scale = scale;
     a.opart = a.ml = nullptr;
     a.nsplit = 1;
+    a.vscale = 1.f;
     if (partial && fwd_split_bytes(B, Hq, Hkv, Tq, Tk, D, dt) > 0) {
         a.nsplit = fa::fwd_nsplit(B, Hq, Hkv, Tq, Tk, D);
         const size_t rows = (size_t)a.nsplit * B * Hq * Tq;
@@ -186,6 +187,85 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  int Hkv, int T, int D, float scale, int causal, fa_dtype dt, void* stream)
 {
     return fa_fwd_kv(q, k, v, o, lse, B, Hq, Hkv, T, T, D, scale, causal, 0, dt, stream);
+}
+
+// ---------------------------------------------------------------------------
+// FP8 (e4m3) forward
+
+size_t fa_fwd_fp8_workspace_bytes(int B, int Hkv, int Tk, int D)
+{
+    if (B < 0 || Hkv < 1 || Tk < 0 || (D != 64 && D != 128)) return 0;
+    return (size_t)B * (size_t)Hkv * (size_t)((Tk + 63) / 64) * 64 * (size_t)D;
+}
+
+fa_status fa_fp8_transpose_v(const void* v, void* vt, int B, int Hkv, int Tk, int D, void* stream)
+{
+    if (B < 0 || Hkv < 1 || Tk < 0) return FA_ERR_SHAPE;
+    if ((long long)B * Hkv * ((Tk + 63) / 64) > 0x7fffffffLL || (long long)Tk * D > 0x7fffffffLL)
+        return FA_ERR_SHAPE;
+    if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+    if ((long long)B * Tk == 0) return FA_OK;
+    if (!v || !vt) return FA_ERR_NULL;
+    if (!aligned(v, 16) || !aligned(vt, 16)) return FA_ERR_ALIGN;
+    return from_hip(fa::launch_fp8_vt(v, vt, B, Hkv, Tk, D, static_cast<hipStream_t>(stream)));
+}
+
+fa_status fa_fwd_fp8_vt(const void* q, const void* k, const void* vt, float q_descale,
+                        float k_descale, float v_descale, void* o, float* lse, int B, int Hq,
+                        int Hkv, int Tq, int Tk, int D, float scale, int causal, int q_offset,
+                        void* stream)
+{
+    const int off = causal ? q_offset : 0;
+    // shape rules of the bf16 forward (a bf16 head bounds an fp8 head too)
+    fa_status st = check_kv(B, Hq, Hkv, Tq, Tk, D, FA_BF16, causal != 0, off);
+    if (st != FA_OK) return st;
+    if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+    if ((st = check_scale(scale)) != FA_OK || (st = check_scale(q_descale)) != FA_OK ||
+        (st = check_scale(k_descale)) != FA_OK || (st = check_scale(v_descale)) != FA_OK)
+        return st;
+    if ((long long)B * Tq == 0) return FA_OK;
+    if (!q || !k || !vt || !o || !lse) return FA_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(vt, 16) || !aligned(o, 16) || !aligned(lse, 4))
+        return FA_ERR_ALIGN;
+    fa::FwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = vt;
+    a.o = o;
+    a.lse = lse;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.Tq = Tq;
+    a.Tk = Tk;
+    a.off = off;
+    a.c = scale * q_descale * k_descale * kLog2e;
+    a.scale = scale * q_descale * k_descale;
+    a.opart = a.ml = nullptr;
+    a.nsplit = 1;
+    a.vscale = v_descale;
+    return from_hip(fa::launch_fwd_fp8(a, D, causal != 0, static_cast<hipStream_t>(stream)));
+}
+
+fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, float q_descale, float k_descale,
+                     float v_descale, void* o, float* lse, void* workspace, int B, int Hq, int Hkv,
+                     int Tq, int Tk, int D, float scale, int causal, int q_offset, void* stream)
+{
+    const int off = causal ? q_offset : 0;
+    fa_status st = check_kv(B, Hq, Hkv, Tq, Tk, D, FA_BF16, causal != 0, off);
+    if (st != FA_OK) return st;
+    if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+    if ((st = check_scale(scale)) != FA_OK || (st = check_scale(q_descale)) != FA_OK ||
+        (st = check_scale(k_descale)) != FA_OK || (st = check_scale(v_descale)) != FA_OK)
+        return st;
+    if ((long long)B * Tq == 0) return FA_OK;
+    if (!q || !k || !v || !o || !lse || !workspace) return FA_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
+        !aligned(workspace, 16))
+        return FA_ERR_ALIGN;
+    if ((st = fa_fp8_transpose_v(v, workspace, B, Hkv, Tk, D, stream)) != FA_OK) return st;
+    return fa_fwd_fp8_vt(q, k, workspace, q_descale, k_descale, v_descale, o, lse, B, Hq, Hkv, Tq, Tk,
+                         D, scale, causal, q_offset, stream);
 }
 
 size_t fa_bwd_kv_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int D, fa_dtype dt)

@@ -23,6 +23,8 @@ struct FwdArgs {
     float* opart;
     float* ml;
     int nsplit;
+    // fp8 forward: descale of V, applied to O (1 for the other element types)
+    float vscale;
 };
 
 struct BwdArgs {
@@ -70,5 +72,9 @@ int fwd_nsplit(int B, int Hq, int Hkv, int Tq, int Tk, int D);
 hipError_t launch_bwd_dkdv_bf16(const BwdArgs& a, int D, bool causal, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, int D, int dtype, bool causal, hipStream_t stream);
 hipError_t launch_bwd_dq_bf16(const BwdArgs& a, int D, bool causal, hipStream_t stream);
+// fp8 (e4m3) forward: a.v is the transposed V that launch_fp8_vt writes
+// (tile-major, [B][Hkv][ceil(Tk/64)][D][64 bytes]); D is 64 or 128
+hipError_t launch_fp8_vt(const void* v, void* vt, int B, int Hkv, int Tk, int D, hipStream_t stream);
+hipError_t launch_fwd_fp8(const FwdArgs& a, int D, bool causal, hipStream_t stream);
 
 }  // namespace fa

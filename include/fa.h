@@ -135,6 +135,50 @@ fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, flo
                        int causal, int q_offset, fa_dtype dt, void* stream);
 
 /*
+ * FP8 forward ("FlashAttention: l'attenzione che non spreca memoria",
+ * «La frontiera», names narrower formats as the next lever for the matrix
+ * units; the pages give no scaling convention).  q, k, v hold e4m3 codes
+ * (OCP e4m3fn: 1 sign, 4 exponent, 3 mantissa bits, largest 448, no
+ * infinities), one byte per element, layouts as above; the real value of an
+ * element is its code times the tensor's descale (q_descale, k_descale,
+ * v_descale: finite, > 0).  The result is the forward of those real values:
+ * o (bf16) and lse (float32, natural log of the sum over visible keys of
+ * exp(scale * q_i . k_j) with the real q, k), as fa_fwd_kv computes them.
+ * Both products run on the e4m3 matrix instructions: the scores are exact
+ * products summed in fp32; the weights P (at most 2^8 relative to a row's
+ * reference, see fa_fwd) are rounded to e4m3 for P V, which bounds the error
+ * of O_id by about 2^-4 sum_j P_ij |v_jd| (relative rounding of each weight)
+ * plus 2^-10 sum_j |v_jd| / l_i (weights in e4m3's subnormal range), l_i the
+ * row sum of the weights relative to the row max.
+ *   fa_fwd_fp8_workspace_bytes: bytes of `workspace`, B * Hkv *
+ *       ceil(Tk / 64) * 64 * D (V transposed, tile by tile; 0 for invalid
+ *       shapes).
+ *   fa_fwd_fp8: D must be 64 or 128 (FA_ERR_UNSUPPORTED otherwise, also for
+ *       a descale that is not finite and positive); workspace: device,
+ *       16-byte aligned, contents on return unspecified; other arguments and
+ *       errors as fa_fwd_kv.  It is fa_fp8_transpose_v into `workspace`
+ *       followed by fa_fwd_fp8_vt.
+ *   fa_fp8_transpose_v: writes V (e4m3 codes, [B][Hkv][Tk][D]) transposed
+ *       into vt (fa_fwd_fp8_workspace_bytes bytes, 16-byte aligned): per kv
+ *       head and 64-key tile t, D rows of 64 bytes, byte q of row d holding
+ *       V[64t + 32(q/32) + 8((q%16)/4) + 4((q/16)%2) + q%4][d] (0 past Tk),
+ *       the key order the product of weights and values reads.  Errors:
+ *       FA_ERR_SHAPE (B < 0, Hkv < 1, Tk < 0, sizes past 2^31),
+ *       FA_ERR_UNSUPPORTED (D), FA_ERR_NULL, FA_ERR_ALIGN, FA_ERR_HIP.
+ *   fa_fwd_fp8_vt: the forward with V given as fa_fp8_transpose_v wrote it
+ *       (a caller that keeps V fixed across calls transposes it once).
+ */
+size_t fa_fwd_fp8_workspace_bytes(int B, int Hkv, int Tk, int D);
+fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, float q_descale, float k_descale,
+                     float v_descale, void* o, float* lse, void* workspace, int B, int Hq, int Hkv,
+                     int Tq, int Tk, int D, float scale, int causal, int q_offset, void* stream);
+fa_status fa_fp8_transpose_v(const void* v, void* vt, int B, int Hkv, int Tk, int D, void* stream);
+fa_status fa_fwd_fp8_vt(const void* q, const void* k, const void* vt, float q_descale,
+                        float k_descale, float v_descale, void* o, float* lse, int B, int Hq,
+                        int Hkv, int Tq, int Tk, int D, float scale, int causal, int q_offset,
+                        void* stream);
+
+/*
  * Bytes of device workspace fa_bwd (fa_bwd_kv) needs: one float32 Delta per
  * query row, B * Hq * Tq * 4 rounded up to 256, followed by one region for the
  * partial sums of the split stages, of the larger of fa_bwd_dkdv_split_bytes

@@ -198,3 +198,47 @@ def test_kv_empty_inputs_are_no_ops(lib):
     assert fwd_kv(lib, q=0, k=0, v=0, o=0, lse=0, B=0) == OK
     assert bwd_kv(lib, [0] * 10, Tq=0, Tk=0) == OK
     assert bwd_kv(lib, [0] * 10, B=0) == OK
+
+
+def fwd_fp8(lib, q=A, k=A, v=A, qd=1.0, kd=1.0, vd=1.0, o=A, lse=A, ws=A, B=1, Hq=2, Hkv=1, Tq=64,
+            Tk=64, D=128, scale=0.1, causal=1, off=0):
+    return lib.fa_fwd_fp8(q, k, v, qd, kd, vd, o, lse, ws, B, Hq, Hkv, Tq, Tk, D, scale, causal, off,
+                          None)
+
+
+def test_fp8_validation(lib):
+    assert fwd_fp8(lib, D=96) == UNSUP
+    assert fwd_fp8(lib, D=32) == UNSUP
+    for bad in (0.0, -1.0, float("nan"), float("inf")):
+        assert fwd_fp8(lib, qd=bad) == UNSUP
+        assert fwd_fp8(lib, kd=bad) == UNSUP
+        assert fwd_fp8(lib, vd=bad) == UNSUP
+    assert fwd_fp8(lib, Hq=3, Hkv=2) == SHAPE
+    assert fwd_fp8(lib, off=-1) == SHAPE
+    assert fwd_fp8(lib, Tk=0) == SHAPE
+    for name in ("q", "k", "v", "o", "lse", "ws"):
+        assert fwd_fp8(lib, **{name: 0}) == NULL
+    assert fwd_fp8(lib, q=A + 8) == ALIGN
+    assert fwd_fp8(lib, ws=A + 4) == ALIGN
+    assert fwd_fp8(lib, lse=A + 2) == ALIGN
+    # nothing to compute: no pointer needed
+    assert fwd_fp8(lib, q=0, k=0, v=0, o=0, lse=0, ws=0, Tq=0) == OK
+    assert lib.fa_fp8_transpose_v(A, A, 1, 2, 64, 96, None) == UNSUP
+    assert lib.fa_fp8_transpose_v(A, A, -1, 2, 64, 128, None) == SHAPE
+    assert lib.fa_fp8_transpose_v(0, A, 1, 2, 64, 128, None) == NULL
+    assert lib.fa_fp8_transpose_v(A, A + 8, 1, 2, 64, 128, None) == ALIGN
+    assert lib.fa_fp8_transpose_v(0, 0, 1, 2, 0, 128, None) == OK
+    # fa_fwd_fp8_vt: validation only (a valid call would launch on fake pointers)
+    assert lib.fa_fwd_fp8_vt(A, A, A, 1.0, 1.0, 1.0, A, A, 1, 2, 1, 64, 64, 96, 0.1, 1, 0,
+                             None) == UNSUP
+    assert lib.fa_fwd_fp8_vt(A, A, 0, 1.0, 1.0, 1.0, A, A, 1, 2, 1, 64, 64, 64, 0.1, 1, 0,
+                             None) == NULL
+    assert lib.fa_fwd_fp8_vt(A, A, A, 1.0, 0.0, 1.0, A, A, 1, 2, 1, 64, 64, 64, 0.1, 1, 0,
+                             None) == UNSUP
+
+
+def test_fp8_workspace_bytes(lib):
+    assert lib.fa_fwd_fp8_workspace_bytes(1, 8, 16384, 128) == 8 * 16384 * 128
+    assert lib.fa_fwd_fp8_workspace_bytes(2, 3, 70, 64) == 2 * 3 * 128 * 64
+    assert lib.fa_fwd_fp8_workspace_bytes(1, 1, 70, 96) == 0
+    assert lib.fa_fwd_fp8_workspace_bytes(0, 1, 70, 64) == 0

@@ -25,6 +25,9 @@ Workloads (layout [B, H, T, D], contiguous):
       against cached keys.
   C5-d96  C5's shape with head dimension 96 (scale 1/sqrt(96)); the credited
       FLOP count uses D = 96.
+  C5-fp8  C5's shape in e4m3 (forward only): q, k, v drawn as above in fp32,
+      multiplied by 16 (exact) and rounded to e4m3 (RNE); each has descale
+      1/16, so the real inputs are N(0,1) values on the e4m3 grid.
 """
 from __future__ import annotations
 
@@ -98,7 +101,11 @@ WORKLOADS = {
     "C5-prefill": Workload("C5-prefill", torch.bfloat16, 1, 32, 8, 4096, 128, True,
                            1 / math.sqrt(128), 5700, Tk=16384),
     "C5-d96": Workload("C5-d96", torch.bfloat16, 1, 32, 8, 16384, 96, True, 1 / math.sqrt(96), 5900),
+    "C5-fp8": Workload("C5-fp8", torch.float8_e4m3fn, 1, 32, 8, 16384, 128, True, 1 / math.sqrt(128),
+                       6100, input_scale=16.0, backward=False),
 }
+
+FP8_AMP = 16.0  # fp8 inputs: codes = N(0,1) * FP8_AMP rounded to e4m3; descale 1 / FP8_AMP
 
 
 def make_inputs(B: int, Hq: int, Hkv: int, T: int, D: int, dtype: torch.dtype, seed: int,
@@ -121,6 +128,17 @@ def make_inputs(B: int, Hq: int, Hkv: int, T: int, D: int, dtype: torch.dtype, s
     return out
 
 
+def make_fp8_inputs(B: int, Hq: int, Hkv: int, T: int, D: int, seed: int, Tk: int | None = None,
+                    amp: float = FP8_AMP) -> tuple[dict, float]:
+    """e4m3 codes of q [B,Hq,T,D], k and v [B,Hkv,Tk,D] (CPU, torch.float8_e4m3fn)
+    and their common descale 1/amp: the fp32 draws of make_inputs times amp (a
+    power of two), rounded to nearest even."""
+    x = make_inputs(B, Hq, Hkv, T, D, torch.float32, seed, with_dout=False, Tk=Tk)
+    return {n: (t * amp).to(torch.float8_e4m3fn) for n, t in x.items()}, 1.0 / amp
+
+
 def workload_inputs(w: Workload) -> dict:
+    if w.dtype == torch.float8_e4m3fn:
+        return make_fp8_inputs(w.B, w.Hq, w.Hkv, w.T, w.D, w.seed, Tk=w.Tkv, amp=w.input_scale)[0]
     return make_inputs(w.B, w.Hq, w.Hkv, w.T, w.D, w.dtype, w.seed, w.input_scale, w.backward,
                        Tk=w.Tkv)

@@ -384,7 +384,9 @@ struct DqBf16Cfg {
     static constexpr int NT = 64 * NW;
     static constexpr int BR = 32 * NW;  // query rows per workgroup
     static constexpr int BC = 64;       // keys per tile
-    static constexpr int NSTAGE = 3;
+    // four stages, two tiles in flight: the stage of tile t - 1 stays intact
+    // through tile t, whose first products use its K
+    static constexpr int NSTAGE = 4;
     static constexpr int AHEAD = 2;
     using KT = SwzTile<DT, BC, NT, D>;  // K: read row-wise and transposed
     using Fmt = DmaTile<bf16, DT, BC, NT>;
@@ -395,9 +397,10 @@ struct DqBf16Cfg {
     // the 16-bit immediate of a DS read
     static constexpr int VBASE = NSTAGE * KT::BYTES;
     static constexpr int SMEM = VBASE + NSTAGE * VT::BYTES;
-    static_assert((NSTAGE - 1) * KT::BYTES + BC * Fmt::ROWBYTES < 65536, "LDS immediates");
-    static_assert((NSTAGE - 1) * VT::BYTES + VT::BYTES < 65536, "LDS immediates");
-    static_assert(AHEAD + 1 <= NSTAGE, "a stage is refilled only after its tile was used");
+    // (the last 16-byte read of a region starts 16 bytes before its end)
+    static_assert((NSTAGE - 1) * KT::BYTES + BC * Fmt::ROWBYTES - 16 < 65536, "LDS immediates");
+    static_assert((NSTAGE - 1) * VT::BYTES + VT::BYTES - 16 < 65536, "LDS immediates");
+    static_assert(AHEAD + 2 <= NSTAGE, "a stage is refilled only after the tile after it was used");
 };
 
 template <int D, bool CAUSAL>
@@ -444,7 +447,7 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
     const int nall = (kend + BC - 1) / BC;
     const int j0 = nall * split / S;
     const int nkv = nall * (split + 1) / S - j0;
-    const int npad = (nkv + NSTAGE - 1) / NSTAGE * NSTAGE;  // padded tiles: all masked
+    const int npad = (nkv + NSTAGE - 1) / NSTAGE * NSTAGE;  // loop bound (tiles past nkv are skipped)
     const int nfull = CAUSAL ? min((qw + a.off + 1) / BC, a.Tk / BC) : a.Tk / BC;
 
     const uint32_t lds0 = lds_addr(smem);
@@ -473,7 +476,8 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
         static_assert(AHEAD == 2, "wait counts assume one tile in flight after the awaited one");
     };
 
-    // zero the stages: padded tiles compute on stages no tile has filled
+    // zero the stages: the first tile's carried products read a stage no tile
+    // has filled yet (with zero dS, and 0 * uninitialised LDS could be NaN)
     for (int off = tid * 16; off < Cfg::SMEM; off += Cfg::NT * 16)
         *reinterpret_cast<u32x4*>(smem + off) = u32x4{0, 0, 0, 0};
     sync_lds();
@@ -519,12 +523,27 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
     settle(Dl);
     sync_lds();
 
+    // dS^T of the previous 32-key block, the B operands of its dQ products,
+    // which run interleaved with the next block's vector work (zero before
+    // the first block: the products then add nothing)
+    Frag<bf16> sp[2];
+    sp[0].v = sp[1].v = bf16x8{};
+    // product m of dQ^T += K^T dS^T for the block whose K^T starts at LDS
+    // offset koff: its K^T fragment, and the product with that fragment
+    auto kt_frag = [&](int m, uint32_t koff) __attribute__((always_inline)) {
+        return ktr.read(m % NDB, koff + 16 * (m / NDB) * Fmt::ROWBYTES);
+    };
+    auto dq_product = [&](int m, const bf16x8& kf) __attribute__((always_inline)) {
+        mma(dq[m % NDB], frag(kf), sp[m / NDB]);
+    };
+
     auto body = [&](auto st_tag, int t) {  // chunk tile t = key tile j0 + t
+        if (t >= nkv) return;  // (uniform) past the chunk
         constexpr int ST = decltype(st_tag)::value;
         constexpr uint32_t KI = ST * KT::BYTES, VIM = ST * VT::BYTES;  // this stage's tiles
         if (t + AHEAD < nkv) issue(t + AHEAD, (ST + AHEAD) % NSTAGE);
         const int j = j0 + t;
-        const bool masked = j >= nfull || t >= nkv;  // diagonal, future or padded tile
+        const bool masked = j >= nfull;  // diagonal or future tile
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
             f32x16 s = f32x16{}, dp = f32x16{};
@@ -538,22 +557,36 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int kj = j * BC + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-                    const bool vis = (t < nkv) && kj < a.Tk && (!CAUSAL || kj <= qrow + a.off);
+                    const bool vis = kj < a.Tk && (!CAUSAL || kj <= qrow + a.off);
                     s[r] = vis ? s[r] : -INFINITY;
                 }
             }
+            // the previous block: this tile's block kb - 1, or the last block
+            // of tile t - 1 (stage ST - 1, intact until the next issue)
+            const uint32_t KP = kb > 0 ? KI + (kb - 1) * 32 * Fmt::ROWBYTES
+                                           : ((ST + NSTAGE - 1) % NSTAGE) * KT::BYTES +
+                                                 (NKB - 1) * 32 * Fmt::ROWBYTES;
+            constexpr int NPROD = 2 * NDB;  // dQ products of one block
+            bf16x8 kr[2];                   // K^T fragments, read one product ahead
+            kr[0] = kt_frag(0, KP);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = fast_exp2(fmaf(s[r], a.c, -L2));  // P^T
-                dp[r] = p * (dp[r] - Dl);                         // dS^T
+            for (int m = 0; m < NPROD; ++m) {
+                if (m + 1 < NPROD) kr[(m + 1) % 2] = kt_frag(m + 1, KP);
+                dq_product(m, kr[m % 2]);
+#pragma unroll
+                for (int r = m * 16 / NPROD; r < (m + 1) * 16 / NPROD; ++r) {
+                    const float p = fast_exp2(fmaf(s[r], a.c, -L2));  // P^T
+                    dp[r] = p * (dp[r] - Dl);                         // dS^T
+                    // formed in this group (pure arithmetic would otherwise be
+                    // placed ahead of all the products)
+                    asm volatile("" : "+v"(dp[r]));
+                }
+                // fenced every two products (measured: every product, or no
+                // fence, ran 2-3 % slower)
+                if (m % 2 == 1) __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const Frag<bf16> sf = acc_frag<bf16>(dp, t);
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-                    mma(dq[db], frag(ktr.read(db, KI + (kb * 32 + 16 * t) * Fmt::ROWBYTES)), sf);
-            }
+            for (int t2 = 0; t2 < 2; ++t2) sp[t2] = acc_frag<bf16>(dp, t2);
         }
         wait_tile(t + 1);
         sync_lds();
@@ -561,6 +594,11 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
 
     for (int t = 0; t < npad; t += NSTAGE)
         unroll_stages(body, t, std::make_integer_sequence<int, NSTAGE>{});
+    if (nkv > 0) {  // the last block's dQ products (its stage is still intact)
+        const uint32_t KP = (uint32_t)(((nkv - 1) % NSTAGE) * KT::BYTES + (NKB - 1) * 32 * Fmt::ROWBYTES);
+#pragma unroll
+        for (int m = 0; m < 2 * NDB; ++m) dq_product(m, kt_frag(m, KP));
+    }
 
     if (qrow < a.Tq) {
         if (S == 1) {

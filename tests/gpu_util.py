@@ -19,6 +19,14 @@ import torch
 # (unit roundoff u = 2^-8) bounds the error by u * (M + |ref|), where M is the
 # sum of the absolute values of the element's terms (returned by the oracle).
 # For those cases an element passes if it meets either bound.
+#
+# The backward's Delta_i = sum_d dO_id O_id is formed from the kernel's own bf16
+# O ("L'attention fusionnée", «La passe arrière»), whose rounding moves Delta by
+# up to u * a_i, a_i = sum_d |dO_id O_id|; through dS_ij = P_ij (dP_ij - Delta_i)
+# that reaches dQ_id as scale * sum_j P_ij |k_jd| * u a_i and dK_jd as
+# scale * sum_i P_ij u a_i |q_id|.  Where P is peaked (large scores) those terms
+# are not covered by the term magnitudes above, so the tests that reach such
+# scales add them (delta_terms) to the rounding bound.
 BF16_UNIT_ROUNDOFF = 2.0 ** -8
 BF16_MAX_ABS = 1e-2
 BF16_REL_L2 = 5e-3
@@ -49,9 +57,32 @@ def metrics(got: np.ndarray, ref: np.ndarray):
     return max_abs, rel_l2
 
 
-def assert_close(name: str, got, ref, dtype, mag=None):
+def delta_terms(q, k, do, o, lse, scale, causal, q_offset=None):
+    """The dQ and dK terms through which the rounding of Delta (from the bf16 O)
+    can move the gradients, per element, without the factor u (fp64; q, k, do,
+    o, lse: the oracle's inputs and outputs)."""
+    B, Hq, Tq, D = q.shape
+    Hkv, Tk = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    off = Tk - Tq if q_offset is None else q_offset
+    a = np.abs(do * o).sum(-1)  # [B, Hq, Tq]
+    tq = np.zeros(q.shape)
+    tk = np.zeros(k.shape)
+    for b in range(B):
+        for h in range(Hq):
+            s = scale * q[b, h] @ k[b, h // G].T
+            if causal:
+                s = np.where(np.arange(Tk)[None, :] <= np.arange(Tq)[:, None] + off, s, -np.inf)
+            P = np.exp(s - lse[b, h][:, None])
+            tq[b, h] = scale * a[b, h][:, None] * (P @ np.abs(k[b, h // G]))
+            tk[b, h // G] += scale * (P * a[b, h][:, None]).T @ np.abs(q[b, h])
+    return tq, tk
+
+
+def assert_close(name: str, got, ref, dtype, mag=None, extra=None):
     """Check got against the oracle's ref; `mag` (bf16 only) enables the
-    rounding bound u * (mag + |ref|) as an alternative per-element bound."""
+    rounding bound u * (mag + |ref|) as an alternative per-element bound, to
+    which `extra` (per element, without the factor u) is added."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
@@ -65,8 +96,9 @@ def assert_close(name: str, got, ref, dtype, mag=None):
         assert max_abs <= BF16_MAX_ABS, f"{name}: max-abs {max_abs:.3e} > {BF16_MAX_ABS}"
     else:
         err = np.abs(got - ref)
+        more = 0.0 if extra is None else np.asarray(extra)
         bound = np.maximum(BF16_MAX_ABS * np.maximum(1.0, np.abs(ref)),
-                           BF16_UNIT_ROUNDOFF * (np.asarray(mag) + np.abs(ref)))
+                           BF16_UNIT_ROUNDOFF * (np.asarray(mag) + np.abs(ref) + more))
         worst = float(np.max(err / bound)) if err.size else 0.0
         assert worst <= 1.0, f"{name}: error {worst:.3f}x the per-element bound"
     return max_abs, rel_l2

@@ -82,3 +82,76 @@ def test_sweep_covers_the_intended_space():
     assert any(c[2] != c[3] for c in CASES)          # GQA
     assert any(c[1] == 2 for c in CASES)             # batch 2
     assert any(c[4] == 1 for c in CASES)             # a single query row
+
+
+def draw_typed_cases(n, seed, dims):
+    rng = random.Random(seed)
+    cases = []
+    for i in range(n):
+        D = rng.choice(dims)
+        G = rng.choice([1, 2, 4])
+        Hkv = rng.choice([1, 2])
+        B = rng.choice([1, 2])
+        causal = rng.random() < 0.6
+        Tq = rng.choice([1, 17, 64, 65, 200, 333])
+        if causal:
+            Tk = Tq + rng.choice([0, 5, 64, 150])
+            off = rng.choice([None, max(0, Tk - Tq - rng.randint(0, 30))])
+        else:
+            Tk = rng.choice([3, 64, 129, 300])
+            off = None
+        cases.append((f"{seed}-{i:02d}", B, G * Hkv, Hkv, Tq, Tk, D, causal, off))
+    return cases
+
+
+FP8_CASES = draw_typed_cases(12, 8, [64, 128])
+FP32_CASES = draw_typed_cases(8, 32, [64, 128])
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", FP8_CASES, ids=[c[0] for c in FP8_CASES])
+def test_sweep_fp8_forward(case):
+    """The e4m3 forward over drawn shapes, held to its derived bound."""
+    from tests.test_gpu_fp8 import assert_fp8_close, lse_bound, real, subnormal_term
+    from workloads import make_fp8_inputs
+    import oracle as orc
+
+    name, B, Hq, Hkv, Tq, Tk, D, causal, off = case
+    q_offset = (Tk - Tq) if off is None else off
+    sc = 1 / math.sqrt(D)
+    x, ds = make_fp8_inputs(B, Hq, Hkv, Tq, D, seed=zlib.crc32(name.encode()) % 100000, Tk=Tk)
+    d = {n: t.cuda() for n, t in x.items()}
+    say(f"sweep fp8 {name}: B={B} Hq={Hq} Hkv={Hkv} Tq={Tq} Tk={Tk} D={D} causal={causal} "
+        f"off={q_offset}")
+    o, lse = fa.fwd_fp8(d["q"], d["k"], d["v"], ds, ds, ds, scale=sc, causal=causal,
+                        q_offset=q_offset)
+    torch.cuda.synchronize()
+    q, k, v = (real(x[n], ds) for n in ("q", "k", "v"))
+    ro, rl, om = orc.fwd(q, k, v, sc, causal, return_mag=True, q_offset=q_offset)
+    assert_fp8_close(f"O {name}", f64(o), ro, om, subnormal_term(q, k, v, sc, causal, q_offset))
+    assert (abs(f64(lse) - rl) <= lse_bound(q, k, sc, causal, q_offset)).all()
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", FP32_CASES, ids=[c[0] for c in FP32_CASES])
+def test_sweep_fp32(case):
+    """The fp32 kernels over drawn shapes (max-abs 1e-5)."""
+    name, B, Hq, Hkv, Tq, Tk, D, causal, off = case
+    q_offset = (Tk - Tq) if off is None else off
+    sc = 1 / math.sqrt(D)
+    x = make_inputs(B, Hq, Hkv, Tq, D, torch.float32, seed=zlib.crc32(name.encode()) % 100000, Tk=Tk)
+    d = {n: t.cuda() for n, t in x.items()}
+    say(f"sweep fp32 {name}: B={B} Hq={Hq} Hkv={Hkv} Tq={Tq} Tk={Tk} D={D} causal={causal} "
+        f"off={q_offset}")
+    o, lse = fa.fwd(d["q"], d["k"], d["v"], scale=sc, causal=causal, q_offset=q_offset)
+    dq, dk, dv = fa.bwd(d["q"], d["k"], d["v"], o, d["dout"], lse, scale=sc, causal=causal,
+                        q_offset=q_offset)
+    torch.cuda.synchronize()
+    q, k, v, do = (x[n].double().numpy() for n in ("q", "k", "v", "dout"))
+    ro, rl = oracle.fwd(q, k, v, sc, causal, q_offset=q_offset)
+    rdq, rdk, rdv = oracle.bwd(q, k, v, do, sc, causal, q_offset=q_offset)
+    assert_close(f"O {name}", f64(o), ro, torch.float32)
+    assert_lse_close(f64(lse), rl, torch.float32)
+    assert_close(f"dQ {name}", f64(dq), rdq, torch.float32)
+    assert_close(f"dK {name}", f64(dk), rdk, torch.float32)
+    assert_close(f"dV {name}", f64(dv), rdv, torch.float32)

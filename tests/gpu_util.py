@@ -79,10 +79,12 @@ def delta_terms(q, k, do, o, lse, scale, causal, q_offset=None):
     return tq, tk
 
 
-def assert_close(name: str, got, ref, dtype, mag=None, extra=None):
+def assert_close(name: str, got, ref, dtype, mag=None, extra=None, target_l2=True):
     """Check got against the oracle's ref; `mag` (bf16 only) enables the
     rounding bound u * (mag + |ref|) as an alternative per-element bound, to
-    which `extra` (per element, without the factor u) is added."""
+    which `extra` (per element, without the factor u) is added.  target_l2=False
+    (shapes beyond the benchmark workloads, with `mag`) drops the whole-tensor
+    rel-L2 target and keeps the per-element bounds."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
@@ -91,7 +93,8 @@ def assert_close(name: str, got, ref, dtype, mag=None, extra=None):
     if dtype == torch.float32:
         assert max_abs <= FP32_MAX_ABS, f"{name}: max-abs {max_abs:.3e} > {FP32_MAX_ABS}"
         return max_abs, rel_l2
-    assert rel_l2 <= BF16_REL_L2, f"{name}: rel-L2 {rel_l2:.3e} > {BF16_REL_L2}"
+    assert rel_l2 <= BF16_REL_L2 or (mag is not None and not target_l2), \
+        f"{name}: rel-L2 {rel_l2:.3e} > {BF16_REL_L2}"
     if mag is None:
         assert max_abs <= BF16_MAX_ABS, f"{name}: max-abs {max_abs:.3e} > {BF16_MAX_ABS}"
     else:

@@ -19,7 +19,7 @@ import torch
 import exact_attention_30_amd as fa
 import oracle
 from tests.gpu_util import BF16_MAX_ABS, BF16_REL_L2, assert_close, assert_lse_close, f64, say
-from workloads import WORKLOADS, workload_inputs
+from workloads import WORKLOADS, make_inputs, workload_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -143,3 +143,56 @@ def test_gradient_identities_all_rows(name):
     rel = float((lhs - rhs).norm() / rhs.norm())
     assert rel < 1e-2, rel
     assert torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all()
+
+
+def dq_row_terms(qi, k, v, doi, oi, lse_i, scale):
+    """For one causal query row (keys 0 .. len(k) - 1 visible): the magnitude
+    scale sum_j |dS_ij k_jd| of dQ's terms, and the term through which the
+    rounding of Delta (from the bf16 O) moves it, without the factor u (fp64)."""
+    s = scale * (k @ qi)
+    p = np.exp(s - lse_i)
+    dp = v @ doi
+    ds = p * (dp - p @ dp)
+    mag = scale * np.abs(ds) @ np.abs(k)
+    delta = scale * float(np.abs(doi * oi).sum()) * (p @ np.abs(k))
+    return mag, delta
+
+
+def test_long_sequence_sampled_rows():
+    """One head at T = 100003 (ragged against every tile size, and long enough
+    that a 32-bit product of two positions would overflow): forward and
+    backward in the library's default configuration, sampled query rows (O,
+    lse, dQ) and the last key rows (dK, dV) against the oracle.  dQ rows sum up
+    to 10^5 terms whose dS add to zero; beyond the benchmark workloads they are
+    held to the per-element rounding bound (with the Delta term), not to the
+    whole-tensor rel-L2 target."""
+    B, Hq, Hkv, T, D = 1, 2, 1, 100003, 64
+    scale = 1 / 8
+    x = make_inputs(B, Hq, Hkv, T, D, torch.bfloat16, seed=100003)
+    d = {k: v.cuda() for k, v in x.items()}
+    say(f"long sequence T={T} D={D}")
+    o, lse = fa.fwd(d["q"], d["k"], d["v"], scale=scale, causal=True)
+    dq, dk, dv = fa.bwd(d["q"], d["k"], d["v"], o, d["dout"], lse, scale=scale, causal=True)
+    torch.cuda.synchronize()
+    o, lse, dq, dk, dv = (t.cpu() for t in (o, lse, dq, dk, dv))
+    del d
+    q, k, v, do = (x[n][0].double().numpy() for n in ("q", "k", "v", "dout"))
+    rows = [0, 1, 255, 256, 65535, 65536, 99999, T - 2, T - 1]
+    for h in range(Hq):
+        qh, dh = q[h][None, None], do[h][None, None]
+        kh, vh = k[0][None, None], v[0][None, None]
+        ro, rl = oracle.fwd_rows(qh, kh, vh, [(0, 0, i) for i in rows], scale, True)
+        rdq = oracle.dq_rows(qh, kh, vh, dh, [(0, 0, i) for i in rows], scale, True)
+        assert_close(f"O rows h{h}", o[0, h, rows].double().numpy(), ro, torch.bfloat16)
+        assert_lse_close(lse[0, h, rows].double().numpy(), rl, torch.bfloat16)
+        terms = [dq_row_terms(q[h, i], k[0, : i + 1], v[0, : i + 1], do[h, i], ro[n], rl[n], scale)
+                 for n, i in enumerate(rows)]
+        mag = np.array([t[0] for t in terms])
+        extra = np.array([t[1] for t in terms])
+        assert_close(f"dQ rows h{h}", dq[0, h, rows].double().numpy(), rdq, torch.bfloat16, mag,
+                     extra, target_l2=False)
+    keys = [T - 1, T - 2, T - 33, T - 64, T - 65, T - 200]
+    rk, rv = oracle.dkdv_rows(q[None], k[0][None, None], v[0][None, None], do[None],
+                              [(0, 0, j) for j in keys], scale, True)
+    assert_close("dK rows", dk[0, 0, keys].double().numpy(), rk, torch.bfloat16)
+    assert_close("dV rows", dv[0, 0, keys].double().numpy(), rv, torch.bfloat16)

@@ -10,7 +10,7 @@
 //
 // MI355X mapping.
 //   * Eight waves of 32 query rows, two per SIMD, each running on its own
-//     (one barrier per tile for the shared LDS stages).  A wave computes
+//     (one barrier per two tiles for the shared LDS stages).  A wave computes
 //     S^T = K Q^T with the 32x32x16 bf16 MFMA, so a lane owns one query
 //     column and its row reductions are in-lane plus one exchange with lane
 //     c ^ 32.  The weights are formed from the S^T registers and fed back as
@@ -24,8 +24,10 @@
 //     wave of a SIMD does the MFMAs and the other the vector work).
 //   * K and V tiles move from HBM to LDS by LDS DMA in read order (no bank
 //     conflicts, one address register per operand) into four stage buffers:
-//     stage t = {K_t, V_{t-2}}, all that iteration t reads, issued three
-//     iterations ahead.
+//     stage t = {K_t, V_{t-2}}, all that iteration t reads.  Stages move
+//     in pairs: at every even iteration a wave waits for the two stages it
+//     is about to read, crosses one barrier and issues the next two into
+//     the buffers the previous pair used.
 //   * Lazy rescale: the reference max of a row only moves when the row max
 //     exceeds it by more than 8 (log2 units), so most tiles skip rescaling O
 //     and l; the weights stay below 2^8, and o and l share the reference.
@@ -55,7 +57,7 @@ struct FwdBf16Cfg {
     static constexpr int NT = 64 * NWAVE;
     static constexpr int BR = 32 * NWAVE;    // query rows per workgroup
     static constexpr int BC = 64;            // keys per tile
-    static constexpr int NSTAGE = 4;
+    static constexpr int NSTAGE = 4;         // two pairs: one read, one in flight
     static constexpr int AHD = 4;            // fragment reads in flight ahead of their MFMA
     using KT = RowFragTile<DT, BC, D>;
     using VT = TrFragTile<DT, BC, D>;
@@ -64,6 +66,7 @@ struct FwdBf16Cfg {
     static constexpr int KI = KT::NDMA / NWAVE;  // DMA instructions per wave per tile
     static constexpr int VI = VT::NDMA / NWAVE;
     static_assert(KT::NDMA % NWAVE == 0 && VT::NDMA % NWAVE == 0, "DMA split");
+    static_assert(NSTAGE == 4, "stages move in pairs");
 };
 
 // The reference max of a row moves only when a weight 2^(s c - mref) of the
@@ -153,14 +156,8 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
                 dma_b128(base + (uint32_t)(KT::BYTES + (w + NWAVE * i) * 1024), r, voff[i]);
         }
     };
-    // DMA instructions of stage t issued by this wave
-    auto stage_ops = [&](int t) {
-        return t > nkv + 1 ? 0 : (t < nkv ? KI : 0) + (t >= 2 ? VI : 0);
-    };
-
     load_stage(0);
     load_stage(1);
-    load_stage(2);
 
     // B operand of S^T = K Q^T: this lane's query row, 8 columns per step
     Frag<bf16> qf[NKS];
@@ -241,22 +238,16 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
         constexpr int NPV = HPV ? NKB * 2 * NDB : 0;   // P V products
         constexpr int N = NS + NPV;
 
-        // stage i has landed (this wave's DMA and, after the barrier, every
-        // wave's); every wave has left iteration i - 1, whose buffer takes
-        // stage i + 3
-        const int ahead = stage_ops(i + 1) + stage_ops(i + 2);
-        if (ahead == 2 * (KI + VI))
-            vm_wait<2 * (KI + VI)>();
-        else if (ahead == (KI + VI) + VI)
-            vm_wait<(KI + VI) + VI>();
-        else if (ahead == 2 * VI)
-            vm_wait<2 * VI>();
-        else if (ahead == VI)
-            vm_wait<VI>();
-        else
+        // Stages move in pairs, one barrier per pair: at an even i, stages i
+        // and i + 1 have landed (this wave's DMA and, after the barrier,
+        // every wave's) and every wave has left iterations i - 2 and i - 1,
+        // whose buffers take stages i + 2 and i + 3.
+        if ((i & 1) == 0) {
             vm_wait<0>();
-        sync_lds();
-        load_stage(i + 3);
+            sync_lds();
+            load_stage(i + 2);
+            load_stage(i + 3);
+        }
 
         if constexpr (HW) {
             if (j0 + i - 1 >= nfull) {

@@ -16,9 +16,12 @@
 // LDS, shared by the eight waves; the group sum of dK and dV therefore stays
 // inside the workgroup and no atomics are needed (the result is bitwise
 // reproducible).  Per query tile a wave runs
-//     S = Q_t K^T, dP = dO_t V^T          (16 MFMAs, row reads of Q_t, dO_t, V)
-//     P, mask, dS, bf16 operands          (vector ALU)
-//     dV^T += dO_t^T P, dK^T += Q_t^T dS  (16 MFMAs, transposed reads)
+//     S = Q_t K^T                    (8 MFMAs, row reads of Q_t), then the mask
+//     dP = dO_t V^T  beside  P        (8 MFMAs, row reads of dO_t and V)
+//     dV^T += dO_t^T P  beside  dS    (8 MFMAs, transposed reads)
+//     dK^T += Q_t^T dS                (8 MFMAs, transposed reads)
+// (MFMA counts for head size 128), the vector work of P and dS placed
+// between the products that do not depend on it.
 // The tiles arrive by explicitly scheduled LDS DMA in four stage buffers at
 // the bottom of LDS, computed in pairs with one barrier per pair (the next
 // pair loads into the previous pair's stages); the loop is unrolled over the
@@ -214,10 +217,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
         constexpr uint32_t QI = ST * STAGE, OI = QI + QT::BYTES;  // Q_t, dO_t in the stage
         f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            mma(s, frag(qrd.read(ks, QI)), kf[ks]);
-            mma(dp, frag(qrd.read(ks, OI)), frag(lds_b128(vrd + (uint32_t)VW::frag_off(0, ks))));
-        }
+        for (int ks = 0; ks < NKS; ++ks) mma(s, frag(qrd.read(ks, QI)), kf[ks]);
         // Tiles wholly visible to this wave take no mask code; the others set
         // the invisible scores to -inf, so that P = 0 there.  Lane c's key
         // kw + c is visible to query qb + row iff c <= qb + off - kw + row.
@@ -236,29 +236,72 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
             bh = 0;
             --bti;
         }
-        // rows of this lane's registers: queries 8*(r/4) + 4g + r%4
+        __builtin_amdgcn_sched_barrier(0);
+
+        // The vector work runs between the products that do not need it, in
+        // this wave's own instruction stream: P between the dP products (from
+        // the third on, once S has left the pipe), dS between the dV products.
+        // Each group is fenced and each result pinned where it is formed.
+        // Rows of this lane's registers: queries 8*(r/4) + 4g + r%4.
+        f32x4 L4[4];
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-            const f32x4 L4 = *reinterpret_cast<const f32x4*>(Ls + 8 * rg + 4 * g);
+        for (int rg = 0; rg < 4; ++rg) L4[rg] = *reinterpret_cast<const f32x4*>(Ls + 8 * rg + 4 * g);
+        Frag<bf16> pf0, pf1;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) s[4 * rg + e] = fast_exp2(fmaf(s[4 * rg + e], a.c, -L4[e]));  // P
-        }
+        for (int ks = 0; ks < NKS; ++ks) {
+            mma(dp, frag(qrd.read(ks, OI)), frag(lds_b128(vrd + (uint32_t)VW::frag_off(0, ks))));
+            if (ks >= 2) {
+                constexpr int per = (16 + NKS - 3) / (NKS - 2);
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-            const f32x4 D4 = *reinterpret_cast<const f32x4*>(Ds + 8 * rg + 4 * g);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dp[4 * rg + e] = s[4 * rg + e] * (dp[4 * rg + e] - D4[e]);  // dS
-        }
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const Frag<bf16> pf = acc_frag<bf16>(s, t);
-            const Frag<bf16> sf = acc_frag<bf16>(dp, t);
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                mma(dv[db], frag(trd.read(db, OI + 16 * t * Fmt::ROWBYTES)), pf);
-                mma(dk[db], frag(trd.read(db, QI + 16 * t * Fmt::ROWBYTES)), sf);
+                for (int r = per * (ks - 2); r < per * (ks - 1) && r < 16; ++r) {
+                    float x = fast_exp2(fmaf(s[r], a.c, -L4[r >> 2][r & 3]));  // P
+                    pin(x);
+                    s[r] = x;
+                }
+                if (ks == NKS - 1) {
+                    pf0 = acc_frag<bf16>(s, 0);
+                    pf1 = acc_frag<bf16>(s, 1);
+                    pin(pf0.v);
+                    pin(pf1.v);
+                }
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
+        f32x4 D4[4];
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) D4[rg] = *reinterpret_cast<const f32x4*>(Ds + 8 * rg + 4 * g);
+        Frag<bf16> sf0, sf1;
+        constexpr int NU = 2 * NDB;                    // dV products
+        constexpr int U0 = NU >= 8 ? 2 : 1;            // first one with dS work beside it
+        constexpr int PER = NU >= 8 ? 4 : (16 + NU - U0 - 1) / (NU - U0);
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            const int t = u / NDB, db = u % NDB;
+            mma(dv[db], frag(trd.read(db, OI + 16 * t * Fmt::ROWBYTES)), t ? pf1 : pf0);
+            if (u >= U0) {
+                const int r0 = PER * (u - U0), r1 = min(16, PER * (u - U0 + 1));
+#pragma unroll
+                for (int r = r0; r < r1; ++r) {
+                    float x = s[r] * (dp[r] - D4[r >> 2][r & 3]);  // dS
+                    pin(x);
+                    dp[r] = x;
+                }
+                if (r0 <= 7 && r1 > 7) {
+                    sf0 = acc_frag<bf16>(dp, 0);
+                    pin(sf0.v);
+                }
+                if (r0 < 16 && r1 >= 16) {
+                    sf1 = acc_frag<bf16>(dp, 1);
+                    pin(sf1.v);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+                mma(dk[db], frag(trd.read(db, QI + 16 * t * Fmt::ROWBYTES)), t ? sf1 : sf0);
         // One barrier per pair (measured 1.4 % faster than one per tile: the
         // waves of a SIMD drift out of phase within the pair).  The next
         // pair's tiles must have landed before it; wave 0, which moved their

@@ -225,6 +225,7 @@ namespace fa {
 // matrix instructions in a fixed order.
 __device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void pin(uint32_t& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(bf16x8& x) { asm volatile("" : "+v"(x)); }
 
 // Empty asm that reads a register value loaded from global memory: the
 // compiler's wait for that load is placed before this point.  Called once

@@ -28,9 +28,10 @@
 // stages and the per-lane read addresses carry the LDS base, so every read is
 // one address register plus an immediate offset, with no address arithmetic
 // in the loop.
-// Tiles wholly visible to a wave carry no mask code; the few others (near the
-// diagonal j = i + off of the causal mask, or padding) take a per-element mask
-// in a rarely taken branch.
+// Tiles wholly visible to a wave carry no mask code; the few that straddle the
+// diagonal j = i + off of the causal mask take a per-element mask in a rarely
+// taken branch, and a wave skips the products of the tiles none of its keys
+// sees (and of the padding tiles that round the loop up to whole stages).
 #include <type_traits>
 #include <utility>
 
@@ -101,7 +102,10 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
     const TileId id = map_tile(blockIdx.x, a.B, a.Hq, a.Hkv, S, nkt, false);
     const int b = id.b, hk = id.h / S, split = id.h % S;
     const int key0 = id.tile * BK;
-    const int kw = key0 + 32 * w;  // first key of this wave
+    // first key of this wave.  Waves w and w + 4 share a SIMD; pairing key
+    // blocks r and 7 - r there gives every SIMD the same number of causal
+    // tiles that one of its waves skips (below).
+    const int kw = key0 + 32 * (w < 4 ? w : 11 - w);
     const int krow = kw + c;       // the key this lane owns
 
     const size_t kvoff = (size_t)(b * a.Hkv + hk) * a.Tk * D;
@@ -117,7 +121,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
     const long npair = (long)G * niq;
     const int p0 = (int)(npair * split / S);
     const int n = (int)(npair * (split + 1) / S) - p0;
-    const int npad = (n + NSTAGE - 1) / NSTAGE * NSTAGE;  // padded tiles: all masked
+    const int npad = (n + NSTAGE - 1) / NSTAGE * NSTAGE;  // padded tiles: skipped
 
     const uint32_t lds0 = lds_addr(stages);
     QT qt;
@@ -148,12 +152,6 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
             --dti;
         }
     };
-    // Zero the stages first: the padded tiles at the end compute on stages no
-    // tile has filled, with all-zero (masked) weights, and 0 * (uninitialised
-    // LDS) could be NaN.
-    for (int off = tid * 16; off < NSTAGE * STAGE; off += Cfg::NT * 16)
-        *reinterpret_cast<u32x4*>(stages + off) = u32x4{0, 0, 0, 0};
-    sync_lds();
     {  // this wave's 32 V rows (rows past T read as zeros)
         const int left = a.Tk - kw;
         const i32x4 r = buffer_rsrc(vh + (size_t)kw * D, left > 0 ? left * D * 2 : 0);
@@ -215,93 +213,98 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
         }
 
         constexpr uint32_t QI = ST * STAGE, OI = QI + QT::BYTES;  // Q_t, dO_t in the stage
-        f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) mma(s, frag(qrd.read(ks, QI)), kf[ks]);
-        // Tiles wholly visible to this wave take no mask code; the others set
-        // the invisible scores to -inf, so that P = 0 there.  Lane c's key
-        // kw + c is visible to query qb + row iff c <= qb + off - kw + row.
         const bool pad = i >= n;
         const int qb = bti * BQ;
-        if (pad || (CAUSAL && qb + a.off < kw + 31)) {
-            asm volatile("");  // keep this a branch
-            const int dlt = pad ? -64 : max(qb + a.off - kw, -64);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = 8 * (r >> 2) + 4 * g + (r & 3);
-                s[r] = c <= dlt + row ? s[r] : -INFINITY;
-            }
-        }
         if (++bh == G) {
             bh = 0;
             --bti;
         }
-        __builtin_amdgcn_sched_barrier(0);
+        // A tile that no key of this wave sees (or a padding tile) adds
+        // nothing: the wave skips its products (the other wave of its SIMD
+        // has the matrix pipe to itself meanwhile) but not the barrier below.
+        if (!(pad || (CAUSAL && qb + BQ - 1 + a.off < kw))) {
+            f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) mma(s, frag(qrd.read(ks, QI)), kf[ks]);
+            // Tiles wholly visible to this wave take no mask code; the others set
+            // the invisible scores to -inf, so that P = 0 there.  Lane c's key
+            // kw + c is visible to query qb + row iff c <= qb + off - kw + row.
+            if (CAUSAL && qb + a.off < kw + 31) {
+                asm volatile("");  // keep this a branch
+                const int dlt = max(qb + a.off - kw, -64);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = 8 * (r >> 2) + 4 * g + (r & 3);
+                    s[r] = c <= dlt + row ? s[r] : -INFINITY;
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
 
-        // The vector work runs between the products that do not need it, in
-        // this wave's own instruction stream: P between the dP products (from
-        // the third on, once S has left the pipe), dS between the dV products.
-        // Each group is fenced and each result pinned where it is formed.
-        // Rows of this lane's registers: queries 8*(r/4) + 4g + r%4.
-        f32x4 L4[4];
+            // The vector work runs between the products that do not need it, in
+            // this wave's own instruction stream: P between the dP products (from
+            // the third on, once S has left the pipe), dS between the dV products.
+            // Each group is fenced and each result pinned where it is formed.
+            // Rows of this lane's registers: queries 8*(r/4) + 4g + r%4.
+            f32x4 L4[4];
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) L4[rg] = *reinterpret_cast<const f32x4*>(Ls + 8 * rg + 4 * g);
-        Frag<bf16> pf0, pf1;
+            for (int rg = 0; rg < 4; ++rg) L4[rg] = *reinterpret_cast<const f32x4*>(Ls + 8 * rg + 4 * g);
+            Frag<bf16> pf0, pf1;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            mma(dp, frag(qrd.read(ks, OI)), frag(lds_b128(vrd + (uint32_t)VW::frag_off(0, ks))));
-            if (ks >= 2) {
-                constexpr int per = (16 + NKS - 3) / (NKS - 2);
+            for (int ks = 0; ks < NKS; ++ks) {
+                mma(dp, frag(qrd.read(ks, OI)), frag(lds_b128(vrd + (uint32_t)VW::frag_off(0, ks))));
+                if (ks >= 2) {
+                    constexpr int per = (16 + NKS - 3) / (NKS - 2);
 #pragma unroll
-                for (int r = per * (ks - 2); r < per * (ks - 1) && r < 16; ++r) {
-                    float x = fast_exp2(fmaf(s[r], a.c, -L4[r >> 2][r & 3]));  // P
-                    pin(x);
-                    s[r] = x;
+                    for (int r = per * (ks - 2); r < per * (ks - 1) && r < 16; ++r) {
+                        float x = fast_exp2(fmaf(s[r], a.c, -L4[r >> 2][r & 3]));  // P
+                        pin(x);
+                        s[r] = x;
+                    }
+                    if (ks == NKS - 1) {
+                        pf0 = acc_frag<bf16>(s, 0);
+                        pf1 = acc_frag<bf16>(s, 1);
+                        pin(pf0.v);
+                        pin(pf1.v);
+                    }
                 }
-                if (ks == NKS - 1) {
-                    pf0 = acc_frag<bf16>(s, 0);
-                    pf1 = acc_frag<bf16>(s, 1);
-                    pin(pf0.v);
-                    pin(pf1.v);
-                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        f32x4 D4[4];
+            f32x4 D4[4];
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) D4[rg] = *reinterpret_cast<const f32x4*>(Ds + 8 * rg + 4 * g);
-        Frag<bf16> sf0, sf1;
-        constexpr int NU = 2 * NDB;                    // dV products
-        constexpr int U0 = NU >= 8 ? 2 : 1;            // first one with dS work beside it
-        constexpr int PER = NU >= 8 ? 4 : (16 + NU - U0 - 1) / (NU - U0);
+            for (int rg = 0; rg < 4; ++rg) D4[rg] = *reinterpret_cast<const f32x4*>(Ds + 8 * rg + 4 * g);
+            Frag<bf16> sf0, sf1;
+            constexpr int NU = 2 * NDB;                    // dV products
+            constexpr int U0 = NU >= 8 ? 2 : 1;            // first one with dS work beside it
+            constexpr int PER = NU >= 8 ? 4 : (16 + NU - U0 - 1) / (NU - U0);
 #pragma unroll
-        for (int u = 0; u < NU; ++u) {
-            const int t = u / NDB, db = u % NDB;
-            mma(dv[db], frag(trd.read(db, OI + 16 * t * Fmt::ROWBYTES)), t ? pf1 : pf0);
-            if (u >= U0) {
-                const int r0 = PER * (u - U0), r1 = min(16, PER * (u - U0 + 1));
+            for (int u = 0; u < NU; ++u) {
+                const int t = u / NDB, db = u % NDB;
+                mma(dv[db], frag(trd.read(db, OI + 16 * t * Fmt::ROWBYTES)), t ? pf1 : pf0);
+                if (u >= U0) {
+                    const int r0 = PER * (u - U0), r1 = min(16, PER * (u - U0 + 1));
 #pragma unroll
-                for (int r = r0; r < r1; ++r) {
-                    float x = s[r] * (dp[r] - D4[r >> 2][r & 3]);  // dS
-                    pin(x);
-                    dp[r] = x;
+                    for (int r = r0; r < r1; ++r) {
+                        float x = s[r] * (dp[r] - D4[r >> 2][r & 3]);  // dS
+                        pin(x);
+                        dp[r] = x;
+                    }
+                    if (r0 <= 7 && r1 > 7) {
+                        sf0 = acc_frag<bf16>(dp, 0);
+                        pin(sf0.v);
+                    }
+                    if (r0 < 16 && r1 >= 16) {
+                        sf1 = acc_frag<bf16>(dp, 1);
+                        pin(sf1.v);
+                    }
                 }
-                if (r0 <= 7 && r1 > 7) {
-                    sf0 = acc_frag<bf16>(dp, 0);
-                    pin(sf0.v);
-                }
-                if (r0 < 16 && r1 >= 16) {
-                    sf1 = acc_frag<bf16>(dp, 1);
-                    pin(sf1.v);
-                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    mma(dk[db], frag(trd.read(db, QI + 16 * t * Fmt::ROWBYTES)), t ? sf1 : sf0);
         }
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-                mma(dk[db], frag(trd.read(db, QI + 16 * t * Fmt::ROWBYTES)), t ? sf1 : sf0);
         // One barrier per pair (measured 1.4 % faster than one per tile: the
         // waves of a SIMD drift out of phase within the pair).  The next
         // pair's tiles must have landed before it; wave 0, which moved their

@@ -37,7 +37,8 @@
 //   * Causal: query row i sees key j iff j <= i + off, where off places the
 //     query rows among the keys (0 when both are the same sequence; the
 //     cuTile kernel's input_pos, «Parte 1»).  Key tiles past the workgroup's
-//     last visible key are not visited; tiles wholly visible to a wave run
+//     last visible key are not visited, and a wave skips the products of
+//     those past its own last row's diagonal; tiles wholly visible to a wave run
 //     without mask code; the others take the per-element mask derived from the
 //     lane's query index and the key index ("Optimización de Flash Attention
 //     ...", «Atención causal» and the K-loop split of «La pila de
@@ -103,7 +104,9 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
     const int b = id.b, hq = id.h / S, split = id.h % S;
     const int hk = hq / (a.Hq / a.Hkv);
     const int q0 = id.tile * BR;
-    const int qw = q0 + 32 * w;   // first query of this wave
+    // first query of this wave.  Waves w and w + 4 share a SIMD; pairing row
+    // blocks r and 7 - r there evens out the causal tiles their waves skip.
+    const int qw = q0 + 32 * (w < 4 ? w : 11 - w);
     const int qrow = qw + c;      // the query this lane owns
 
     const bf16* qh = static_cast<const bf16*>(a.q) + (size_t)(b * a.Hq + hq) * a.Tq * D;
@@ -221,9 +224,9 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
         return t;
     };
 
-    // Iteration i (parity P of i): S_i = Q K_i^T into s[P] (HS: i < nkv),
+    // Iteration i (parity P of i): S_i = Q K_i^T into s[P] (HS: i < nkw),
     // O^T += V_{i-2}^T P_{i-2}^T from pf[P] (HPV: i >= 2), and the weights of
-    // tile i - 1 from s[P ^ 1] into pf[P ^ 1] (HW: 1 <= i <= nkv), the three
+    // tile i - 1 from s[P ^ 1] into pf[P ^ 1] (HW: 1 <= i <= nkw), the three
     // interleaved in one instruction stream.  The weights use the current
     // reference; when some weight of a lane may exceed 2^8 (its share of the
     // tile sum does), or a row has no reference yet, the tile takes the
@@ -347,35 +350,52 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
     using T = std::true_type;
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
-    // Iterations 0 and 1 are the same for every nkv (with nkv = 1, the
-    // product S_1 of iteration 1 reads a stage no tile filled and is never
-    // used): no register state then lives across the branch below.
-    iteration(0, P0{}, T{}, F{}, F{});
-    iteration(1, P1{}, T{}, T{}, F{});
-    if (nkv == 1) {
-        iteration(2, P0{}, F{}, F{}, T{});
-    } else {
-        int i = 2;
-        for (; i + 1 < nkv; i += 2) {
-            iteration(i, P0{}, T{}, T{}, T{});
-            iteration(i + 1, P1{}, T{}, T{}, T{});
-        }
-        if (i < nkv) iteration(i++, P0{}, T{}, T{}, T{});
-        // i == nkv.  The last two iterations exist in one parity only: with
-        // nkv odd, S_{nkv-1} and P_{nkv-2} move to the registers that parity
-        // expects (a copy once per workgroup instead of a second version of
-        // the code, across which the compiler spills).
-        if (nkv & 1) {
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                s[1][kb] = s[0][kb];
-#pragma unroll
-                for (int u = 0; u < 2; ++u) pf[0][kb][u] = pf[1][kb][u];
+    // The wave computes the first nkw tiles of the chunk, those that some of
+    // its rows see (causal: the tiles past its last row's diagonal are
+    // skipped; the other wave of its SIMD has the matrix pipe meanwhile), and
+    // then only keeps issuing its share of the workgroup's loads and crossing
+    // the barriers: every wave runs i = 0 .. nkv + 1 in order, each even i
+    // with one barrier.  nkw = 0 only for a chunk none of its rows sees, which
+    // leaves o = 0, l = 0 and no reference, as masking every score would.
+    const int nkw = CAUSAL ? min(nkv, max(0, (qw + 32 + a.off + BC - 1) / BC - j0)) : nkv;
+    if (nkw > 0) {
+        // Iterations 0 and 1 are the same for every nkw (with nkw = 1, the
+        // product S_1 of iteration 1 is never used): no register state then
+        // lives across the branch below.
+        iteration(0, P0{}, T{}, F{}, F{});
+        iteration(1, P1{}, T{}, T{}, F{});
+        if (nkw == 1) {
+            iteration(2, P0{}, F{}, F{}, T{});
+        } else {
+            int i = 2;
+            for (; i + 1 < nkw; i += 2) {
+                iteration(i, P0{}, T{}, T{}, T{});
+                iteration(i + 1, P1{}, T{}, T{}, T{});
             }
+            if (i < nkw) iteration(i++, P0{}, T{}, T{}, T{});
+            // i == nkw.  The last two iterations exist in one parity only:
+            // with nkw odd, S_{nkw-1} and P_{nkw-2} move to the registers that
+            // parity expects (a copy once per wave instead of a second version
+            // of the code, across which the compiler spills).
+            if (nkw & 1) {
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+                    s[1][kb] = s[0][kb];
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) pf[0][kb][u] = pf[1][kb][u];
+                }
+            }
+            iteration(nkw, P0{}, F{}, T{}, T{});
+            iteration(nkw + 1, P1{}, F{}, F{}, T{});
         }
-        iteration(nkv, P0{}, F{}, T{}, T{});
-        iteration(nkv + 1, P1{}, F{}, F{}, T{});
     }
+    for (int i = nkw > 0 ? nkw + 2 : 0; i <= nkv + 1; ++i)
+        if ((i & 1) == 0) {
+            vm_wait<0>();
+            sync_lds();
+            load_stage(i + 2);
+            load_stage(i + 3);
+        }
 
     // epilogue: divide by l, store O (this lane: query qrow, columns
     // 32db + 8rg + 4g + i) and lse

@@ -400,7 +400,7 @@ static hipError_t sum_partials(const float* part, void* out, long plane, int S, 
 // dQ kernel.  One workgroup of eight waves per (batch, query head, block of
 // 256 query rows), two waves per SIMD; wave w owns 32 queries and keeps Q and
 // dO of them in registers.  Key tiles of 64 rows walk past in the forward's
-// order, K and V by LDS DMA two tiles ahead into three stage buffers (K
+// order, K and V by LDS DMA two tiles ahead into four stage buffers (K
 // swizzled, read row-wise and transposed; V in read order; every read one
 // address register plus an immediate offset).  Per
 // 32-key block a wave forms S^T = K Q^T and dP^T = V dO^T with keys as rows,
@@ -463,8 +463,10 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
     const int b = id.b, hq = id.h / S, split = id.h % S;
     const int hk = hq / (a.Hq / a.Hkv);
     const int q0 = id.tile * BR;
-    const int qw = q0 + 32 * w;  // first query of this wave
-    const int qrow = qw + c;     // the query this lane owns
+    // first query of this wave.  Waves w and w + 4 share a SIMD; pairing row
+    // blocks r and 7 - r there evens out the causal tiles their waves skip.
+    const int qw = q0 + 32 * (w < 4 ? w : 11 - w);
+    const int qrow = qw + c;  // the query this lane owns
 
     const size_t qoff = (size_t)(b * a.Hq + hq) * a.Tq * D;
     const size_t kvoff = (size_t)(b * a.Hkv + hk) * a.Tk * D;
@@ -480,6 +482,10 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
     const int nkv = nall * (split + 1) / S - j0;
     const int npad = (nkv + NSTAGE - 1) / NSTAGE * NSTAGE;  // loop bound (tiles past nkv are skipped)
     const int nfull = CAUSAL ? min((qw + a.off + 1) / BC, a.Tk / BC) : a.Tk / BC;
+    // the first nkw tiles of the chunk are those some row of this wave sees;
+    // past them the wave only issues its share of the loads and crosses the
+    // barriers
+    const int nkw = CAUSAL ? min(nkv, max(0, (qw + 32 + a.off + BC - 1) / BC - j0)) : nkv;
 
     const uint32_t lds0 = lds_addr(smem);
     KT kt;
@@ -575,49 +581,58 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
         if (t + AHEAD < nkv) issue(t + AHEAD, (ST + AHEAD) % NSTAGE);
         const int j = j0 + t;
         const bool masked = j >= nfull;  // diagonal or future tile
+        if (t >= nkw) {
+            if (t == nkw && nkw > 0) {  // the dQ products of the wave's last block
+                constexpr uint32_t KP =
+                    ((ST + NSTAGE - 1) % NSTAGE) * KT::BYTES + (NKB - 1) * 32 * Fmt::ROWBYTES;
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                mma(s, frag(krd.read(ks, KI + kb * 32 * Fmt::ROWBYTES)), qf[ks]);
-                mma(dp, frag(lds_b128(vrd + VIM + (uint32_t)VT::frag_off(kb, ks))), of[ks]);
+                for (int m = 0; m < 2 * NDB; ++m) dq_product(m, kt_frag(m, KP));
             }
-            if (masked) {
-                asm volatile("");  // keep this a branch
+        } else {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int kj = j * BC + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-                    const bool vis = kj < a.Tk && (!CAUSAL || kj <= qrow + a.off);
-                    s[r] = vis ? s[r] : -INFINITY;
+            for (int kb = 0; kb < NKB; ++kb) {
+                f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    mma(s, frag(krd.read(ks, KI + kb * 32 * Fmt::ROWBYTES)), qf[ks]);
+                    mma(dp, frag(lds_b128(vrd + VIM + (uint32_t)VT::frag_off(kb, ks))), of[ks]);
                 }
-            }
-            // the previous block: this tile's block kb - 1, or the last block
-            // of tile t - 1 (stage ST - 1, intact until the next issue)
-            const uint32_t KP = kb > 0 ? KI + (kb - 1) * 32 * Fmt::ROWBYTES
-                                           : ((ST + NSTAGE - 1) % NSTAGE) * KT::BYTES +
-                                                 (NKB - 1) * 32 * Fmt::ROWBYTES;
-            constexpr int NPROD = 2 * NDB;  // dQ products of one block
-            bf16x8 kr[2];                   // K^T fragments, read one product ahead
-            kr[0] = kt_frag(0, KP);
+                if (masked) {
+                    asm volatile("");  // keep this a branch
 #pragma unroll
-            for (int m = 0; m < NPROD; ++m) {
-                if (m + 1 < NPROD) kr[(m + 1) % 2] = kt_frag(m + 1, KP);
-                dq_product(m, kr[m % 2]);
-#pragma unroll
-                for (int r = m * 16 / NPROD; r < (m + 1) * 16 / NPROD; ++r) {
-                    const float p = fast_exp2(fmaf(s[r], a.c, -L2));  // P^T
-                    dp[r] = p * (dp[r] - Dl);                         // dS^T
-                    // formed in this group (pure arithmetic would otherwise be
-                    // placed ahead of all the products)
-                    asm volatile("" : "+v"(dp[r]));
+                    for (int r = 0; r < 16; ++r) {
+                        const int kj = j * BC + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+                        const bool vis = kj < a.Tk && (!CAUSAL || kj <= qrow + a.off);
+                        s[r] = vis ? s[r] : -INFINITY;
+                    }
                 }
-                // fenced every two products (measured: every product, or no
-                // fence, ran 2-3 % slower)
-                if (m % 2 == 1) __builtin_amdgcn_sched_barrier(0);
-            }
+                // the previous block: this tile's block kb - 1, or the last block
+                // of tile t - 1 (stage ST - 1, intact until the next issue)
+                const uint32_t KP = kb > 0 ? KI + (kb - 1) * 32 * Fmt::ROWBYTES
+                                               : ((ST + NSTAGE - 1) % NSTAGE) * KT::BYTES +
+                                                     (NKB - 1) * 32 * Fmt::ROWBYTES;
+                constexpr int NPROD = 2 * NDB;  // dQ products of one block
+                bf16x8 kr[2];                   // K^T fragments, read one product ahead
+                kr[0] = kt_frag(0, KP);
 #pragma unroll
-            for (int t2 = 0; t2 < 2; ++t2) sp[t2] = acc_frag<bf16>(dp, t2);
+                for (int m = 0; m < NPROD; ++m) {
+                    if (m + 1 < NPROD) kr[(m + 1) % 2] = kt_frag(m + 1, KP);
+                    dq_product(m, kr[m % 2]);
+#pragma unroll
+                    for (int r = m * 16 / NPROD; r < (m + 1) * 16 / NPROD; ++r) {
+                        const float p = fast_exp2(fmaf(s[r], a.c, -L2));  // P^T
+                        dp[r] = p * (dp[r] - Dl);                         // dS^T
+                        // formed in this group (pure arithmetic would otherwise be
+                        // placed ahead of all the products)
+                        asm volatile("" : "+v"(dp[r]));
+                    }
+                    // fenced every two products (measured: every product, or no
+                    // fence, ran 2-3 % slower)
+                    if (m % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+                }
+#pragma unroll
+                for (int t2 = 0; t2 < 2; ++t2) sp[t2] = acc_frag<bf16>(dp, t2);
+            }
         }
         wait_tile(t + 1);
         sync_lds();
@@ -625,7 +640,7 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
 
     for (int t = 0; t < npad; t += NSTAGE)
         unroll_stages(body, t, std::make_integer_sequence<int, NSTAGE>{});
-    if (nkv > 0) {  // the last block's dQ products (its stage is still intact)
+    if (nkw == nkv && nkv > 0) {  // the last block's dQ products (its stage is still intact)
         const uint32_t KP = (uint32_t)(((nkv - 1) % NSTAGE) * KT::BYTES + (NKB - 1) * 32 * Fmt::ROWBYTES);
 #pragma unroll
         for (int m = 0; m < 2 * NDB; ++m) dq_product(m, kt_frag(m, KP));

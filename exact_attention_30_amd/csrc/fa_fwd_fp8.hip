@@ -33,7 +33,9 @@
 //     16 in bf16; the same software pipeline as the bf16 forward (products
 //     S_i, P_{i-2} V_{i-2} interleaved with the weights of tile i - 1), the
 //     same lazy reference (moved only when a weight could exceed 2^8, so every
-//     weight fits e4m3, whose largest value is 448), masks and causal offset.
+//     weight fits e4m3, whose largest value is 448), masks and causal offset,
+//     stages moving in pairs through four buffers with one barrier per pair,
+//     and causal waves computing only the tiles their rows see.
 #include <type_traits>
 
 #include "fa_device.hpp"
@@ -81,22 +83,6 @@ __device__ __forceinline__ i32x8 join(const bf16x8& lo, const bf16x8& hi)
 {
     const u32x4 l = __builtin_bit_cast(u32x4, lo), h = __builtin_bit_cast(u32x4, hi);
     return i32x8{(int)l[0], (int)l[1], (int)l[2], (int)l[3], (int)h[0], (int)h[1], (int)h[2], (int)h[3]};
-}
-
-// vm_wait for a run-time count of DMA instructions left in flight (0 .. 8)
-__device__ __forceinline__ void vm_wait_upto8(int n)
-{
-    switch (n) {
-    case 8: vm_wait<8>(); break;
-    case 7: vm_wait<7>(); break;
-    case 6: vm_wait<6>(); break;
-    case 5: vm_wait<5>(); break;
-    case 4: vm_wait<4>(); break;
-    case 3: vm_wait<3>(); break;
-    case 2: vm_wait<2>(); break;
-    case 1: vm_wait<1>(); break;
-    default: vm_wait<0>(); break;
-    }
 }
 
 // V^T pre-pass: vt[b][hk][t][d][q] = V[b][hk][64t + vt_key(q)][d] (zero past
@@ -156,7 +142,9 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(FwdArgs a)
     const int b = id.b, hq = id.h;
     const int hk = hq / (a.Hq / a.Hkv);
     const int q0 = id.tile * BR;
-    const int qw = q0 + 32 * w;  // first query of this wave
+    // first query of this wave (row blocks r and 7 - r on one SIMD, as in the
+    // bf16 forward)
+    const int qw = q0 + 32 * (w < 4 ? w : 11 - w);
     const int qrow = qw + c;     // the query this lane owns
     const int ntk = (a.Tk + BC - 1) / BC;
 
@@ -173,8 +161,6 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(FwdArgs a)
     // DMA blocks (1 KiB) of a tile are spread over the waves: block f is
     // issued by wave f % NWAVE
     constexpr int KB = KT::NDMA, VB = VT::NDMA;
-    const int kcnt = w < KB ? (KB - 1 - w) / NWAVE + 1 : 0;
-    const int vcnt = w < VB ? (VB - 1 - w) / NWAVE + 1 : 0;
 
     // Stage t = {K_t (t < nkv), V^T_{t-2} (2 <= t <= nkv + 1)} in buffer
     // t % NSTAGE: everything iteration t reads from LDS.
@@ -192,13 +178,8 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(FwdArgs a)
                 dma_b128(base + (uint32_t)(KT::BYTES + f * 1024), r, VT::dma_off(f, lane));
         }
     };
-    auto stage_ops = [&](int t) {
-        return t > nkv + 1 ? 0 : (t < nkv ? kcnt : 0) + (t >= 2 ? vcnt : 0);
-    };
-
     load_stage(0);
     load_stage(1);
-    load_stage(2);
 
     // B operand of S^T = K Q^T: this lane's query row, columns 64ks + 32h +
     // 16g + i in byte 16h + i (zeros past Tq)
@@ -281,12 +262,13 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(FwdArgs a)
         constexpr int NPV = HPV ? NDB : 0;
         constexpr int N = NS + NPV;
 
-        // stage i has landed (this wave's DMA and, after the barrier, every
-        // wave's); every wave has left iteration i - 1, whose buffer takes
-        // stage i + 3
-        vm_wait_upto8(stage_ops(i + 1) + stage_ops(i + 2));
-        sync_lds();
-        load_stage(i + 3);
+        // stages move in pairs, one barrier per pair (as in the bf16 forward)
+        if ((i & 1) == 0) {
+            vm_wait<0>();
+            sync_lds();
+            load_stage(i + 2);
+            load_stage(i + 3);
+        }
 
         if constexpr (HW) {
             if (i - 1 >= nfull) {
@@ -381,28 +363,39 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(FwdArgs a)
     using T = std::true_type;
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
-    // iterations 0 and 1 are the same for every nkv (with nkv = 1 the
-    // product S_1 reads a stage no tile filled and is never used)
+    // The wave computes the tiles some of its rows see (nkw >= 1: every row
+    // sees key 0), then only issues its share of the loads and crosses the
+    // barriers; every wave runs i = 0 .. nkv + 1 in order (as in the bf16
+    // forward).  Iterations 0 and 1 are the same for every nkw (with nkw = 1
+    // the product S_1 is never used).
+    const int nkw = CAUSAL ? min(nkv, (qw + 32 + a.off + BC - 1) / BC) : nkv;
     iteration(0, P0{}, T{}, F{}, F{});
     iteration(1, P1{}, T{}, T{}, F{});
-    if (nkv == 1) {
+    if (nkw == 1) {
         iteration(2, P0{}, F{}, F{}, T{});
     } else {
         int i = 2;
-        for (; i + 1 < nkv; i += 2) {
+        for (; i + 1 < nkw; i += 2) {
             iteration(i, P0{}, T{}, T{}, T{});
             iteration(i + 1, P1{}, T{}, T{}, T{});
         }
-        if (i < nkv) iteration(i++, P0{}, T{}, T{}, T{});
+        if (i < nkw) iteration(i++, P0{}, T{}, T{}, T{});
         // one parity for the last two iterations (see the bf16 forward)
-        if (nkv & 1) {
+        if (nkw & 1) {
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) s[1][kb] = s[0][kb];
             pf[0] = pf[1];
         }
-        iteration(nkv, P0{}, F{}, T{}, T{});
-        iteration(nkv + 1, P1{}, F{}, F{}, T{});
+        iteration(nkw, P0{}, F{}, T{}, T{});
+        iteration(nkw + 1, P1{}, F{}, F{}, T{});
     }
+    for (int i = nkw + 2; i <= nkv + 1; ++i)
+        if ((i & 1) == 0) {
+            vm_wait<0>();
+            sync_lds();
+            load_stage(i + 2);
+            load_stage(i + 3);
+        }
 
     // epilogue: O = vscale * o / l (bf16; this lane: query qrow, columns
     // 32db + 8rg + 4g + e), lse = ln 2 (mref + log2 l)

@@ -59,7 +59,7 @@ struct FwdBf16Cfg {
     static constexpr int BR = 32 * NWAVE;    // query rows per workgroup
     static constexpr int BC = 64;            // keys per tile
     static constexpr int NSTAGE = 4;         // two pairs: one read, one in flight
-    static constexpr int AHD = 4;            // fragment reads in flight ahead of their MFMA
+    static constexpr int AHD = 3;            // fragment reads in flight ahead of their MFMA
     using KT = RowFragTile<DT, BC, D>;
     using VT = TrFragTile<DT, BC, D>;
     static constexpr int STAGE = KT::BYTES + VT::BYTES;

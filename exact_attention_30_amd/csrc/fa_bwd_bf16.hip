@@ -513,10 +513,11 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
         static_assert(AHEAD == 2, "wait counts assume one tile in flight after the awaited one");
     };
 
-    // zero the stages: the first tile's carried products read a stage no tile
-    // has filled yet (with zero dS, and 0 * uninitialised LDS could be NaN)
-    for (int off = tid * 16; off < Cfg::SMEM; off += Cfg::NT * 16)
-        *reinterpret_cast<u32x4*>(smem + off) = u32x4{0, 0, 0, 0};
+    // zero the K tile of the last stage: the first tile's carried products
+    // read it before any tile has filled it (with zero dS, and 0 * uninitialised
+    // LDS could be NaN); no other read precedes its stage's DMA
+    for (int off = tid * 16; off < KT::BYTES; off += Cfg::NT * 16)
+        *reinterpret_cast<u32x4*>(smem + (NSTAGE - 1) * KT::BYTES + off) = u32x4{0, 0, 0, 0};
     sync_lds();
     for (int t = 0; t < AHEAD && t < nkv; ++t) issue(t, t);
 

@@ -352,12 +352,27 @@ def main():
     fpart = torch.empty(max(fa.fwd_split_bytes(w.B, w.Hq, w.Hkv, w.T, w.Tkv, w.D, w.dtype), 16),
                         dtype=torch.uint8, device=dev)
 
+    # bf16: the backward as fa_bwd runs it (the dQ kernel forms Delta, then
+    # dK/dV); fp32: preprocess, dK/dV, dQ
+    fused = w.dtype == torch.bfloat16
+    names = ["fwd", "dq", "dkdv"] if fused else ["fwd", "pre", "dkdv", "dq"]
+
     def step(ev=None):
         if ev:
             ev[0].record()
         fa.fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse, partial=fpart)
         if ev:
             ev[1].record()
+        if fused:
+            fa.bwd_dq_delta(q, k, v, o, do, lse, scale=w.scale, causal=w.causal, dq=dq, delta=delta,
+                            partial=part)
+            if ev:
+                ev[2].record()
+            fa.bwd_dkdv(q, k, v, do, lse, delta, scale=w.scale, causal=w.causal, dk=dk, dv=dv,
+                        partial=part)
+            if ev:
+                ev[3].record()
+            return
         fa.bwd_preprocess(o, do, delta)
         if ev:
             ev[2].record()
@@ -374,7 +389,8 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] warm-up done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    nev = len(names) + 1
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -383,19 +399,29 @@ def main():
     wall = time.perf_counter() - t0
     print(f"[bench] timed {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
 
-    names = ["fwd", "pre", "dkdv", "dq"]
     per = {n: 0.0 for n in names}
     for ev in events:
         for i, n in enumerate(names):
             per[n] += ev[i].elapsed_time(ev[i + 1])
     per = {n: t / args.steps for n, t in per.items()}
-    gpu_span = events[0][0].elapsed_time(events[-1][4]) / args.steps
+    gpu_span = events[0][0].elapsed_time(events[-1][nev - 1]) / args.steps
     ms_per_step = max(wall * 1e3 / args.steps, gpu_span)
+    bwd_ms = sum(per[n] for n in names if n != "fwd")
+    if fused:
+        # the preprocess kernel on its own, after the timed region (its HBM rate)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        pre_delta = torch.empty_like(delta)
+        fa.bwd_preprocess(o, do, pre_delta)
+        e0.record()
+        for _ in range(20):
+            fa.bwd_preprocess(o, do, pre_delta)
+        e1.record()
+        torch.cuda.synchronize()
+        per["pre"] = e0.elapsed_time(e1) / 20
 
     fwd_flop, bwd_flop = w.fwd_flop, w.bwd_flop
     value = (fwd_flop + bwd_flop) / (ms_per_step * 1e-3) / 1e12
     fwd_tflops = fwd_flop / (per["fwd"] * 1e-3) / 1e12
-    bwd_ms = per["pre"] + per["dkdv"] + per["dq"]
     bwd_tflops = bwd_flop / (bwd_ms * 1e-3) / 1e12
     pre_bytes = 2 * w.B * w.Hq * w.T * w.D * q.element_size() + 4 * w.B * w.Hq * w.T
 
@@ -445,6 +471,8 @@ def main():
             "fwd_tflops": round(fwd_tflops, 2), "fwd_pct_peak": round(100 * fwd_tflops / peak, 2),
             "bwd_tflops": round(bwd_tflops, 2), "bwd_pct_peak": round(100 * bwd_tflops / peak, 2),
             "pre_gbps": round(pre_bytes / (per["pre"] * 1e-3) / 1e9, 1),
+            "bwd_path": ("dQ kernel forms Delta, then dK/dV (as fa_bwd); pre_ms: the preprocess "
+                         "kernel timed on its own" if fused else "preprocess, dK/dV, dQ"),
         },
         "roofline": roofline,
         "cpu_baseline": None,

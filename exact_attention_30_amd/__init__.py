@@ -61,6 +61,8 @@ SIGNATURES = {
     "fa_bwd_dq_split_bytes": ([_i, _i, _i, _i, _i, _i, _i], ctypes.c_size_t),
     "fa_bwd_dq_split": ([_vp, _vp, _vp, _vp, _fp, _fp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i,
                          _i, _i, _vp], ctypes.c_int),
+    "fa_bwd_dq_delta": ([_vp, _vp, _vp, _vp, _vp, _fp, _fp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f,
+                         _i, _i, _i, _vp], ctypes.c_int),
     "fa_fwd_split_bytes": ([_i, _i, _i, _i, _i, _i, _i], ctypes.c_size_t),
     "fa_fwd_split": ([_vp, _vp, _vp, _vp, _fp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _i, _i, _vp],
                      ctypes.c_int),
@@ -337,6 +339,27 @@ def bwd_dkdv(q, k, v, dout, lse, delta, scale=None, causal: bool = True, dk=None
         _check(lib.fa_bwd_dkdv_kv(*ptrs, B, Hq, Hkv, Tq, Tk, D, _scale(scale, D), int(bool(causal)),
                                   off, dt, _stream(q)), "fa_bwd_dkdv_kv")
     return dk, dv
+
+
+def bwd_dq_delta(q, k, v, o, dout, lse, scale=None, causal: bool = True, dq=None, delta=None,
+                 q_offset=None, partial=None):
+    """dQ forming Delta itself (fa_bwd_dq_delta, bf16): returns (dq, delta),
+    delta bitwise as bwd_preprocess would give it, for bwd_dkdv to read."""
+    B, Hq, Hkv, Tq, Tk, D = _dims(q, k, v)
+    dt = _dtype_code(q, k, v, o, dout)
+    off = _offset(Tq, Tk, q_offset)
+    dq = torch.empty_like(q) if dq is None else dq
+    if delta is None:
+        delta = torch.empty(B, Hq, Tq, dtype=torch.float32, device=q.device)
+    need = dq_split_bytes(B, Hq, Hkv, Tq, Tk, D, q.dtype)
+    if partial is not None and partial.numel() * partial.element_size() < need:
+        raise ValueError("partial buffer too small")
+    _check(library().fa_bwd_dq_delta(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                     dout.data_ptr(), lse.data_ptr(), delta.data_ptr(), dq.data_ptr(),
+                                     partial.data_ptr() if partial is not None and need else None,
+                                     B, Hq, Hkv, Tq, Tk, D, _scale(scale, D), int(bool(causal)), off,
+                                     dt, _stream(q)), "fa_bwd_dq_delta")
+    return dq, delta
 
 
 def bwd_dq(q, k, v, dout, lse, delta, scale=None, causal: bool = True, dq=None, q_offset=None,

@@ -70,6 +70,8 @@ void fill_bwd(fa::BwdArgs& a, const void* q, const void* k, const void* v, const
     a.scale = scale;
     a.part = nullptr;
     a.nsplit = 1;
+    a.o = nullptr;
+    a.delta_out = nullptr;
 }
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -363,10 +365,26 @@ fa_status fa_bwd_dkdv_kv(const void* q, const void* k, const void* v, const void
                              scale, causal, q_offset, dt, stream);
 }
 
+// The dQ stage; with o set (bf16), the kernel forms Delta itself and writes
+// it to `delta` instead of reading it.
+static fa_status dq_enqueue(const void* q, const void* k, const void* v, const void* dout,
+                            const float* lse, float* delta, const void* o, void* dq, void* partial,
+                            int B, int Hq, int Hkv, int Tq, int Tk, int D, float scale, int causal,
+                            int q_offset, fa_dtype dt, void* stream);
+
 fa_status fa_bwd_dq_split(const void* q, const void* k, const void* v, const void* dout,
                           const float* lse, const float* delta, void* dq, void* partial, int B,
                           int Hq, int Hkv, int Tq, int Tk, int D, float scale, int causal,
                           int q_offset, fa_dtype dt, void* stream)
+{
+    return dq_enqueue(q, k, v, dout, lse, const_cast<float*>(delta), nullptr, dq, partial, B, Hq,
+                      Hkv, Tq, Tk, D, scale, causal, q_offset, dt, stream);
+}
+
+static fa_status dq_enqueue(const void* q, const void* k, const void* v, const void* dout,
+                            const float* lse, float* delta, const void* o, void* dq, void* partial,
+                            int B, int Hq, int Hkv, int Tq, int Tk, int D, float scale, int causal,
+                            int q_offset, fa_dtype dt, void* stream)
 {
     const int off = causal ? q_offset : 0;
     bool skip = false;
@@ -378,11 +396,31 @@ fa_status fa_bwd_dq_split(const void* q, const void* k, const void* v, const voi
     fa::BwdArgs a;
     fill_bwd(a, q, k, v, dout, lse, delta, B, Hq, Hkv, Tq, Tk, off, scale);
     a.dq = dq;
+    if (o) {
+        a.o = o;
+        a.delta_out = delta;
+    }
     if (partial && dq_split_bytes(B, Hq, Hkv, Tq, Tk, D, dt) > 0) {
         a.part = static_cast<float*>(partial);
         a.nsplit = fa::dq_nsplit(B, Hq, Hkv, Tq, Tk, D);
     }
     return from_hip(fa::launch_bwd_dq(a, D, dtype_code(dt), causal != 0, static_cast<hipStream_t>(stream)));
+}
+
+fa_status fa_bwd_dq_delta(const void* q, const void* k, const void* v, const void* o,
+                          const void* dout, const float* lse, float* delta, void* dq, void* partial,
+                          int B, int Hq, int Hkv, int Tq, int Tk, int D, float scale, int causal,
+                          int q_offset, fa_dtype dt, void* stream)
+{
+    fa_status st = check_kv(B, Hq, Hkv, Tq, Tk, D, dt, causal != 0, causal ? q_offset : 0);
+    if (st != FA_OK) return st;
+    if (dt != FA_BF16) return FA_ERR_UNSUPPORTED;
+    if ((long long)B * Tq * Tk > 0) {
+        if (!o) return FA_ERR_NULL;
+        if (!aligned(o, 16)) return FA_ERR_ALIGN;
+    }
+    return dq_enqueue(q, k, v, dout, lse, delta, o, dq, partial, B, Hq, Hkv, Tq, Tk, D, scale,
+                      causal, q_offset, dt, stream);
 }
 
 fa_status fa_bwd_dq_kv(const void* q, const void* k, const void* v, const void* dout,
@@ -436,6 +474,15 @@ fa_status fa_bwd_kv(const void* q, const void* k, const void* v, const void* o, 
                               align256((size_t)B * (size_t)Hq * (size_t)Tq * sizeof(float))
                         : nullptr;
     if (!workspace) partial = nullptr;
+    if (dt == FA_BF16) {
+        // dQ first: its kernel holds dO of its rows and forms Delta as the
+        // preprocess kernel would (the same bits), for dK/dV to read
+        if (rows && (st = fa_bwd_dq_delta(q, k, v, o, dout, lse, delta, dq, partial, B, Hq, Hkv,
+                                          Tq, Tk, D, scale, causal, q_offset, dt, stream)) != FA_OK)
+            return st;
+        return fa_bwd_dkdv_split(q, k, v, dout, lse, delta, dk, dv, partial, B, Hq, Hkv, Tq, Tk, D,
+                                 scale, causal, q_offset, dt, stream);
+    }
     if (rows && (st = fa_bwd_preprocess(o, dout, delta, B, Hq, Tq, D, dt, stream)) != FA_OK) return st;
     if ((st = fa_bwd_dkdv_split(q, k, v, dout, lse, delta, dk, dv, partial, B, Hq, Hkv, Tq, Tk, D,
                                 scale, causal, q_offset, dt, stream)) != FA_OK)

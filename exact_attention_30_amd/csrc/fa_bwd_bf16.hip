@@ -513,6 +513,14 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
         static_assert(AHEAD == 2, "wait counts assume one tile in flight after the awaited one");
     };
 
+    // O of this lane's row, when the kernel forms Delta (loads issued first,
+    // so their latency passes under the set-up below)
+    Frag<bf16> orow[NKS];
+    if (a.delta_out) {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+            orow[ks] = global_frag<bf16>(static_cast<const bf16*>(a.o) + qoff, qrow, a.Tq, D, 16 * ks + 8 * g);
+    }
     // zero the K tile of the last stage: the first tile's carried products
     // read it before any tile has filled it (with zero dS, and 0 * uninitialised
     // LDS could be NaN); no other read precedes its stage's DMA
@@ -529,10 +537,32 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
         of[ks] = global_frag<bf16>(static_cast<const bf16*>(a.dout) + qoff, qrow, a.Tq, D, 16 * ks + 8 * g);
     }
     float L2 = 0.f, Dl = 0.f;
+    const size_t rix = (size_t)(b * a.Hq + hq) * a.Tq + qrow;  // this lane's row of lse, Delta
     if (qrow < a.Tq) {
-        const size_t r = (size_t)(b * a.Hq + hq) * a.Tq + qrow;
-        L2 = a.lse[r] * kLog2e;
-        Dl = a.delta[r];
+        L2 = a.lse[rix] * kLog2e;
+        if (!a.delta_out) Dl = a.delta[rix];
+    }
+    if (a.delta_out) {
+        // Delta = sum_d dO O of this lane's row, formed here and written for
+        // the dK/dV kernel, in the order of the preprocess kernel, so the
+        // bits are the same: an fma chain over each 8 columns (the lane's
+        // chunks 2ks + g), then chunk pairs from the highest bit of the chunk
+        // index down; g, the lowest, is added last across the lane pair.
+        static_assert((NKS & (NKS - 1)) == 0, "the chunk pairs assume a power of two");
+        float vs[NKS];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            float acc = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc = fmaf((float)orow[ks].v[e], (float)of[ks].v[e], acc);
+            vs[ks] = acc;
+        }
+#pragma unroll
+        for (int bit = NKS / 2; bit >= 1; bit /= 2)
+#pragma unroll
+            for (int ks = 0; ks < bit; ++ks) vs[ks] += vs[ks + bit];
+        Dl = pair_sum(vs[0]);
+        if (qrow < a.Tq && g == 0 && split == 0) a.delta_out[rix] = Dl;
     }
 
     SwzRowFrags<Fmt, Cfg::DT> krd;  // K rows (A of S^T)

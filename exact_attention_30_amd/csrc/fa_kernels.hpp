@@ -48,6 +48,10 @@ struct BwdArgs {
     // writes fp32 partial sums, and a reduction adds them
     float* part;
     int nsplit;
+    // dQ kernel (bf16) only: with delta_out set, it forms Delta of its rows
+    // from o and dout itself, reads no delta and writes Delta to delta_out
+    const void* o;
+    float* delta_out;
 };
 
 struct PreArgs {

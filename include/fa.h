@@ -194,8 +194,10 @@ size_t fa_bwd_kv_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int D, 
  * lse, Delta = rowsum(dout * o) replaces the Jacobian term, and two kernels
  * (one for dK/dV per key tile, one for dQ per query tile walking keys in the
  * forward's order) avoid atomic additions, so results are bitwise
- * reproducible run to run.  Equivalent to fa_bwd_preprocess, fa_bwd_dkdv and
- * fa_bwd_dq enqueued in that order.
+ * reproducible run to run.  The results are bitwise those of
+ * fa_bwd_preprocess, fa_bwd_dkdv and fa_bwd_dq; for bf16 the dQ kernel forms
+ * Delta itself (in the preprocess kernel's order) and runs first, writing
+ * Delta into the workspace for the dK/dV kernel.
  *   q, k, v, o, lse: as produced for/by fa_fwd with the same scale and causal;
  *   dout [B,Hq,T,D] (device, read); dq [B,Hq,T,D], dk/dv [B,Hkv,T,D]
  *   (device, written); workspace: fa_bwd_workspace_bytes(...) bytes of device
@@ -282,6 +284,23 @@ size_t fa_bwd_dq_split_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int D, fa_d
 fa_status fa_bwd_dq_split(const void* q, const void* k, const void* v, const void* dout,
                           const float* lse, const float* delta, void* dq, void* partial, int B,
                           int Hq, int Hkv, int Tq, int Tk, int D, float scale, int causal,
+                          int q_offset, fa_dtype dt, void* stream);
+
+/*
+ * The dQ stage forming Delta itself, as fa_bwd and fa_bwd_kv run it in bf16
+ * (Delta = rowsum(dout * o), "L'attention fusionnée", «La passe arrière»):
+ * the dQ kernel already holds dout of its query rows, also reads o, and
+ * writes Delta in the summation order of the preprocess kernel (bitwise the
+ * output of fa_bwd_preprocess) before using it; run it before the dK/dV
+ * stage, which reads that Delta.  Saves the preprocess launch.
+ *   o [B,Hq,Tq,D] (device, read); delta [B,Hq,Tq] float32 (device,
+ *   written); q, k, v, dout, lse, dq, partial and the sizes as
+ *   fa_bwd_dq_split.  bf16 only: FA_ERR_UNSUPPORTED for fp32; the other
+ *   errors as fa_bwd_dq_split, FA_ERR_NULL / FA_ERR_ALIGN also for o.
+ */
+fa_status fa_bwd_dq_delta(const void* q, const void* k, const void* v, const void* o,
+                          const void* dout, const float* lse, float* delta, void* dq, void* partial,
+                          int B, int Hq, int Hkv, int Tq, int Tk, int D, float scale, int causal,
                           int q_offset, fa_dtype dt, void* stream);
 
 /* Static, human-readable name of a status code. */

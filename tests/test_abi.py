@@ -242,3 +242,20 @@ def test_fp8_workspace_bytes(lib):
     assert lib.fa_fwd_fp8_workspace_bytes(2, 3, 70, 64) == 2 * 3 * 128 * 64
     assert lib.fa_fwd_fp8_workspace_bytes(1, 1, 70, 96) == 0
     assert lib.fa_fwd_fp8_workspace_bytes(0, 1, 70, 64) == 0
+
+
+def test_dq_delta_validation(lib):
+    """fa_bwd_dq_delta: bf16 only, o required and aligned (validation only: a
+    valid call would launch on fake pointers)."""
+    def call(q=A, k=A, v=A, o=A, do=A, lse=A, delta=A, dq=A, Hq=2, Hkv=1, Tq=64, Tk=64, D=64,
+             dt=BF16):
+        return lib.fa_bwd_dq_delta(q, k, v, o, do, lse, delta, dq, None, 1, Hq, Hkv, Tq, Tk, D, 0.1,
+                                   1, 0, dt, None)
+    assert call(dt=FP32) == UNSUP
+    assert call(D=80) == UNSUP
+    assert call(Hq=3, Hkv=2) == SHAPE
+    assert call(o=0) == NULL
+    assert call(delta=0) == NULL
+    assert call(o=A + 8) == ALIGN
+    # no query row: nothing to compute, no query-side pointer needed
+    assert call(q=0, o=0, do=0, lse=0, delta=0, dq=0, Tq=0) == OK

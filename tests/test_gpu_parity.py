@@ -244,15 +244,22 @@ def test_bitwise_deterministic():
         assert torch.equal(a, b)
 
 
-def test_stage_entry_points_equal_fa_bwd():
-    """fa_bwd is preprocess + dK/dV + dQ in that order."""
-    x = to_dev(make_inputs(2, 4, 4, 333, 64, bf16, seed=10))
-    say("stages")
+@pytest.mark.parametrize("shape", [(2, 4, 4, 333, 64), (1, 4, 2, 700, 128), (2, 2, 1, 300, 96),
+                                   (1, 8, 2, 2048, 128)])
+def test_stage_entry_points_equal_fa_bwd(shape):
+    """fa_bwd gives bitwise the results of preprocess + dK/dV + dQ: in bf16
+    its dQ kernel forms Delta itself, in the preprocess kernel's order, and
+    the Delta it leaves in the workspace equals the preprocess output."""
+    B, Hq, Hkv, T, D = shape
+    x = to_dev(make_inputs(B, Hq, Hkv, T, D, bf16, seed=10 + D))
+    say(f"stages B={B} Hq={Hq} Hkv={Hkv} T={T} D={D}")
     o, l = fa.fwd(x["q"], x["k"], x["v"], causal=True)
-    dq, dk, dv = fa.bwd(x["q"], x["k"], x["v"], o, x["dout"], l, causal=True)
+    ws = torch.empty(fa.bwd_workspace_bytes(B, Hq, Hkv, T, D), dtype=torch.uint8, device="cuda")
+    dq, dk, dv = fa.bwd(x["q"], x["k"], x["v"], o, x["dout"], l, causal=True, workspace=ws)
     delta = fa.bwd_preprocess(o, x["dout"])
-    part = torch.empty(max(fa.dkdv_split_bytes(2, 4, 4, 333, 333, 64),
-                           fa.dq_split_bytes(2, 4, 4, 333, 333, 64), 16), dtype=torch.uint8,
+    assert torch.equal(ws[:B * Hq * T * 4].view(torch.float32).view(B, Hq, T), delta)
+    part = torch.empty(max(fa.dkdv_split_bytes(B, Hq, Hkv, T, T, D),
+                           fa.dq_split_bytes(B, Hq, Hkv, T, T, D), 16), dtype=torch.uint8,
                        device="cuda")
     dk2, dv2 = fa.bwd_dkdv(x["q"], x["k"], x["v"], x["dout"], l, delta, causal=True, partial=part)
     dq2 = fa.bwd_dq(x["q"], x["k"], x["v"], x["dout"], l, delta, causal=True, partial=part)

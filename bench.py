@@ -316,7 +316,7 @@ def main():
         gemm_reference()
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: the library runs on one GPU only (asked for --gpus {args.gpus}); "
               "sharding by kv group across GPUs is not built.", file=sys.stderr)
         sys.exit(2)
 

@@ -255,21 +255,27 @@ def cpu_baseline(w, x, target_s: float):
     """Time the oracle's fwd + bwd on a bounded sample of the workload, sized
     to take about target_s seconds: whole kv groups (all their query heads,
     every position) when one head is cheap enough, else a causal prefix of
-    query head 0 and its kv head."""
+    query head 0 and its kv head.  Returns (record, outputs): for whole kv
+    groups, outputs holds the oracle's O, lse, dQ, dK, dV of groups
+    0 .. n-1 of batch 0 (for the parity errors), else None."""
     import oracle
 
     orc = oracle.default()
     G = w.Hq // w.Hkv
+    outputs = None
 
     def run(ngroups, tp):
+        nonlocal outputs
         sl = (slice(0, 1), slice(0, ngroups * G), slice(0, tp))
         kl = (slice(0, 1), slice(0, ngroups), slice(0, tp))
         q, do = x["q"][sl].double().numpy(), x["dout"][sl].double().numpy()
         k, v = x["k"][kl].double().numpy(), x["v"][kl].double().numpy()
         t0 = time.perf_counter()
-        orc.fwd(q, k, v, w.scale, w.causal)
-        orc.bwd(q, k, v, do, w.scale, w.causal)
-        return time.perf_counter() - t0
+        o, lse = orc.fwd(q, k, v, w.scale, w.causal)
+        dq, dk, dv = orc.bwd(q, k, v, do, w.scale, w.causal)
+        elapsed = time.perf_counter() - t0
+        outputs = {"ngroups": ngroups, "o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
+        return elapsed
 
     # calibrate on one query head (one kv head, G = 1 slice) and a short prefix
     def run_head(tp):
@@ -304,7 +310,39 @@ def cpu_baseline(w, x, target_s: float):
         "kind": "oracle",
         "sample": f"fp64 oracle fwd+bwd on {what} ({elapsed:.1f} s)",
         "seconds": round(elapsed, 2),
-    }
+    }, (outputs if tp == w.T else None)
+
+
+def parity_errors(w, gpu: dict, ref: dict) -> dict:
+    """Errors of the GPU outputs of the timed steps against the oracle's on
+    every element of kv groups 0 .. n-1 of batch 0: max-abs (relative above
+    |ref| = 1, as the bf16 target reads it; absolute for fp32) and rel-L2 for
+    O, dQ, dK, dV, max-abs for lse, with the target tolerance."""
+    import numpy as np
+    import torch
+
+    n = ref["ngroups"]
+    G = w.Hq // w.Hkv
+    bf = w.dtype == torch.bfloat16
+    out = {"slice": f"batch 0, kv heads 0-{n - 1}, query heads 0-{n * G - 1}, every position",
+           "tolerance": ("max-abs <= 1e-2 (relative above |ref| = 1) and rel-L2 <= 5e-3; "
+                         "lse max-abs <= 1e-3" if bf else "max-abs <= 1e-5")}
+    ok = True
+    for name, heads in (("o", n * G), ("lse", n * G), ("dq", n * G), ("dk", n), ("dv", n)):
+        got = gpu[name][:1, :heads].double().cpu().numpy()
+        r = ref[name]
+        err = got - r
+        if name == "lse":
+            m = float(np.max(np.abs(err)))
+            out[name] = {"max_abs": m}
+            ok &= m <= (1e-3 if bf else 1e-5)
+            continue
+        m = float(np.max(np.abs(err) / (np.maximum(1.0, np.abs(r)) if bf else 1.0)))
+        rel = float(np.linalg.norm(err) / np.linalg.norm(r))
+        out[name] = {"max_abs": m, "rel_l2": rel}
+        ok &= (m <= 1e-2 and rel <= 5e-3) if bf else m <= 1e-5
+    out["pass"] = bool(ok)
+    return out
 
 
 def main():
@@ -479,7 +517,9 @@ def main():
     }
     if not args.no_cpu_baseline and w.Tkv == w.T:  # the sample takes prefixes of one sequence
         print("[bench] timing the oracle on a bounded sample", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds)
+        out["cpu_baseline"], ref = cpu_baseline(w, x, args.cpu_seconds)
+        if ref is not None:
+            out["parity"] = parity_errors(w, {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}, ref)
     print(json.dumps(out), flush=True)
 
 

@@ -125,6 +125,17 @@ def _dims(q, k, v):
     return B, Hq, Hkv, Tq, Tk, D
 
 
+def _expect(t, shape, name, dtype=None):
+    """Raise ValueError unless tensor t has the given shape (and dtype): the
+    kernels read and write exactly that many elements."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
 def _offset(Tq, Tk, q_offset) -> int:
     return Tk - Tq if q_offset is None else int(q_offset)
 
@@ -141,6 +152,17 @@ def _dtype_code(*ts) -> int:
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
     return _DTYPES[dt]
+
+
+def _same_device(ref, *ts):
+    """Every given tensor is a contiguous tensor on ref's GPU."""
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda or t.device != ref.device:
+            raise ValueError("all tensors must be on the same GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
 
 
 def _scale(scale, D) -> float:
@@ -160,7 +182,10 @@ def fwd(q, k, v, scale=None, causal: bool = True, out=None, lse=None, q_offset=N
     `partial` (a device tensor of at least fwd_split_bytes(...) bytes) calls
     fa_fwd_split, which splits key ranges when the shapes call for it."""
     B, Hq, Hkv, Tq, Tk, D = _dims(q, k, v)
-    dt = _dtype_code(q, k, v)
+    _expect(out, q.shape, "out", q.dtype)
+    _expect(lse, (B, Hq, Tq), "lse", torch.float32)
+    dt = _dtype_code(q, k, v, *(t for t in (out,) if t is not None))
+    _same_device(q, lse, partial)
     off = _offset(Tq, Tk, q_offset)
     o = torch.empty_like(q) if out is None else out
     l = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device) if lse is None else lse
@@ -216,11 +241,17 @@ def fwd_fp8_vt(q, k, vt, v_shape, q_descale, k_descale, v_descale, scale=None,
                causal: bool = True, out=None, lse=None, q_offset=None):
     """fwd_fp8 with V already transposed by fp8_transpose_v (fa_fwd_fp8_vt);
     v_shape is the shape of the V it came from."""
-    _fp8_check(q, k)
     B, Hq, Tq, D = q.shape
     Hkv, Tk = k.shape[1], k.shape[2]
     if tuple(k.shape) != tuple(v_shape) or k.shape[0] != B or k.shape[3] != D:
         raise ValueError("shape mismatch")
+    _expect(out, q.shape, "out", torch.bfloat16)
+    _expect(lse, (B, Hq, Tq), "lse", torch.float32)
+    _fp8_check(q, k)
+    _same_device(q, vt, out, lse)
+    need = fwd_fp8_workspace_bytes(B, Hkv, Tk, D)
+    if vt.numel() * vt.element_size() < need:
+        raise ValueError("vt too small")
     off = _offset(Tq, Tk, q_offset)
     o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device) if out is None else out
     l = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device) if lse is None else lse
@@ -238,7 +269,10 @@ def fwd_fp8(q, k, v, q_descale, k_descale, v_descale, scale=None, causal: bool =
     float32); calls fa_fwd_fp8.  `workspace` (uint8 device tensor of at least
     fwd_fp8_workspace_bytes(...) bytes) is allocated when not given."""
     B, Hq, Hkv, Tq, Tk, D = _dims(q, k, v)
+    _expect(out, q.shape, "out", torch.bfloat16)
+    _expect(lse, (B, Hq, Tq), "lse", torch.float32)
     _fp8_check(q, k, v)
+    _same_device(q, out, lse, workspace)
     off = _offset(Tq, Tk, q_offset)
     o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device) if out is None else out
     l = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device) if lse is None else lse
@@ -279,10 +313,15 @@ def bwd(q, k, v, o, dout, lse, scale=None, causal: bool = True, workspace=None, 
     bwd_workspace_bytes(...) bytes.  Calls fa_bwd when Tq == Tk and the
     offset is 0, else fa_bwd_kv (same q_offset as the forward)."""
     B, Hq, Hkv, Tq, Tk, D = _dims(q, k, v)
-    dt = _dtype_code(q, k, v, o, dout)
+    _expect(o, q.shape, "o")
+    _expect(dout, q.shape, "dout")
+    _expect(lse, (B, Hq, Tq), "lse", torch.float32)
+    if grads is not None:
+        for t, like, name in zip(grads, (q, k, v), ("dq", "dk", "dv")):
+            _expect(t, like.shape, name, q.dtype)
+    dt = _dtype_code(q, k, v, o, dout, *(grads or ()))
+    _same_device(q, lse, workspace)
     off = _offset(Tq, Tk, q_offset)
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Tq):
-        raise ValueError("lse must be float32 [B,Hq,Tq]")
     dq, dk, dv = grads if grads is not None else (torch.empty_like(q), torch.empty_like(k),
                                                   torch.empty_like(v))
     ws_bytes = bwd_workspace_bytes(B, Hq, Hkv, Tq, D, q.dtype, Tk=Tk)
@@ -304,8 +343,13 @@ def bwd(q, k, v, o, dout, lse, scale=None, causal: bool = True, workspace=None, 
 
 def bwd_preprocess(o, dout, delta=None):
     """delta = rowsum(dout * o) as float32 [B, Hq, T]."""
+    if o.dim() != 4:
+        raise ValueError("o must be [B,Hq,T,D]")
     B, Hq, T, D = o.shape
+    _expect(dout, o.shape, "dout")
+    _expect(delta, (B, Hq, T), "delta", torch.float32)
     dt = _dtype_code(o, dout)
+    _same_device(o, delta)
     d = torch.empty((B, Hq, T), dtype=torch.float32, device=o.device) if delta is None else delta
     _check(library().fa_bwd_preprocess(o.data_ptr(), dout.data_ptr(), d.data_ptr(), B, Hq, T, D,
                                        dt, _stream(o)), "fa_bwd_preprocess")
@@ -318,7 +362,13 @@ def bwd_dkdv(q, k, v, dout, lse, delta, scale=None, causal: bool = True, dk=None
     bytes) the query side is split over more workgroups when the shapes call
     for it (fa_bwd_dkdv_split)."""
     B, Hq, Hkv, Tq, Tk, D = _dims(q, k, v)
-    dt = _dtype_code(q, k, v, dout)
+    _expect(dout, q.shape, "dout")
+    _expect(lse, (B, Hq, Tq), "lse", torch.float32)
+    _expect(delta, (B, Hq, Tq), "delta", torch.float32)
+    _expect(dk, k.shape, "dk", k.dtype)
+    _expect(dv, v.shape, "dv", v.dtype)
+    dt = _dtype_code(q, k, v, dout, *(t for t in (dk, dv) if t is not None))
+    _same_device(q, lse, delta, partial)
     off = _offset(Tq, Tk, q_offset)
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
@@ -346,7 +396,13 @@ def bwd_dq_delta(q, k, v, o, dout, lse, scale=None, causal: bool = True, dq=None
     """dQ forming Delta itself (fa_bwd_dq_delta, bf16): returns (dq, delta),
     delta bitwise as bwd_preprocess would give it, for bwd_dkdv to read."""
     B, Hq, Hkv, Tq, Tk, D = _dims(q, k, v)
-    dt = _dtype_code(q, k, v, o, dout)
+    _expect(o, q.shape, "o")
+    _expect(dout, q.shape, "dout")
+    _expect(lse, (B, Hq, Tq), "lse", torch.float32)
+    _expect(delta, (B, Hq, Tq), "delta", torch.float32)
+    _expect(dq, q.shape, "dq", q.dtype)
+    dt = _dtype_code(q, k, v, o, dout, *(t for t in (dq,) if t is not None))
+    _same_device(q, lse, delta, partial)
     off = _offset(Tq, Tk, q_offset)
     dq = torch.empty_like(q) if dq is None else dq
     if delta is None:
@@ -367,7 +423,12 @@ def bwd_dq(q, k, v, dout, lse, delta, scale=None, causal: bool = True, dq=None, 
     """dQ; with `partial` (at least dq_split_bytes(...) bytes) the key range is
     split over more workgroups when the shapes call for it (fa_bwd_dq_split)."""
     B, Hq, Hkv, Tq, Tk, D = _dims(q, k, v)
-    dt = _dtype_code(q, k, v, dout)
+    _expect(dout, q.shape, "dout")
+    _expect(lse, (B, Hq, Tq), "lse", torch.float32)
+    _expect(delta, (B, Hq, Tq), "delta", torch.float32)
+    _expect(dq, q.shape, "dq", q.dtype)
+    dt = _dtype_code(q, k, v, dout, *(t for t in (dq,) if t is not None))
+    _same_device(q, lse, delta, partial)
     off = _offset(Tq, Tk, q_offset)
     dq = torch.empty_like(q) if dq is None else dq
     lib = library()

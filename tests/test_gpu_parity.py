@@ -13,7 +13,9 @@ import torch
 
 import exact_attention_30_amd as fa
 import oracle
-from tests.gpu_util import assert_close, assert_lse_close, f64, say, to_dev
+from tests import lazy_model
+from tests.gpu_util import (assert_close, assert_lse_close, emulated_fwd, emulated_grads, f64, say,
+                            to_dev)
 from workloads import WORKLOADS, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -34,7 +36,13 @@ CASES = {
     "t70_d96_causal": (1, 2, 2, 70, 96, bf16, True, 1 / math.sqrt(96)),
     "t333_d96_full_gqa": (1, 4, 2, 333, 96, bf16, False, 1 / math.sqrt(96)),
     "t1000_d96_causal_gqa4": (1, 4, 1, 1000, 96, bf16, True, 1 / math.sqrt(96)),
+    "t333_d128_causal_gqa3_bhkv8": (2, 12, 4, 333, 128, bf16, True, 1 / math.sqrt(128)),
+    "t700_d64_full_gqa3": (1, 6, 2, 700, 64, bf16, False, 1 / 8),
+    "t300_d128_causal_gqa8": (1, 16, 2, 300, 128, bf16, True, 1 / math.sqrt(128)),
+    "t200_d64_causal_gqa8_bhkv8": (4, 16, 2, 200, 64, bf16, True, 1 / 8),
+    "t1100_d96_causal_gqa8": (1, 8, 1, 1100, 96, bf16, True, 1 / math.sqrt(96)),
     "fp32_t200_d128": (1, 2, 1, 200, 128, fp32, True, 1 / math.sqrt(128)),
+    "fp32_t150_d64_gqa3": (1, 3, 1, 150, 64, fp32, True, 1 / 8),
     "fp32_t70_d64_full": (1, 2, 2, 70, 64, fp32, False, 1 / 8),
 }
 
@@ -49,16 +57,18 @@ def case_inputs(name):
 
 @functools.lru_cache(maxsize=None)
 def reference(name):
-    """Oracle outputs and, for the cases beyond the benchmark workloads, the
-    per-element term magnitudes used by the rounding bound."""
+    """Oracle outputs and, for the bf16 cases beyond the benchmark workloads,
+    the emulation of the method's bf16 roundings (gpu_util)."""
     B, Hq, Hkv, T, D, dt, causal, scale = CASES[name]
     x = case_inputs(name)
     q, k, v, do = (x[n].double().numpy() for n in ("q", "k", "v", "dout"))
-    o, lse, om = oracle.fwd(q, k, v, scale, causal, return_mag=True)
-    dq, dk, dv, mags = oracle.bwd(q, k, v, do, scale, causal, return_mag=True)
-    if name in WORKLOADS:  # the target tolerance alone
-        om, mags = None, (None, None, None)
-    return (o, lse, dq, dk, dv), (om, *mags)
+    o, lse = oracle.fwd(q, k, v, scale, causal)
+    dq, dk, dv = oracle.bwd(q, k, v, do, scale, causal)
+    if name in WORKLOADS or dt == fp32:  # the target tolerance alone
+        return (o, lse, dq, dk, dv), (None, None, None, None)
+    xs = {"q": q, "k": k, "v": v, "dout": do}
+    eo = emulated_fwd(xs, scale, causal)
+    return (o, lse, dq, dk, dv), (eo, *emulated_grads(xs, eo, lse, scale, causal))
 
 
 @pytest.mark.parametrize("name", list(CASES))
@@ -68,8 +78,8 @@ def test_forward_matches_oracle(name):
     say(f"fwd {name} B={B} Hq={Hq} Hkv={Hkv} T={T} D={D} {dt} causal={causal}")
     o, lse = fa.fwd(x["q"], x["k"], x["v"], scale=scale, causal=causal)
     torch.cuda.synchronize()
-    (ro, rlse, *_), (om, *_) = reference(name)
-    assert_close("O", f64(o), ro, dt, om)
+    (ro, rlse, *_), (eo, *_) = reference(name)
+    assert_close("O", f64(o), ro, dt, eo)
     assert_lse_close(f64(lse), rlse, dt)
 
 
@@ -81,10 +91,10 @@ def test_backward_matches_oracle(name):
     o, lse = fa.fwd(x["q"], x["k"], x["v"], scale=scale, causal=causal)
     dq, dk, dv = fa.bwd(x["q"], x["k"], x["v"], o, x["dout"], lse, scale=scale, causal=causal)
     torch.cuda.synchronize()
-    (_, _, rdq, rdk, rdv), (_, mq, mk, mv) = reference(name)
-    assert_close("dQ", f64(dq), rdq, dt, mq)
-    assert_close("dK", f64(dk), rdk, dt, mk)
-    assert_close("dV", f64(dv), rdv, dt, mv)
+    (_, _, rdq, rdk, rdv), (_, eq, ek, ev) = reference(name)
+    assert_close("dQ", f64(dq), rdq, dt, eq)
+    assert_close("dK", f64(dk), rdk, dt, ek)
+    assert_close("dV", f64(dv), rdv, dt, ev)
 
 
 @pytest.mark.parametrize("dt,D", [(bf16, 64), (bf16, 96), (bf16, 128), (fp32, 64), (fp32, 128)])
@@ -189,14 +199,27 @@ def test_rows_of_P_sum_to_one():
 # Invariants of the GPU path
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("causal", [True, False])
-def test_gqa_equals_repeated_kv(causal):
+@pytest.mark.parametrize("causal,G,B,Hkv,T,D", [(True, 4, 1, 2, 400, 128), (False, 4, 1, 2, 400, 128),
+                                                (True, 3, 2, 4, 333, 128), (False, 3, 1, 2, 700, 64),
+                                                (True, 8, 1, 2, 1100, 64), (False, 8, 4, 2, 200, 128)])
+def test_gqa_equals_repeated_kv(causal, G, B, Hkv, T, D):
     """Grouped heads read the same K/V as multi-head attention on K/V repeated
-    along heads: identical O, lse, dQ; dK/dV equal the group sums."""
-    B, Hq, Hkv, T, D = 1, 8, 2, 400, 128
-    x = to_dev(make_inputs(B, Hq, Hkv, T, D, bf16, seed=7))
-    kr = x["k"].repeat_interleave(4, 1).contiguous()
-    vr = x["v"].repeat_interleave(4, 1).contiguous()
+    along heads: identical O, lse, dQ; dK/dV equal the group sums.  Group
+    sizes 3, 4 and 8, with B*Hkv a multiple of 8 and not; the forward both
+    unsplit and split (where the shapes split)."""
+    Hq = G * Hkv
+    x = to_dev(make_inputs(B, Hq, Hkv, T, D, bf16, seed=7 + G))
+    kr = x["k"].repeat_interleave(G, 1).contiguous()
+    vr = x["v"].repeat_interleave(G, 1).contiguous()
+    nbytes = fa.fwd_split_bytes(B, Hq, Hkv, T, T, D)
+    if nbytes:
+        part = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        say(f"gqa split forward G={G} causal={causal}")
+        o1, l1 = fa.fwd(x["q"], x["k"], x["v"], causal=causal, partial=part)
+        o2, l2 = fa.fwd(x["q"], kr, vr, causal=causal,
+                        partial=torch.empty(fa.fwd_split_bytes(B, Hq, Hq, T, T, D), dtype=torch.uint8,
+                                            device="cuda"))
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
     say(f"gqa vs mha causal={causal}")
     o1, l1 = fa.fwd(x["q"], x["k"], x["v"], causal=causal)
     o2, l2 = fa.fwd(x["q"], kr, vr, causal=causal)
@@ -207,7 +230,7 @@ def test_gqa_equals_repeated_kv(causal):
     for a, b in ((g1[1], g2[1]), (g1[2], g2[2])):
         # GQA sums the group in fp32 and rounds once; the reference rounds
         # each head to bf16 before summing
-        ref = b.double().reshape(B, Hkv, 4, T, D).sum(2)
+        ref = b.double().reshape(B, Hkv, G, T, D).sum(2)
         err = (a.double() - ref).abs().max().item()
         assert err <= 1e-2 * max(1.0, ref.abs().max().item())
 
@@ -244,25 +267,36 @@ def test_bitwise_deterministic():
         assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("shape", [(2, 4, 4, 333, 64), (1, 4, 2, 700, 128), (2, 2, 1, 300, 96),
-                                   (1, 8, 2, 2048, 128)])
+@pytest.mark.parametrize("shape", [(2, 4, 4, 333, 333, 64, True, None),
+                                   (1, 4, 2, 700, 700, 128, True, None),
+                                   (2, 2, 1, 300, 300, 96, True, None),
+                                   (1, 8, 2, 2048, 2048, 128, True, None),
+                                   (1, 4, 2, 700, 700, 128, False, None),
+                                   (1, 2, 1, 1500, 1500, 64, False, None),
+                                   (1, 4, 2, 300, 900, 128, True, 250),
+                                   (1, 2, 1, 1000, 2500, 64, True, None),
+                                   (1, 4, 1, 257, 513, 128, False, None)])
 def test_stage_entry_points_equal_fa_bwd(shape):
-    """fa_bwd gives bitwise the results of preprocess + dK/dV + dQ: in bf16
-    its dQ kernel forms Delta itself, in the preprocess kernel's order, and
-    the Delta it leaves in the workspace equals the preprocess output."""
-    B, Hq, Hkv, T, D = shape
-    x = to_dev(make_inputs(B, Hq, Hkv, T, D, bf16, seed=10 + D))
-    say(f"stages B={B} Hq={Hq} Hkv={Hkv} T={T} D={D}")
-    o, l = fa.fwd(x["q"], x["k"], x["v"], causal=True)
-    ws = torch.empty(fa.bwd_workspace_bytes(B, Hq, Hkv, T, D), dtype=torch.uint8, device="cuda")
-    dq, dk, dv = fa.bwd(x["q"], x["k"], x["v"], o, x["dout"], l, causal=True, workspace=ws)
+    """fa_bwd (fa_bwd_kv for Tq != Tk or an offset) gives bitwise the results
+    of preprocess + dK/dV + dQ: in bf16 its dQ kernel forms Delta itself, in
+    the preprocess kernel's order, and the Delta it leaves in the workspace
+    equals the preprocess output.  Causal and not, Tq != Tk with and without
+    an offset off the tile grid, and shapes whose stages split."""
+    B, Hq, Hkv, Tq, Tk, D, causal, off = shape
+    x = to_dev(make_inputs(B, Hq, Hkv, Tq, D, bf16, seed=10 + D + Tk, Tk=Tk))
+    say(f"stages B={B} Hq={Hq} Hkv={Hkv} Tq={Tq} Tk={Tk} D={D} causal={causal} off={off}")
+    kw = dict(causal=causal, q_offset=off)
+    o, l = fa.fwd(x["q"], x["k"], x["v"], **kw)
+    ws = torch.empty(fa.bwd_workspace_bytes(B, Hq, Hkv, Tq, D, Tk=Tk), dtype=torch.uint8,
+                     device="cuda")
+    dq, dk, dv = fa.bwd(x["q"], x["k"], x["v"], o, x["dout"], l, workspace=ws, **kw)
     delta = fa.bwd_preprocess(o, x["dout"])
-    assert torch.equal(ws[:B * Hq * T * 4].view(torch.float32).view(B, Hq, T), delta)
-    part = torch.empty(max(fa.dkdv_split_bytes(B, Hq, Hkv, T, T, D),
-                           fa.dq_split_bytes(B, Hq, Hkv, T, T, D), 16), dtype=torch.uint8,
+    assert torch.equal(ws[:B * Hq * Tq * 4].view(torch.float32).view(B, Hq, Tq), delta)
+    part = torch.empty(max(fa.dkdv_split_bytes(B, Hq, Hkv, Tq, Tk, D),
+                           fa.dq_split_bytes(B, Hq, Hkv, Tq, Tk, D), 16), dtype=torch.uint8,
                        device="cuda")
-    dk2, dv2 = fa.bwd_dkdv(x["q"], x["k"], x["v"], x["dout"], l, delta, causal=True, partial=part)
-    dq2 = fa.bwd_dq(x["q"], x["k"], x["v"], x["dout"], l, delta, causal=True, partial=part)
+    dk2, dv2 = fa.bwd_dkdv(x["q"], x["k"], x["v"], x["dout"], l, delta, partial=part, **kw)
+    dq2 = fa.bwd_dq(x["q"], x["k"], x["v"], x["dout"], l, delta, partial=part, **kw)
     assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
 
 
@@ -292,9 +326,13 @@ def test_split_dkdv(shape):
         # the two fp32 sums differ in order only: at most one bf16 step apart
         assert np.all(np.abs(a - b) <= 2.0 ** -7 * np.maximum(np.abs(b), 1e-30) + 1e-6)
     q, k, v, do = (x[n].double().cpu().numpy() for n in ("q", "k", "v", "dout"))
-    _, rdk, rdv, mags = oracle.bwd(q, k, v, do, 1 / math.sqrt(D), True, return_mag=True)
-    assert_close("dK split", f64(dk1), rdk, bf16, mags[1])
-    assert_close("dV split", f64(dv1), rdv, bf16, mags[2])
+    sc = 1 / math.sqrt(D)
+    ro, rl = oracle.fwd(q, k, v, sc, True)
+    _, rdk, rdv = oracle.bwd(q, k, v, do, sc, True)
+    xs = {"q": q, "k": k, "v": v, "dout": do}
+    _, ek, ev = emulated_grads(xs, emulated_fwd(xs, sc, True), rl, sc, True)
+    assert_close("dK split", f64(dk1), rdk, bf16, ek)
+    assert_close("dV split", f64(dv1), rdv, bf16, ev)
 
 
 def test_no_device_allocation_by_the_library():
@@ -344,8 +382,12 @@ def test_split_dq(shape):
     a, b = f64(dq1), f64(dq0)
     assert np.all(np.abs(a - b) <= 2.0 ** -7 * np.abs(b) + 1e-6)
     q, k, v, do = (x[n].double().cpu().numpy() for n in ("q", "k", "v", "dout"))
-    rdq, _, _, mags = oracle.bwd(q, k, v, do, 1 / math.sqrt(D), True, return_mag=True)
-    assert_close("dQ split", a, rdq, bf16, mags[0])
+    sc = 1 / math.sqrt(D)
+    ro, rl = oracle.fwd(q, k, v, sc, True)
+    rdq, _, _ = oracle.bwd(q, k, v, do, sc, True)
+    xs = {"q": q, "k": k, "v": v, "dout": do}
+    eq, _, _ = emulated_grads(xs, emulated_fwd(xs, sc, True), rl, sc, True)
+    assert_close("dQ split", a, rdq, bf16, eq)
 
 
 @pytest.mark.parametrize("shape", [(1, 1, 1, 2048, 2048, 128), (1, 4, 2, 700, 700, 64),
@@ -371,6 +413,8 @@ def test_split_forward(shape):
     a, b = f64(o1), f64(o0)
     assert np.all(np.abs(a - b) <= 2.0 ** -7 * np.abs(b) + 1e-3)
     q, k, v = (x[n].double().cpu().numpy() for n in ("q", "k", "v"))
-    ro, rl, om = oracle.fwd(q, k, v, 1 / math.sqrt(D), True, return_mag=True)
-    assert_close("O split", a, ro, bf16, om)
+    ro, rl = oracle.fwd(q, k, v, 1 / math.sqrt(D), True)
+    eo = emulated_fwd({"q": q, "k": k, "v": v}, 1 / math.sqrt(D), True, Tk - Tq,
+                      S=lazy_model.nsplit(B, Hq, Tq, Tk))
+    assert_close("O split", a, ro, bf16, eo)
     assert_lse_close(f64(l1), rl, bf16)

@@ -25,13 +25,15 @@ import os
 
 import torch
 
-__all__ = ["fwd", "bwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "bwd_workspace_bytes",
+__all__ = ["fwd", "bwd", "bwd_noalloc", "NOALLOC_SCRATCH_BYTES", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "bwd_workspace_bytes",
            "dkdv_split_bytes", "dq_split_bytes", "fwd_split_bytes", "FAError", "library",
            "LIB_PATH", "version"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 FA_BF16, FA_FP32 = 0, 1
+# FA_NOALLOC_SCRATCH_BYTES of include/fa.h: the static scratch of fa_bwd_noalloc
+NOALLOC_SCRATCH_BYTES = 64 << 20
 _DTYPES = {torch.bfloat16: FA_BF16, torch.float32: FA_FP32}
 
 # names and argument lists of every entry point in include/fa.h
@@ -72,6 +74,8 @@ SIGNATURES = {
     "fa_fp8_transpose_v": ([_vp, _vp, _i, _i, _i, _i, _vp], ctypes.c_int),
     "fa_fwd_fp8_vt": ([_vp, _vp, _vp, _f, _f, _f, _vp, _fp, _i, _i, _i, _i, _i, _i, _f, _i, _i,
                        _vp], ctypes.c_int),
+    "fa_bwd_noalloc": ([_vp, _vp, _vp, _vp, _vp, _fp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i,
+                        _i, _i, _vp], ctypes.c_int),
     "fa_status_string": ([_i], ctypes.c_char_p),
     "fa_version": ([], ctypes.c_char_p),
 }
@@ -338,6 +342,33 @@ def bwd(q, k, v, o, dout, lse, scale=None, causal: bool = True, workspace=None, 
     else:
         _check(lib.fa_bwd_kv(*ptrs, B, Hq, Hkv, Tq, Tk, D, _scale(scale, D), int(bool(causal)), off,
                              dt, _stream(q)), "fa_bwd_kv")
+    return dq, dk, dv
+
+
+def bwd_noalloc(q, k, v, o, dout, lse, scale=None, causal: bool = True, grads=None,
+                q_offset=None):
+    """bwd through fa_bwd_noalloc: the library takes its workspace from a
+    static per-GPU scratch instead of a buffer (raises FAError with status
+    FA_ERR_SCRATCH = 6 for shapes whose workspace exceeds
+    NOALLOC_SCRATCH_BYTES).  Allocates nothing when `grads` = (dq, dk, dv) is
+    given.  Calls on one GPU share the scratch: overlapping calls race."""
+    B, Hq, Hkv, Tq, Tk, D = _dims(q, k, v)
+    _expect(o, q.shape, "o")
+    _expect(dout, q.shape, "dout")
+    _expect(lse, (B, Hq, Tq), "lse", torch.float32)
+    if grads is not None:
+        for t, like, name in zip(grads, (q, k, v), ("dq", "dk", "dv")):
+            _expect(t, like.shape, name, q.dtype)
+    dt = _dtype_code(q, k, v, o, dout, *(grads or ()))
+    _same_device(q, lse)
+    off = _offset(Tq, Tk, q_offset)
+    dq, dk, dv = grads if grads is not None else (torch.empty_like(q), torch.empty_like(k),
+                                                  torch.empty_like(v))
+    with torch.cuda.device(q.device):  # the library uses the current device's scratch
+        _check(library().fa_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                        dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                        dv.data_ptr(), B, Hq, Hkv, Tq, Tk, D, _scale(scale, D),
+                                        int(bool(causal)), off, dt, _stream(q)), "fa_bwd_noalloc")
     return dq, dk, dv
 
 

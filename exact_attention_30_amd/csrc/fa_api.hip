@@ -4,8 +4,15 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/fa.h"
 #include "fa_kernels.hpp"
+
+// Workspace of fa_bwd_noalloc: one copy on every GPU the library runs on.  In
+// host code this name is only a handle for hipGetSymbolAddress; kernels get
+// the device address it returns.
+static __device__ __align__(256) unsigned char scratch[FA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -105,6 +112,30 @@ size_t shared_split_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int D, fa_dtyp
 
 }  // namespace
 
+namespace {
+
+// Device address of `scratch` on each device, looked up once per device with
+// that device current.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch[kMaxDevices] = {};
+
+fa_status scratch_address(void** out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FA_ERR_HIP;
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return FA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* fa_version(void) { return "0.3.0"; }
@@ -118,6 +149,7 @@ const char* fa_status_string(fa_status s)
     case FA_ERR_UNSUPPORTED: return "unsupported head dimension, dtype or scale";
     case FA_ERR_ALIGN: return "misaligned pointer";
     case FA_ERR_HIP: return "HIP runtime error";
+    case FA_ERR_SCRATCH: return "workspace larger than the static scratch of fa_bwd_noalloc";
     }
     return "unknown status";
 }
@@ -489,6 +521,22 @@ fa_status fa_bwd_kv(const void* q, const void* k, const void* v, const void* o, 
         return st;
     return fa_bwd_dq_split(q, k, v, dout, lse, delta, dq, partial, B, Hq, Hkv, Tq, Tk, D, scale,
                            causal, q_offset, dt, stream);
+}
+
+fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                         int Hq, int Hkv, int Tq, int Tk, int D, float scale, int causal,
+                         int q_offset, fa_dtype dt, void* stream)
+{
+    fa_status st = check_kv(B, Hq, Hkv, Tq, Tk, D, dt, causal != 0, causal ? q_offset : 0);
+    if (st != FA_OK) return st;
+    if ((st = check_scale(scale)) != FA_OK) return st;
+    if (fa_bwd_kv_workspace_bytes(B, Hq, Hkv, Tq, Tk, D, dt) > FA_NOALLOC_SCRATCH_BYTES)
+        return FA_ERR_SCRATCH;
+    void* ws = nullptr;
+    if ((long long)B * Tq * Tk > 0 && (st = scratch_address(&ws)) != FA_OK) return st;
+    return fa_bwd_kv(q, k, v, o, dout, lse, dq, dk, dv, ws, B, Hq, Hkv, Tq, Tk, D, scale, causal,
+                     q_offset, dt, stream);
 }
 
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,

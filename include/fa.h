@@ -85,7 +85,8 @@ typedef enum {
     FA_ERR_SHAPE = 2,
     FA_ERR_UNSUPPORTED = 3,
     FA_ERR_ALIGN = 4,
-    FA_ERR_HIP = 5
+    FA_ERR_HIP = 5,
+    FA_ERR_SCRATCH = 6 /* fa_bwd_noalloc: the shapes need more than its static scratch */
 } fa_status;
 
 /*
@@ -302,6 +303,36 @@ fa_status fa_bwd_dq_delta(const void* q, const void* k, const void* v, const voi
                           const void* dout, const float* lse, float* delta, void* dq, void* partial,
                           int B, int Hq, int Hkv, int Tq, int Tk, int D, float scale, int causal,
                           int q_offset, fa_dtype dt, void* stream);
+
+/*
+ * Size of the static scratch of fa_bwd_noalloc, per GPU: 64 MiB.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * fa_bwd_kv for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same kernels, with the workspace taken from a static device array of the
+ * library (FA_NOALLOC_SCRATCH_BYTES, one copy on every GPU the library runs
+ * on, held until the process ends) instead of a caller buffer.  The call
+ * allocates nothing and calls no allocating routine.
+ *   Arguments, layouts, results and errors: as fa_bwd_kv without `workspace`
+ *   (the results are bitwise those of fa_bwd_kv), plus FA_ERR_SCRATCH when
+ *   fa_bwd_kv_workspace_bytes(...) of these shapes exceeds
+ *   FA_NOALLOC_SCRATCH_BYTES (checked after the shape and dtype checks,
+ *   before anything is enqueued).  `stream` must belong to the current
+ *   device: the scratch used is the current device's, whose address the
+ *   first call on each device looks up (FA_ERR_HIP if that fails).
+ *   Every call on one GPU shares that GPU's scratch and leaves its own
+ *   contents there; nothing in it needs clearing between calls (Delta and
+ *   every partial sum are written before they are read).  Calls that overlap
+ *   on one GPU (different streams, or host threads) race on the scratch: run
+ *   them on one stream, one after the other.
+ */
+fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                         int Hq, int Hkv, int Tq, int Tk, int D, float scale, int causal,
+                         int q_offset, fa_dtype dt, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* fa_status_string(fa_status s);

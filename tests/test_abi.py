@@ -12,7 +12,7 @@ import exact_attention_30_amd as fa
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa.h")
 
-OK, NULL, SHAPE, UNSUP, ALIGN, HIP = range(6)
+OK, NULL, SHAPE, UNSUP, ALIGN, HIP, SCRATCH = range(7)
 BF16, FP32 = 0, 1
 
 
@@ -43,7 +43,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_status_strings(lib):
-    for s in range(6):
+    for s in range(7):
         assert lib.fa_status_string(s)
     assert lib.fa_version().decode().count(".") == 2
 
@@ -259,3 +259,29 @@ def test_dq_delta_validation(lib):
     assert call(o=A + 8) == ALIGN
     # no query row: nothing to compute, no query-side pointer needed
     assert call(q=0, o=0, do=0, lse=0, delta=0, dq=0, Tq=0) == OK
+
+
+def test_noalloc_scratch_size_matches_the_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define FA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == fa.NOALLOC_SCRATCH_BYTES
+
+
+def noalloc(lib, B=1, Hq=4, Hkv=1, Tq=16384, Tk=16384, D=128, scale=0.1, causal=1, off=0,
+            dt=BF16):
+    return lib.fa_bwd_noalloc(*[A] * 9, B, Hq, Hkv, Tq, Tk, D, scale, causal, off, dt, None)
+
+
+def test_noalloc_rejects_on_the_host(lib):
+    """Shape and dtype errors come first, then the scratch limit; nothing is
+    enqueued (these calls never reach the HIP runtime)."""
+    assert noalloc(lib, Hq=5, Hkv=2) == SHAPE
+    assert noalloc(lib, D=96, dt=FP32) == UNSUP
+    assert noalloc(lib, scale=0.0) == UNSUP
+    # one kv group at T = 16384 (its dK/dV stage splits: 2 x 8 chunks x 8 MiB
+    # of fp32 partial sums, past the 64 MiB scratch)
+    need = lib.fa_bwd_kv_workspace_bytes(1, 4, 1, 16384, 16384, 128, BF16)
+    assert need > fa.NOALLOC_SCRATCH_BYTES
+    assert noalloc(lib) == SCRATCH
+    # Delta alone: 8 x 32 x 131072 rows x 4 bytes = 128 MiB
+    assert noalloc(lib, B=8, Hq=32, Hkv=8, Tq=131072, Tk=131072) == SCRATCH

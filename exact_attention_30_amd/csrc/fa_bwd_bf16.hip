@@ -184,12 +184,13 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
 #pragma unroll
     for (int db = 0; db < NDB; ++db) dk[db] = dv[db] = f32x16{};
 
-    // L of the tile in stage st (natural log) -> L * log2(e), in place, by
-    // wave 0, whose own DMA moved it
+    // The stats of the tile in stage st, in place, by the wave whose own DMA
+    // moved them: L (natural log) -> -L*log2(e)/c (wave 0) and Delta ->
+    // -Delta (wave 1), the initial values of the S and dP accumulators.
     auto convert_l = [&](int st) {
-        if (w == 0 && lane < BQ) {
-            float* Ls = reinterpret_cast<float*>(stages + st * STAGE + 2 * QT::BYTES);
-            Ls[lane] *= kLog2e;
+        if (w < 2 && lane < BQ) {
+            float* x = reinterpret_cast<float*>(stages + st * STAGE + 2 * QT::BYTES + 256 * w);
+            x[lane] = w == 0 ? -(x[lane] * kLog2e) / a.c : -x[lane];
         }
     };
 
@@ -223,9 +224,39 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
         // nothing: the wave skips its products (the other wave of its SIMD
         // has the matrix pipe to itself meanwhile) but not the barrier below.
         if (!(pad || (CAUSAL && qb + BQ - 1 + a.off < kw))) {
-            f32x16 s = f32x16{}, dp = f32x16{};
+            // S starts at -L*log2(e)/c and dP at -Delta of their query rows
+            // (rows 8*(r/4) + 4g + r%4 of this lane's registers; waves 0 and 1
+            // prepared them in the stage): after the products c*s is the
+            // exponent of P and dp is dP - Delta.  Every operand fragment is
+            // read ahead of its product (S: two products ahead, the others
+            // one), into registers the other phases do not use.
+            f32x16 s, dp;
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) mma(s, frag(qrd.read(ks, QI)), kf[ks]);
+            for (int rg = 0; rg < 4; ++rg) {
+                const f32x4 l4 = *reinterpret_cast<const f32x4*>(Ls + 8 * rg + 4 * g);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s[4 * rg + e] = l4[e];
+            }
+            {
+                constexpr int SAH = 2;
+                bf16x8 qr[SAH + 1];
+#pragma unroll
+                for (int ks = 0; ks < SAH; ++ks) qr[ks] = qrd.read(ks, QI);
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    if (ks + SAH < NKS) qr[(ks + SAH) % (SAH + 1)] = qrd.read(ks + SAH, QI);
+                    if (ks == NKS / 2) {
+#pragma unroll
+                        for (int rg = 0; rg < 4; ++rg) {
+                            const f32x4 d4 = *reinterpret_cast<const f32x4*>(Ds + 8 * rg + 4 * g);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) dp[4 * rg + e] = d4[e];
+                        }
+                    }
+                    mma(s, frag(qr[ks % (SAH + 1)]), kf[ks]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
             // Tiles wholly visible to this wave take no mask code; the others set
             // the invisible scores to -inf, so that P = 0 there.  Lane c's key
             // kw + c is visible to query qb + row iff c <= qb + off - kw + row.
@@ -244,66 +275,82 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
             // this wave's own instruction stream: P between the dP products (from
             // the third on, once S has left the pipe), dS between the dV products.
             // Each group is fenced and each result pinned where it is formed.
-            // Rows of this lane's registers: queries 8*(r/4) + 4g + r%4.
-            f32x4 L4[4];
-#pragma unroll
-            for (int rg = 0; rg < 4; ++rg) L4[rg] = *reinterpret_cast<const f32x4*>(Ls + 8 * rg + 4 * g);
             Frag<bf16> pf0, pf1;
+            {
+                constexpr int PAH = 1;
+                bf16x8 ro[PAH + 1], rv[PAH + 1];  // dO and V fragments, PAH products ahead
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                mma(dp, frag(qrd.read(ks, OI)), frag(lds_b128(vrd + (uint32_t)VW::frag_off(0, ks))));
-                if (ks >= 2) {
-                    constexpr int per = (16 + NKS - 3) / (NKS - 2);
-#pragma unroll
-                    for (int r = per * (ks - 2); r < per * (ks - 1) && r < 16; ++r) {
-                        float x = fast_exp2(fmaf(s[r], a.c, -L4[r >> 2][r & 3]));  // P
-                        pin(x);
-                        s[r] = x;
-                    }
-                    if (ks == NKS - 1) {
-                        pf0 = acc_frag<bf16>(s, 0);
-                        pf1 = acc_frag<bf16>(s, 1);
-                        pin(pf0.v);
-                        pin(pf1.v);
-                    }
+                for (int j = 0; j < PAH; ++j) {
+                    ro[j] = qrd.read(j, OI);
+                    rv[j] = lds_b128(vrd + (uint32_t)VW::frag_off(0, j));
                 }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            f32x4 D4[4];
 #pragma unroll
-            for (int rg = 0; rg < 4; ++rg) D4[rg] = *reinterpret_cast<const f32x4*>(Ds + 8 * rg + 4 * g);
+                for (int ks = 0; ks < NKS; ++ks) {
+                    if (ks + PAH < NKS) {
+                        ro[(ks + PAH) % (PAH + 1)] = qrd.read(ks + PAH, OI);
+                        rv[(ks + PAH) % (PAH + 1)] = lds_b128(vrd + (uint32_t)VW::frag_off(0, ks + PAH));
+                    }
+                    mma(dp, frag(ro[ks % (PAH + 1)]), frag(rv[ks % (PAH + 1)]));
+                    if (ks >= 2) {
+                        constexpr int per = (16 + NKS - 3) / (NKS - 2);
+#pragma unroll
+                        for (int r = per * (ks - 2); r < per * (ks - 1) && r < 16; ++r) {
+                            float x = fast_exp2(s[r] * a.c);  // P
+                            pin(x);
+                            s[r] = x;
+                        }
+                        if (ks == NKS - 1) {
+                            pf0 = acc_frag<bf16>(s, 0);
+                            pf1 = acc_frag<bf16>(s, 1);
+                            pin(pf0.v);
+                            pin(pf1.v);
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            // dV and dK products: transposed fragments of dO (dV) and Q (dK),
+            // one product ahead
             Frag<bf16> sf0, sf1;
             constexpr int NU = 2 * NDB;                    // dV products
             constexpr int U0 = NU >= 8 ? 2 : 1;            // first one with dS work beside it
             constexpr int PER = NU >= 8 ? 4 : (16 + NU - U0 - 1) / (NU - U0);
+            auto tr_read = [&](int u) -> bf16x8 {         // fragment of dV (u < NU) or dK product
+                const int v = u % NU, t = v / NDB, db = v % NDB;
+                return trd.read(db, (u < NU ? OI : QI) + 16 * t * Fmt::ROWBYTES);
+            };
+            constexpr int TAH = 2;
+            bf16x8 rt[TAH + 1];
 #pragma unroll
-            for (int u = 0; u < NU; ++u) {
-                const int t = u / NDB, db = u % NDB;
-                mma(dv[db], frag(trd.read(db, OI + 16 * t * Fmt::ROWBYTES)), t ? pf1 : pf0);
-                if (u >= U0) {
-                    const int r0 = PER * (u - U0), r1 = min(16, PER * (u - U0 + 1));
+            for (int j = 0; j < TAH; ++j) rt[j] = tr_read(j);
 #pragma unroll
-                    for (int r = r0; r < r1; ++r) {
-                        float x = s[r] * (dp[r] - D4[r >> 2][r & 3]);  // dS
-                        pin(x);
-                        dp[r] = x;
+            for (int u = 0; u < 2 * NU; ++u) {
+                if (u + TAH < 2 * NU) rt[(u + TAH) % (TAH + 1)] = tr_read(u + TAH);
+                const int t = (u % NU) / NDB, db = (u % NU) % NDB;
+                if (u < NU) {
+                    mma(dv[db], frag(rt[u % (TAH + 1)]), t ? pf1 : pf0);
+                    if (u >= U0) {
+                        const int r0 = PER * (u - U0), r1 = min(16, PER * (u - U0 + 1));
+#pragma unroll
+                        for (int r = r0; r < r1; ++r) {
+                            float x = s[r] * dp[r];  // dS = P (dP - Delta)
+                            pin(x);
+                            dp[r] = x;
+                        }
+                        if (r0 <= 7 && r1 > 7) {
+                            sf0 = acc_frag<bf16>(dp, 0);
+                            pin(sf0.v);
+                        }
+                        if (r0 < 16 && r1 >= 16) {
+                            sf1 = acc_frag<bf16>(dp, 1);
+                            pin(sf1.v);
+                        }
                     }
-                    if (r0 <= 7 && r1 > 7) {
-                        sf0 = acc_frag<bf16>(dp, 0);
-                        pin(sf0.v);
-                    }
-                    if (r0 < 16 && r1 >= 16) {
-                        sf1 = acc_frag<bf16>(dp, 1);
-                        pin(sf1.v);
-                    }
+                } else {
+                    mma(dk[db], frag(rt[u % (TAH + 1)]), t ? sf1 : sf0);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-                    mma(dk[db], frag(trd.read(db, QI + 16 * t * Fmt::ROWBYTES)), t ? sf1 : sf0);
         }
         // One barrier per pair (measured 1.4 % faster than one per tile: the
         // waves of a SIMD drift out of phase within the pair).  The next
@@ -623,10 +670,27 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
                 f32x16 s = f32x16{}, dp = f32x16{};
+                {
+                    // K and V fragments, one step ahead of their products
+                    auto kread = [&](int ks) { return krd.read(ks, KI + kb * 32 * Fmt::ROWBYTES); };
+                    auto vread = [&](int ks) {
+                        return lds_b128(vrd + VIM + (uint32_t)VT::frag_off(kb, ks));
+                    };
+                    bf16x8 rk[3], rv[3];
+                    rk[0] = kread(0);
+                    rv[0] = vread(0);
+                    rk[1] = kread(1);
+                    rv[1] = vread(1);
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    mma(s, frag(krd.read(ks, KI + kb * 32 * Fmt::ROWBYTES)), qf[ks]);
-                    mma(dp, frag(lds_b128(vrd + VIM + (uint32_t)VT::frag_off(kb, ks))), of[ks]);
+                    for (int ks = 0; ks < NKS; ++ks) {
+                        if (ks + 2 < NKS) {
+                            rk[(ks + 2) % 3] = kread(ks + 2);
+                            rv[(ks + 2) % 3] = vread(ks + 2);
+                        }
+                        mma(s, frag(rk[ks % 3]), qf[ks]);
+                        mma(dp, frag(rv[ks % 3]), of[ks]);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
                 }
                 if (masked) {
                     asm volatile("");  // keep this a branch

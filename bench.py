@@ -3,8 +3,10 @@
 One step = the whole hot path once: fa_fwd, then the three stages of fa_bwd
 (Delta preprocess, dK/dV, dQ), on seeded synthetic inputs already resident in
 HBM.  W untimed warm-up steps, then K timed steps bracketed by device
-synchronisation; HIP events recorded on the launch stream around every kernel
-give per-kernel averages over the timed region.
+synchronisation, with nothing recorded between their kernels (--graph: each
+the replay of one captured step, a HIP graph).  K more steps with HIP events
+recorded on the launch stream between the kernels give the per-kernel
+averages.
 
 Throughput is credited FLOP / time with forward FLOP = 4*B*Hq*T^2*D (halved
 when causal) and backward = 2.5x forward ("FlashAttention: l'attenzione che non
@@ -54,6 +56,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="C5")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--graph", action="store_true",
+                   help="time replays of a captured HIP graph of one step instead of eager steps")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target duration of the oracle sample")
     p.add_argument("--gemm-reference", action="store_true",
@@ -427,23 +431,46 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] warm-up done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
+    # The timed region: K steps with nothing between their kernels (events
+    # between kernels leave the GPU idle for a few microseconds each), eager,
+    # or with --graph each the replay of one captured step (a HIP graph: the
+    # kernels of a step go to the GPU in one launch).
+    run, launch = step, "eager"
+    if args.graph:
+        try:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                step()
+            run, launch = graph.replay, "graph"
+        except RuntimeError as e:
+            print(f"[bench] graph capture failed ({e}); timing eager steps", file=sys.stderr,
+                  flush=True)
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_span = e0.elapsed_time(e1) / args.steps
+    ms_per_step = max(wall * 1e3 / args.steps, gpu_span)
+    print(f"[bench] timed {args.steps} steps ({launch}) in {wall:.3f} s", file=sys.stderr,
+          flush=True)
+
+    # Kernel durations: K more eager steps with events between the kernels
     nev = len(names) + 1
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for i in range(args.steps):
         step(events[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    print(f"[bench] timed {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
-
     per = {n: 0.0 for n in names}
     for ev in events:
         for i, n in enumerate(names):
             per[n] += ev[i].elapsed_time(ev[i + 1])
     per = {n: t / args.steps for n, t in per.items()}
-    gpu_span = events[0][0].elapsed_time(events[-1][nev - 1]) / args.steps
-    ms_per_step = max(wall * 1e3 / args.steps, gpu_span)
     bwd_ms = sum(per[n] for n in names if n != "fwd")
     if fused:
         # the preprocess kernel on its own, after the timed region (its HBM rate)
@@ -511,6 +538,8 @@ def main():
             "pre_gbps": round(pre_bytes / (per["pre"] * 1e-3) / 1e9, 1),
             "bwd_path": ("dQ kernel forms Delta, then dK/dV (as fa_bwd); pre_ms: the preprocess "
                          "kernel timed on its own" if fused else "preprocess, dK/dV, dQ"),
+            "step_launch": launch,
+            "kernel_ms": "events between the kernels of K eager steps after the timed region",
         },
         "roofline": roofline,
         "cpu_baseline": None,

@@ -243,7 +243,8 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(FwdArgs a)
                     p[e] = fast_exp2(fmaf(st[kb][r + e], a.c, -msub));
                     sum += p[e];
                 }
-                int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+                // the low half first (the high half it keeps is overwritten next)
+                int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], pt[(16 * kb + r) / 4], false);
                 wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wd, true);
                 pt[(16 * kb + r) / 4] = wd;
             }
@@ -302,7 +303,9 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(FwdArgs a)
             if (t >= 3 && (t - 3) % 2 == 0 && t - 2 < NE) {
                 const int e = t - 3;  // bytes e, e + 1 of the operand
                 if (e % 4 == 0) {
-                    pw[e / 4] = __builtin_amdgcn_cvt_pk_fp8_f32(px[e], px[e + 1], 0, false);
+                    // the low half; the high half it keeps (tile i - 3's
+                    // weights, already used) is overwritten two steps later
+                    pw[e / 4] = __builtin_amdgcn_cvt_pk_fp8_f32(px[e], px[e + 1], pw[e / 4], false);
                 } else {
                     int wd = __builtin_amdgcn_cvt_pk_fp8_f32(px[e], px[e + 1], pw[e / 4], true);
                     // formed here, not sunk with its weights live to the end

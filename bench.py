@@ -258,8 +258,8 @@ def forward_only_fp8(args, w, q, k, v, lse):
 def cpu_baseline(w, x, target_s: float):
     """Time the oracle's fwd + bwd on a bounded sample of the workload, sized
     to take about target_s seconds: whole kv groups (all their query heads,
-    every position) when one head is cheap enough, else a causal prefix of
-    query head 0 and its kv head.  Returns (record, outputs): for whole kv
+    every position) when one group takes at most twice that, else a causal
+    prefix of query head 0 and its kv head.  Returns (record, outputs): for whole kv
     groups, outputs holds the oracle's O, lse, dQ, dK, dV of groups
     0 .. n-1 of batch 0 (for the parity errors), else None."""
     import oracle
@@ -290,10 +290,12 @@ def cpu_baseline(w, x, target_s: float):
         orc.bwd(q, k, v, do, w.scale, w.causal)
         return time.perf_counter() - t0
 
-    cal = min(2048, w.T)
+    run_head(min(256, w.T))  # the first call starts the oracle's thread pool
+    cal = min(4096, w.T)
     t_cal = run_head(cal)
     t_head = t_cal * (w.T / cal) ** 2  # work grows as T^2
-    if t_head * G <= target_s:
+    # whole kv groups (the parity slice) while one fits in twice the target
+    if t_head * G <= 2 * target_s:
         ngroups = max(1, min(w.B * w.Hkv, int(target_s / (t_head * G))))
         ngroups = min(ngroups, w.Hkv)
         tp, nheads = w.T, ngroups * G

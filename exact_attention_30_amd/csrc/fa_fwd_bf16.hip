@@ -53,7 +53,9 @@ namespace fa {
 
 template <int D>  // head size of the tensors in memory
 struct FwdBf16Cfg {
-    static constexpr int DT = tile_dim(D);   // head size of the tiles and products
+    // head size of the tiles and products: D itself (the read-order tiles take
+    // any multiple of 32 columns, so D = 96 needs no padding here)
+    static constexpr int DT = D;
     static constexpr int NWAVE = 8;          // waves per workgroup (two per SIMD)
     static constexpr int NT = 64 * NWAVE;
     static constexpr int BR = 32 * NWAVE;    // query rows per workgroup
@@ -64,9 +66,11 @@ struct FwdBf16Cfg {
     using VT = TrFragTile<DT, BC, D>;
     static constexpr int STAGE = KT::BYTES + VT::BYTES;
     static constexpr int SMEM = NSTAGE * STAGE;
-    static constexpr int KI = KT::NDMA / NWAVE;  // DMA instructions per wave per tile
-    static constexpr int VI = VT::NDMA / NWAVE;
-    static_assert(KT::NDMA % NWAVE == 0 && VT::NDMA % NWAVE == 0, "DMA split");
+    // DMA instructions per wave per tile, at most: 1 KiB block f goes to wave
+    // f % NWAVE (D = 96: 12 blocks, two for waves 0-3, one for waves 4-7)
+    static constexpr int KI = (KT::NDMA + NWAVE - 1) / NWAVE;
+    static constexpr int VI = (VT::NDMA + NWAVE - 1) / NWAVE;
+    static_assert(DT % 32 == 0, "32-column blocks");
     static_assert(NSTAGE == 4, "stages move in pairs");
 };
 
@@ -83,7 +87,7 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
     using VT = typename Cfg::VT;
     constexpr int BR = Cfg::BR, BC = Cfg::BC, NWAVE = Cfg::NWAVE;
     constexpr int KI = Cfg::KI, VI = Cfg::VI;
-    constexpr int DT = Cfg::DT;   // tile head size (D in memory; padding columns are zeros)
+    constexpr int DT = Cfg::DT;   // tile head size (= D)
     constexpr int NKB = BC / 32;  // 32-key blocks per tile
     constexpr int NDB = DT / 32;  // 32-column blocks of the head dimension
     constexpr int NKS = DT / 16;  // 16-deep steps over the head dimension
@@ -135,10 +139,13 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
 
     // this thread's DMA source offsets (same for every tile)
     uint32_t koff[KI], voff[VI];
+    // (past the last block, D = 96: a valid offset that no DMA uses)
 #pragma unroll
-    for (int i = 0; i < KI; ++i) koff[i] = KT::dma_off(w + NWAVE * i, lane);
+    for (int i = 0; i < KI; ++i)
+        koff[i] = KT::dma_off(KT::NDMA % NWAVE == 0 ? w + NWAVE * i : min(w + NWAVE * i, KT::NDMA - 1), lane);
 #pragma unroll
-    for (int i = 0; i < VI; ++i) voff[i] = VT::dma_off(w + NWAVE * i, lane);
+    for (int i = 0; i < VI; ++i)
+        voff[i] = VT::dma_off(VT::NDMA % NWAVE == 0 ? w + NWAVE * i : min(w + NWAVE * i, VT::NDMA - 1), lane);
 
     // Stage t = {K_t (t < nkv), V_{t-2} (2 <= t <= nkv + 1)} in buffer
     // t % NSTAGE: everything iteration t reads from LDS.
@@ -149,14 +156,17 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
             const int row0 = (j0 + t) * BC;
             const i32x4 r = buffer_rsrc(kh + (size_t)row0 * D, (a.Tk - row0) * D * 2);
 #pragma unroll
-            for (int i = 0; i < KI; ++i) dma_b128(base + (uint32_t)((w + NWAVE * i) * 1024), r, koff[i]);
+            for (int i = 0; i < KI; ++i)
+                if (KT::NDMA % NWAVE == 0 || w + NWAVE * i < KT::NDMA)  // (uniform per wave)
+                    dma_b128(base + (uint32_t)((w + NWAVE * i) * 1024), r, koff[i]);
         }
         if (t >= 2 && t <= nkv + 1) {
             const int row0 = (j0 + t - 2) * BC;
             const i32x4 r = buffer_rsrc(vh + (size_t)row0 * D, (a.Tk - row0) * D * 2);
 #pragma unroll
             for (int i = 0; i < VI; ++i)
-                dma_b128(base + (uint32_t)(KT::BYTES + (w + NWAVE * i) * 1024), r, voff[i]);
+                if (VT::NDMA % NWAVE == 0 || w + NWAVE * i < VT::NDMA)
+                    dma_b128(base + (uint32_t)(KT::BYTES + (w + NWAVE * i) * 1024), r, voff[i]);
         }
     };
     load_stage(0);
@@ -408,7 +418,6 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
                 for (int rg = 0; rg < 4; ++rg) {
-                    if (db * 32 + 8 * rg + 4 * g >= D) continue;  // padding columns
                     f32x4 x;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) x[e] = o[db][4 * rg + e];
@@ -428,7 +437,6 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
-                if (db * 32 + 8 * rg + 4 * g >= D) continue;  // padding columns
                 bf16x4 x;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) x[e] = (bf16)(o[db][4 * rg + e] * inv);

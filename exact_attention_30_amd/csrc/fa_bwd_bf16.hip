@@ -80,8 +80,10 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
     using Fmt = typename Cfg::Fmt;
     using VW = typename Cfg::VW;
     constexpr int BK = Cfg::BK, BQ = Cfg::BQ, NSTAGE = Cfg::NSTAGE, STAGE = Cfg::STAGE;
-    constexpr int NDB = Cfg::DT / 32;  // tile head size (D in memory; padding columns are zeros)
-    constexpr int NKS = Cfg::DT / 16;
+    // Products run over the D columns of the tensors; the LDS tiles are
+    // Cfg::DT wide (D = 96: 128, the last 32 columns zeros that no product reads)
+    constexpr int NDB = D / 32;  // 32-column blocks
+    constexpr int NKS = D / 16;  // 16-deep steps over the head dimension
     constexpr int QW = Cfg::QNT / 64;  // waves that move Q and dO tiles
 
     extern __shared__ __align__(1024) unsigned char smem[];
@@ -377,7 +379,6 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
 #pragma unroll
                 for (int rg = 0; rg < 4; ++rg) {
                     const int col = db * 32 + 8 * rg + 4 * g;
-                    if (col >= D) continue;  // padding columns
                     bf16x4 x, y;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -397,7 +398,6 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
 #pragma unroll
                 for (int rg = 0; rg < 4; ++rg) {
                     const int col = db * 32 + 8 * rg + 4 * g;
-                    if (col >= D) continue;  // padding columns
                     f32x4 x, y;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -491,8 +491,10 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
     constexpr int BR = Cfg::BR, BC = Cfg::BC, NSTAGE = Cfg::NSTAGE, NWAVE = Cfg::NW;
     constexpr int AHEAD = Cfg::AHEAD;
     constexpr int NKB = BC / 32;
-    constexpr int NDB = Cfg::DT / 32;  // tile head size (D in memory; padding columns are zeros)
-    constexpr int NKS = Cfg::DT / 16;
+    // Products run over the D columns of the tensors; the LDS tiles are
+    // Cfg::DT wide (D = 96: 128, the last 32 columns zeros that no product reads)
+    constexpr int NDB = D / 32;  // 32-column blocks
+    constexpr int NKS = D / 16;  // 16-deep steps over the head dimension
     constexpr int VPT = KT::NI + Cfg::VI;  // DMA instructions per tile and wave
 
     extern __shared__ __align__(1024) unsigned char smem[];
@@ -595,17 +597,23 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
         // bits are the same: an fma chain over each 8 columns (the lane's
         // chunks 2ks + g), then chunk pairs from the highest bit of the chunk
         // index down; g, the lowest, is added last across the lane pair.
-        static_assert((NKS & (NKS - 1)) == 0, "the chunk pairs assume a power of two");
-        float vs[NKS];
+        // The pairs run over the tile width's chunks (a power of two), the
+        // padding chunks (D = 96) adding +0, as the preprocess kernel's lanes
+        // past D do.
+        constexpr int NKT = Cfg::DT / 16;
+        static_assert((NKT & (NKT - 1)) == 0, "the chunk pairs assume a power of two");
+        float vs[NKT];
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
+        for (int ks = 0; ks < NKT; ++ks) {
             float acc = 0.f;
+            if (ks < NKS) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc = fmaf((float)orow[ks].v[e], (float)of[ks].v[e], acc);
+                for (int e = 0; e < 8; ++e) acc = fmaf((float)orow[ks].v[e], (float)of[ks].v[e], acc);
+            }
             vs[ks] = acc;
         }
 #pragma unroll
-        for (int bit = NKS / 2; bit >= 1; bit /= 2)
+        for (int bit = NKT / 2; bit >= 1; bit /= 2)
 #pragma unroll
             for (int ks = 0; ks < bit; ++ks) vs[ks] += vs[ks + bit];
         Dl = pair_sum(vs[0]);
@@ -748,7 +756,6 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
                 for (int rg = 0; rg < 4; ++rg) {
-                    if (db * 32 + 8 * rg + 4 * g >= D) continue;  // padding columns
                     bf16x4 x;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) x[e] = (bf16)(dq[db][4 * rg + e] * a.scale);
@@ -760,7 +767,6 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
                 for (int rg = 0; rg < 4; ++rg) {
-                    if (db * 32 + 8 * rg + 4 * g >= D) continue;  // padding columns
                     f32x4 x;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) x[e] = dq[db][4 * rg + e];

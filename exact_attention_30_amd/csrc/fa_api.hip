@@ -209,6 +209,12 @@ size_t fa_fwd_split_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int D, fa_dtyp
     return fwd_split_bytes(B, Hq, Hkv, Tq, Tk, D, dt);
 }
 
+int fa_fwd_block_rows(int B, int Hq, int Tq, int D, fa_dtype dt)
+{
+    if (check_kv(B, Hq, Hq, Tq, Tq, D, dt, false, 0) != FA_OK) return 0;
+    return dt == FA_BF16 ? fa::fwd_rows(B, Hq, Tq, D) : 128;
+}
+
 fa_status fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
                     int Hkv, int Tq, int Tk, int D, float scale, int causal, int q_offset,
                     fa_dtype dt, void* stream)

@@ -10,7 +10,9 @@
 //
 // MI355X mapping.
 //   * Eight waves of 32 query rows, two per SIMD, each running on its own
-//     (one barrier per two tiles for the shared LDS stages).  A wave computes
+//     (one barrier per two tiles for the shared LDS stages); at D = 64 on
+//     small grids four waves, two workgroups per compute unit (the tile
+//     table, fwd_rows).  A wave computes
 //     S^T = K Q^T with the 32x32x16 bf16 MFMA, so a lane owns one query
 //     column and its row reductions are in-lane plus one exchange with lane
 //     c ^ 32.  The weights are formed from the S^T registers and fed back as
@@ -51,12 +53,12 @@
 
 namespace fa {
 
-template <int D>  // head size of the tensors in memory
+template <int D, int NW>  // head size of the tensors in memory; waves per workgroup
 struct FwdBf16Cfg {
     // head size of the tiles and products: D itself (the read-order tiles take
     // any multiple of 32 columns, so D = 96 needs no padding here)
     static constexpr int DT = D;
-    static constexpr int NWAVE = 8;          // waves per workgroup (two per SIMD)
+    static constexpr int NWAVE = NW;         // 8: two per SIMD; 4: one, two workgroups per CU
     static constexpr int NT = 64 * NWAVE;
     static constexpr int BR = 32 * NWAVE;    // query rows per workgroup
     static constexpr int BC = 64;            // keys per tile
@@ -67,7 +69,7 @@ struct FwdBf16Cfg {
     static constexpr int STAGE = KT::BYTES + VT::BYTES;
     static constexpr int SMEM = NSTAGE * STAGE;
     // DMA instructions per wave per tile, at most: 1 KiB block f goes to wave
-    // f % NWAVE (D = 96: 12 blocks, two for waves 0-3, one for waves 4-7)
+    // f % NWAVE (D = 96: 12 blocks over 8 waves, two for waves 0-3, one for 4-7)
     static constexpr int KI = (KT::NDMA + NWAVE - 1) / NWAVE;
     static constexpr int VI = (VT::NDMA + NWAVE - 1) / NWAVE;
     static_assert(DT % 32 == 0, "32-column blocks");
@@ -79,10 +81,10 @@ struct FwdBf16Cfg {
 constexpr float kRescaleThresholdBf16 = 8.0f;
 constexpr float kMaxWeightBf16 = 256.0f;  // 2^kRescaleThresholdBf16
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
+template <int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
 {
-    using Cfg = FwdBf16Cfg<D>;
+    using Cfg = FwdBf16Cfg<D, NW>;
     using KT = typename Cfg::KT;
     using VT = typename Cfg::VT;
     constexpr int BR = Cfg::BR, BC = Cfg::BC, NWAVE = Cfg::NWAVE;
@@ -108,9 +110,10 @@ __global__ __launch_bounds__(512, 1) void fwd_bf16_kernel(FwdArgs a)
     const int b = id.b, hq = id.h / S, split = id.h % S;
     const int hk = hq / (a.Hq / a.Hkv);
     const int q0 = id.tile * BR;
-    // first query of this wave.  Waves w and w + 4 share a SIMD; pairing row
-    // blocks r and 7 - r there evens out the causal tiles their waves skip.
-    const int qw = q0 + 32 * (w < 4 ? w : 11 - w);
+    // first query of this wave.  With eight waves, w and w + 4 share a SIMD;
+    // pairing row blocks r and 7 - r there evens out the causal tiles their
+    // waves skip.  With four, each wave has a SIMD of the workgroup to itself.
+    const int qw = NWAVE == 4 ? q0 + 32 * w : q0 + 32 * (w < 4 ? w : 11 - w);
     const int qrow = qw + c;      // the query this lane owns
 
     const bf16* qh = static_cast<const bf16*>(a.q) + (size_t)(b * a.Hq + hq) * a.Tq * D;
@@ -486,12 +489,12 @@ __global__ __launch_bounds__(256) void merge_chunks_kernel(const float* opart, c
     if (c8 == 0) lse[row] = (M + log2f(L)) * kLn2;
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int NW>
 static hipError_t launch_t(const FwdArgs& a, hipStream_t stream)
 {
-    using Cfg = FwdBf16Cfg<D>;
-    static_assert(Cfg::SMEM <= 160 * 1024, "LDS budget");
-    auto kern = fwd_bf16_kernel<D, CAUSAL>;
+    using Cfg = FwdBf16Cfg<D, NW>;
+    static_assert(Cfg::SMEM * (8 / NW) <= 160 * 1024, "LDS budget");
+    auto kern = fwd_bf16_kernel<D, CAUSAL, NW>;
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::SMEM);
     if (attr != hipSuccess) return attr;
@@ -507,38 +510,60 @@ static hipError_t launch_t(const FwdArgs& a, hipStream_t stream)
     return hipGetLastError();
 }
 
+// The forward's static tile table: query rows per workgroup, from the
+// shapes.  At D = 64 a workgroup's four stage buffers take 64 KiB, so two
+// workgroups of four waves (128 rows) share a compute unit, and they run
+// independently (no barrier couples their waves).  Where the 256-row blocks
+// alone are fewer than two per compute unit, 128-row blocks are faster
+// (measured, unsplit 128 against the best 256-row split: causal B=2 Hq=8
+// T=4096 68.6 -> 61.8 us; T=512 19.2 -> 16.1 us); on larger grids they were
+// 5-8 % slower.  Everywhere else: 256 rows, eight waves.
+int fwd_rows(int B, int Hq, int Tq, int D)
+{
+    const long blocks256 = (long)((Tq + 255) / 256) * B * Hq;
+    return (D == 64 && blocks256 < 512) ? 128 : 256;
+}
+
 // Chunks of the key range per query block: about two workgroups per compute
 // unit when the query blocks alone are too few, at most 8, and at least 4 key
-// tiles per chunk.
+// tiles per chunk (8 with 128-row blocks, whose short chunks measured slower
+// than one: T=512 16.1 us unsplit, 17.6 in two chunks).
 int fwd_nsplit(int B, int Hq, int Hkv, int Tq, int Tk, int D)
 {
     (void)Hkv;
-    (void)D;
     constexpr long kTarget = 512;
-    const long wgs = (long)((Tq + 255) / 256) * B * Hq;
+    const int br = fwd_rows(B, Hq, Tq, D);
+    const long wgs = (long)((Tq + br - 1) / br) * B * Hq;
     if (wgs <= 0 || wgs >= kTarget) return 1;
     long s = (kTarget + wgs - 1) / wgs;
     s = s < 8 ? s : 8;
     const long tiles = (Tk + 63) / 64;
-    const long cap = tiles / 4 > 1 ? tiles / 4 : 1;
+    const long per = br == 128 ? 8 : 4;
+    const long cap = tiles / per > 1 ? tiles / per : 1;
     return (int)(s < cap ? s : cap);
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, int D, bool causal, hipStream_t stream)
 {
-    if (D == 64) return causal ? launch_t<64, true>(a, stream) : launch_t<64, false>(a, stream);
-    if (D == 96) return causal ? launch_t<96, true>(a, stream) : launch_t<96, false>(a, stream);
-    return causal ? launch_t<128, true>(a, stream) : launch_t<128, false>(a, stream);
+    if (D == 64) {
+        if (fwd_rows(a.B, a.Hq, a.Tq, D) == 128)
+            return causal ? launch_t<64, true, 4>(a, stream) : launch_t<64, false, 4>(a, stream);
+        return causal ? launch_t<64, true, 8>(a, stream) : launch_t<64, false, 8>(a, stream);
+    }
+    if (D == 96) return causal ? launch_t<96, true, 8>(a, stream) : launch_t<96, false, 8>(a, stream);
+    return causal ? launch_t<128, true, 8>(a, stream) : launch_t<128, false, 8>(a, stream);
 }
 
 // Every kernel variant is instantiated explicitly: referencing a kernel
 // template only from a launcher has left some instantiations without their
 // host-side handle.
-template __global__ void fwd_bf16_kernel<64, true>(FwdArgs);
-template __global__ void fwd_bf16_kernel<64, false>(FwdArgs);
-template __global__ void fwd_bf16_kernel<96, true>(FwdArgs);
-template __global__ void fwd_bf16_kernel<96, false>(FwdArgs);
-template __global__ void fwd_bf16_kernel<128, true>(FwdArgs);
-template __global__ void fwd_bf16_kernel<128, false>(FwdArgs);
+template __global__ void fwd_bf16_kernel<64, true, 8>(FwdArgs);
+template __global__ void fwd_bf16_kernel<64, false, 8>(FwdArgs);
+template __global__ void fwd_bf16_kernel<64, true, 4>(FwdArgs);
+template __global__ void fwd_bf16_kernel<64, false, 4>(FwdArgs);
+template __global__ void fwd_bf16_kernel<96, true, 8>(FwdArgs);
+template __global__ void fwd_bf16_kernel<96, false, 8>(FwdArgs);
+template __global__ void fwd_bf16_kernel<128, true, 8>(FwdArgs);
+template __global__ void fwd_bf16_kernel<128, false, 8>(FwdArgs);
 
 }  // namespace fa

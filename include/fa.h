@@ -131,6 +131,18 @@ fa_status fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float*
  *       fa_fwd_kv.  O and lse agree with the unsplit forward to rounding.
  */
 size_t fa_fwd_split_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int D, fa_dtype dt);
+
+/*
+ * Query rows per workgroup of the forward for these shapes (its static tile
+ * table; the blocked loop of "FlashAttention: l'attenzione che non spreca
+ * memoria", «L'idea: lavorare a tessere», the tile sizes of "Optimización de
+ * Flash Attention ...", «La pila de optimización»).  bf16: 256 (eight waves),
+ * or 128 (four waves, two workgroups per compute unit) at D = 64 when the
+ * 256-row blocks number fewer than 512; fp32: 128.  The split rule counts
+ * these blocks.  Unsplit, a row's O and lse do not depend on this choice.
+ * Host only; returns 0 for shapes or types the forward rejects.
+ */
+int fa_fwd_block_rows(int B, int Hq, int Tq, int D, fa_dtype dt);
 fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
                        void* partial, int B, int Hq, int Hkv, int Tq, int Tk, int D, float scale,
                        int causal, int q_offset, fa_dtype dt, void* stream);

@@ -120,9 +120,13 @@ class Emulation:
 
     def __init__(self, x: dict, lse_ref, scale, causal, q_offset=None, S=1):
         """lse_ref: the oracle's lse of every row, or None to have the oracle
-        compute it when first needed."""
+        compute it when first needed.  The query blocks are those the library
+        picks for these shapes (lazy_model.block_rows)."""
+        from tests import lazy_model as lm
+
         self.x = {n: np.asarray(a, np.float64) for n, a in x.items()}
         q, k = self.x["q"], self.x["k"]
+        self.block = lm.block_rows(q.shape[0], q.shape[1], q.shape[2], q.shape[3])
         self.G = q.shape[1] // k.shape[1]
         self.off = k.shape[2] - q.shape[2] if q_offset is None else q_offset
         self._lse = None if lse_ref is None else np.asarray(lse_ref, np.float64)
@@ -155,7 +159,7 @@ class Emulation:
                                                            round_p=em.bf16_torch)[0]
             else:
                 o, _ = lm.forward(q, k, v, self.scale, self.causal, self.off, S=self.S,
-                                  round_p=em.bf16)
+                                  round_p=em.bf16, block=self.block)
             self._o = em.bf16(o)
         return self._o
 

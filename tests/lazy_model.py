@@ -39,14 +39,24 @@ MUTANTS = ("no_o_rescale", "no_l_rescale", "stale_weights", "alpha_inverted",
            "prev_tile_unscaled", "never_move")
 
 
-def nsplit(B, Hq, Tq, Tk):
+def block_rows(B, Hq, Tq, D):
+    """Query rows per workgroup of the bf16 forward (the library's tile
+    table): 128 at D = 64 when the 256-row blocks number fewer than 512,
+    else 256."""
+    n256 = ((Tq + BLOCK - 1) // BLOCK) * B * Hq
+    return 128 if D == 64 and n256 < 512 else BLOCK
+
+
+def nsplit(B, Hq, Tq, Tk, D):
     """Chunks per query block of the split forward: about 512 workgroups,
-    at most 8 chunks, at least 4 key tiles per chunk (the library's rule)."""
-    wgs = ((Tq + BLOCK - 1) // BLOCK) * B * Hq
+    at most 8 chunks, at least 4 key tiles per chunk, 8 with 128-row blocks
+    (the library's rule)."""
+    br = block_rows(B, Hq, Tq, D)
+    wgs = ((Tq + br - 1) // br) * B * Hq
     if wgs <= 0 or wgs >= 512:
         return 1
     s = min(8, (512 + wgs - 1) // wgs)
-    cap = max(1, ((Tk + TILE - 1) // TILE) // 4)
+    cap = max(1, ((Tk + TILE - 1) // TILE) // (8 if br == 128 else 4))
     return min(s, cap)
 
 
@@ -57,22 +67,23 @@ def _fp32(x):
 
 
 def forward_head(q, k, v, scale, causal, q_offset=0, S=1, round_p=None, mutant=None, record=None,
-                 blocks=None):
-    """O [Tq, D] and lse [Tq] of one head.  round_p rounds the weights that
-    enter P V (not the sum l), e.g. to bf16; mutant is one of MUTANTS.  With
-    `blocks` (query block indices), only those blocks' rows are computed (the
-    others are left zero)."""
+                 blocks=None, block=BLOCK):
+    """O [Tq, D] and lse [Tq] of one head, in query blocks of `block` rows
+    (which only matters with S > 1: they set where the chunks start).
+    round_p rounds the weights that enter P V (not the sum l), e.g. to bf16;
+    mutant is one of MUTANTS.  With `blocks` (query block indices), only
+    those blocks' rows are computed (the others are left zero)."""
     Tq, D = q.shape
     Tk = k.shape[0]
     c = scale * LOG2E
     out = np.zeros((Tq, D))
     lse = np.zeros(Tq)
     ntk = (Tk + TILE - 1) // TILE
-    for q0 in range(0, Tq, BLOCK):
-        if blocks is not None and q0 // BLOCK not in blocks:
+    for q0 in range(0, Tq, block):
+        if blocks is not None and q0 // block not in blocks:
             continue
-        rows = np.arange(q0, min(q0 + BLOCK, Tq))
-        kend = min(q0 + BLOCK + q_offset, Tk) if causal else Tk
+        rows = np.arange(q0, min(q0 + block, Tq))
+        kend = min(q0 + block + q_offset, Tk) if causal else Tk
         nall = (kend + TILE - 1) // TILE
         s_blk = (q[rows] @ k[:nall * TILE].T) * c  # log2 units
         if causal:
@@ -197,7 +208,8 @@ def _nkw(i, j0, j1, Tk, causal, off):
     return min(nkv, max(0, (qw + 32 + off + TILE - 1) // TILE - j0))
 
 
-def forward(q, k, v, scale, causal, q_offset=None, S=1, round_p=None, mutant=None, record=None):
+def forward(q, k, v, scale, causal, q_offset=None, S=1, round_p=None, mutant=None, record=None,
+            block=BLOCK):
     """O [B,Hq,Tq,D], lse [B,Hq,Tq] over all heads (GQA: kv head h // G)."""
     B, Hq, Tq, D = q.shape
     Hkv, Tk = k.shape[1], k.shape[2]
@@ -209,7 +221,8 @@ def forward(q, k, v, scale, causal, q_offset=None, S=1, round_p=None, mutant=Non
         for h in range(Hq):
             rec = [] if record is not None else None
             o[b, h], lse[b, h] = forward_head(q[b, h], k[b, h // G], v[b, h // G], scale, causal,
-                                              off if causal else 0, S, round_p, mutant, rec)
+                                              off if causal else 0, S, round_p, mutant, rec,
+                                              block=block)
             if rec is not None:
                 for e in rec:
                     e.update(b=b, h=h)

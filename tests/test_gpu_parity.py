@@ -390,7 +390,28 @@ def test_split_dq(shape):
     assert_close("dQ split", a, rdq, bf16, eq)
 
 
-@pytest.mark.parametrize("shape", [(1, 1, 1, 2048, 2048, 128), (1, 4, 2, 700, 700, 64),
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("Hq,Hkv,T", [(16, 8, 4096), (24, 8, 3000)])
+def test_forward_tile_invariance(causal, Hq, Hkv, T):
+    """The forward's static tile table (the tile sizes of "Optimización de
+    Flash Attention ...", «La pila de optimización»): at D = 64 a grid of
+    fewer than 512 blocks of 256 rows runs 128-row workgroups of four waves,
+    a larger one 256-row workgroups of eight.  Unsplit, a row's result does
+    not depend on that choice: the heads of a batch of one (128-row blocks)
+    equal, bit for bit, the same heads inside a batch of two (256-row
+    blocks)."""
+    D = 64
+    assert fa.fwd_block_rows(1, Hq, T, D) == 128 and fa.fwd_block_rows(2, Hq, T, D) == 256
+    x = to_dev(make_inputs(2, Hq, Hkv, T, D, bf16, seed=31 + T))
+    say(f"tile invariance Hq={Hq} Hkv={Hkv} T={T} causal={causal}")
+    o2, l2 = fa.fwd(x["q"], x["k"], x["v"], causal=causal)
+    o1, l1 = fa.fwd(x["q"][:1].contiguous(), x["k"][:1].contiguous(), x["v"][:1].contiguous(),
+                    causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2[:1]) and torch.equal(l1, l2[:1])
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1, 2048, 2048, 128), (1, 4, 2, 1500, 1500, 64),
                                    (2, 2, 1, 300, 2000, 128), (1, 2, 1, 600, 1800, 96)])
 def test_split_forward(shape):
     """Few query blocks: the forward splits each block's key range into
@@ -415,6 +436,6 @@ def test_split_forward(shape):
     q, k, v = (x[n].double().cpu().numpy() for n in ("q", "k", "v"))
     ro, rl = oracle.fwd(q, k, v, 1 / math.sqrt(D), True)
     eo = emulated_fwd({"q": q, "k": k, "v": v}, 1 / math.sqrt(D), True, Tk - Tq,
-                      S=lazy_model.nsplit(B, Hq, Tq, Tk))
+                      S=lazy_model.nsplit(B, Hq, Tq, Tk, D))
     assert_close("O split", a, ro, bf16, eo)
     assert_lse_close(f64(l1), rl, bf16)

@@ -65,7 +65,7 @@ def test_sweep_forward_backward(case):
     ro, rl = oracle.fwd(q, k, v, sc, causal, q_offset=q_offset)
     rdq, rdk, rdv = oracle.bwd(q, k, v, do, sc, causal, q_offset=q_offset)
     xs = {"q": q, "k": k, "v": v, "dout": do}
-    eo = emulated_fwd(xs, sc, causal, q_offset, S=lazy_model.nsplit(B, Hq, Tq, Tk))
+    eo = emulated_fwd(xs, sc, causal, q_offset, S=lazy_model.nsplit(B, Hq, Tq, Tk, D))
     assert_close(f"O {name}", f64(o), ro, torch.bfloat16, eo)
     assert_lse_close(f64(lse), rl, torch.bfloat16)
     # scales up to 0.3 at D = 128 make P peaked: the rounding of Delta counts

@@ -121,7 +121,7 @@ def test_inputs_reach_the_branch(name, S):
 
 def test_split_case_moves_inside_later_chunks():
     B, Hq, Hkv, Tq, Tk, D, causal, off, seed, big = ALL[SPLIT_CASE]
-    assert lm.nsplit(B, Hq, Tq, Tk) == 8
+    assert lm.nsplit(B, Hq, Tq, Tk, D) == 8
     moves = [e for e in events(SPLIT_CASE, 8) if e["kind"] == "move"]
     assert any(e["chunk"] >= 1 and e["local"] == 1 for e in moves)
     assert any(e["chunk"] >= 1 and e["tile"] == e["row_last"] for e in moves)

@@ -66,7 +66,7 @@ SIGNATURES = {
     "fa_bwd_dq_delta": ([_vp, _vp, _vp, _vp, _vp, _fp, _fp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f,
                          _i, _i, _i, _vp], ctypes.c_int),
     "fa_fwd_split_bytes": ([_i, _i, _i, _i, _i, _i, _i], ctypes.c_size_t),
-    "fa_fwd_block_rows": ([_i, _i, _i, _i, _i], _i),
+    "fa_block_rows": ([_i, _i, _i, _i, _i, _i], _i),
     "fa_fwd_split": ([_vp, _vp, _vp, _vp, _fp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _i, _i, _vp],
                      ctypes.c_int),
     "fa_fwd_fp8_workspace_bytes": ([_i, _i, _i, _i], ctypes.c_size_t),
@@ -180,10 +180,14 @@ def fwd_split_bytes(B, Hq, Hkv, Tq, Tk, D, dtype=torch.bfloat16) -> int:
     return int(library().fa_fwd_split_bytes(B, Hq, Hkv, Tq, Tk, D, _DTYPES[dtype]))
 
 
-def fwd_block_rows(B, Hq, Tq, D, dtype=torch.bfloat16) -> int:
-    """Query rows per workgroup the forward uses for these shapes (its tile
-    table; 0 for shapes it rejects)."""
-    return int(library().fa_fwd_block_rows(B, Hq, Tq, D, _DTYPES[dtype]))
+STAGES = {"fwd": 0, "dq": 1, "dkdv": 2}
+
+
+def block_rows(stage, B, H, T, D, dtype=torch.bfloat16) -> int:
+    """Rows of one workgroup's block for these shapes (the tile table):
+    stage "fwd" or "dq" (query rows; H = Hq, T = Tq) or "dkdv" (keys;
+    H = Hkv, T = Tk); 0 for shapes the kernels reject."""
+    return int(library().fa_block_rows(STAGES[stage], B, H, T, D, _DTYPES[dtype]))
 
 
 def fwd(q, k, v, scale=None, causal: bool = True, out=None, lse=None, q_offset=None,

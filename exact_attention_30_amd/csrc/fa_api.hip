@@ -209,10 +209,15 @@ size_t fa_fwd_split_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int D, fa_dtyp
     return fwd_split_bytes(B, Hq, Hkv, Tq, Tk, D, dt);
 }
 
-int fa_fwd_block_rows(int B, int Hq, int Tq, int D, fa_dtype dt)
+int fa_block_rows(fa_stage stage, int B, int H, int T, int D, fa_dtype dt)
 {
-    if (check_kv(B, Hq, Hq, Tq, Tq, D, dt, false, 0) != FA_OK) return 0;
-    return dt == FA_BF16 ? fa::fwd_rows(B, Hq, Tq, D) : 128;
+    if (check_kv(B, H, H, T, T, D, dt, false, 0) != FA_OK) return 0;
+    switch (stage) {
+    case FA_STAGE_FWD: return dt == FA_BF16 ? fa::fwd_rows(B, H, T, D) : 128;
+    case FA_STAGE_DQ: return dt == FA_BF16 ? fa::dq_rows(B, H, T, D) : 128;
+    case FA_STAGE_DKDV: return dt == FA_BF16 ? fa::dkdv_keys(B, H, T, D) : 128;
+    }
+    return 0;
 }
 
 fa_status fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,

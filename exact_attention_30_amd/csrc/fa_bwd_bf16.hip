@@ -41,10 +41,10 @@
 
 namespace fa {
 
-template <int D>  // head size of the tensors in memory
+template <int D, int NWV>  // head size of the tensors in memory; waves per workgroup
 struct DkdvBf16Cfg {
     static constexpr int DT = tile_dim(D);  // head size of the tiles and products
-    static constexpr int NW = 8;
+    static constexpr int NW = NWV;          // 8: two per SIMD; 4: one, several workgroups per CU
     static constexpr int NT = 64 * NW;
     static constexpr int BK = 32 * NW;  // keys per workgroup
     static constexpr int BQ = 32;       // query rows per tile
@@ -72,10 +72,10 @@ __device__ __forceinline__ void unroll_stages(F& f, int i, std::integer_sequence
     (f(std::integral_constant<int, K>{}, i + K), ...);
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
+template <int D, bool CAUSAL, int NWV>
+__global__ __launch_bounds__(64 * NWV, 8 / NWV) void dkdv_bf16_kernel(BwdArgs a)
 {
-    using Cfg = DkdvBf16Cfg<D>;
+    using Cfg = DkdvBf16Cfg<D, NWV>;
     using QT = typename Cfg::QT;
     using Fmt = typename Cfg::Fmt;
     using VW = typename Cfg::VW;
@@ -104,10 +104,11 @@ __global__ __launch_bounds__(512, 1) void dkdv_bf16_kernel(BwdArgs a)
     const TileId id = map_tile(blockIdx.x, a.B, a.Hq, a.Hkv, S, nkt, false);
     const int b = id.b, hk = id.h / S, split = id.h % S;
     const int key0 = id.tile * BK;
-    // first key of this wave.  Waves w and w + 4 share a SIMD; pairing key
-    // blocks r and 7 - r there gives every SIMD the same number of causal
-    // tiles that one of its waves skips (below).
-    const int kw = key0 + 32 * (w < 4 ? w : 11 - w);
+    // first key of this wave.  With eight waves, w and w + 4 share a SIMD;
+    // pairing key blocks r and 7 - r there gives every SIMD the same number
+    // of causal tiles that one of its waves skips (below).  With four, each
+    // wave has a SIMD of the workgroup to itself.
+    const int kw = Cfg::NW == 4 ? key0 + 32 * w : key0 + 32 * (w < 4 ? w : 11 - w);
     const int krow = kw + c;       // the key this lane owns
 
     const size_t kvoff = (size_t)(b * a.Hkv + hk) * a.Tk * D;
@@ -455,10 +456,10 @@ static hipError_t sum_partials(const float* part, void* out, long plane, int S, 
 // dQ^T += K^T dS^T with dS^T straight from registers; K^T is read transposed
 // from the K tile.  No atomics: each dQ row is owned by one wave.
 // ---------------------------------------------------------------------------
-template <int D>  // head size of the tensors in memory
+template <int D, int NWV>  // head size of the tensors in memory; waves per workgroup
 struct DqBf16Cfg {
     static constexpr int DT = tile_dim(D);  // head size of the tiles and products
-    static constexpr int NW = 8;
+    static constexpr int NW = NWV;          // 8: two per SIMD; 4: one, two workgroups per CU
     static constexpr int NT = 64 * NW;
     static constexpr int BR = 32 * NW;  // query rows per workgroup
     static constexpr int BC = 64;       // keys per tile
@@ -481,10 +482,10 @@ struct DqBf16Cfg {
     static_assert(AHEAD + 2 <= NSTAGE, "a stage is refilled only after the tile after it was used");
 };
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
+template <int D, bool CAUSAL, int NWV>
+__global__ __launch_bounds__(64 * NWV, 8 / NWV) void dq_bf16_kernel(BwdArgs a)
 {
-    using Cfg = DqBf16Cfg<D>;
+    using Cfg = DqBf16Cfg<D, NWV>;
     using KT = typename Cfg::KT;
     using Fmt = typename Cfg::Fmt;
     using VT = typename Cfg::VT;
@@ -512,9 +513,10 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
     const int b = id.b, hq = id.h / S, split = id.h % S;
     const int hk = hq / (a.Hq / a.Hkv);
     const int q0 = id.tile * BR;
-    // first query of this wave.  Waves w and w + 4 share a SIMD; pairing row
-    // blocks r and 7 - r there evens out the causal tiles their waves skip.
-    const int qw = q0 + 32 * (w < 4 ? w : 11 - w);
+    // first query of this wave.  With eight waves, w and w + 4 share a SIMD;
+    // pairing row blocks r and 7 - r there evens out the causal tiles their
+    // waves skip.  With four, each wave has a SIMD of the workgroup to itself.
+    const int qw = NWAVE == 4 ? q0 + 32 * w : q0 + 32 * (w < 4 ? w : 11 - w);
     const int qrow = qw + c;  // the query this lane owns
 
     const size_t qoff = (size_t)(b * a.Hq + hq) * a.Tq * D;
@@ -776,12 +778,12 @@ __global__ __launch_bounds__(512, 1) void dq_bf16_kernel(BwdArgs a)
     }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int NWV>
 static hipError_t launch_dq(const BwdArgs& a, hipStream_t stream)
 {
-    using Cfg = DqBf16Cfg<D>;
-    static_assert(Cfg::SMEM <= 160 * 1024, "LDS budget");
-    auto kern = dq_bf16_kernel<D, CAUSAL>;
+    using Cfg = DqBf16Cfg<D, NWV>;
+    static_assert(Cfg::SMEM * (8 / NWV) <= 160 * 1024, "LDS budget");
+    auto kern = dq_bf16_kernel<D, CAUSAL, NWV>;
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::SMEM);
     if (attr != hipSuccess) return attr;
@@ -795,17 +797,21 @@ static hipError_t launch_dq(const BwdArgs& a, hipStream_t stream)
 
 hipError_t launch_bwd_dq_bf16(const BwdArgs& a, int D, bool causal, hipStream_t stream)
 {
-    if (D == 64) return causal ? launch_dq<64, true>(a, stream) : launch_dq<64, false>(a, stream);
-    if (D == 96) return causal ? launch_dq<96, true>(a, stream) : launch_dq<96, false>(a, stream);
-    return causal ? launch_dq<128, true>(a, stream) : launch_dq<128, false>(a, stream);
+    if (D == 64) {
+        if (dq_rows(a.B, a.Hq, a.Tq, D) == 128)
+            return causal ? launch_dq<64, true, 4>(a, stream) : launch_dq<64, false, 4>(a, stream);
+        return causal ? launch_dq<64, true, 8>(a, stream) : launch_dq<64, false, 8>(a, stream);
+    }
+    if (D == 96) return causal ? launch_dq<96, true, 8>(a, stream) : launch_dq<96, false, 8>(a, stream);
+    return causal ? launch_dq<128, true, 8>(a, stream) : launch_dq<128, false, 8>(a, stream);
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int NWV>
 static hipError_t launch_dkdv(const BwdArgs& a, hipStream_t stream)
 {
-    using Cfg = DkdvBf16Cfg<D>;
-    static_assert(Cfg::SMEM <= 160 * 1024, "LDS budget");
-    auto kern = dkdv_bf16_kernel<D, CAUSAL>;
+    using Cfg = DkdvBf16Cfg<D, NWV>;
+    static_assert(Cfg::SMEM * (8 / NWV) <= 160 * 1024, "LDS budget");
+    auto kern = dkdv_bf16_kernel<D, CAUSAL, NWV>;
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::SMEM);
     if (attr != hipSuccess) return attr;
@@ -819,6 +825,16 @@ static hipError_t launch_dkdv(const BwdArgs& a, hipStream_t stream)
     return sum_partials(a.part + (size_t)a.nsplit * plane, a.dv, plane, a.nsplit, 1.f, stream);
 }
 
+// The dK/dV kernel's tile table: keys per workgroup.  At D = 64 a workgroup
+// of four waves (128 keys) needs about 50 KiB of LDS, so several share a
+// compute unit; used where the 256-key blocks number fewer than kDkdvSmall.
+constexpr long kDkdvSmall = 256;
+int dkdv_keys(int B, int Hkv, int Tk, int D)
+{
+    const long blocks256 = (long)((Tk + 255) / 256) * B * Hkv;
+    return (D == 64 && blocks256 < kDkdvSmall) ? 128 : 256;
+}
+
 // Chunks per key block for the bf16 dK/dV kernel: enough workgroups for about
 // two per compute unit when the key blocks alone are too few (few kv heads,
 // short keys), at most 8, and at least 8 (query head, query tile) pairs per
@@ -826,9 +842,9 @@ static hipError_t launch_dkdv(const BwdArgs& a, hipStream_t stream)
 // workspace from the shapes alone.
 int dkdv_nsplit(int B, int Hq, int Hkv, int Tq, int Tk, int D)
 {
-    (void)D;
     constexpr long kTarget = 512;
-    const long wgs = (long)((Tk + 255) / 256) * B * Hkv;
+    const int bk = dkdv_keys(B, Hkv, Tk, D);
+    const long wgs = (long)((Tk + bk - 1) / bk) * B * Hkv;
     if (wgs <= 0 || wgs >= kTarget) return 1;
     long s = (kTarget + wgs - 1) / wgs;
     s = s < 8 ? s : 8;
@@ -837,44 +853,65 @@ int dkdv_nsplit(int B, int Hq, int Hkv, int Tq, int Tk, int D)
     return (int)(s < cap ? s : cap);
 }
 
+// The dQ kernel's tile table: query rows per workgroup.  At D = 64 its
+// stages take 64 KiB, so two workgroups of four waves (128 rows) share a
+// compute unit.  Measured against 256-row blocks split in two (one process):
+// causal B=2 Hq=8 T=512 18.1 -> 14.7 us, but T=4096 (256 blocks of 256
+// rows) 83.0 -> 84.7 us; so 128 rows where the 256-row blocks number fewer
+// than the 256 compute units.
+int dq_rows(int B, int Hq, int Tq, int D)
+{
+    const long blocks256 = (long)((Tq + 255) / 256) * B * Hq;
+    return (D == 64 && blocks256 < 256) ? 128 : 256;
+}
+
 // Chunks of the key range per query block for the bf16 dQ kernel: about two
 // workgroups per compute unit when the query blocks alone are too few, at
-// most 8, and at least 4 key tiles per chunk.
+// most 8, and at least 4 key tiles per chunk (8 with 128-row blocks).
 int dq_nsplit(int B, int Hq, int Hkv, int Tq, int Tk, int D)
 {
     (void)Hkv;
-    (void)D;
     constexpr long kTarget = 512;
-    const long wgs = (long)((Tq + 255) / 256) * B * Hq;
+    const int br = dq_rows(B, Hq, Tq, D);
+    const long wgs = (long)((Tq + br - 1) / br) * B * Hq;
     if (wgs <= 0 || wgs >= kTarget) return 1;
     long s = (kTarget + wgs - 1) / wgs;
     s = s < 8 ? s : 8;
     const long tiles = (Tk + 63) / 64;
-    const long cap = tiles / 4 > 1 ? tiles / 4 : 1;
+    const long per = br == 128 ? 8 : 4;
+    const long cap = tiles / per > 1 ? tiles / per : 1;
     return (int)(s < cap ? s : cap);
 }
 
 hipError_t launch_bwd_dkdv_bf16(const BwdArgs& a, int D, bool causal, hipStream_t stream)
 {
-    if (D == 64) return causal ? launch_dkdv<64, true>(a, stream) : launch_dkdv<64, false>(a, stream);
-    if (D == 96) return causal ? launch_dkdv<96, true>(a, stream) : launch_dkdv<96, false>(a, stream);
-    return causal ? launch_dkdv<128, true>(a, stream) : launch_dkdv<128, false>(a, stream);
+    if (D == 64) {
+        if (dkdv_keys(a.B, a.Hkv, a.Tk, D) == 128)
+            return causal ? launch_dkdv<64, true, 4>(a, stream) : launch_dkdv<64, false, 4>(a, stream);
+        return causal ? launch_dkdv<64, true, 8>(a, stream) : launch_dkdv<64, false, 8>(a, stream);
+    }
+    if (D == 96) return causal ? launch_dkdv<96, true, 8>(a, stream) : launch_dkdv<96, false, 8>(a, stream);
+    return causal ? launch_dkdv<128, true, 8>(a, stream) : launch_dkdv<128, false, 8>(a, stream);
 }
 
 // Every kernel variant is instantiated explicitly: referencing a kernel
 // template only from a launcher has left some instantiations without their
 // host-side handle.
-template __global__ void dkdv_bf16_kernel<64, true>(BwdArgs);
-template __global__ void dkdv_bf16_kernel<64, false>(BwdArgs);
-template __global__ void dkdv_bf16_kernel<96, true>(BwdArgs);
-template __global__ void dkdv_bf16_kernel<96, false>(BwdArgs);
-template __global__ void dkdv_bf16_kernel<128, true>(BwdArgs);
-template __global__ void dkdv_bf16_kernel<128, false>(BwdArgs);
-template __global__ void dq_bf16_kernel<64, true>(BwdArgs);
-template __global__ void dq_bf16_kernel<64, false>(BwdArgs);
-template __global__ void dq_bf16_kernel<96, true>(BwdArgs);
-template __global__ void dq_bf16_kernel<96, false>(BwdArgs);
-template __global__ void dq_bf16_kernel<128, true>(BwdArgs);
-template __global__ void dq_bf16_kernel<128, false>(BwdArgs);
+template __global__ void dkdv_bf16_kernel<64, true, 8>(BwdArgs);
+template __global__ void dkdv_bf16_kernel<64, false, 8>(BwdArgs);
+template __global__ void dkdv_bf16_kernel<64, true, 4>(BwdArgs);
+template __global__ void dkdv_bf16_kernel<64, false, 4>(BwdArgs);
+template __global__ void dkdv_bf16_kernel<96, true, 8>(BwdArgs);
+template __global__ void dkdv_bf16_kernel<96, false, 8>(BwdArgs);
+template __global__ void dkdv_bf16_kernel<128, true, 8>(BwdArgs);
+template __global__ void dkdv_bf16_kernel<128, false, 8>(BwdArgs);
+template __global__ void dq_bf16_kernel<64, true, 8>(BwdArgs);
+template __global__ void dq_bf16_kernel<64, false, 8>(BwdArgs);
+template __global__ void dq_bf16_kernel<64, true, 4>(BwdArgs);
+template __global__ void dq_bf16_kernel<64, false, 4>(BwdArgs);
+template __global__ void dq_bf16_kernel<96, true, 8>(BwdArgs);
+template __global__ void dq_bf16_kernel<96, false, 8>(BwdArgs);
+template __global__ void dq_bf16_kernel<128, true, 8>(BwdArgs);
+template __global__ void dq_bf16_kernel<128, false, 8>(BwdArgs);
 
 }  // namespace fa

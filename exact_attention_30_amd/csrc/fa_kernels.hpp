@@ -74,6 +74,8 @@ int dq_nsplit(int B, int Hq, int Hkv, int Tq, int Tk, int D);
 // chunks the bf16 forward splits each query block's key range into
 int fwd_nsplit(int B, int Hq, int Hkv, int Tq, int Tk, int D);
 int fwd_rows(int B, int Hq, int Tq, int D);  // query rows per workgroup, bf16 forward
+int dq_rows(int B, int Hq, int Tq, int D);   // query rows per workgroup, bf16 dQ
+int dkdv_keys(int B, int Hkv, int Tk, int D);  // keys per workgroup, bf16 dK/dV
 hipError_t launch_bwd_dkdv_bf16(const BwdArgs& a, int D, bool causal, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, int D, int dtype, bool causal, hipStream_t stream);
 hipError_t launch_bwd_dq_bf16(const BwdArgs& a, int D, bool causal, hipStream_t stream);

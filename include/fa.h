@@ -133,16 +133,23 @@ fa_status fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float*
 size_t fa_fwd_split_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int D, fa_dtype dt);
 
 /*
- * Query rows per workgroup of the forward for these shapes (its static tile
- * table; the blocked loop of "FlashAttention: l'attenzione che non spreca
- * memoria", «L'idea: lavorare a tessere», the tile sizes of "Optimización de
- * Flash Attention ...", «La pila de optimización»).  bf16: 256 (eight waves),
- * or 128 (four waves, two workgroups per compute unit) at D = 64 when the
- * 256-row blocks number fewer than 512; fp32: 128.  The split rule counts
- * these blocks.  Unsplit, a row's O and lse do not depend on this choice.
- * Host only; returns 0 for shapes or types the forward rejects.
+ * The static tile table of the bf16 kernels (the blocked loops of
+ * "FlashAttention: l'attenzione che non spreca memoria", «L'idea: lavorare a
+ * tessere»; the tile sizes of "Optimización de Flash Attention ...", «La pila
+ * de optimización»): the rows of one workgroup's block for these shapes.
+ *   FA_STAGE_FWD: query rows of the forward; 256 (eight waves), or 128 (four
+ *       waves, two workgroups per compute unit) at D = 64 when the 256-row
+ *       blocks number fewer than 512.
+ *   FA_STAGE_DQ: query rows of the dQ stage; 128 at D = 64 when the 256-row
+ *       blocks number fewer than 256, else 256.
+ *   FA_STAGE_DKDV: keys of the dK/dV stage (H = Hkv, T = Tk); 128 at D = 64
+ *       when the 256-key blocks number fewer than 256, else 256.
+ * fp32: 128 always (four waves of 32).  The split rules count these
+ * blocks; unsplit, no result depends on the choice.  Host only; returns 0 for
+ * shapes, types or stages the kernels reject.
  */
-int fa_fwd_block_rows(int B, int Hq, int Tq, int D, fa_dtype dt);
+typedef enum { FA_STAGE_FWD = 0, FA_STAGE_DQ = 1, FA_STAGE_DKDV = 2 } fa_stage;
+int fa_block_rows(fa_stage stage, int B, int H, int T, int D, fa_dtype dt);
 fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
                        void* partial, int B, int Hq, int Hkv, int Tq, int Tk, int D, float scale,
                        int causal, int q_offset, fa_dtype dt, void* stream);

@@ -285,3 +285,31 @@ def test_noalloc_rejects_on_the_host(lib):
     assert noalloc(lib) == SCRATCH
     # Delta alone: 8 x 32 x 131072 rows x 4 bytes = 128 MiB
     assert noalloc(lib, B=8, Hq=32, Hkv=8, Tq=131072, Tk=131072) == SCRATCH
+
+
+def test_block_rows_table(lib):
+    """fa_block_rows reports the tile table documented in fa.h (host only)."""
+    from tests import lazy_model
+
+    lib.fa_block_rows.argtypes = [ctypes.c_int] * 6
+    lib.fa_block_rows.restype = ctypes.c_int
+    FWD, DQ, DKDV = 0, 1, 2
+    BF16, FP32 = 0, 1
+    # forward: 128 rows at D = 64 below 512 blocks of 256 rows
+    assert lib.fa_block_rows(FWD, 2, 8, 4096, 64, BF16) == 128   # 256 blocks
+    assert lib.fa_block_rows(FWD, 2, 16, 4096, 64, BF16) == 256  # 512 blocks
+    assert lib.fa_block_rows(FWD, 1, 4, 1000, 128, BF16) == 256
+    assert lib.fa_block_rows(FWD, 1, 4, 1000, 96, BF16) == 256
+    # dQ and dK/dV: 128 at D = 64 below 256 blocks
+    assert lib.fa_block_rows(DQ, 2, 8, 512, 64, BF16) == 128
+    assert lib.fa_block_rows(DQ, 2, 8, 4096, 64, BF16) == 256
+    assert lib.fa_block_rows(DKDV, 2, 8, 512, 64, BF16) == 128
+    assert lib.fa_block_rows(DKDV, 2, 8, 4096, 64, BF16) == 256
+    for st in (FWD, DQ, DKDV):
+        assert lib.fa_block_rows(st, 1, 2, 100, 64, FP32) == 128
+        assert lib.fa_block_rows(st, 1, 2, 100, 80, BF16) == 0   # unsupported D
+        assert lib.fa_block_rows(st, -1, 2, 100, 64, BF16) == 0  # a shape error
+    assert lib.fa_block_rows(3, 1, 2, 100, 64, BF16) == 0         # no such stage
+    # the test-side model of the forward follows the same table
+    for B, H, T, D in ((2, 8, 4096, 64), (2, 16, 4096, 64), (1, 4, 1500, 64), (1, 4, 700, 128)):
+        assert lib.fa_block_rows(FWD, B, H, T, D, BF16) == lazy_model.block_rows(B, H, T, D)

@@ -401,7 +401,7 @@ def test_forward_tile_invariance(causal, Hq, Hkv, T):
     equal, bit for bit, the same heads inside a batch of two (256-row
     blocks)."""
     D = 64
-    assert fa.fwd_block_rows(1, Hq, T, D) == 128 and fa.fwd_block_rows(2, Hq, T, D) == 256
+    assert fa.block_rows("fwd", 1, Hq, T, D) == 128 and fa.block_rows("fwd", 2, Hq, T, D) == 256
     x = to_dev(make_inputs(2, Hq, Hkv, T, D, bf16, seed=31 + T))
     say(f"tile invariance Hq={Hq} Hkv={Hkv} T={T} causal={causal}")
     o2, l2 = fa.fwd(x["q"], x["k"], x["v"], causal=causal)
@@ -409,6 +409,47 @@ def test_forward_tile_invariance(causal, Hq, Hkv, T):
                     causal=causal)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2[:1]) and torch.equal(l1, l2[:1])
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_dq_tile_invariance(causal):
+    """The dQ stage's tile table: at D = 64, fewer than 256 blocks of 256
+    rows run 128-row workgroups of four waves, more run 256-row workgroups.
+    Unsplit, a row's dQ (and the Delta the stage forms) does not depend on
+    that choice: a batch of one (128-row blocks) equals, bit for bit, the same
+    heads inside a batch of two (256-row blocks)."""
+    Hq, Hkv, T, D = 16, 8, 2048, 64
+    assert fa.block_rows("dq", 1, Hq, T, D) == 128 and fa.block_rows("dq", 2, Hq, T, D) == 256
+    x = to_dev(make_inputs(2, Hq, Hkv, T, D, bf16, seed=57))
+    say(f"dQ tile invariance Hq={Hq} Hkv={Hkv} T={T} causal={causal}")
+    o, lse = fa.fwd(x["q"], x["k"], x["v"], causal=causal)
+    one = {n: t[:1].contiguous() for n, t in x.items()}
+    dq2, d2 = fa.bwd_dq_delta(x["q"], x["k"], x["v"], o, x["dout"], lse, causal=causal)
+    dq1, d1 = fa.bwd_dq_delta(one["q"], one["k"], one["v"], o[:1].contiguous(), one["dout"],
+                              lse[:1].contiguous(), causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(dq1, dq2[:1]) and torch.equal(d1, d2[:1])
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_dkdv_tile_invariance(causal):
+    """The dK/dV stage's tile table: at D = 64, fewer than 256 blocks of 256
+    keys run 128-key workgroups of four waves, more run 256-key workgroups.
+    A wave visits the same query tiles in the same order either way, so
+    unsplit, dK and dV of a batch of one (128-key blocks) equal, bit for bit,
+    the same kv heads inside a batch of two (256-key blocks)."""
+    Hq, Hkv, T, D = 16, 8, 4096, 64
+    assert fa.block_rows("dkdv", 1, Hkv, T, D) == 128 and fa.block_rows("dkdv", 2, Hkv, T, D) == 256
+    x = to_dev(make_inputs(2, Hq, Hkv, T, D, bf16, seed=58))
+    say(f"dK/dV tile invariance Hq={Hq} Hkv={Hkv} T={T} causal={causal}")
+    o, lse = fa.fwd(x["q"], x["k"], x["v"], causal=causal)
+    delta = fa.bwd_preprocess(o, x["dout"])
+    one = {n: t[:1].contiguous() for n, t in x.items()}
+    dk2, dv2 = fa.bwd_dkdv(x["q"], x["k"], x["v"], x["dout"], lse, delta, causal=causal)
+    dk1, dv1 = fa.bwd_dkdv(one["q"], one["k"], one["v"], one["dout"], lse[:1].contiguous(),
+                           delta[:1].contiguous(), causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(dk1, dk2[:1]) and torch.equal(dv1, dv2[:1])
 
 
 @pytest.mark.parametrize("shape", [(1, 1, 1, 2048, 2048, 128), (1, 4, 2, 1500, 1500, 64),

@@ -415,14 +415,19 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void dkdv_bf16_kernel(BwdArgs a)
 // out = scale * (sum of the S fp32 partials part[s * plane + .]), added in
 // chunk order (so the result does not depend on scheduling), rounded to
 // bf16.  One thread per 8 consecutive elements; n8 = plane / 8.
-__global__ __launch_bounds__(256) void sum_partials_kernel(const float* part, bf16* out, long n8,
-                                                           long plane, int S, float scale)
+__global__ __launch_bounds__(256) void sum_partials_kernel(const float* part, bf16* out0, bf16* out1,
+                                                           long n8, long plane, int S, float scale0,
+                                                           float scale1)
 {
     const long i = (long)blockIdx.x * 256 + threadIdx.x;
     if (i >= n8) return;
+    // blockIdx.y: the first tensor's S planes, or the second's after them
+    const bool second = blockIdx.y == 1;
+    const float* base = part + (second ? (size_t)S * plane : 0);
+    const float scale = second ? scale1 : scale0;
     f32x4 lo = {}, hi = {};
     for (int s = 0; s < S; ++s) {
-        const f32x4* p = reinterpret_cast<const f32x4*>(part + (size_t)s * plane) + 2 * i;
+        const f32x4* p = reinterpret_cast<const f32x4*>(base + (size_t)s * plane) + 2 * i;
         lo += p[0];
         hi += p[1];
     }
@@ -432,15 +437,18 @@ __global__ __launch_bounds__(256) void sum_partials_kernel(const float* part, bf
         x[e] = (bf16)(lo[e] * scale);
         x[4 + e] = (bf16)(hi[e] * scale);
     }
-    reinterpret_cast<bf16x8*>(out)[i] = x;
+    reinterpret_cast<bf16x8*>(second ? out1 : out0)[i] = x;
 }
 
-static hipError_t sum_partials(const float* part, void* out, long plane, int S, float scale,
-                               hipStream_t stream)
+// out0 (and out1, when given: dK and dV in one launch) = scale * the sum, in
+// chunk order, of the S fp32 partial planes of each (out1's follow out0's)
+static hipError_t sum_partials(const float* part, void* out0, void* out1, long plane, int S,
+                               float scale0, float scale1, hipStream_t stream)
 {
     const long n8 = plane / 8;
-    hipLaunchKernelGGL(sum_partials_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream,
-                       part, static_cast<bf16*>(out), n8, plane, S, scale);
+    hipLaunchKernelGGL(sum_partials_kernel, dim3((unsigned)((n8 + 255) / 256), out1 ? 2 : 1), dim3(256),
+                       0, stream, part, static_cast<bf16*>(out0), static_cast<bf16*>(out1), n8, plane,
+                       S, scale0, scale1);
     return hipGetLastError();
 }
 
@@ -792,7 +800,8 @@ static hipError_t launch_dq(const BwdArgs& a, hipStream_t stream)
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Cfg::NT), Cfg::SMEM, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1) return e;
-    return sum_partials(a.part, a.dq, (long)a.B * a.Hq * a.Tq * D, a.nsplit, a.scale, stream);
+    return sum_partials(a.part, a.dq, nullptr, (long)a.B * a.Hq * a.Tq * D, a.nsplit, a.scale, 0.f,
+                        stream);
 }
 
 hipError_t launch_bwd_dq_bf16(const BwdArgs& a, int D, bool causal, hipStream_t stream)
@@ -821,8 +830,7 @@ static hipError_t launch_dkdv(const BwdArgs& a, hipStream_t stream)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1) return e;
     const long plane = (long)a.B * a.Hkv * a.Tk * D;
-    if ((e = sum_partials(a.part, a.dk, plane, a.nsplit, a.scale, stream)) != hipSuccess) return e;
-    return sum_partials(a.part + (size_t)a.nsplit * plane, a.dv, plane, a.nsplit, 1.f, stream);
+    return sum_partials(a.part, a.dk, a.dv, plane, a.nsplit, a.scale, 1.f, stream);
 }
 
 // The dK/dV kernel's tile table: keys per workgroup.  At D = 64 a workgroup

@@ -56,6 +56,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="C5")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--atomic-bwd", action="store_true",
+                   help="time fa_bwd against fa_bwd_atomic (dQ by atomic adds) on a D = 64 "
+                        "workload; prints its own JSON line")
     p.add_argument("--graph", action="store_true",
                    help="time replays of a captured HIP graph of one step instead of eager steps")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -110,6 +113,57 @@ def gemm_reference():
     print(json.dumps({"gemm_reference": f"torch.matmul bf16 {n}x{n}x{n}, random N(0,1)",
                       "ms": round(ms, 4), "tflops": round(tf, 1),
                       "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}), flush=True)
+
+
+def atomic_bwd_compare(args):
+    """The two backward formulations of "L'attention fusionnée", «La passe
+    arrière», on one D = 64 workload: fa_bwd (a dQ kernel that recomputes S and
+    dP, then dK/dV) against fa_bwd_atomic (one dK/dV kernel that adds dQ with
+    atomic adds), alternated over K rounds on the same inputs; prints one JSON
+    line with each one's median time and credited TFLOP/s."""
+    import statistics
+
+    import torch
+
+    import exact_attention_30_amd as fa
+    from workloads import WORKLOADS, workload_inputs
+
+    w = WORKLOADS[args.workload]
+    if w.D != 64 or w.dtype != torch.bfloat16 or w.Tkv != w.T or not w.backward:
+        sys.exit(f"bench.py --atomic-bwd: {w.name} is not a bf16 D = 64 fwd+bwd workload with "
+                 "equal lengths (fa_bwd_atomic's scope)")
+    d = {k: v.cuda() for k, v in workload_inputs(w).items()}
+    q, k, v, do = d["q"], d["k"], d["v"], d["dout"]
+    o, lse = fa.fwd(q, k, v, scale=w.scale, causal=w.causal)
+    ws2 = torch.empty(max(fa.bwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.T, w.D), 16),
+                      dtype=torch.uint8, device="cuda")
+    wsa = torch.empty(max(fa.bwd_atomic_workspace_bytes(w.B, w.Hq, w.T, w.D), 16),
+                      dtype=torch.uint8, device="cuda")
+    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    runs = {
+        "two_kernel": lambda: fa.bwd(q, k, v, o, do, lse, scale=w.scale, causal=w.causal,
+                                     workspace=ws2, grads=grads),
+        "atomic": lambda: fa.bwd_atomic(q, k, v, o, do, lse, scale=w.scale, causal=w.causal,
+                                        workspace=wsa, grads=grads),
+    }
+    for f in runs.values():
+        for _ in range(max(args.warmup, 1)):
+            f()
+    torch.cuda.synchronize()
+    times = {n: [] for n in runs}
+    for _ in range(args.steps):
+        for n, f in runs.items():
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            f()
+            e1.record()
+            torch.cuda.synchronize()
+            times[n].append(e0.elapsed_time(e1))
+    out = {"atomic_bwd_compare": describe(w), "steps": args.steps}
+    for n, t in times.items():
+        ms = statistics.median(t)
+        out[n] = {"ms": round(ms, 4), "credited_tflops": round(w.bwd_flop / (ms * 1e-3) / 1e12, 2)}
+    print(json.dumps(out), flush=True)
 
 
 def gemm_flop(w, n_gemm):
@@ -355,6 +409,9 @@ def main():
     args = parse()
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
+        return
+    if args.atomic_bwd:
+        atomic_bwd_compare(args)
         return
     if args.gemm_reference:
         gemm_reference()

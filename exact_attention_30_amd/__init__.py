@@ -67,6 +67,9 @@ SIGNATURES = {
                          _i, _i, _i, _vp], ctypes.c_int),
     "fa_fwd_split_bytes": ([_i, _i, _i, _i, _i, _i, _i], ctypes.c_size_t),
     "fa_block_rows": ([_i, _i, _i, _i, _i, _i], _i),
+    "fa_bwd_atomic_workspace_bytes": ([_i, _i, _i, _i, _i], ctypes.c_size_t),
+    "fa_bwd_atomic": ([_vp, _vp, _vp, _vp, _vp, _fp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i,
+                       _i, _vp], ctypes.c_int),
     "fa_fwd_split": ([_vp, _vp, _vp, _vp, _fp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _i, _i, _vp],
                      ctypes.c_int),
     "fa_fwd_fp8_workspace_bytes": ([_i, _i, _i, _i], ctypes.c_size_t),
@@ -353,6 +356,42 @@ def bwd(q, k, v, o, dout, lse, scale=None, causal: bool = True, workspace=None, 
     else:
         _check(lib.fa_bwd_kv(*ptrs, B, Hq, Hkv, Tq, Tk, D, _scale(scale, D), int(bool(causal)), off,
                              dt, _stream(q)), "fa_bwd_kv")
+    return dq, dk, dv
+
+
+def bwd_atomic_workspace_bytes(B, Hq, T, D, dtype=torch.bfloat16) -> int:
+    """Bytes of the workspace of bwd_atomic (0: unsupported shapes)."""
+    return int(library().fa_bwd_atomic_workspace_bytes(B, Hq, T, D, _DTYPES[dtype]))
+
+
+def bwd_atomic(q, k, v, o, dout, lse, scale=None, causal: bool = True, workspace=None, grads=None):
+    """The single-kernel backward with dQ accumulated by atomic adds
+    (fa_bwd_atomic; bf16, D = 64, equal query and key lengths); returns
+    (dq, dk, dv).  dK, dV are bitwise those of bwd_dkdv; dQ is not bitwise
+    reproducible."""
+    B, Hq, Hkv, Tq, Tk, D = _dims(q, k, v)
+    if Tq != Tk:
+        raise ValueError("bwd_atomic takes equal query and key lengths")
+    _expect(o, q.shape, "o")
+    _expect(dout, q.shape, "dout")
+    _expect(lse, (B, Hq, Tq), "lse", torch.float32)
+    if grads is not None:
+        for t, like, name in zip(grads, (q, k, v), ("dq", "dk", "dv")):
+            _expect(t, like.shape, name, q.dtype)
+    dt = _dtype_code(q, k, v, o, dout, *(grads or ()))
+    _same_device(q, lse, workspace)
+    dq, dk, dv = grads if grads is not None else (torch.empty_like(q), torch.empty_like(k),
+                                                  torch.empty_like(v))
+    ws_bytes = bwd_atomic_workspace_bytes(B, Hq, Tq, D, q.dtype)
+    ws = workspace if workspace is not None else torch.empty(max(ws_bytes, 16), dtype=torch.uint8,
+                                                             device=q.device)
+    if ws.numel() * ws.element_size() < ws_bytes:
+        raise ValueError("workspace too small")
+    _check(library().fa_bwd_atomic(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                   dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                   dv.data_ptr(), ws.data_ptr(), B, Hq, Hkv, Tq, D,
+                                   _scale(scale, D), int(bool(causal)), dt, _stream(q)),
+           "fa_bwd_atomic")
     return dq, dk, dv
 
 

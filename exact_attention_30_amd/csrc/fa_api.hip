@@ -558,4 +558,40 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                      causal, 0, dt, stream);
 }
 
+size_t fa_bwd_atomic_workspace_bytes(int B, int Hq, int T, int D, fa_dtype dt)
+{
+    if (check_kv(B, Hq, Hq, T, T, D, dt, false, 0) != FA_OK || dt != FA_BF16 || D != 64) return 0;
+    const size_t rows = (size_t)B * (size_t)Hq * (size_t)T;
+    return align256(rows * sizeof(float)) + rows * (size_t)D * sizeof(float);
+}
+
+fa_status fa_bwd_atomic(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        void* workspace, int B, int Hq, int Hkv, int T, int D, float scale,
+                        int causal, fa_dtype dt, void* stream)
+{
+    fa_status st = check_kv(B, Hq, Hkv, T, T, D, dt, causal != 0, 0);
+    if (st != FA_OK) return st;
+    if ((st = check_scale(scale)) != FA_OK) return st;
+    if (dt != FA_BF16 || D != 64) return FA_ERR_UNSUPPORTED;
+    if ((long long)B * T == 0) return FA_OK;
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) return FA_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+        !aligned(dout, 16) || !aligned(lse, 4) || !aligned(dq, 16) || !aligned(dk, 16) ||
+        !aligned(dv, 16) || !aligned(workspace, 16))
+        return FA_ERR_ALIGN;
+    // workspace: Delta, then the fp32 dQ accumulator
+    float* delta = static_cast<float*>(workspace);
+    float* acc = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                          align256((size_t)B * (size_t)Hq * (size_t)T * sizeof(float)));
+    if ((st = fa_bwd_preprocess(o, dout, delta, B, Hq, T, D, dt, stream)) != FA_OK) return st;
+    fa::BwdArgs a;
+    fill_bwd(a, q, k, v, dout, lse, delta, B, Hq, Hkv, T, T, 0, scale);
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.part = acc;
+    return from_hip(fa::launch_bwd_atomic_bf16(a, causal != 0, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

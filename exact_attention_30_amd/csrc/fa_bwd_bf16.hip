@@ -41,7 +41,8 @@
 
 namespace fa {
 
-template <int D, int NWV>  // head size of the tensors in memory; waves per workgroup
+// ADQ: the variant that also accumulates dQ with atomic adds (below)
+template <int D, int NWV, bool ADQ = false>  // head size in memory; waves per workgroup
 struct DkdvBf16Cfg {
     static constexpr int DT = tile_dim(D);  // head size of the tiles and products
     static constexpr int NW = NWV;          // 8: two per SIMD; 4: one, several workgroups per CU
@@ -58,7 +59,11 @@ struct DkdvBf16Cfg {
     using VW = RowFragTile<DT, 32, D>;  // V rows of one wave, in read order
     static constexpr int STATS = 512;  // L*log2(e) (64 floats) and Delta (64 floats)
     static constexpr int STAGE = 2 * QT::BYTES + STATS;
-    static constexpr int SMEM = NSTAGE * STAGE + NW * VW::BYTES;
+    // ADQ: per wave a 32 x 32 bf16 tile of dS (row query, column key) and a
+    // 32 x D fp32 tile of its part of dQ
+    static constexpr int DSW = 32 * 32 * 2;
+    static constexpr int RED = 32 * D * 4;
+    static constexpr int SMEM = NSTAGE * STAGE + NW * VW::BYTES + (ADQ ? NW * (DSW + RED) : 0);
     // every read offset of a stage fits the 16-bit immediate of a DS read
     static_assert((NSTAGE - 1) * STAGE + QT::BYTES + 16 * Fmt::ROWBYTES < 65536, "LDS immediates");
     static_assert(NSTAGE == 4, "two pairs of stages");
@@ -72,10 +77,12 @@ __device__ __forceinline__ void unroll_stages(F& f, int i, std::integer_sequence
     (f(std::integral_constant<int, K>{}, i + K), ...);
 }
 
-template <int D, bool CAUSAL, int NWV>
+template <int D, bool CAUSAL, int NWV, bool ADQ = false>
 __global__ __launch_bounds__(64 * NWV, 8 / NWV) void dkdv_bf16_kernel(BwdArgs a)
 {
-    using Cfg = DkdvBf16Cfg<D, NWV>;
+    using Cfg = DkdvBf16Cfg<D, NWV, ADQ>;
+    static_assert(!ADQ || (D == 64 && NWV == 8 && Cfg::NT * 4 == 32 * D),
+                  "the atomic dQ variant: D = 64, eight waves, four dQ elements per thread");
     using QT = typename Cfg::QT;
     using Fmt = typename Cfg::Fmt;
     using VW = typename Cfg::VW;
@@ -89,6 +96,9 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void dkdv_bf16_kernel(BwdArgs a)
     extern __shared__ __align__(1024) unsigned char smem[];
     unsigned char* stages = smem;
     unsigned char* Vs = smem + NSTAGE * STAGE;  // V rows of wave w at Vs + w * VW::BYTES
+    // ADQ: this wave's dS tile, and the waves' dQ parts [w][32][D]
+    [[maybe_unused]] unsigned char* dsw = Vs + Cfg::NW * VW::BYTES + (ADQ ? (threadIdx.x >> 6) * Cfg::DSW : 0);
+    [[maybe_unused]] float* red = reinterpret_cast<float*>(Vs + Cfg::NW * VW::BYTES + (ADQ ? Cfg::NW * Cfg::DSW : 0));
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -168,6 +178,21 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void dkdv_bf16_kernel(BwdArgs a)
     Frag<bf16> kf[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) kf[ks] = global_frag<bf16>(kh, krow, a.Tk, D, 16 * ks + 8 * g);
+    // ADQ: the B operand of dQ = dS K over this wave's 32 keys: for step t
+    // (keys 16t .. 16t + 15) and column block db, lane (g, c) holds
+    // K[kw + 16t + 8g + e][32db + c], e = 0..7 (zero past Tk)
+    [[maybe_unused]] bf16x8 ktf[ADQ ? 2 : 1][ADQ ? NDB : 1];
+    if constexpr (ADQ) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int key = kw + 16 * t + 8 * g + e;
+                    ktf[t][db][e] = key < a.Tk ? kh[(size_t)key * D + 32 * db + c] : (bf16)0.f;
+                }
+    }
 
     // Q, dO rows (A of S, dP) and Q^T, dO^T (A of dK^T, dV^T) in the
     // stages; V rows 32w + c (B of dP) in read order
@@ -219,6 +244,8 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void dkdv_bf16_kernel(BwdArgs a)
         constexpr uint32_t QI = ST * STAGE, OI = QI + QT::BYTES;  // Q_t, dO_t in the stage
         const bool pad = i >= n;
         const int qb = bti * BQ;
+        const int hq_t = hk * G + bh;  // this tile's query head
+        (void)hq_t;
         if (++bh == G) {
             bh = 0;
             --bti;
@@ -226,7 +253,8 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void dkdv_bf16_kernel(BwdArgs a)
         // A tile that no key of this wave sees (or a padding tile) adds
         // nothing: the wave skips its products (the other wave of its SIMD
         // has the matrix pipe to itself meanwhile) but not the barrier below.
-        if (!(pad || (CAUSAL && qb + BQ - 1 + a.off < kw))) {
+        const bool work = !(pad || (CAUSAL && qb + BQ - 1 + a.off < kw));
+        if (work) {
             // S starts at -L*log2(e)/c and dP at -Delta of their query rows
             // (rows 8*(r/4) + 4g + r%4 of this lane's registers; waves 0 and 1
             // prepared them in the stage): after the products c*s is the
@@ -353,6 +381,55 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void dkdv_bf16_kernel(BwdArgs a)
                     mma(dk[db], frag(rt[u % (TAH + 1)]), t ? sf1 : sf0);
                 }
                 __builtin_amdgcn_sched_barrier(0);
+            }
+            if constexpr (ADQ) {
+                // dS, rounded to bf16 as the dK product uses it, into this
+                // wave's tile (row query 8(r/4) + 4g + r%4, column key c),
+                // read back as the A operand of dQ = dS K (row query c, keys
+                // 16t + 8g .. + 7), then this wave's part of the tile's dQ
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    reinterpret_cast<bf16*>(dsw)[(8 * (r >> 2) + 4 * g + (r & 3)) * 32 + c] = (bf16)dp[r];
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                f32x16 dqa[NDB];
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) dqa[db] = f32x16{};
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const bf16x8 af = *reinterpret_cast<const bf16x8*>(dsw + (c * 32 + 16 * t + 8 * g) * 2);
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db)
+                        dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, ktf[t][db], dqa[db], 0, 0, 0);
+                }
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        red[((tid >> 6) * 32 + 8 * (r >> 2) + 4 * g + (r & 3)) * D + 32 * db + c] = dqa[db][r];
+            }
+        }
+        if constexpr (ADQ) {
+            // The tile's dQ: the waves' parts summed in wave order (a wave
+            // that skipped the tile adds zeros) and added to the fp32 dQ of
+            // its rows with atomic adds (a.part: [B][Hq][Tq][D], zeroed
+            // before the launch; dK/dV workgroups of other keys add theirs)
+            if (!pad) {
+                if (!work) {
+#pragma unroll
+                    for (int r = 0; r < 32 * D / 64; ++r) red[((tid >> 6) * 32) * D + r * 64 + lane] = 0.f;
+                }
+                sync_lds();
+                const int e0 = 4 * tid;  // 32 x D = 2048 elements, four per thread
+                const int qr = e0 / D, d = e0 % D;
+                f32x4 sum = {};
+#pragma unroll
+                for (int ww = 0; ww < Cfg::NW; ++ww) sum += *reinterpret_cast<const f32x4*>(red + (ww * 32 + qr) * D + d);
+                if (qb + qr < a.Tq) {
+                    float* dst = a.part + ((size_t)(b * a.Hq + hq_t) * a.Tq + qb + qr) * D + d;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) unsafeAtomicAdd(dst + e, sum[e]);
+                }
+                sync_lds();
             }
         }
         // One barrier per pair (measured 1.4 % faster than one per tile: the
@@ -815,12 +892,12 @@ hipError_t launch_bwd_dq_bf16(const BwdArgs& a, int D, bool causal, hipStream_t 
     return causal ? launch_dq<128, true, 8>(a, stream) : launch_dq<128, false, 8>(a, stream);
 }
 
-template <int D, bool CAUSAL, int NWV>
+template <int D, bool CAUSAL, int NWV, bool ADQ = false>
 static hipError_t launch_dkdv(const BwdArgs& a, hipStream_t stream)
 {
-    using Cfg = DkdvBf16Cfg<D, NWV>;
+    using Cfg = DkdvBf16Cfg<D, NWV, ADQ>;
     static_assert(Cfg::SMEM * (8 / NWV) <= 160 * 1024, "LDS budget");
-    auto kern = dkdv_bf16_kernel<D, CAUSAL, NWV>;
+    auto kern = dkdv_bf16_kernel<D, CAUSAL, NWV, ADQ>;
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::SMEM);
     if (attr != hipSuccess) return attr;
@@ -902,6 +979,49 @@ hipError_t launch_bwd_dkdv_bf16(const BwdArgs& a, int D, bool causal, hipStream_
     return causal ? launch_dkdv<128, true, 8>(a, stream) : launch_dkdv<128, false, 8>(a, stream);
 }
 
+// The single-kernel backward of the pages' FA2 description ("L'attention
+// fusionnée", «La passe arrière»: dK and dV in registers, dQ accumulated with
+// atomic adds), at D = 64: the fp32 dQ accumulator in a.part ([B][Hq][Tq][D])
+// is zeroed, the dK/dV kernel adds every tile's dQ to it, and a last kernel
+// scales and rounds it into a.dq.  The order of the atomic adds varies from
+// run to run, so dQ is not bitwise reproducible (dK, dV are).
+__global__ __launch_bounds__(256) void zero_f32_kernel(float* p, long n4)
+{
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i < n4) reinterpret_cast<f32x4*>(p)[i] = f32x4{};
+}
+
+__global__ __launch_bounds__(256) void dq_from_acc_kernel(const float* acc, bf16* dq, long n8, float scale)
+{
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n8) return;
+    const f32x4* p = reinterpret_cast<const f32x4*>(acc) + 2 * i;
+    const f32x4 lo = p[0], hi = p[1];
+    bf16x8 x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        x[e] = (bf16)(lo[e] * scale);
+        x[4 + e] = (bf16)(hi[e] * scale);
+    }
+    reinterpret_cast<bf16x8*>(dq)[i] = x;
+}
+
+hipError_t launch_bwd_atomic_bf16(const BwdArgs& a0, bool causal, hipStream_t stream)
+{
+    BwdArgs a = a0;
+    a.nsplit = 1;
+    const long n = (long)a.B * a.Hq * a.Tq * 64;
+    hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, stream,
+                       a.part, n / 4);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = causal ? launch_dkdv<64, true, 8, true>(a, stream) : launch_dkdv<64, false, 8, true>(a, stream);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(dq_from_acc_kernel, dim3((unsigned)((n / 8 + 255) / 256)), dim3(256), 0, stream,
+                       a.part, static_cast<bf16*>(a.dq), n / 8, a.scale);
+    return hipGetLastError();
+}
+
 // Every kernel variant is instantiated explicitly: referencing a kernel
 // template only from a launcher has left some instantiations without their
 // host-side handle.
@@ -913,6 +1033,8 @@ template __global__ void dkdv_bf16_kernel<96, true, 8>(BwdArgs);
 template __global__ void dkdv_bf16_kernel<96, false, 8>(BwdArgs);
 template __global__ void dkdv_bf16_kernel<128, true, 8>(BwdArgs);
 template __global__ void dkdv_bf16_kernel<128, false, 8>(BwdArgs);
+template __global__ void dkdv_bf16_kernel<64, true, 8, true>(BwdArgs);
+template __global__ void dkdv_bf16_kernel<64, false, 8, true>(BwdArgs);
 template __global__ void dq_bf16_kernel<64, true, 8>(BwdArgs);
 template __global__ void dq_bf16_kernel<64, false, 8>(BwdArgs);
 template __global__ void dq_bf16_kernel<64, true, 4>(BwdArgs);

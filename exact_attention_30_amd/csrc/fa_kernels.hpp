@@ -77,6 +77,9 @@ int fwd_rows(int B, int Hq, int Tq, int D);  // query rows per workgroup, bf16 f
 int dq_rows(int B, int Hq, int Tq, int D);   // query rows per workgroup, bf16 dQ
 int dkdv_keys(int B, int Hkv, int Tk, int D);  // keys per workgroup, bf16 dK/dV
 hipError_t launch_bwd_dkdv_bf16(const BwdArgs& a, int D, bool causal, hipStream_t stream);
+// dK/dV with dQ accumulated by atomic adds (bf16, D = 64); a.part: the fp32
+// dQ accumulator [B][Hq][Tq][64]
+hipError_t launch_bwd_atomic_bf16(const BwdArgs& a, bool causal, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, int D, int dtype, bool causal, hipStream_t stream);
 hipError_t launch_bwd_dq_bf16(const BwdArgs& a, int D, bool causal, hipStream_t stream);
 // fp8 (e4m3) forward: a.v is the transposed V that launch_fp8_vt writes

@@ -133,6 +133,29 @@ fa_status fa_fwd_kv(const void* q, const void* k, const void* v, void* o, float*
 size_t fa_fwd_split_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int D, fa_dtype dt);
 
 /*
+ * The single-kernel backward of the FA2 formulation ("L'attention fusionnée",
+ * «La passe arrière»: a workgroup keeps dK and dV of its keys in registers and
+ * adds its share of dQ to the rows' accumulators with atomic adds), built as an
+ * alternative to fa_bwd for comparison; fa_bwd is faster on this GPU (its dQ
+ * kernel recomputes S and dP instead of moving dQ through atomics).  bf16,
+ * D = 64 and Tq = Tk (offset 0) only.
+ *   fa_bwd_atomic_workspace_bytes: bytes of `workspace` (0: unsupported
+ *       shapes): Delta [B][Hq][T], then an fp32 dQ accumulator [B][Hq][T][D].
+ *   fa_bwd_atomic: the preprocess (Delta), a zero fill of the accumulator, the
+ *       dK/dV kernel accumulating dQ per 32-row query tile (the workgroup's
+ *       eight waves summed in LDS, then one fp32 atomic add per element), and
+ *       a kernel writing dq = bf16(scale * accumulator).  dK and dV are bitwise
+ *       those of fa_bwd_dkdv; dQ agrees with fa_bwd to rounding but is not
+ *       bitwise reproducible (the order of the atomic adds varies).
+ *       FA_ERR_UNSUPPORTED for other dtypes or head sizes.
+ */
+size_t fa_bwd_atomic_workspace_bytes(int B, int Hq, int T, int D, fa_dtype dt);
+fa_status fa_bwd_atomic(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        void* workspace, int B, int Hq, int Hkv, int T, int D, float scale,
+                        int causal, fa_dtype dt, void* stream);
+
+/*
  * The static tile table of the bf16 kernels (the blocked loops of
  * "FlashAttention: l'attenzione che non spreca memoria", «L'idea: lavorare a
  * tessere»; the tile sizes of "Optimización de Flash Attention ...", «La pila

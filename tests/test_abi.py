@@ -313,3 +313,23 @@ def test_block_rows_table(lib):
     # the test-side model of the forward follows the same table
     for B, H, T, D in ((2, 8, 4096, 64), (2, 16, 4096, 64), (1, 4, 1500, 64), (1, 4, 700, 128)):
         assert lib.fa_block_rows(FWD, B, H, T, D, BF16) == lazy_model.block_rows(B, H, T, D)
+
+
+def test_atomic_backward_validation(lib):
+    """fa_bwd_atomic: bf16 at D = 64 only; other sizes or types are refused on
+    the host before anything is enqueued (null pointers are never touched)."""
+    f = lib.fa_bwd_atomic
+    f.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_void_p] + [ctypes.c_void_p] * 4 +
+                  [ctypes.c_int] * 5 + [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p])
+    f.restype = ctypes.c_int
+    n = [None] * 10
+    UNSUP = 3
+    assert f(*n, 1, 4, 2, 100, 128, 0.1, 1, 0, None) == UNSUP   # D = 128
+    assert f(*n, 1, 4, 2, 100, 96, 0.1, 1, 0, None) == UNSUP    # D = 96
+    assert f(*n, 1, 4, 2, 100, 64, 0.1, 1, 1, None) == UNSUP    # fp32
+    assert f(*n, 0, 4, 2, 100, 64, 0.1, 1, 0, None) == 0        # empty: a no-op
+    g = lib.fa_bwd_atomic_workspace_bytes
+    g.argtypes = [ctypes.c_int] * 5
+    g.restype = ctypes.c_size_t
+    assert g(2, 8, 512, 64, 0) == 2 * 8 * 512 * 4 + 2 * 8 * 512 * 64 * 4
+    assert g(2, 8, 512, 128, 0) == 0 and g(2, 8, 512, 64, 1) == 0

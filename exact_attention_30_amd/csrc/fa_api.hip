@@ -36,8 +36,8 @@ fa_status check_kv(int B, int Hq, int Hkv, int Tq, int Tk, int D, fa_dtype dt, b
     const long long krows = (long long)B * Hkv * (((long long)Tk + 31) / 32);
     if (qrows > 0x7fffffffLL || krows > 0x7fffffffLL) return FA_ERR_SHAPE;
     if (dt != FA_BF16 && dt != FA_FP32) return FA_ERR_UNSUPPORTED;
-    // 64 and 128 in both types; 96 in bf16, which runs the 128-wide tiles
-    // with the last 32 columns read as zero and never stored
+    // 64 and 128 in both types; 96 in bf16 (the forward on 96-column tiles,
+    // the backward on 128-column LDS tiles whose last 32 columns read as zero)
     if (D != 64 && D != 128 && !(D == 96 && dt == FA_BF16)) return FA_ERR_UNSUPPORTED;
     // one head of one tensor is addressed through a buffer resource whose
     // byte range is a signed 32-bit count

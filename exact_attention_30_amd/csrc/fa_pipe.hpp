@@ -42,9 +42,10 @@ __device__ __forceinline__ i32x4 buffer_rsrc(const void* base, int bytes)
                  __builtin_amdgcn_readfirstlane(bytes), kBufferFlags};
 }
 
-// Head sizes whose rows are not a power-of-two number of 16-byte chunks run
-// on the tiles of the next supported size: columns D .. tile_dim(D) - 1 are
-// zeros in every tile (they add nothing to any product) and are never stored.
+// LDS tile width of the backward kernels, whose swizzled tiles need a
+// power-of-two number of 16-byte chunks per row: D = 96 is stored 128 wide,
+// columns D .. tile_dim(D) - 1 zeros that no product reads and no store
+// writes.  (The forward's read-order tiles take D itself.)
 __host__ __device__ constexpr int tile_dim(int D) { return D == 96 ? 128 : D; }
 
 // Byte offset fetched for element (row, col) of a [rows][DS] bf16 array: a

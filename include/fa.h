@@ -27,8 +27,9 @@
  *
  * Head dimensions.  D = 64 and 128 in both element types; D = 96 in bf16 (the
  * 96-component queries and keys that "L'attention fusionnée", «Ce qui reste»,
- * names as the case its kernels could not reach), computed with the 128-wide
- * tiles and the last 32 columns taken as zero.
+ * names as the case its kernels could not reach): the forward on 96-column
+ * tiles; the backward's products over the 96 columns, on 128-column LDS tiles
+ * whose last 32 columns are zeros.
  *
  * Layouts.  All tensors are contiguous, row-major, element type `dt`:
  *     q, o, dout, dq : [B][Hq][Tq][D]

@@ -81,6 +81,9 @@ struct FwdBf16Cfg {
 constexpr float kRescaleThresholdBf16 = 8.0f;
 constexpr float kMaxWeightBf16 = 256.0f;  // 2^kRescaleThresholdBf16
 
+// Where an iteration of the forward issues its stage loads (see the kernel)
+enum { kIssueBarrier = 0, kIssueEven = 1, kIssueOdd = 2, kIssueTop = 3 };
+
 template <int D, bool CAUSAL, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
 {
@@ -172,6 +175,28 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
                     dma_b128(base + (uint32_t)(KT::BYTES + (w + NWAVE * i) * 1024), r, voff[i]);
         }
     };
+    // One DMA instruction of stage t, without a branch (it is issued between
+    // the products of an iteration, where a branch would cut the scheduled
+    // block): part j < KI is K block w + NWAVE j, the others V blocks.  A
+    // part of the stage that holds no tile (K_t with t >= nkv) gets a
+    // resource of no records: it reads nothing and writes zeros to a region
+    // that no iteration reads.
+    auto dma_part = [&](int t, int j) __attribute__((always_inline)) {
+        const uint32_t base = lds0 + (uint32_t)((t % Cfg::NSTAGE) * Cfg::STAGE);
+        if (j < KI) {
+            if (!(KT::NDMA % NWAVE == 0 || w + NWAVE * j < KT::NDMA)) return;  // (uniform per wave)
+            const int row0 = (j0 + t) * BC;
+            const i32x4 r = buffer_rsrc(kh + (size_t)row0 * D, t < nkv ? (a.Tk - row0) * D * 2 : 0);
+            dma_b128_nofence(base + (uint32_t)((w + NWAVE * j) * 1024), r, koff[j]);
+        } else {
+            const int jv = j - KI;
+            if (!(VT::NDMA % NWAVE == 0 || w + NWAVE * jv < VT::NDMA)) return;
+            const int row0 = (j0 + t - 2) * BC;
+            const i32x4 r =
+                buffer_rsrc(vh + (size_t)row0 * D, (t >= 2 && t <= nkv + 1) ? (a.Tk - row0) * D * 2 : 0);
+            dma_b128_nofence(base + (uint32_t)(KT::BYTES + (w + NWAVE * jv) * 1024), r, voff[jv]);
+        }
+    };
     load_stage(0);
     load_stage(1);
 
@@ -247,7 +272,20 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
     // a new reference where it rose by more than 8, O and l rescaled, weights
     // recomputed.  O then includes P_{i-2} V_{i-2}, formed with the old
     // reference, so the rescale applies to it too.
-    auto iteration = [&](int i, auto par, auto hs, auto hw, auto hpv) __attribute__((always_inline)) {
+    //
+    // Stage loads (ISSUE): the buffers of stages i + 2 and i + 3 are free
+    // from the barrier of an even i on.  Issued all at once there, the two
+    // stages' DMA writes reach LDS in one burst that stalls every wave's
+    // fragment reads; instead an even iteration spreads stage i + 2's
+    // instructions over its products (kIssueEven) and the odd iteration after
+    // it stage i + 3's (kIssueOdd).  Iterations whose parity is known only at
+    // run time issue at the top (kIssueTop: an even one both stages after its
+    // barrier, an odd one its stage i + 2, the even one before it having
+    // spread its own); kIssueBarrier is the plain form, both stages at an
+    // even barrier, nothing at an odd i.
+    auto iteration = [&](int i, auto par, auto hs, auto hw, auto hpv, auto issue) __attribute__((always_inline)) {
+        constexpr int ISSUE = decltype(issue)::value;
+        constexpr bool SPREAD = ISSUE == kIssueEven || ISSUE == kIssueOdd;
         constexpr int P = decltype(par)::value;
         constexpr bool HS = decltype(hs)::value, HW = decltype(hw)::value, HPV = decltype(hpv)::value;
         constexpr int NS = HS ? NKS * NKB : 0;         // score products
@@ -261,8 +299,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
         if ((i & 1) == 0) {
             vm_wait<0>();
             sync_lds();
+            if constexpr (!SPREAD) {
+                load_stage(i + 2);
+                load_stage(i + 3);
+            }
+        } else if constexpr (ISSUE == kIssueTop) {
             load_stage(i + 2);
-            load_stage(i + 3);
         }
 
         if constexpr (HW) {
@@ -308,9 +350,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
             }
         };
         if constexpr (N == 0) {
+            static_assert(!SPREAD, "no products to spread the loads over");
 #pragma unroll
             for (int t = 0; t < NSTEP; ++t) step(t);
         }
+        // stage i + 2's DMA parts go with products 0, STR, 2 STR, ...
+        constexpr int NPART = KI + VI;
+        constexpr int STR = N >= 4 * NPART ? 4 : N / (NPART > 0 ? NPART : 1);
+        static_assert(!SPREAD || STR >= 1, "a product for every DMA part");
 #pragma unroll
         for (int k = 0; k < N; ++k) {
             if (k + AHD < N) ring[(k + AHD) % RING] = frag_read(i, product(k + AHD), NSc{});
@@ -331,6 +378,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
             }
 #pragma unroll
             for (int t = k * NSTEP / (N > 0 ? N : 1); t < (k + 1) * NSTEP / (N > 0 ? N : 1); ++t) step(t);
+            if constexpr (SPREAD)
+                if (k % STR == 0 && k / STR < NPART) dma_part(i + 2, k / STR);
             __builtin_amdgcn_sched_barrier(0);
         }
 
@@ -375,17 +424,21 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
         // Iterations 0 and 1 are the same for every nkw (with nkw = 1, the
         // product S_1 of iteration 1 is never used): no register state then
         // lives across the branch below.
-        iteration(0, P0{}, T{}, F{}, F{});
-        iteration(1, P1{}, T{}, T{}, F{});
+        using IE = std::integral_constant<int, kIssueEven>;
+        using IO = std::integral_constant<int, kIssueOdd>;
+        using IT = std::integral_constant<int, kIssueTop>;
+        using IB = std::integral_constant<int, kIssueBarrier>;
+        iteration(0, P0{}, T{}, F{}, F{}, IE{});
+        iteration(1, P1{}, T{}, T{}, F{}, IO{});
         if (nkw == 1) {
-            iteration(2, P0{}, F{}, F{}, T{});
+            iteration(2, P0{}, F{}, F{}, T{}, IB{});
         } else {
             int i = 2;
             for (; i + 1 < nkw; i += 2) {
-                iteration(i, P0{}, T{}, T{}, T{});
-                iteration(i + 1, P1{}, T{}, T{}, T{});
+                iteration(i, P0{}, T{}, T{}, T{}, IE{});
+                iteration(i + 1, P1{}, T{}, T{}, T{}, IO{});
             }
-            if (i < nkw) iteration(i++, P0{}, T{}, T{}, T{});
+            if (i < nkw) iteration(i++, P0{}, T{}, T{}, T{}, IE{});
             // i == nkw.  The last two iterations exist in one parity only:
             // with nkw odd, S_{nkw-1} and P_{nkw-2} move to the registers that
             // parity expects (a copy once per wave instead of a second version
@@ -398,8 +451,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
                     for (int u = 0; u < 2; ++u) pf[0][kb][u] = pf[1][kb][u];
                 }
             }
-            iteration(nkw, P0{}, F{}, T{}, T{});
-            iteration(nkw + 1, P1{}, F{}, F{}, T{});
+            // (nkw odd: iteration nkw - 1 was even and spread its stage)
+            iteration(nkw, P0{}, F{}, T{}, T{}, IT{});
+            iteration(nkw + 1, P1{}, F{}, F{}, T{}, IB{});
         }
     }
     for (int i = nkw > 0 ? nkw + 2 : 0; i <= nkv + 1; ++i)

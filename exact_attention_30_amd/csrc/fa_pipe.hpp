@@ -73,6 +73,15 @@ __device__ __forceinline__ void dma_b128(uint32_t lds, const i32x4& rsrc, uint32
                  : "memory");
 }
 
+// The same DMA without the memory clobber, for loads issued between the
+// products of an iteration: the compiler may then keep LDS reads of other
+// buffers where they are scheduled.  The destination must not be read before
+// a later `vm_wait` and `sync_lds`, whose clobbers order it.
+__device__ __forceinline__ void dma_b128_nofence(uint32_t lds, const i32x4& rsrc, uint32_t voff)
+{
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(rsrc), "{m0}"(lds));
+}
+
 // Wait until at most N of this wave's vector-memory loads are outstanding.
 template <int N>
 __device__ __forceinline__ void vm_wait()

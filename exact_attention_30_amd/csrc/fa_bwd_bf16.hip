@@ -236,10 +236,38 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void dkdv_bf16_kernel(BwdArgs a)
         const unsigned char* dOs = Qs + QT::BYTES;
         const float* Ls = reinterpret_cast<const float*>(dOs + QT::BYTES);
         const float* Ds = Ls + 64;
-        if constexpr (ST % 2 == 0) {  // the next pair, into the previous pair's stages
-            if (i + 2 < n) issue((ST + 2) % NSTAGE);
-            if (i + 3 < n) issue((ST + 3) % NSTAGE);
+        // Tile i + 2 goes into stage ST + 2, which no wave reads after the
+        // barrier that ended the previous pair.  Its Q tile is issued between
+        // this tile's score products rather than with the rest at the top:
+        // loads issued together reach LDS in one burst that stalls every
+        // wave's fragment reads.  (Spreading dO too makes the compiler spill.)
+        // A tile past the chunk gets resources of no records: its DMAs read
+        // nothing and fill a stage that no tile reads.
+        const bool ld = i + 2 < n;
+        const int lhq = dhq, lti = dti;  // the cursor's tile, then the cursor moves on
+        {
+            const bool wrap = dhq + 1 == (hk + 1) * G;
+            dhq = ld ? (wrap ? hk * G : dhq + 1) : dhq;
+            dti = (ld && wrap) ? dti - 1 : dti;
         }
+        const uint32_t lbase = lds0 + (uint32_t)(((ST + 2) % NSTAGE) * STAGE);
+        if (w < 2) {  // L (wave 0) or Delta (wave 1)
+            const float* src = (w == 0 ? a.lse : a.delta) + (size_t)(b * a.Hq + lhq) * a.Tq + lti * BQ;
+            const i32x4 r = buffer_rsrc(src, ld ? (a.Tq - lti * BQ) * 4 : 0);
+            dma_b32(lbase + 2 * QT::BYTES + 256 * w, r, (uint32_t)(lane * 4));
+        }
+        i32x4 rq, ro;
+        {
+            const int row0 = lti * BQ;
+            const size_t off = ((size_t)(b * a.Hq + lhq) * a.Tq + row0) * D;
+            const int bytes = ld ? (a.Tq - row0) * D * 2 : 0;
+            rq = buffer_rsrc(static_cast<const bf16*>(a.q) + off, bytes);
+            ro = buffer_rsrc(static_cast<const bf16*>(a.dout) + off, bytes);
+        }
+        auto part = [&](int k) __attribute__((always_inline)) {  // 0: Q, 1: dO
+            if (QW < Cfg::NW && w >= QW) return;  // (uniform per wave)
+            dma_b128_nofence(lbase + (uint32_t)(k * QT::BYTES + w * 1024), k == 0 ? rq : ro, qt.voff[0]);
+        };
 
         constexpr uint32_t QI = ST * STAGE, OI = QI + QT::BYTES;  // Q_t, dO_t in the stage
         const bool pad = i >= n;
@@ -254,6 +282,8 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void dkdv_bf16_kernel(BwdArgs a)
         // nothing: the wave skips its products (the other wave of its SIMD
         // has the matrix pipe to itself meanwhile) but not the barrier below.
         const bool work = !(pad || (CAUSAL && qb + BQ - 1 + a.off < kw));
+        part(1);
+        if (!work) part(0);
         if (work) {
             // S starts at -L*log2(e)/c and dP at -Delta of their query rows
             // (rows 8*(r/4) + 4g + r%4 of this lane's registers; waves 0 and 1
@@ -285,6 +315,7 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void dkdv_bf16_kernel(BwdArgs a)
                         }
                     }
                     mma(s, frag(qr[ks % (SAH + 1)]), kf[ks]);
+                    if (ks == 1) part(0);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }

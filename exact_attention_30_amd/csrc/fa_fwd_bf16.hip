@@ -81,9 +81,6 @@ struct FwdBf16Cfg {
 constexpr float kRescaleThresholdBf16 = 8.0f;
 constexpr float kMaxWeightBf16 = 256.0f;  // 2^kRescaleThresholdBf16
 
-// Where an iteration of the forward issues its stage loads (see the kernel)
-enum { kIssueBarrier = 0, kIssueEven = 1, kIssueOdd = 2, kIssueTop = 3 };
-
 template <int D, bool CAUSAL, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
 {

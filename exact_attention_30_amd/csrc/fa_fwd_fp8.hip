@@ -178,6 +178,25 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(FwdArgs a)
                 dma_b128(base + (uint32_t)(KT::BYTES + f * 1024), r, VT::dma_off(f, lane));
         }
     };
+    // One DMA instruction of stage t without a branch, for iterations that
+    // spread their loads over the products (as the bf16 forward does): part
+    // 0 is this wave's K block, part 1 its V^T block; a part of a stage that
+    // holds no tile gets a resource of no records (reads nothing, fills a
+    // region that no iteration reads).
+    static_assert(KB <= NWAVE && VB <= NWAVE, "at most one block of each tile per wave");
+    auto dma_part = [&](int t, int j) __attribute__((always_inline)) {
+        const uint32_t base = lds0 + (uint32_t)((t % Cfg::NSTAGE) * Cfg::STAGE);
+        if (j == 0) {
+            if (KB < NWAVE && w >= KB) return;  // (uniform per wave)
+            const int row0 = t * BC;
+            const i32x4 r = buffer_rsrc(kh + (size_t)row0 * D, t < nkv ? (a.Tk - row0) * D : 0);
+            dma_b128_nofence(base + (uint32_t)(w * 1024), r, KT::dma_off(w, lane));
+        } else {
+            if (VB < NWAVE && w >= VB) return;
+            const i32x4 r = buffer_rsrc(vth + (size_t)(t - 2) * D * 64, (t >= 2 && t <= nkv + 1) ? D * 64 : 0);
+            dma_b128_nofence(base + (uint32_t)(KT::BYTES + w * 1024), r, VT::dma_off(w, lane));
+        }
+    };
     load_stage(0);
     load_stage(1);
 
@@ -256,7 +275,12 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(FwdArgs a)
     // from s[P ^ 1] into pf[P ^ 1] (HW), interleaved in one instruction
     // stream; then the reference update when some weight may exceed 2^8 or a
     // row has no reference yet (as in the bf16 forward).
-    auto iteration = [&](int i, auto par, auto hs, auto hw, auto hpv) __attribute__((always_inline)) {
+    // ISSUE: where the iteration issues stage loads (kIssue* of the bf16
+    // forward: an even iteration spreads stage i + 2 over its products, the
+    // odd one after it stage i + 3)
+    auto iteration = [&](int i, auto par, auto hs, auto hw, auto hpv, auto issue) __attribute__((always_inline)) {
+        constexpr int ISSUE = decltype(issue)::value;
+        constexpr bool SPREAD = ISSUE == kIssueEven || ISSUE == kIssueOdd;
         constexpr int P = decltype(par)::value;
         constexpr bool HS = decltype(hs)::value, HW = decltype(hw)::value, HPV = decltype(hpv)::value;
         constexpr int NS = HS ? NKS * NKB : 0;
@@ -267,8 +291,12 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(FwdArgs a)
         if ((i & 1) == 0) {
             vm_wait<0>();
             sync_lds();
+            if constexpr (!SPREAD) {
+                load_stage(i + 2);
+                load_stage(i + 3);
+            }
+        } else if constexpr (ISSUE == kIssueTop) {
             load_stage(i + 2);
-            load_stage(i + 3);
         }
 
         if constexpr (HW) {
@@ -315,9 +343,13 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(FwdArgs a)
             }
         };
         if constexpr (N == 0) {
+            static_assert(!SPREAD, "no products to spread the loads over");
 #pragma unroll
             for (int t = 0; t < NSTEP; ++t) step(t);
         }
+        // stage i + 2's two DMA parts go with products 0 and STR
+        constexpr int STR = N >= 8 ? 4 : N / 2;
+        static_assert(!SPREAD || STR >= 1, "a product for every DMA part");
 #pragma unroll
         for (int k = 0; k < N; ++k) {
             if (k + AHD < N) ring[(k + AHD) % RING] = frag_read(i, product(k + AHD), NSc{});
@@ -334,6 +366,8 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(FwdArgs a)
             }
 #pragma unroll
             for (int t = k * NSTEP / (N > 0 ? N : 1); t < (k + 1) * NSTEP / (N > 0 ? N : 1); ++t) step(t);
+            if constexpr (SPREAD)
+                if (k % STR == 0 && k / STR < 2) dma_part(i + 2, k / STR);
             __builtin_amdgcn_sched_barrier(0);
         }
 
@@ -372,25 +406,29 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(FwdArgs a)
     // forward).  Iterations 0 and 1 are the same for every nkw (with nkw = 1
     // the product S_1 is never used).
     const int nkw = CAUSAL ? min(nkv, (qw + 32 + a.off + BC - 1) / BC) : nkv;
-    iteration(0, P0{}, T{}, F{}, F{});
-    iteration(1, P1{}, T{}, T{}, F{});
+    using IE = std::integral_constant<int, kIssueEven>;
+    using IO = std::integral_constant<int, kIssueOdd>;
+    using IT = std::integral_constant<int, kIssueTop>;
+    using IB = std::integral_constant<int, kIssueBarrier>;
+    iteration(0, P0{}, T{}, F{}, F{}, IE{});
+    iteration(1, P1{}, T{}, T{}, F{}, IO{});
     if (nkw == 1) {
-        iteration(2, P0{}, F{}, F{}, T{});
+        iteration(2, P0{}, F{}, F{}, T{}, IB{});
     } else {
         int i = 2;
         for (; i + 1 < nkw; i += 2) {
-            iteration(i, P0{}, T{}, T{}, T{});
-            iteration(i + 1, P1{}, T{}, T{}, T{});
+            iteration(i, P0{}, T{}, T{}, T{}, IE{});
+            iteration(i + 1, P1{}, T{}, T{}, T{}, IO{});
         }
-        if (i < nkw) iteration(i++, P0{}, T{}, T{}, T{});
+        if (i < nkw) iteration(i++, P0{}, T{}, T{}, T{}, IE{});
         // one parity for the last two iterations (see the bf16 forward)
         if (nkw & 1) {
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) s[1][kb] = s[0][kb];
             pf[0] = pf[1];
         }
-        iteration(nkw, P0{}, F{}, T{}, T{});
-        iteration(nkw + 1, P1{}, F{}, F{}, T{});
+        iteration(nkw, P0{}, F{}, T{}, T{}, IT{});
+        iteration(nkw + 1, P1{}, F{}, F{}, T{}, IB{});
     }
     for (int i = nkw + 2; i <= nkv + 1; ++i)
         if ((i & 1) == 0) {

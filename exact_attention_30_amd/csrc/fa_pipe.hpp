@@ -82,6 +82,13 @@ __device__ __forceinline__ void dma_b128_nofence(uint32_t lds, const i32x4& rsrc
     asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(rsrc), "{m0}"(lds));
 }
 
+// Where an iteration of a forward kernel (two stages per barrier) issues
+// its stage loads: kIssueBarrier, both stages of the next pair at an even
+// iteration's barrier; kIssueEven / kIssueOdd, stage i + 2 spread over the
+// products of an even / odd iteration; kIssueTop, at the top of an iteration
+// whose parity is known only at run time.
+enum { kIssueBarrier = 0, kIssueEven = 1, kIssueOdd = 2, kIssueTop = 3 };
+
 // Wait until at most N of this wave's vector-memory loads are outstanding.
 template <int N>
 __device__ __forceinline__ void vm_wait()

@@ -23,8 +23,9 @@
 // (MFMA counts for head size 128), the vector work of P and dS placed
 // between the products that do not depend on it.
 // The tiles arrive by explicitly scheduled LDS DMA in four stage buffers at
-// the bottom of LDS, computed in pairs with one barrier per pair (the next
-// pair loads into the previous pair's stages); the loop is unrolled over the
+// the bottom of LDS, computed in pairs with one barrier per pair (each tile
+// loads the tile two ahead into a stage of the previous pair, its Q between
+// the score products); the loop is unrolled over the
 // stages and the per-lane read addresses carry the LDS base, so every read is
 // one address register plus an immediate offset, with no address arithmetic
 // in the loop.
@@ -50,7 +51,8 @@ struct DkdvBf16Cfg {
     static constexpr int BK = 32 * NW;  // keys per workgroup
     static constexpr int BQ = 32;       // query rows per tile
     // LDS stage buffers: tiles are computed in pairs with one barrier per
-    // pair, and the next pair's two tiles load into the previous pair's stages
+    // pair, and the next pair's two tiles load into the previous pair's
+    // stages (each while the tile two before it is computed)
     static constexpr int NSTAGE = 4;
     // Q and dO tiles: 32 rows; D = 64 needs only four waves to move them
     static constexpr int QNT = (BQ * DT / 8 >= NT) ? NT : BQ * DT / 8;
@@ -172,7 +174,7 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void dkdv_bf16_kernel(BwdArgs a)
 #pragma unroll
         for (int f = 0; f < VW::NDMA; ++f) dma_b128(vb + (uint32_t)(f * 1024), r, VW::dma_off(f, lane));
     }
-    for (int t = 0; t < 2 && t < n; ++t) issue(t);  // the first pair, stages 0 and 1
+    for (int t = 0; t < 2 && t < n; ++t) issue(t);  // the first pair, stages 0 and 1 (then per tile, below)
 
     // B operand of S = Q K^T: this lane's key row, 8 columns per 16-deep step
     Frag<bf16> kf[NKS];

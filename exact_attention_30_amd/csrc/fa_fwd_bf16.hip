@@ -28,8 +28,9 @@
 //     conflicts, one address register per operand) into four stage buffers:
 //     stage t = {K_t, V_{t-2}}, all that iteration t reads.  Stages move
 //     in pairs: at every even iteration a wave waits for the two stages it
-//     is about to read, crosses one barrier and issues the next two into
-//     the buffers the previous pair used.
+//     is about to read and crosses one barrier; the buffers the previous
+//     pair used then take the next two, whose DMA instructions the even
+//     iteration and the odd one after it spread over their products.
 //   * Lazy rescale: the reference max of a row only moves when the row max
 //     exceeds it by more than 8 (log2 units), so most tiles skip rescaling O
 //     and l; the weights stay below 2^8, and o and l share the reference.

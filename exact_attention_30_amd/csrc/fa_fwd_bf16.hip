@@ -64,7 +64,10 @@ struct FwdBf16Cfg {
     static constexpr int BR = 32 * NWAVE;    // query rows per workgroup
     static constexpr int BC = 64;            // keys per tile
     static constexpr int NSTAGE = 4;         // two pairs: one read, one in flight
-    static constexpr int AHD = 3;            // fragment reads in flight ahead of their MFMA
+    // fragment reads in flight ahead of their MFMA (measured in one process:
+    // at D = 64 two ahead 1.1-1.3 % faster than three at C3 and C4; at
+    // D = 96 and 128 two, three and four the same within 0.2 %, five spills)
+    static constexpr int AHD = D == 64 ? 2 : 3;
     using KT = RowFragTile<DT, BC, D>;
     using VT = TrFragTile<DT, BC, D>;
     static constexpr int STAGE = KT::BYTES + VT::BYTES;

@@ -572,7 +572,9 @@ static hipError_t sum_partials(const float* part, void* out0, void* out1, long p
 // 32-key block a wave forms S^T = K Q^T and dP^T = V dO^T with keys as rows,
 // P^T = exp2(S^T c - L), dS^T = P^T (dP^T - Delta), and accumulates
 // dQ^T += K^T dS^T with dS^T straight from registers; K^T is read transposed
-// from the K tile.  No atomics: each dQ row is owned by one wave.
+// from the K tile.  A block's dQ products run beside the next block's vector
+// work, the tile's last block's at its end.  No atomics: each dQ row is owned
+// by one wave.
 // ---------------------------------------------------------------------------
 template <int D, int NWV>  // head size of the tensors in memory; waves per workgroup
 struct DqBf16Cfg {
@@ -581,8 +583,9 @@ struct DqBf16Cfg {
     static constexpr int NT = 64 * NW;
     static constexpr int BR = 32 * NW;  // query rows per workgroup
     static constexpr int BC = 64;       // keys per tile
-    // four stages, two tiles in flight: the stage of tile t - 1 stays intact
-    // through tile t, whose first products use its K
+    // four stages, the tile two ahead loading into the stage of tile t - 2
+    // (one barrier per tile) or, with pairs, the next pair into the previous
+    // pair's stages
     static constexpr int NSTAGE = 4;
     static constexpr int AHEAD = 2;
     using KT = SwzTile<DT, BC, NT, D>;  // K: read row-wise and transposed
@@ -597,13 +600,11 @@ struct DqBf16Cfg {
     // (the last 16-byte read of a region starts 16 bytes before its end)
     static_assert((NSTAGE - 1) * KT::BYTES + BC * Fmt::ROWBYTES - 16 < 65536, "LDS immediates");
     static_assert((NSTAGE - 1) * VT::BYTES + VT::BYTES - 16 < 65536, "LDS immediates");
-    static_assert(AHEAD + 2 <= NSTAGE, "a stage is refilled only after the tile after it was used");
-    // Barriers: one per pair of tiles (D = 64), or one per tile.  With pairs
-    // the last block's dQ products are carried only from an even tile into
-    // the odd one after it; an odd tile ends with its own, and the next pair
-    // loads into the previous pair's stages.  Measured in one process against
-    // one barrier per tile: D = 64 dQ 4.7 % (C3) and 6.5 % (C2) faster, D = 96
-    // 4.1 % and D = 128 3.9 % slower, bitwise the same.
+    static_assert(AHEAD + 1 <= NSTAGE, "a stage is refilled only after the barrier that ends its tile");
+    // Barriers: one per pair of tiles at D = 64 (the next pair loads into
+    // the previous pair's stages), one per tile otherwise.  Measured in one
+    // process: pairs 1.4 % (C3) and 3.6 % (C2) faster than one per tile at
+    // D = 64, 3.9 % slower at D = 128 and 4.1 % at D = 96, bitwise the same.
     static constexpr bool PAIRS = D == 64;
 };
 
@@ -697,12 +698,6 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void dq_bf16_kernel(BwdArgs a)
         for (int ks = 0; ks < NKS; ++ks)
             orow[ks] = global_frag<bf16>(static_cast<const bf16*>(a.o) + qoff, qrow, a.Tq, D, 16 * ks + 8 * g);
     }
-    // zero the K tile of the last stage: the first tile's carried products
-    // read it before any tile has filled it (with zero dS, and 0 * uninitialised
-    // LDS could be NaN); no other read precedes its stage's DMA
-    for (int off = tid * 16; off < KT::BYTES; off += Cfg::NT * 16)
-        *reinterpret_cast<u32x4*>(smem + (NSTAGE - 1) * KT::BYTES + off) = u32x4{0, 0, 0, 0};
-    sync_lds();
     for (int t = 0; t < AHEAD && t < nkv; ++t) issue(t, t);
 
     // B operands of S^T = K Q^T and dP^T = V dO^T: this lane's query row
@@ -773,11 +768,9 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void dq_bf16_kernel(BwdArgs a)
     settle(Dl);
     sync_lds();
 
-    // dS^T of the previous 32-key block, the B operands of its dQ products,
-    // which run interleaved with the next block's vector work (zero before
-    // the first block: the products then add nothing)
+    // dS^T of the previous 32-key block of the tile, the B operands of its
+    // dQ products, which run interleaved with the next block's vector work
     Frag<bf16> sp[2];
-    sp[0].v = sp[1].v = bf16x8{};
     // product m of dQ^T += K^T dS^T for the block whose K^T starts at LDS
     // offset koff: its K^T fragment, and the product with that fragment
     auto kt_frag = [&](int m, uint32_t koff) __attribute__((always_inline)) {
@@ -804,18 +797,9 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void dq_bf16_kernel(BwdArgs a)
         } else if (t + AHEAD < nkv) {
             issue(t + AHEAD, (ST + AHEAD) % NSTAGE);
         }
-        // carried products: the previous tile's last block, into this tile
-        constexpr bool CARRY_IN = !Cfg::PAIRS || ST % 2 == 1;
         const int j = j0 + t;
         const bool masked = j >= nfull;  // diagonal or future tile
-        if (t >= nkw) {
-            if (CARRY_IN && t == nkw && nkw > 0) {  // the dQ products of the wave's last block
-                constexpr uint32_t KP =
-                    ((ST + NSTAGE - 1) % NSTAGE) * KT::BYTES + (NKB - 1) * 32 * Fmt::ROWBYTES;
-#pragma unroll
-                for (int m = 0; m < 2 * NDB; ++m) dq_product(m, kt_frag(m, KP));
-            }
-        } else {
+        if (t < nkw) {
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
                 f32x16 s = f32x16{}, dp = f32x16{};
@@ -850,19 +834,16 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void dq_bf16_kernel(BwdArgs a)
                         s[r] = vis ? s[r] : -INFINITY;
                     }
                 }
-                // the previous block: this tile's block kb - 1, or the last block
-                // of tile t - 1 (stage ST - 1, intact until the next issue)
-                const uint32_t KP = kb > 0 ? KI + (kb - 1) * 32 * Fmt::ROWBYTES
-                                               : ((ST + NSTAGE - 1) % NSTAGE) * KT::BYTES +
-                                                     (NKB - 1) * 32 * Fmt::ROWBYTES;
+                // P and dS of this block beside the dQ products of the block
+                // before it (none for the first block of the tile)
+                const uint32_t KP = KI + (kb > 0 ? kb - 1 : 0) * 32 * Fmt::ROWBYTES;
                 constexpr int NPROD = 2 * NDB;  // dQ products of one block
-                const bool prev = CARRY_IN || kb > 0;  // a previous block to finish
                 bf16x8 kr[2];                   // K^T fragments, read one product ahead
-                if (prev) kr[0] = kt_frag(0, KP);
+                if (kb > 0) kr[0] = kt_frag(0, KP);
 #pragma unroll
                 for (int m = 0; m < NPROD; ++m) {
-                    if (prev && m + 1 < NPROD) kr[(m + 1) % 2] = kt_frag(m + 1, KP);
-                    if (prev) dq_product(m, kr[m % 2]);
+                    if (kb > 0 && m + 1 < NPROD) kr[(m + 1) % 2] = kt_frag(m + 1, KP);
+                    if (kb > 0) dq_product(m, kr[m % 2]);
 #pragma unroll
                     for (int r = m * 16 / NPROD; r < (m + 1) * 16 / NPROD; ++r) {
                         const float p = fast_exp2(fmaf(s[r], a.c, -L2));  // P^T
@@ -878,11 +859,10 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void dq_bf16_kernel(BwdArgs a)
 #pragma unroll
                 for (int t2 = 0; t2 < 2; ++t2) sp[t2] = acc_frag<bf16>(dp, t2);
             }
-            if constexpr (Cfg::PAIRS && ST % 2 == 1) {  // an odd tile finishes its last block
-                constexpr uint32_t KL = KI + (NKB - 1) * 32 * Fmt::ROWBYTES;
+            // the tile's last block
+            constexpr uint32_t KL = KI + (NKB - 1) * 32 * Fmt::ROWBYTES;
 #pragma unroll
-                for (int m = 0; m < 2 * NDB; ++m) dq_product(m, kt_frag(m, KL));
-            }
+            for (int m = 0; m < 2 * NDB; ++m) dq_product(m, kt_frag(m, KL));
         }
         if constexpr (!Cfg::PAIRS) {
             wait_tile(t + 1);
@@ -892,12 +872,6 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void dq_bf16_kernel(BwdArgs a)
 
     for (int t = 0; t < npad; t += NSTAGE)
         unroll_stages(body, t, std::make_integer_sequence<int, NSTAGE>{});
-    if (nkw == nkv && nkv > 0 && (!Cfg::PAIRS || (nkv - 1) % 2 == 0)) {
-        // the last block's dQ products, if not yet run (its stage is still intact)
-        const uint32_t KP = (uint32_t)(((nkv - 1) % NSTAGE) * KT::BYTES + (NKB - 1) * 32 * Fmt::ROWBYTES);
-#pragma unroll
-        for (int m = 0; m < 2 * NDB; ++m) dq_product(m, kt_frag(m, KP));
-    }
 
     if (qrow < a.Tq) {
         if (S == 1) {

@@ -838,12 +838,15 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void dq_bf16_kernel(BwdArgs a)
                 // before it (none for the first block of the tile)
                 const uint32_t KP = KI + (kb > 0 ? kb - 1 : 0) * 32 * Fmt::ROWBYTES;
                 constexpr int NPROD = 2 * NDB;  // dQ products of one block
-                bf16x8 kr[2];                   // K^T fragments, read one product ahead
-                if (kb > 0) kr[0] = kt_frag(0, KP);
+                bf16x8 kr[3];                   // K^T fragments, read two products ahead
+                if (kb > 0) {
+                    kr[0] = kt_frag(0, KP);
+                    kr[1] = kt_frag(1, KP);
+                }
 #pragma unroll
                 for (int m = 0; m < NPROD; ++m) {
-                    if (kb > 0 && m + 1 < NPROD) kr[(m + 1) % 2] = kt_frag(m + 1, KP);
-                    if (kb > 0) dq_product(m, kr[m % 2]);
+                    if (kb > 0 && m + 2 < NPROD) kr[(m + 2) % 3] = kt_frag(m + 2, KP);
+                    if (kb > 0) dq_product(m, kr[m % 3]);
 #pragma unroll
                     for (int r = m * 16 / NPROD; r < (m + 1) * 16 / NPROD; ++r) {
                         const float p = fast_exp2(fmaf(s[r], a.c, -L2));  // P^T
@@ -861,8 +864,16 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void dq_bf16_kernel(BwdArgs a)
             }
             // the tile's last block
             constexpr uint32_t KL = KI + (NKB - 1) * 32 * Fmt::ROWBYTES;
+            {
+                bf16x8 kr[3];
+                kr[0] = kt_frag(0, KL);
+                kr[1] = kt_frag(1, KL);
 #pragma unroll
-            for (int m = 0; m < 2 * NDB; ++m) dq_product(m, kt_frag(m, KL));
+                for (int m = 0; m < 2 * NDB; ++m) {
+                    if (m + 2 < 2 * NDB) kr[(m + 2) % 3] = kt_frag(m + 2, KL);
+                    dq_product(m, kr[m % 3]);
+                }
+            }
         }
         if constexpr (!Cfg::PAIRS) {
             wait_tile(t + 1);

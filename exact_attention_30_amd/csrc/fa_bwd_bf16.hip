@@ -113,9 +113,23 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void dkdv_bf16_kernel(BwdArgs a)
     // causal: the first key blocks see the most query rows; the nsplit chunks
     // of one key block are neighbours (and share an XCD where possible)
     const int S = a.nsplit;
-    const TileId id = map_tile(blockIdx.x, a.B, a.Hq, a.Hkv, S, nkt, false);
+    // kpair: workgroup m takes key blocks m and nkt - 1 - m (one block for
+    // the middle one when nkt is odd), which together see the same number of
+    // query tiles whatever m is
+    const TileId id = map_tile(blockIdx.x, a.B, a.Hq, a.Hkv, S, a.kpair ? (nkt + 1) / 2 : nkt, false);
     const int b = id.b, hk = id.h / S, split = id.h % S;
-    const int key0 = id.tile * BK;
+    const int npass = a.kpair && nkt - 1 - id.tile != id.tile ? 2 : 1;
+    // With kpair a key block in the upper half of the 256-key blocks walks
+    // its query tiles upward, the others downward.  The workgroups of a kv
+    // head then read the same Q and dO tile at the same time: all start
+    // their first block at the last tile, and each starts its second one at
+    // the tile where those that switched before it have arrived.  The rule
+    // depends on the keys alone, so 128- and 256-key blocks add the same
+    // terms in the same order.
+    const int nkt256 = (a.Tk + 255) / 256;
+    for (int pass = 0; pass < npass; ++pass) {
+    const int key0 = (pass == 0 ? id.tile : nkt - 1 - id.tile) * BK;
+    const int dir = a.kpair && key0 / 256 >= (nkt256 + 1) / 2 ? 1 : -1;
     // first key of this wave.  With eight waves, w and w + 4 share a SIMD;
     // pairing key blocks r and 7 - r there gives every SIMD the same number
     // of causal tiles that one of its waves skips (below).  With four, each
@@ -149,7 +163,7 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void dkdv_bf16_kernel(BwdArgs a)
     // head then reads the same tile at about the same time, so the tiles are
     // fetched from memory once per L2 rather than once per workgroup.
     // DMA cursor: (query head, query tile) of the next tile to issue
-    int dhq = hk * G + p0 % G, dti = nq - 1 - p0 / G;
+    int dhq = hk * G + p0 % G, dti = dir < 0 ? nq - 1 - p0 / G : i0 + p0 / G;
     auto issue = [&](int st) {
         const uint32_t base = lds0 + (uint32_t)(st * STAGE);
         if (w < QW) {
@@ -164,7 +178,7 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void dkdv_bf16_kernel(BwdArgs a)
         }
         if (++dhq == (hk + 1) * G) {
             dhq = hk * G;
-            --dti;
+            dti += dir;
         }
     };
     {  // this wave's 32 V rows (rows past T read as zeros)
@@ -230,7 +244,7 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void dkdv_bf16_kernel(BwdArgs a)
     convert_l(0);
     convert_l(1);
     sync_lds();
-    int bti = nq - 1 - p0 / G, bh = p0 % G;  // query tile and head (in the group) being computed
+    int bti = dir < 0 ? nq - 1 - p0 / G : i0 + p0 / G, bh = p0 % G;  // query tile and head being computed
 
     auto body = [&](auto st_tag, int i) {
         constexpr int ST = decltype(st_tag)::value;
@@ -250,7 +264,7 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void dkdv_bf16_kernel(BwdArgs a)
         {
             const bool wrap = dhq + 1 == (hk + 1) * G;
             dhq = ld ? (wrap ? hk * G : dhq + 1) : dhq;
-            dti = (ld && wrap) ? dti - 1 : dti;
+            dti = (ld && wrap) ? dti + dir : dti;
         }
         const uint32_t lbase = lds0 + (uint32_t)(((ST + 2) % NSTAGE) * STAGE);
         if (w < 2) {  // L (wave 0) or Delta (wave 1)
@@ -278,7 +292,7 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void dkdv_bf16_kernel(BwdArgs a)
         (void)hq_t;
         if (++bh == G) {
             bh = 0;
-            --bti;
+            bti += dir;
         }
         // A tile that no key of this wave sees (or a padding tile) adds
         // nothing: the wave skips its products (the other wave of its SIMD
@@ -520,6 +534,7 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void dkdv_bf16_kernel(BwdArgs a)
                 }
         }
     }
+    }  // pass
 }
 
 // out = scale * (sum of the S fp32 partials part[s * plane + .]), added in
@@ -950,8 +965,12 @@ static hipError_t launch_dkdv(const BwdArgs& a, hipStream_t stream)
         reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::SMEM);
     if (attr != hipSuccess) return attr;
     const int nkt = (a.Tk + Cfg::BK - 1) / Cfg::BK;
-    const long grid = (long)nkt * a.B * a.Hkv * a.nsplit;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Cfg::NT), Cfg::SMEM, stream, a);
+    BwdArgs p = a;
+    // pairs of key blocks balance causal work only when every block's query
+    // range ends at the last tile (no offset) and the blocks are not split
+    p.kpair = CAUSAL && a.nsplit == 1 && a.off == 0 && a.Tq == a.Tk;
+    const long grid = (long)(p.kpair ? (nkt + 1) / 2 : nkt) * a.B * a.Hkv * a.nsplit;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Cfg::NT), Cfg::SMEM, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1) return e;
     const long plane = (long)a.B * a.Hkv * a.Tk * D;

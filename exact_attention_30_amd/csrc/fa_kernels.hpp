@@ -52,6 +52,9 @@ struct BwdArgs {
     // from o and dout itself, reads no delta and writes Delta to delta_out
     const void* o;
     float* delta_out;
+    // dK/dV kernel (bf16) only: with kpair set, workgroup m takes key blocks
+    // m and nkt - 1 - m (set by its launcher)
+    int kpair = 0;
 };
 
 struct PreArgs {

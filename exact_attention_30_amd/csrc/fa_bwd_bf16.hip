@@ -70,6 +70,8 @@ struct DkdvBf16Cfg {
     static_assert((NSTAGE - 1) * STAGE + QT::BYTES + 16 * Fmt::ROWBYTES < 65536, "LDS immediates");
     static_assert(NSTAGE == 4, "two pairs of stages");
     static_assert(QT::NI == 1, "one Q and one dO instruction per loading wave");
+    // a workgroup may take a pair of key blocks (kpair)
+    static constexpr bool PAIRABLE = D != 64;
 };
 
 // f(stage, i + K) for K = 0 .. N-1, with the stage as a compile-time constant
@@ -113,12 +115,16 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void dkdv_bf16_kernel(BwdArgs a)
     // causal: the first key blocks see the most query rows; the nsplit chunks
     // of one key block are neighbours (and share an XCD where possible)
     const int S = a.nsplit;
+    // Key-block pairs are compiled only where they pay: at D = 64 the loop
+    // over two blocks costs registers (occupancy 3 -> 2) and measured 1.7-1.9 %
+    // slower at C2 and C3, which do not use it.
+    constexpr bool PAIRABLE = DkdvBf16Cfg<D, NWV, ADQ>::PAIRABLE;
     // kpair: workgroup m takes key blocks m and nkt - 1 - m (one block for
     // the middle one when nkt is odd), which together see the same number of
     // query tiles whatever m is
-    const TileId id = map_tile(blockIdx.x, a.B, a.Hq, a.Hkv, S, a.kpair ? (nkt + 1) / 2 : nkt, false);
+    const TileId id = map_tile(blockIdx.x, a.B, a.Hq, a.Hkv, S, PAIRABLE && a.kpair ? (nkt + 1) / 2 : nkt, false);
     const int b = id.b, hk = id.h / S, split = id.h % S;
-    const int npass = a.kpair && nkt - 1 - id.tile != id.tile ? 2 : 1;
+    const int npass = PAIRABLE && a.kpair && nkt - 1 - id.tile != id.tile ? 2 : 1;
     // With kpair a key block in the upper half of the 256-key blocks walks
     // its query tiles upward, the others downward.  The workgroups of a kv
     // head then read the same Q and dO tile at the same time: all start
@@ -127,9 +133,9 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void dkdv_bf16_kernel(BwdArgs a)
     // depends on the keys alone, so 128- and 256-key blocks add the same
     // terms in the same order.
     const int nkt256 = (a.Tk + 255) / 256;
-    for (int pass = 0; pass < npass; ++pass) {
-    const int key0 = (pass == 0 ? id.tile : nkt - 1 - id.tile) * BK;
-    const int dir = a.kpair && key0 / 256 >= (nkt256 + 1) / 2 ? 1 : -1;
+    // the work of one key block (first key key0), its query tiles walked
+    // down (dir < 0) or up
+    auto run_block = [&](const int key0, const int dir) __attribute__((always_inline)) {
     // first key of this wave.  With eight waves, w and w + 4 share a SIMD;
     // pairing key blocks r and 7 - r there gives every SIMD the same number
     // of causal tiles that one of its waves skips (below).  With four, each
@@ -534,7 +540,15 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void dkdv_bf16_kernel(BwdArgs a)
                 }
         }
     }
-    }  // pass
+    };
+    if constexpr (PAIRABLE) {
+        for (int pass = 0; pass < npass; ++pass) {
+            const int key0 = (pass == 0 ? id.tile : nkt - 1 - id.tile) * BK;
+            run_block(key0, a.kpair && key0 / 256 >= (nkt256 + 1) / 2 ? 1 : -1);
+        }
+    } else {
+        run_block(id.tile * BK, -1);
+    }
 }
 
 // out = scale * (sum of the S fp32 partials part[s * plane + .]), added in
@@ -968,7 +982,7 @@ static hipError_t launch_dkdv(const BwdArgs& a, hipStream_t stream)
     BwdArgs p = a;
     // pairs of key blocks balance causal work only when every block's query
     // range ends at the last tile (no offset) and the blocks are not split
-    p.kpair = CAUSAL && a.nsplit == 1 && a.off == 0 && a.Tq == a.Tk;
+    p.kpair = Cfg::PAIRABLE && CAUSAL && a.nsplit == 1 && a.off == 0 && a.Tq == a.Tk;
     const long grid = (long)(p.kpair ? (nkt + 1) / 2 : nkt) * a.B * a.Hkv * a.nsplit;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Cfg::NT), Cfg::SMEM, stream, p);
     hipError_t e = hipGetLastError();

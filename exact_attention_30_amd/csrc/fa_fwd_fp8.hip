@@ -312,10 +312,10 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(FwdArgs a)
         // at e + 3; the steps are spread over the products
         constexpr int NE = HW ? 16 * NKB : 0;
         constexpr int NSTEP = HW ? NE + 3 : 0;
-        auto product = [](int k) {  // alternate score and P V products
-            if (NS == 0 || NPV == 0) return k;
-            return (k % 2 == 0) ? k / 2 : NS + k / 2;
-        };
+        // products in order: the score products (ks outer, kb inner), then
+        // the P V products, whose operand P is the same for all four (an
+        // order that alternates the two kinds measured about 1 % slower)
+        auto product = [](int k) { return k; };
         using NSc = std::integral_constant<int, NS>;
         i32x8 ring[RING];
 #pragma unroll

@@ -213,6 +213,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
     u32x4 pf[2][NKB][2];       // P of tile i - 1 (being formed) and of tile i - 2 (B of P V),
                                // bf16 pairs
     float mref = -INFINITY;    // reference max, log2 units
+    // the exponent's offset: mref, or 0 while the row has no reference;
+    // noref: some row of the wave has none yet (both change with mref only)
+    float msub = 0.f;
+    bool noref = true;
     float l = 0.f;             // this lane's share of the row sum
 
     // fragment k of iteration t: score products first, then P V products
@@ -314,7 +318,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
                 mask_tile(s[P ^ 1], i - 1);
             }
         }
-        const float msub = (mref == -INFINITY) ? 0.f : mref;
 
         // One group per product: the MFMA, the fragment read of the product
         // AHD later, and a share of the weights, which move through four
@@ -384,7 +387,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
         }
 
         if constexpr (HW) {
-            if (__builtin_amdgcn_ballot_w64(lt > kMaxWeightBf16 || mref == -INFINITY)) {
+            if (noref || __builtin_amdgcn_ballot_w64(lt > kMaxWeightBf16)) {
                 float mt = -INFINITY;
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb)
@@ -401,7 +404,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
 #pragma unroll
                     for (int db = 0; db < NDB; ++db) o[db] *= alpha;
                     mref = mnew;
-                    lt = weights(s[P ^ 1], pf[P ^ 1], (mref == -INFINITY) ? 0.f : mref);
+                    msub = (mref == -INFINITY) ? 0.f : mref;
+                    noref = __builtin_amdgcn_ballot_w64(mref == -INFINITY) != 0;
+                    lt = weights(s[P ^ 1], pf[P ^ 1], msub);
                 }
             }
             l += lt;

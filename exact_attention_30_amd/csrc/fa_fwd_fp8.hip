@@ -220,6 +220,10 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(FwdArgs a)
     f32x16 s[2][NKB];  // S^T of tile i (being computed) and of tile i - 1
     i32x8 pf[2];       // P of tile i - 1 (being formed) and of tile i - 2, e4m3
     float mref = -INFINITY;  // reference max, log2 units
+    // the exponent's offset: mref, or 0 while the row has no reference;
+    // noref: some row of the wave has none yet (both change with mref only)
+    float msub = 0.f;
+    bool noref = true;
     float l = 0.f;           // this lane's share of the row sum
 
     // A fragment of product k of iteration t: score products first (K rows),
@@ -305,7 +309,6 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(FwdArgs a)
                 mask_tile(s[P ^ 1], i - 1);
             }
         }
-        const float msub = (mref == -INFINITY) ? 0.f : mref;
 
         // weight element e (register e % 16 of block e / 16) moves through
         // four steps: fma at step e, exp2 at e + 1, sum at e + 2, e4m3 pair
@@ -372,7 +375,7 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(FwdArgs a)
         }
 
         if constexpr (HW) {
-            if (__builtin_amdgcn_ballot_w64(lt > kFp8MaxWeight || mref == -INFINITY)) {
+            if (noref || __builtin_amdgcn_ballot_w64(lt > kFp8MaxWeight)) {
                 float mt = -INFINITY;
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb)
@@ -389,7 +392,9 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(FwdArgs a)
 #pragma unroll
                     for (int db = 0; db < NDB; ++db) o[db] *= alpha;
                     mref = mnew;
-                    lt = weights(s[P ^ 1], pf[P ^ 1], (mref == -INFINITY) ? 0.f : mref);
+                    msub = (mref == -INFINITY) ? 0.f : mref;
+                    noref = __builtin_amdgcn_ballot_w64(mref == -INFINITY) != 0;
+                    lt = weights(s[P ^ 1], pf[P ^ 1], msub);
                 }
             }
             l += lt;

@@ -157,45 +157,45 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
     // Stage t = {K_t (t < nkv), V_{t-2} (2 <= t <= nkv + 1)} in buffer
     // t % NSTAGE: everything iteration t reads from LDS.
     const uint32_t lds0 = lds_addr(smem);
+    // One buffer resource per head for K and one for V (reads past Tk return
+    // zeros); a tile's rows enter through the lane offset, so the loads of a
+    // tile need no per-tile resource.
+    const i32x4 krs = buffer_rsrc(kh, a.Tk * D * 2), vrs = buffer_rsrc(vh, a.Tk * D * 2);
+    auto tile_off = [&](int jl) { return (uint32_t)((j0 + jl) * BC * D * 2); };  // chunk tile jl
     auto load_stage = [&](int t) {
         const uint32_t base = lds0 + (uint32_t)((t % Cfg::NSTAGE) * Cfg::STAGE);
         if (t < nkv) {
-            const int row0 = (j0 + t) * BC;
-            const i32x4 r = buffer_rsrc(kh + (size_t)row0 * D, (a.Tk - row0) * D * 2);
+            const uint32_t ro = tile_off(t);
 #pragma unroll
             for (int i = 0; i < KI; ++i)
                 if (KT::NDMA % NWAVE == 0 || w + NWAVE * i < KT::NDMA)  // (uniform per wave)
-                    dma_b128(base + (uint32_t)((w + NWAVE * i) * 1024), r, koff[i]);
+                    dma_b128(base + (uint32_t)((w + NWAVE * i) * 1024), krs, koff[i] + ro);
         }
         if (t >= 2 && t <= nkv + 1) {
-            const int row0 = (j0 + t - 2) * BC;
-            const i32x4 r = buffer_rsrc(vh + (size_t)row0 * D, (a.Tk - row0) * D * 2);
+            const uint32_t ro = tile_off(t - 2);
 #pragma unroll
             for (int i = 0; i < VI; ++i)
                 if (VT::NDMA % NWAVE == 0 || w + NWAVE * i < VT::NDMA)
-                    dma_b128(base + (uint32_t)(KT::BYTES + (w + NWAVE * i) * 1024), r, voff[i]);
+                    dma_b128(base + (uint32_t)(KT::BYTES + (w + NWAVE * i) * 1024), vrs, voff[i] + ro);
         }
     };
     // One DMA instruction of stage t, without a branch (it is issued between
     // the products of an iteration, where a branch would cut the scheduled
     // block): part j < KI is K block w + NWAVE j, the others V blocks.  A
-    // part of the stage that holds no tile (K_t with t >= nkv) gets a
-    // resource of no records: it reads nothing and writes zeros to a region
-    // that no iteration reads.
+    // part of the stage that holds no tile (K_t with t >= nkv) gets an offset
+    // past the resource's records: it reads nothing and writes zeros to a
+    // region that no iteration reads.
     auto dma_part = [&](int t, int j) __attribute__((always_inline)) {
         const uint32_t base = lds0 + (uint32_t)((t % Cfg::NSTAGE) * Cfg::STAGE);
         if (j < KI) {
             if (!(KT::NDMA % NWAVE == 0 || w + NWAVE * j < KT::NDMA)) return;  // (uniform per wave)
-            const int row0 = (j0 + t) * BC;
-            const i32x4 r = buffer_rsrc(kh + (size_t)row0 * D, t < nkv ? (a.Tk - row0) * D * 2 : 0);
-            dma_b128_nofence(base + (uint32_t)((w + NWAVE * j) * 1024), r, koff[j]);
+            const uint32_t ro = t < nkv ? tile_off(t) : kPastEnd;
+            dma_b128_nofence(base + (uint32_t)((w + NWAVE * j) * 1024), krs, koff[j] + ro);
         } else {
             const int jv = j - KI;
             if (!(VT::NDMA % NWAVE == 0 || w + NWAVE * jv < VT::NDMA)) return;
-            const int row0 = (j0 + t - 2) * BC;
-            const i32x4 r =
-                buffer_rsrc(vh + (size_t)row0 * D, (t >= 2 && t <= nkv + 1) ? (a.Tk - row0) * D * 2 : 0);
-            dma_b128_nofence(base + (uint32_t)(KT::BYTES + (w + NWAVE * jv) * 1024), r, voff[jv]);
+            const uint32_t ro = (t >= 2 && t <= nkv + 1) ? tile_off(t - 2) : kPastEnd;
+            dma_b128_nofence(base + (uint32_t)(KT::BYTES + (w + NWAVE * jv) * 1024), vrs, voff[jv] + ro);
         }
     };
     load_stage(0);

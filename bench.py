@@ -405,6 +405,38 @@ def parity_errors(w, gpu: dict, ref: dict) -> dict:
     return out
 
 
+def float32_results_errors(w, q, k, v, do, fpart, ref: dict) -> dict:
+    """One more forward and backward of the same inputs with float32 results
+    (FA_BF16_F32OUT: the same kernels, O and the gradients stored without the
+    final rounding to bf16), after the timed region, against the oracle's
+    outputs on the same kv groups: the stated target read literally, max |err|
+    absolute and rel-L2."""
+    import numpy as np
+    import torch
+
+    o, lse = fa.fwd(q, k, v, scale=w.scale, causal=w.causal, partial=fpart, out_dtype=torch.float32)
+    dq, dk, dv = fa.bwd(q, k, v, o, do, lse, scale=w.scale, causal=w.causal)
+    torch.cuda.synchronize()
+    n = ref["ngroups"]
+    G = w.Hq // w.Hkv
+    out = {"slice": f"batch 0, kv heads 0-{n - 1}, query heads 0-{n * G - 1}, every position",
+           "tolerance": "max |err| <= 1e-2 absolute and rel-L2 <= 5e-3; lse max-abs <= 1e-3"}
+    ok = True
+    for name, t, heads in (("o", o, n * G), ("lse", lse, n * G), ("dq", dq, n * G), ("dk", dk, n),
+                           ("dv", dv, n)):
+        err = t[:1, :heads].double().cpu().numpy() - ref[name]
+        m = float(np.max(np.abs(err)))
+        if name == "lse":
+            out[name] = {"max_abs": m}
+            ok &= m <= 1e-3
+            continue
+        rel = float(np.linalg.norm(err) / np.linalg.norm(ref[name]))
+        out[name] = {"max_abs": m, "rel_l2": rel}
+        ok &= m <= 1e-2 and rel <= 5e-3
+    out["pass"] = bool(ok)
+    return out
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
@@ -608,6 +640,8 @@ def main():
         out["cpu_baseline"], ref = cpu_baseline(w, x, args.cpu_seconds)
         if ref is not None:
             out["parity"] = parity_errors(w, {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}, ref)
+            if fused:
+                out["parity_float32_results"] = float32_results_errors(w, q, k, v, do, fpart, ref)
     print(json.dumps(out), flush=True)
 
 

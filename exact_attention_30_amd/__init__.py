@@ -31,7 +31,7 @@ __all__ = ["fwd", "bwd", "bwd_noalloc", "NOALLOC_SCRATCH_BYTES", "bwd_preprocess
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
-FA_BF16, FA_FP32 = 0, 1
+FA_BF16, FA_FP32, FA_BF16_F32OUT = 0, 1, 2
 # FA_NOALLOC_SCRATCH_BYTES of include/fa.h: the static scratch of fa_bwd_noalloc
 NOALLOC_SCRATCH_BYTES = 64 << 20
 _DTYPES = {torch.bfloat16: FA_BF16, torch.float32: FA_FP32}
@@ -162,6 +162,28 @@ def _dtype_code(*ts) -> int:
     return _DTYPES[dt]
 
 
+def _out_code(in_dtype, out_dtype) -> int:
+    """fa_dtype of a call whose inputs have in_dtype and whose results have
+    out_dtype: the same type, or float32 results of bfloat16 inputs
+    (FA_BF16_F32OUT: the bf16 kernels' results stored unrounded)."""
+    if out_dtype == in_dtype and in_dtype in _DTYPES:
+        return _DTYPES[in_dtype]
+    if in_dtype == torch.bfloat16 and out_dtype == torch.float32:
+        return FA_BF16_F32OUT
+    raise TypeError(f"results of {out_dtype} for inputs of {in_dtype}: use the inputs' dtype, "
+                    "or float32 for bfloat16 inputs")
+
+
+def _result_dtype(q, given, out_dtype):
+    """dtype of the results: that of the preallocated tensor `given`, else
+    out_dtype, else q's."""
+    if given is not None:
+        if out_dtype is not None and given.dtype != out_dtype:
+            raise TypeError(f"preallocated result is {given.dtype}, out_dtype {out_dtype}")
+        return given.dtype
+    return q.dtype if out_dtype is None else out_dtype
+
+
 def _same_device(ref, *ts):
     """Every given tensor is a contiguous tensor on ref's GPU."""
     for t in ts:
@@ -194,18 +216,22 @@ def block_rows(stage, B, H, T, D, dtype=torch.bfloat16) -> int:
 
 
 def fwd(q, k, v, scale=None, causal: bool = True, out=None, lse=None, q_offset=None,
-        partial=None):
+        partial=None, out_dtype=None):
     """Forward pass; returns (o, lse).  `out`/`lse` may be preallocated.
+    With bfloat16 inputs, out_dtype=torch.float32 (or a float32 `out`) stores
+    O unrounded (FA_BF16_F32OUT).
     Calls fa_fwd when Tq == Tk and the offset is 0, else fa_fwd_kv; with
     `partial` (a device tensor of at least fwd_split_bytes(...) bytes) calls
     fa_fwd_split, which splits key ranges when the shapes call for it."""
     B, Hq, Hkv, Tq, Tk, D = _dims(q, k, v)
-    _expect(out, q.shape, "out", q.dtype)
+    odt = _result_dtype(q, out, out_dtype)
+    _expect(out, q.shape, "out", odt)
     _expect(lse, (B, Hq, Tq), "lse", torch.float32)
-    dt = _dtype_code(q, k, v, *(t for t in (out,) if t is not None))
-    _same_device(q, lse, partial)
+    dt = _out_code(q.dtype, odt)
+    _dtype_code(q, k, v)
+    _same_device(q, out, lse, partial)
     off = _offset(Tq, Tk, q_offset)
-    o = torch.empty_like(q) if out is None else out
+    o = torch.empty(q.shape, dtype=odt, device=q.device) if out is None else out
     l = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device) if lse is None else lse
     lib = library()
     if partial is not None:
@@ -326,7 +352,8 @@ def dkdv_split_bytes(B, Hq, Hkv, Tq, Tk, D, dtype=torch.bfloat16) -> int:
 
 def bwd(q, k, v, o, dout, lse, scale=None, causal: bool = True, workspace=None, grads=None,
         q_offset=None):
-    """Backward pass; returns (dq, dk, dv).  `grads` = (dq, dk, dv) may be
+    """Backward pass; returns (dq, dk, dv), of o's dtype (float32 o with
+    bfloat16 inputs: FA_BF16_F32OUT, gradients stored unrounded).  `grads` = (dq, dk, dv) may be
     preallocated; `workspace` is a uint8 device tensor of at least
     bwd_workspace_bytes(...) bytes.  Calls fa_bwd when Tq == Tk and the
     offset is 0, else fa_bwd_kv (same q_offset as the forward)."""
@@ -336,12 +363,15 @@ def bwd(q, k, v, o, dout, lse, scale=None, causal: bool = True, workspace=None, 
     _expect(lse, (B, Hq, Tq), "lse", torch.float32)
     if grads is not None:
         for t, like, name in zip(grads, (q, k, v), ("dq", "dk", "dv")):
-            _expect(t, like.shape, name, q.dtype)
-    dt = _dtype_code(q, k, v, o, dout, *(grads or ()))
+            _expect(t, like.shape, name, o.dtype)
+    dt = _out_code(q.dtype, o.dtype)  # float32 o with bf16 inputs: float32 gradients
+    _dtype_code(q, k, v, dout)
+    _same_device(q, o, *(grads or ()))
     _same_device(q, lse, workspace)
     off = _offset(Tq, Tk, q_offset)
-    dq, dk, dv = grads if grads is not None else (torch.empty_like(q), torch.empty_like(k),
-                                                  torch.empty_like(v))
+    dq, dk, dv = grads if grads is not None else (torch.empty_like(q, dtype=o.dtype),
+                                                  torch.empty_like(k, dtype=o.dtype),
+                                                  torch.empty_like(v, dtype=o.dtype))
     ws_bytes = bwd_workspace_bytes(B, Hq, Hkv, Tq, D, q.dtype, Tk=Tk)
     ws = workspace if workspace is not None else torch.empty(max(ws_bytes, 16), dtype=torch.uint8,
                                                              device=q.device)
@@ -408,12 +438,15 @@ def bwd_noalloc(q, k, v, o, dout, lse, scale=None, causal: bool = True, grads=No
     _expect(lse, (B, Hq, Tq), "lse", torch.float32)
     if grads is not None:
         for t, like, name in zip(grads, (q, k, v), ("dq", "dk", "dv")):
-            _expect(t, like.shape, name, q.dtype)
-    dt = _dtype_code(q, k, v, o, dout, *(grads or ()))
+            _expect(t, like.shape, name, o.dtype)
+    dt = _out_code(q.dtype, o.dtype)  # float32 o with bf16 inputs: float32 gradients
+    _dtype_code(q, k, v, dout)
+    _same_device(q, o, *(grads or ()))
     _same_device(q, lse)
     off = _offset(Tq, Tk, q_offset)
-    dq, dk, dv = grads if grads is not None else (torch.empty_like(q), torch.empty_like(k),
-                                                  torch.empty_like(v))
+    dq, dk, dv = grads if grads is not None else (torch.empty_like(q, dtype=o.dtype),
+                                                  torch.empty_like(k, dtype=o.dtype),
+                                                  torch.empty_like(v, dtype=o.dtype))
     with torch.cuda.device(q.device):  # the library uses the current device's scratch
         _check(library().fa_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                         dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
@@ -429,8 +462,9 @@ def bwd_preprocess(o, dout, delta=None):
     B, Hq, T, D = o.shape
     _expect(dout, o.shape, "dout")
     _expect(delta, (B, Hq, T), "delta", torch.float32)
-    dt = _dtype_code(o, dout)
-    _same_device(o, delta)
+    dt = _out_code(dout.dtype, o.dtype)  # float32 o with bf16 dout: FA_BF16_F32OUT
+    _dtype_code(dout)
+    _same_device(dout, o, delta)
     d = torch.empty((B, Hq, T), dtype=torch.float32, device=o.device) if delta is None else delta
     _check(library().fa_bwd_preprocess(o.data_ptr(), dout.data_ptr(), d.data_ptr(), B, Hq, T, D,
                                        dt, _stream(o)), "fa_bwd_preprocess")
@@ -438,21 +472,23 @@ def bwd_preprocess(o, dout, delta=None):
 
 
 def bwd_dkdv(q, k, v, dout, lse, delta, scale=None, causal: bool = True, dk=None, dv=None,
-             q_offset=None, partial=None):
-    """dK, dV; with `partial` (a device tensor of at least dkdv_split_bytes(...)
+             q_offset=None, partial=None, out_dtype=None):
+    """dK, dV (of out_dtype: as the inputs, or float32 for bfloat16 inputs); with `partial` (a device tensor of at least dkdv_split_bytes(...)
     bytes) the query side is split over more workgroups when the shapes call
     for it (fa_bwd_dkdv_split)."""
     B, Hq, Hkv, Tq, Tk, D = _dims(q, k, v)
     _expect(dout, q.shape, "dout")
     _expect(lse, (B, Hq, Tq), "lse", torch.float32)
     _expect(delta, (B, Hq, Tq), "delta", torch.float32)
-    _expect(dk, k.shape, "dk", k.dtype)
-    _expect(dv, v.shape, "dv", v.dtype)
-    dt = _dtype_code(q, k, v, dout, *(t for t in (dk, dv) if t is not None))
-    _same_device(q, lse, delta, partial)
+    odt = _result_dtype(q, dk if dk is not None else dv, out_dtype)
+    _expect(dk, k.shape, "dk", odt)
+    _expect(dv, v.shape, "dv", odt)
+    dt = _out_code(q.dtype, odt)
+    _dtype_code(q, k, v, dout)
+    _same_device(q, dk, dv, lse, delta, partial)
     off = _offset(Tq, Tk, q_offset)
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    dk = torch.empty_like(k, dtype=odt) if dk is None else dk
+    dv = torch.empty_like(v, dtype=odt) if dv is None else dv
     lib = library()
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), lse.data_ptr(),
             delta.data_ptr(), dk.data_ptr(), dv.data_ptr())
@@ -481,11 +517,12 @@ def bwd_dq_delta(q, k, v, o, dout, lse, scale=None, causal: bool = True, dq=None
     _expect(dout, q.shape, "dout")
     _expect(lse, (B, Hq, Tq), "lse", torch.float32)
     _expect(delta, (B, Hq, Tq), "delta", torch.float32)
-    _expect(dq, q.shape, "dq", q.dtype)
-    dt = _dtype_code(q, k, v, o, dout, *(t for t in (dq,) if t is not None))
-    _same_device(q, lse, delta, partial)
+    _expect(dq, q.shape, "dq", o.dtype)
+    dt = _out_code(q.dtype, o.dtype)  # float32 o with bf16 inputs: float32 dq
+    _dtype_code(q, k, v, dout)
+    _same_device(q, o, dq, lse, delta, partial)
     off = _offset(Tq, Tk, q_offset)
-    dq = torch.empty_like(q) if dq is None else dq
+    dq = torch.empty_like(q, dtype=o.dtype) if dq is None else dq
     if delta is None:
         delta = torch.empty(B, Hq, Tq, dtype=torch.float32, device=q.device)
     need = dq_split_bytes(B, Hq, Hkv, Tq, Tk, D, q.dtype)
@@ -500,18 +537,20 @@ def bwd_dq_delta(q, k, v, o, dout, lse, scale=None, causal: bool = True, dq=None
 
 
 def bwd_dq(q, k, v, dout, lse, delta, scale=None, causal: bool = True, dq=None, q_offset=None,
-           partial=None):
-    """dQ; with `partial` (at least dq_split_bytes(...) bytes) the key range is
+           partial=None, out_dtype=None):
+    """dQ (of out_dtype: as the inputs, or float32 for bfloat16 inputs); with `partial` (at least dq_split_bytes(...) bytes) the key range is
     split over more workgroups when the shapes call for it (fa_bwd_dq_split)."""
     B, Hq, Hkv, Tq, Tk, D = _dims(q, k, v)
     _expect(dout, q.shape, "dout")
     _expect(lse, (B, Hq, Tq), "lse", torch.float32)
     _expect(delta, (B, Hq, Tq), "delta", torch.float32)
-    _expect(dq, q.shape, "dq", q.dtype)
-    dt = _dtype_code(q, k, v, dout, *(t for t in (dq,) if t is not None))
-    _same_device(q, lse, delta, partial)
+    odt = _result_dtype(q, dq, out_dtype)
+    _expect(dq, q.shape, "dq", odt)
+    dt = _out_code(q.dtype, odt)
+    _dtype_code(q, k, v, dout)
+    _same_device(q, dq, lse, delta, partial)
     off = _offset(Tq, Tk, q_offset)
-    dq = torch.empty_like(q) if dq is None else dq
+    dq = torch.empty_like(q, dtype=odt) if dq is None else dq
     lib = library()
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), lse.data_ptr(),
             delta.data_ptr(), dq.data_ptr())

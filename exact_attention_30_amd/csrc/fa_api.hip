@@ -23,6 +23,10 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 // Shape and option checks shared by every entry point; `D`/`dt` may be
 // ignored by passing D = 64, dt = FA_BF16.  Tq query rows against Tk key rows;
 // `off` (causal only) places query row i at key position i + off.
+// bf16 inputs: the bf16 kernels, whose results are rounded to bf16 (FA_BF16)
+// or stored as float32 (FA_BF16_F32OUT)
+bool bf16_in(fa_dtype dt) { return dt == FA_BF16 || dt == FA_BF16_F32OUT; }
+
 fa_status check_kv(int B, int Hq, int Hkv, int Tq, int Tk, int D, fa_dtype dt, bool causal, int off)
 {
     if (B < 0 || Tq < 0 || Tk < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return FA_ERR_SHAPE;
@@ -35,12 +39,13 @@ fa_status check_kv(int B, int Hq, int Hkv, int Tq, int Tk, int D, fa_dtype dt, b
     const long long qrows = (long long)B * Hq * (((long long)Tq + 31) / 32);
     const long long krows = (long long)B * Hkv * (((long long)Tk + 31) / 32);
     if (qrows > 0x7fffffffLL || krows > 0x7fffffffLL) return FA_ERR_SHAPE;
-    if (dt != FA_BF16 && dt != FA_FP32) return FA_ERR_UNSUPPORTED;
+    if (dt != FA_BF16 && dt != FA_FP32 && dt != FA_BF16_F32OUT) return FA_ERR_UNSUPPORTED;
     // 64 and 128 in both types; 96 in bf16 (the forward on 96-column tiles,
     // the backward on 128-column LDS tiles whose last 32 columns read as zero)
-    if (D != 64 && D != 128 && !(D == 96 && dt == FA_BF16)) return FA_ERR_UNSUPPORTED;
+    if (D != 64 && D != 128 && !(D == 96 && bf16_in(dt))) return FA_ERR_UNSUPPORTED;
     // one head of one tensor is addressed through a buffer resource whose
-    // byte range is a signed 32-bit count
+    // byte range is a signed 32-bit count (the float32 outputs of
+    // FA_BF16_F32OUT held to the same bound)
     const long long esz = dt == FA_BF16 ? 2 : 4;
     if ((long long)Tq * D * esz > 0x7fffffffLL || (long long)Tk * D * esz > 0x7fffffffLL)
         return FA_ERR_SHAPE;
@@ -54,7 +59,8 @@ fa_status check_scale(float scale)
 
 fa_status from_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
-int dtype_code(fa_dtype dt) { return dt == FA_BF16 ? 0 : 1; }
+// kernel family: 0 the bf16 kernels, 1 the fp32 kernels
+int dtype_code(fa_dtype dt) { return bf16_in(dt) ? 0 : 1; }
 
 void fill_bwd(fa::BwdArgs& a, const void* q, const void* k, const void* v, const void* dout,
               const float* lse, const float* delta, int B, int Hq, int Hkv, int Tq, int Tk,
@@ -86,7 +92,7 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 // bytes of fp32 partial sums the split dK/dV stage uses (0: no split)
 size_t split_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int D, fa_dtype dt)
 {
-    if (dt != FA_BF16 || (long long)B * Tk == 0) return 0;
+    if (!bf16_in(dt) || (long long)B * Tk == 0) return 0;
     const int S = fa::dkdv_nsplit(B, Hq, Hkv, Tq, Tk, D);
     if (S <= 1) return 0;
     return align256((size_t)2 * S * (size_t)B * Hkv * (size_t)Tk * D * sizeof(float));
@@ -95,7 +101,7 @@ size_t split_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int D, fa_dtype dt)
 // bytes of fp32 partial sums the split dQ stage uses (0: no split)
 size_t dq_split_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int D, fa_dtype dt)
 {
-    if (dt != FA_BF16 || (long long)B * Tq == 0) return 0;
+    if (!bf16_in(dt) || (long long)B * Tq == 0) return 0;
     const int S = fa::dq_nsplit(B, Hq, Hkv, Tq, Tk, D);
     if (S <= 1) return 0;
     return align256((size_t)S * (size_t)B * Hq * (size_t)Tq * D * sizeof(float));
@@ -157,7 +163,7 @@ const char* fa_status_string(fa_status s)
 // bytes of the forward's chunk partials: numerators, then (max, sum) pairs
 size_t fwd_split_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int D, fa_dtype dt)
 {
-    if (dt != FA_BF16 || (long long)B * Tq == 0) return 0;
+    if (!bf16_in(dt) || (long long)B * Tq == 0) return 0;
     const int S = fa::fwd_nsplit(B, Hq, Hkv, Tq, Tk, D);
     if (S <= 1) return 0;
     const size_t rows = (size_t)S * B * Hq * Tq;
@@ -194,6 +200,7 @@ fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, flo
     a.opart = a.ml = nullptr;
     a.nsplit = 1;
     a.vscale = 1.f;
+    a.of32 = dt == FA_BF16_F32OUT;
     if (partial && fwd_split_bytes(B, Hq, Hkv, Tq, Tk, D, dt) > 0) {
         a.nsplit = fa::fwd_nsplit(B, Hq, Hkv, Tq, Tk, D);
         const size_t rows = (size_t)a.nsplit * B * Hq * Tq;
@@ -213,9 +220,9 @@ int fa_block_rows(fa_stage stage, int B, int H, int T, int D, fa_dtype dt)
 {
     if (check_kv(B, H, H, T, T, D, dt, false, 0) != FA_OK) return 0;
     switch (stage) {
-    case FA_STAGE_FWD: return dt == FA_BF16 ? fa::fwd_rows(B, H, T, D) : 128;
-    case FA_STAGE_DQ: return dt == FA_BF16 ? fa::dq_rows(B, H, T, D) : 128;
-    case FA_STAGE_DKDV: return dt == FA_BF16 ? fa::dkdv_keys(B, H, T, D) : 128;
+    case FA_STAGE_FWD: return bf16_in(dt) ? fa::fwd_rows(B, H, T, D) : 128;
+    case FA_STAGE_DQ: return bf16_in(dt) ? fa::dq_rows(B, H, T, D) : 128;
+    case FA_STAGE_DKDV: return bf16_in(dt) ? fa::dkdv_keys(B, H, T, D) : 128;
     }
     return 0;
 }
@@ -350,7 +357,9 @@ fa_status fa_bwd_preprocess(const void* o, const void* dout, float* delta, int B
     a.dout = dout;
     a.delta = delta;
     a.rows = (long)B * Hq * T;
-    return from_hip(fa::launch_bwd_pre(a, D, dtype_code(dt), static_cast<hipStream_t>(stream)));
+    // kernel instance: 0 bf16 O and dO, 1 float32 both, 2 float32 O with bf16 dO
+    const int code = dt == FA_BF16_F32OUT ? 2 : dtype_code(dt);
+    return from_hip(fa::launch_bwd_pre(a, D, code, static_cast<hipStream_t>(stream)));
 }
 
 // Checks shared by the two backward kernels' entry points.  `skip` is set
@@ -392,6 +401,7 @@ fa_status fa_bwd_dkdv_split(const void* q, const void* k, const void* v, const v
     fill_bwd(a, q, k, v, dout, lse, delta, B, Hq, Hkv, Tq, Tk, off, scale);
     a.dk = dk;
     a.dv = dv;
+    a.gf32 = dt == FA_BF16_F32OUT;
     if (partial && split_bytes(B, Hq, Hkv, Tq, Tk, D, dt) > 0) {
         a.part = static_cast<float*>(partial);
         a.nsplit = fa::dkdv_nsplit(B, Hq, Hkv, Tq, Tk, D);
@@ -439,6 +449,7 @@ static fa_status dq_enqueue(const void* q, const void* k, const void* v, const v
     fa::BwdArgs a;
     fill_bwd(a, q, k, v, dout, lse, delta, B, Hq, Hkv, Tq, Tk, off, scale);
     a.dq = dq;
+    a.gf32 = dt == FA_BF16_F32OUT;
     if (o) {
         a.o = o;
         a.delta_out = delta;
@@ -457,10 +468,23 @@ fa_status fa_bwd_dq_delta(const void* q, const void* k, const void* v, const voi
 {
     fa_status st = check_kv(B, Hq, Hkv, Tq, Tk, D, dt, causal != 0, causal ? q_offset : 0);
     if (st != FA_OK) return st;
-    if (dt != FA_BF16) return FA_ERR_UNSUPPORTED;
+    if (!bf16_in(dt)) return FA_ERR_UNSUPPORTED;
     if ((long long)B * Tq * Tk > 0) {
         if (!o) return FA_ERR_NULL;
         if (!aligned(o, 16)) return FA_ERR_ALIGN;
+    }
+    if (dt == FA_BF16_F32OUT) {
+        // float32 O: Delta from the preprocess kernel (the same bits as the
+        // dQ kernel's own for an O of bf16 values), then the dQ kernel
+        bool skip = false;
+        const int off = causal ? q_offset : 0;
+        st = bwd_check(q, k, v, dout, lse, delta, B, Hq, Hkv, Tq, Tk, D, scale, causal, off, dt, skip);
+        if (st != FA_OK || skip || Tq == 0) return st;
+        if (!dq) return FA_ERR_NULL;
+        if (!aligned(dq, 16) || !aligned(partial, 16)) return FA_ERR_ALIGN;
+        if ((st = fa_bwd_preprocess(o, dout, delta, B, Hq, Tq, D, dt, stream)) != FA_OK) return st;
+        return fa_bwd_dq_split(q, k, v, dout, lse, delta, dq, partial, B, Hq, Hkv, Tq, Tk, D, scale,
+                               causal, q_offset, dt, stream);
     }
     return dq_enqueue(q, k, v, dout, lse, delta, o, dq, partial, B, Hq, Hkv, Tq, Tk, D, scale,
                       causal, q_offset, dt, stream);

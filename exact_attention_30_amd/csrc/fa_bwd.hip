@@ -34,7 +34,12 @@ __host__ __device__ constexpr int pre_lanes()
     return p;
 }
 
-template <class E, int D>
+// E: element type of dO (and of O); EO: element type of O, float32 with
+// bf16 dO when O was stored unrounded.  A lane takes the 16 bytes of dO that
+// hold its CH columns and the O of those columns, so with EO = float and
+// E = bf16 the fma chain runs over the same columns in the same order as with
+// a bf16 O: an O holding bf16 values gives the same bits.
+template <class E, int D, class EO = E>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(PreArgs a)
 {
     constexpr int CH = 16 / (int)sizeof(E);
@@ -45,13 +50,21 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(PreArgs a)
     const int col = (tid % LPR) * CH;
     float acc = 0.f;
     if (row < a.rows && col < D) {  // lanes past the end of a row add nothing
-        const E* o = static_cast<const E*>(a.o) + row * D + col;
+        const EO* o = static_cast<const EO*>(a.o) + row * D + col;
         const E* d = static_cast<const E*>(a.dout) + row * D + col;
-        if constexpr (sizeof(E) == 2) {
+        if constexpr (sizeof(E) == 2 && sizeof(EO) == 2) {
             const bf16x8 x = *reinterpret_cast<const bf16x8*>(o);
             const bf16x8 y = *reinterpret_cast<const bf16x8*>(d);
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc = fmaf((float)x[e], (float)y[e], acc);
+        } else if constexpr (sizeof(E) == 2) {
+            const f32x4 x0 = reinterpret_cast<const f32x4*>(o)[0];
+            const f32x4 x1 = reinterpret_cast<const f32x4*>(o)[1];
+            const bf16x8 y = *reinterpret_cast<const bf16x8*>(d);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc = fmaf(x0[e], (float)y[e], acc);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc = fmaf(x1[e], (float)y[4 + e], acc);
         } else {
             const f32x4 x = *reinterpret_cast<const f32x4*>(o);
             const f32x4 y = *reinterpret_cast<const f32x4*>(d);
@@ -415,18 +428,23 @@ __global__ __launch_bounds__(NW * 64, sizeof(E) == 2 ? 8 / NW : 1) void bwd_dq_k
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-template <class E, int D>
+template <class E, int D, class EO = E>
 static hipError_t launch_pre_t(const PreArgs& a, hipStream_t stream)
 {
     constexpr int LPR = pre_lanes<E, D>();
     constexpr int RPB = 256 / LPR;
     const long grid = (a.rows + RPB - 1) / RPB;
-    hipLaunchKernelGGL((bwd_pre_kernel<E, D>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((bwd_pre_kernel<E, D, EO>), dim3((unsigned)grid), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
+// dtype 0: bf16 O and dO; 1: float32 O and dO; 2: float32 O, bf16 dO
 hipError_t launch_bwd_pre(const PreArgs& a, int D, int dtype, hipStream_t stream)
 {
+    if (dtype == 2) {
+        if (D == 96) return launch_pre_t<bf16, 96, float>(a, stream);
+        return D == 64 ? launch_pre_t<bf16, 64, float>(a, stream) : launch_pre_t<bf16, 128, float>(a, stream);
+    }
     if (dtype == 0) {
         if (D == 96) return launch_pre_t<bf16, 96>(a, stream);
         return D == 64 ? launch_pre_t<bf16, 64>(a, stream) : launch_pre_t<bf16, 128>(a, stream);
@@ -493,6 +511,9 @@ template __global__ void bwd_pre_kernel<bf16, 96>(PreArgs);
 template __global__ void bwd_pre_kernel<bf16, 128>(PreArgs);
 template __global__ void bwd_pre_kernel<float, 64>(PreArgs);
 template __global__ void bwd_pre_kernel<float, 128>(PreArgs);
+template __global__ void bwd_pre_kernel<bf16, 64, float>(PreArgs);
+template __global__ void bwd_pre_kernel<bf16, 96, float>(PreArgs);
+template __global__ void bwd_pre_kernel<bf16, 128, float>(PreArgs);
 template __global__ void bwd_dq_kernel<float, 64, kDqNW, kDqBC, true>(BwdArgs);
 template __global__ void bwd_dq_kernel<float, 64, kDqNW, kDqBC, false>(BwdArgs);
 template __global__ void bwd_dq_kernel<float, 128, kDqNW, kDqBC, true>(BwdArgs);

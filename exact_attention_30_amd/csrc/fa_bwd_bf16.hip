@@ -502,7 +502,24 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void dkdv_bf16_kernel(BwdArgs a)
 
     // this lane: key krow, columns 32db + 8rg + 4g + e
     if (krow < a.Tk) {
-        if (S == 1) {
+        if (S == 1 && a.gf32) {  // float32 gradients: the same values, not rounded
+            float* dkh = static_cast<float*>(a.dk) + kvoff + (size_t)krow * D;
+            float* dvh = static_cast<float*>(a.dv) + kvoff + (size_t)krow * D;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg) {
+                    const int col = db * 32 + 8 * rg + 4 * g;
+                    f32x4 x, y;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        x[e] = dk[db][4 * rg + e] * a.scale;
+                        y[e] = dv[db][4 * rg + e];
+                    }
+                    *reinterpret_cast<f32x4*>(dkh + col) = x;
+                    *reinterpret_cast<f32x4*>(dvh + col) = y;
+                }
+        } else if (S == 1) {
             bf16* dkh = static_cast<bf16*>(a.dk) + kvoff + (size_t)krow * D;
             bf16* dvh = static_cast<bf16*>(a.dv) + kvoff + (size_t)krow * D;
 #pragma unroll
@@ -553,10 +570,11 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void dkdv_bf16_kernel(BwdArgs a)
 
 // out = scale * (sum of the S fp32 partials part[s * plane + .]), added in
 // chunk order (so the result does not depend on scheduling), rounded to
-// bf16.  One thread per 8 consecutive elements; n8 = plane / 8.
-__global__ __launch_bounds__(256) void sum_partials_kernel(const float* part, bf16* out0, bf16* out1,
+// bf16, or stored as float32 with f32 set.  One thread per 8 consecutive
+// elements; n8 = plane / 8.
+__global__ __launch_bounds__(256) void sum_partials_kernel(const float* part, void* out0, void* out1,
                                                            long n8, long plane, int S, float scale0,
-                                                           float scale1)
+                                                           float scale1, int f32)
 {
     const long i = (long)blockIdx.x * 256 + threadIdx.x;
     if (i >= n8) return;
@@ -570,24 +588,30 @@ __global__ __launch_bounds__(256) void sum_partials_kernel(const float* part, bf
         lo += p[0];
         hi += p[1];
     }
+    void* out = second ? out1 : out0;
+    if (f32) {
+        f32x4* op = static_cast<f32x4*>(out) + 2 * i;
+        op[0] = lo * scale;
+        op[1] = hi * scale;
+        return;
+    }
     bf16x8 x;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         x[e] = (bf16)(lo[e] * scale);
         x[4 + e] = (bf16)(hi[e] * scale);
     }
-    reinterpret_cast<bf16x8*>(second ? out1 : out0)[i] = x;
+    static_cast<bf16x8*>(out)[i] = x;
 }
 
 // out0 (and out1, when given: dK and dV in one launch) = scale * the sum, in
 // chunk order, of the S fp32 partial planes of each (out1's follow out0's)
 static hipError_t sum_partials(const float* part, void* out0, void* out1, long plane, int S,
-                               float scale0, float scale1, hipStream_t stream)
+                               float scale0, float scale1, int f32, hipStream_t stream)
 {
     const long n8 = plane / 8;
     hipLaunchKernelGGL(sum_partials_kernel, dim3((unsigned)((n8 + 255) / 256), out1 ? 2 : 1), dim3(256),
-                       0, stream, part, static_cast<bf16*>(out0), static_cast<bf16*>(out1), n8, plane,
-                       S, scale0, scale1);
+                       0, stream, part, out0, out1, n8, plane, S, scale0, scale1, f32);
     return hipGetLastError();
 }
 
@@ -914,7 +938,18 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void dq_bf16_kernel(BwdArgs a)
         unroll_stages(body, t, std::make_integer_sequence<int, NSTAGE>{});
 
     if (qrow < a.Tq) {
-        if (S == 1) {
+        if (S == 1 && a.gf32) {  // float32 dQ: the same values, not rounded
+            float* dqh = static_cast<float*>(a.dq) + qoff + (size_t)qrow * D;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg) {
+                    f32x4 x;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) x[e] = dq[db][4 * rg + e] * a.scale;
+                    *reinterpret_cast<f32x4*>(dqh + db * 32 + 8 * rg + 4 * g) = x;
+                }
+        } else if (S == 1) {
             bf16* dqh = static_cast<bf16*>(a.dq) + qoff + (size_t)qrow * D;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
@@ -955,7 +990,7 @@ static hipError_t launch_dq(const BwdArgs& a, hipStream_t stream)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1) return e;
     return sum_partials(a.part, a.dq, nullptr, (long)a.B * a.Hq * a.Tq * D, a.nsplit, a.scale, 0.f,
-                        stream);
+                        a.gf32, stream);
 }
 
 hipError_t launch_bwd_dq_bf16(const BwdArgs& a, int D, bool causal, hipStream_t stream)
@@ -988,7 +1023,7 @@ static hipError_t launch_dkdv(const BwdArgs& a, hipStream_t stream)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1) return e;
     const long plane = (long)a.B * a.Hkv * a.Tk * D;
-    return sum_partials(a.part, a.dk, a.dv, plane, a.nsplit, a.scale, 1.f, stream);
+    return sum_partials(a.part, a.dk, a.dv, plane, a.nsplit, a.scale, 1.f, a.gf32, stream);
 }
 
 // The dK/dV kernel's tile table: keys per workgroup.  At D = 64 a workgroup

@@ -494,16 +494,30 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
     }
     const float inv = 1.f / lt;
     if (qrow < a.Tq) {
-        bf16* oh = static_cast<bf16*>(a.o) + ((size_t)(b * a.Hq + hq) * a.Tq + qrow) * D;
+        const size_t orow = ((size_t)(b * a.Hq + hq) * a.Tq + qrow) * D;
+        if (a.of32) {  // O as float32: the same values, not rounded to bf16
+            float* oh = static_cast<float*>(a.o) + orow;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+            for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-                bf16x4 x;
+                for (int rg = 0; rg < 4; ++rg) {
+                    f32x4 x;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) x[e] = (bf16)(o[db][4 * rg + e] * inv);
-                *reinterpret_cast<bf16x4*>(oh + db * 32 + 8 * rg + 4 * g) = x;
-            }
+                    for (int e = 0; e < 4; ++e) x[e] = o[db][4 * rg + e] * inv;
+                    *reinterpret_cast<f32x4*>(oh + db * 32 + 8 * rg + 4 * g) = x;
+                }
+        } else {
+            bf16* oh = static_cast<bf16*>(a.o) + orow;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg) {
+                    bf16x4 x;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) x[e] = (bf16)(o[db][4 * rg + e] * inv);
+                    *reinterpret_cast<bf16x4*>(oh + db * 32 + 8 * rg + 4 * g) = x;
+                }
+        }
         if (g == 0) a.lse[(size_t)(b * a.Hq + hq) * a.Tq + qrow] = (mref + __log2f(lt)) * kLn2;
     }
 }
@@ -516,10 +530,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a)
 //     lse = ln 2 * (M + log2 sum_s w_s l_s).
 // A chunk that saw no key has m_s = -inf and weight 0; chunk 0 always holds
 // key 0, which every row sees, so M is finite.  One thread per 8 consecutive
-// elements of a row.
+// elements of a row.  O is written as bf16, or as float32 with of32 set.
 template <int D>
 __global__ __launch_bounds__(256) void merge_chunks_kernel(const float* opart, const float* ml,
-                                                           bf16* o, float* lse, long rows, int S)
+                                                           void* o, float* lse, long rows, int S,
+                                                           int of32)
 {
     const long i = (long)blockIdx.x * 256 + threadIdx.x;
     if (i >= rows * (D / 8)) return;
@@ -538,13 +553,19 @@ __global__ __launch_bounds__(256) void merge_chunks_kernel(const float* opart, c
         hi += w * p[1];
     }
     const float inv = 1.f / L;
-    bf16x8 x;
+    if (of32) {
+        f32x4* op = reinterpret_cast<f32x4*>(static_cast<float*>(o) + row * D + c8);
+        op[0] = lo * inv;
+        op[1] = hi * inv;
+    } else {
+        bf16x8 x;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        x[e] = (bf16)(lo[e] * inv);
-        x[4 + e] = (bf16)(hi[e] * inv);
+        for (int e = 0; e < 4; ++e) {
+            x[e] = (bf16)(lo[e] * inv);
+            x[4 + e] = (bf16)(hi[e] * inv);
+        }
+        *reinterpret_cast<bf16x8*>(static_cast<bf16*>(o) + row * D + c8) = x;
     }
-    *reinterpret_cast<bf16x8*>(o + row * D + c8) = x;
     if (c8 == 0) lse[row] = (M + log2f(L)) * kLn2;
 }
 
@@ -565,7 +586,7 @@ static hipError_t launch_t(const FwdArgs& a, hipStream_t stream)
     const long rows = (long)a.B * a.Hq * a.Tq;
     const long n8 = rows * (D / 8);
     hipLaunchKernelGGL(merge_chunks_kernel<D>, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0,
-                       stream, a.opart, a.ml, static_cast<bf16*>(a.o), a.lse, rows, a.nsplit);
+                       stream, a.opart, a.ml, a.o, a.lse, rows, a.nsplit, a.of32);
     return hipGetLastError();
 }
 

@@ -25,6 +25,8 @@ struct FwdArgs {
     int nsplit;
     // fp8 forward: descale of V, applied to O (1 for the other element types)
     float vscale;
+    // bf16 forward: O (and the merge's O) stored as float32, not rounded to bf16
+    int of32 = 0;
 };
 
 struct BwdArgs {
@@ -55,6 +57,9 @@ struct BwdArgs {
     // dK/dV kernel (bf16) only: with kpair set, workgroup m takes key blocks
     // m and nkt - 1 - m (set by its launcher)
     int kpair = 0;
+    // bf16 kernels: dQ, dK, dV (and the partial-sum reductions' results)
+    // stored as float32, not rounded to bf16
+    int gf32 = 0;
 };
 
 struct PreArgs {

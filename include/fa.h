@@ -77,7 +77,15 @@ extern "C" {
 
 typedef enum {
     FA_BF16 = 0, /* bfloat16 inputs/outputs; bf16 MFMA with fp32 accumulation */
-    FA_FP32 = 1  /* float32 inputs/outputs; fp32 MFMA with fp32 accumulation */
+    FA_FP32 = 1, /* float32 inputs/outputs; fp32 MFMA with fp32 accumulation */
+    /* bfloat16 q, k, v, dout; float32 o, dq, dk, dv.  The FA_BF16 kernels
+     * and arithmetic, with each result stored as the float32 it was before
+     * the rounding to bf16 (so bf16(result) is the FA_BF16 result bit for
+     * bit).  The backward reads this float32 o; its Delta comes from the
+     * preprocess kernel, whose bits equal the FA_BF16 backward's own Delta
+     * when o holds bf16 values.  Accepted wherever FA_BF16 is, except
+     * fa_bwd_atomic (FA_ERR_UNSUPPORTED); the fp8 calls take no dtype. */
+    FA_BF16_F32OUT = 2
 } fa_dtype;
 
 typedef enum {
@@ -339,8 +347,10 @@ fa_status fa_bwd_dq_split(const void* q, const void* k, const void* v, const voi
  * stage, which reads that Delta.  Saves the preprocess launch.
  *   o [B,Hq,Tq,D] (device, read); delta [B,Hq,Tq] float32 (device,
  *   written); q, k, v, dout, lse, dq, partial and the sizes as
- *   fa_bwd_dq_split.  bf16 only: FA_ERR_UNSUPPORTED for fp32; the other
- *   errors as fa_bwd_dq_split, FA_ERR_NULL / FA_ERR_ALIGN also for o.
+ *   fa_bwd_dq_split.  bf16 inputs only: FA_ERR_UNSUPPORTED for fp32; with
+ *   FA_BF16_F32OUT (float32 o) it runs fa_bwd_preprocess, then
+ *   fa_bwd_dq_split, with the same results.  The other errors as
+ *   fa_bwd_dq_split, FA_ERR_NULL / FA_ERR_ALIGN also for o.
  */
 fa_status fa_bwd_dq_delta(const void* q, const void* k, const void* v, const void* o,
                           const void* dout, const float* lse, float* delta, void* dq, void* partial,

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa.h")
 
 OK, NULL, SHAPE, UNSUP, ALIGN, HIP, SCRATCH = range(7)
-BF16, FP32 = 0, 1
+BF16, FP32, BF16_F32OUT = 0, 1, 2
 
 
 def declared_functions():
@@ -333,3 +333,31 @@ def test_atomic_backward_validation(lib):
     g.restype = ctypes.c_size_t
     assert g(2, 8, 512, 64, 0) == 2 * 8 * 512 * 4 + 2 * 8 * 512 * 64 * 4
     assert g(2, 8, 512, 128, 0) == 0 and g(2, 8, 512, 64, 1) == 0
+
+
+def test_bf16_with_float32_results(lib):
+    """FA_BF16_F32OUT: the bf16 kernels' checks, tile table and workspace
+    sizes; D = 96 accepted; refused by the atomic backward only."""
+    assert fwd(lib, D=96, q=0, dt=BF16_F32OUT) == NULL
+    p = [A] * 10
+    p[0] = 0
+    assert bwd(lib, p, D=96, dt=BF16_F32OUT) == NULL
+    assert lib.fa_bwd_preprocess(0, A, A, 1, 2, 64, 96, BF16_F32OUT, None) == NULL
+    assert fwd(lib, D=80, dt=BF16_F32OUT) == UNSUP
+    assert fwd(lib, Hq=3, Hkv=2, dt=BF16_F32OUT) == SHAPE
+    for args in ((1, 32, 8, 16384, 128), (2, 3, 1, 5, 64), (1, 4, 1, 2048, 96)):
+        assert (lib.fa_bwd_workspace_bytes(*args, BF16_F32OUT) ==
+                lib.fa_bwd_workspace_bytes(*args, BF16))
+    for args in ((1, 4, 1, 2048, 2048, 128), (2, 8, 8, 512, 512, 64)):
+        assert lib.fa_fwd_split_bytes(*args, BF16_F32OUT) == lib.fa_fwd_split_bytes(*args, BF16)
+        assert (lib.fa_bwd_dq_split_bytes(*args, BF16_F32OUT) ==
+                lib.fa_bwd_dq_split_bytes(*args, BF16))
+    for stage in range(3):
+        for args in ((2, 8, 4096, 64), (1, 32, 16384, 128)):
+            assert (lib.fa_block_rows(stage, *args, BF16_F32OUT) ==
+                    lib.fa_block_rows(stage, *args, BF16))
+    f = lib.fa_bwd_atomic
+    f.argtypes = ([ctypes.c_void_p] * 10 + [ctypes.c_int] * 5 +
+                  [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p])
+    f.restype = ctypes.c_int
+    assert f(*[None] * 10, 1, 4, 2, 100, 64, 0.1, 1, BF16_F32OUT, None) == UNSUP

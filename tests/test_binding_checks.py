@@ -19,7 +19,7 @@ Q, K, V = t(B, Hq, T, D), t(B, Hkv, T, D), t(B, Hkv, T, D)
 LSE = t(B, Hq, T, dtype=torch.float32)
 
 
-@pytest.mark.parametrize("kw", [dict(out=t(B, Hq, T - 1, D)), dict(out=t(B, Hq, T, D, dtype=torch.float32)),
+@pytest.mark.parametrize("kw", [dict(out=t(B, Hq, T - 1, D)), dict(out=t(B, Hq, T, D - 1, dtype=torch.float32)),
                                 dict(lse=t(B, Hq, T - 1, dtype=torch.float32)),
                                 dict(lse=t(B, Hq, T))])
 def test_fwd_outputs(kw):
@@ -38,6 +38,42 @@ def test_fwd_outputs(kw):
 def test_bwd_operands(o, dout, lse, grads):
     with pytest.raises(ValueError, match=SHAPE_ERR):
         fa.bwd(Q, K, V, o, dout, lse, grads=grads)
+
+
+@pytest.mark.parametrize("call", [
+    lambda: fa.fwd(Q, K, V, out=t(B, Hq, T, D, dtype=torch.float16)),
+    lambda: fa.fwd(Q, K, V, out_dtype=torch.float16),
+    lambda: fa.fwd(Q, K, V, out=t(B, Hq, T, D), out_dtype=torch.float32),
+    lambda: fa.fwd(Q.float(), K.float(), V.float(), out_dtype=torch.bfloat16),
+    lambda: fa.bwd(Q.float(), K.float(), V.float(), Q, Q.float(), LSE),
+    lambda: fa.bwd_dkdv(Q, K, V, Q, LSE, LSE, out_dtype=torch.float16),
+    lambda: fa.bwd_dq(Q.float(), K.float(), V.float(), Q.float(), LSE, LSE, out_dtype=torch.bfloat16),
+    lambda: fa.bwd_preprocess(Q, Q.float()),
+])
+def test_result_dtype_choices(call):
+    """Results take the inputs' dtype, or float32 for bfloat16 inputs
+    (FA_BF16_F32OUT); any other choice is a TypeError before the library."""
+    with pytest.raises(TypeError):
+        call()
+
+
+def test_float32_results_of_bf16_inputs_pass_the_checks():
+    """float32 O, gradients and preallocated results of bfloat16 inputs pass
+    the dtype and shape checks and stop only at the device check (CPU
+    tensors here)."""
+    f = lambda *s: t(*s, dtype=torch.float32)  # noqa: E731
+    for call in (lambda: fa.fwd(Q, K, V, out_dtype=torch.float32),
+                 lambda: fa.fwd(Q, K, V, out=f(B, Hq, T, D)),
+                 lambda: fa.bwd(Q, K, V, f(B, Hq, T, D), Q, LSE),
+                 lambda: fa.bwd(Q, K, V, f(B, Hq, T, D), Q, LSE,
+                                grads=(f(B, Hq, T, D), f(B, Hkv, T, D), f(B, Hkv, T, D))),
+                 lambda: fa.bwd_preprocess(f(B, Hq, T, D), Q),
+                 lambda: fa.bwd_dkdv(Q, K, V, Q, LSE, LSE, out_dtype=torch.float32),
+                 lambda: fa.bwd_dq(Q, K, V, Q, LSE, LSE, dq=f(B, Hq, T, D))):
+        with pytest.raises(ValueError, match="same GPU"):
+            call()
+    with pytest.raises(ValueError, match=SHAPE_ERR):  # grads must take o's dtype
+        fa.bwd(Q, K, V, f(B, Hq, T, D), Q, LSE, grads=(Q, K, V))
 
 
 def test_stage_operands():

@@ -414,6 +414,8 @@ def float32_results_errors(w, q, k, v, do, fpart, ref: dict) -> dict:
     import numpy as np
     import torch
 
+    import exact_attention_30_amd as fa
+
     o, lse = fa.fwd(q, k, v, scale=w.scale, causal=w.causal, partial=fpart, out_dtype=torch.float32)
     dq, dk, dv = fa.bwd(q, k, v, o, do, lse, scale=w.scale, causal=w.causal)
     torch.cuda.synchronize()

@@ -433,7 +433,8 @@ def float32_results_errors(w, q, k, v, do, fpart, ref: dict) -> dict:
             ok &= m <= 1e-3
             continue
         rel = float(np.linalg.norm(err) / np.linalg.norm(ref[name]))
-        out[name] = {"max_abs": m, "rel_l2": rel}
+        out[name] = {"max_abs": m, "rel_l2": rel, "elements_past_1e-2": int(np.sum(np.abs(err) > 1e-2)),
+                     "elements": int(err.size)}
         ok &= m <= 1e-2 and rel <= 5e-3
     out["pass"] = bool(ok)
     return out
